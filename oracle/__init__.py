@@ -1,0 +1,162 @@
+"""fp64 CPU oracle for log-domain Sinkhorn (squared-Euclidean cost).
+
+TEST INFRASTRUCTURE.  Only ``tests/``, the smoke check in ``__graft_entry__``
+and the CPU-baseline leg of ``bench.py`` may import this package.  The HIP
+library never calls it and shares no code with it.
+
+The arithmetic lives in ``sinkhorn_oracle.c`` (plain loops, fp64, OpenMP over
+rows); this module compiles it with gcc and wraps it with ctypes.  Inputs are
+converted to float64 copies of whatever values the caller passes (for bf16
+problems: the exact bf16 values).
+
+Method (page "FlashSinkhorn: IO-aware entropic OT on GPU", section
+"Methodology", part 1): f_i <- -eps LSE_j[(g_j - C_ij)/eps + log b_j] with
+C_ij = ||x_i - y_j||^2, then the mirrored update for g with the new f.
+
+Parity status of each function:
+  half_step / half_step_f / half_step_g : pinned (plan marginals after a
+      half-step, m=1 and n=1 closed forms, large-eps expansion, symmetry)
+  solve            : pinned (gauge shift, dual ascent, eps->0 assignment limit,
+                     invariances, fixed points of the closed forms)
+  plan_marginals   : pinned (closed forms; numpy brute force in the tests)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sinkhorn_oracle.c")
+_LIB = os.path.join(_HERE, "_sinkhorn_oracle.so")
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I64 = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, IEEE semantics: no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    lib.oracle_threads.argtypes = [ctypes.c_int]
+    lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_half_step.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _D, _D, _D,
+                                     _D, ctypes.c_double, _I64, ctypes.c_int64, _D, ctypes.c_int]
+    lib.oracle_half_step.restype = None
+    lib.oracle_solve.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _D, _D, _D, _D,
+                                 _D, ctypes.c_int64, ctypes.c_int64, _D, _D, ctypes.c_int]
+    lib.oracle_solve.restype = None
+    lib.oracle_plan_marginals.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _D, _D,
+                                          _D, _D, _D, _D, ctypes.c_double, _D, _D, ctypes.c_int]
+    lib.oracle_plan_marginals.restype = None
+    _lib = lib
+    return lib
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(x: np.ndarray):
+    return x.ctypes.data_as(_D)
+
+
+def threads_used(threads: Optional[int] = None) -> int:
+    """Threads the oracle's parallel loops use for a request (None = default)."""
+    return int(_load().oracle_threads(int(threads or 0)))
+
+
+def half_step(P, Q, w, h, eps: float, rows=None, threads: Optional[int] = None) -> np.ndarray:
+    """out[r] = -eps * LSE_j[(h_j - ||P[rows[r]] - Q_j||^2)/eps + log w_j] (2-D inputs)."""
+    lib = _load()
+    P, Q, w, h = _f64(P), _f64(Q), _f64(w), _f64(h)
+    np_, d = P.shape
+    nq = Q.shape[0]
+    assert Q.shape[1] == d and w.shape == (nq,) and h.shape == (nq,)
+    if rows is None:
+        out = np.empty(np_, dtype=np.float64)
+        lib.oracle_half_step(np_, nq, d, _ptr(P), _ptr(Q), _ptr(w), _ptr(h), float(eps),
+                             None, np_, _ptr(out), int(threads or 0))
+    else:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        assert rows.ndim == 1 and (rows.size == 0 or (rows.min() >= 0 and rows.max() < np_))
+        out = np.empty(rows.size, dtype=np.float64)
+        lib.oracle_half_step(np_, nq, d, _ptr(P), _ptr(Q), _ptr(w), _ptr(h), float(eps),
+                             rows.ctypes.data_as(_I64), rows.size, _ptr(out), int(threads or 0))
+    return out
+
+
+def half_step_f(X, Y, b, g, eps: float, rows=None, threads=None) -> np.ndarray:
+    """f_i = -eps LSE_j[(g_j - C_ij)/eps + log b_j] for one problem ([n,d], [m,d])."""
+    return half_step(X, Y, b, g, eps, rows=rows, threads=threads)
+
+
+def half_step_g(X, Y, a, f, eps: float, rows=None, threads=None) -> np.ndarray:
+    """g_j = -eps LSE_i[(f_i - C_ij)/eps + log a_i] for one problem ([n,d], [m,d])."""
+    return half_step(Y, X, a, f, eps, rows=rows, threads=threads)
+
+
+def solve(X, Y, a, b, eps, iters: int, g0=None, threads: Optional[int] = None):
+    """Run `iters` alternating iterations (f then g) from g = g0 (default 0).
+
+    Accepts single ([n,d]) or batched ([B,n,d]) problems; eps is a scalar or an
+    array of length iters (a per-iteration schedule).  Returns fp64 (f, g).
+    """
+    lib = _load()
+    X, Y, a, b = _f64(X), _f64(Y), _f64(a), _f64(b)
+    batched = X.ndim == 3
+    if not batched:
+        X, Y, a, b = X[None], Y[None], a[None], b[None]
+    B, n, d = X.shape
+    m = Y.shape[1]
+    e = np.atleast_1d(_f64(eps))
+    assert e.size in (1, iters)
+    f = np.zeros((B, n), dtype=np.float64)
+    g = np.zeros((B, m), dtype=np.float64) if g0 is None else _f64(np.broadcast_to(g0, (B, m))).copy()
+    for p in range(B):
+        Xp, Yp = np.ascontiguousarray(X[p]), np.ascontiguousarray(Y[p])
+        ap, bp = np.ascontiguousarray(a[p]), np.ascontiguousarray(b[p])
+        fp, gp = np.ascontiguousarray(f[p]), np.ascontiguousarray(g[p])
+        lib.oracle_solve(n, m, d, _ptr(Xp), _ptr(Yp), _ptr(ap), _ptr(bp), _ptr(e), e.size,
+                         int(iters), _ptr(fp), _ptr(gp), int(threads or 0))
+        f[p], g[p] = fp, gp
+    if not batched:
+        return f[0], g[0]
+    return f, g
+
+
+def plan_marginals(X, Y, a, b, f, g, eps: float, threads: Optional[int] = None):
+    """Row and column sums of P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps)."""
+    lib = _load()
+    X, Y, a, b, f, g = (_f64(v) for v in (X, Y, a, b, f, g))
+    n, d = X.shape
+    m = Y.shape[0]
+    row = np.empty(n, dtype=np.float64)
+    col = np.empty(m, dtype=np.float64)
+    lib.oracle_plan_marginals(n, m, d, _ptr(X), _ptr(Y), _ptr(a), _ptr(b), _ptr(f), _ptr(g),
+                              float(eps), _ptr(row), _ptr(col), int(threads or 0))
+    return row, col
+
+
+def marginal_error(X, Y, a, b, f, g, eps: float, threads: Optional[int] = None):
+    """L1 deviations (sum_i |row_i - a_i|, sum_j |col_j - b_j|) of the plan's marginals."""
+    row, col = plan_marginals(X, Y, a, b, f, g, eps, threads=threads)
+    return float(np.abs(row - _f64(a)).sum()), float(np.abs(col - _f64(b)).sum())
