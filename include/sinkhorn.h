@@ -1,0 +1,125 @@
+/*
+ * sinkhorn.h -- C ABI of the MI355X (gfx950) log-domain Sinkhorn half-step library.
+ *
+ * The method (page "FlashSinkhorn: IO-aware entropic OT on GPU", section
+ * "Methodology", part 1, Proposition 1): for squared-Euclidean cost
+ * C_ij = ||x_i - y_j||^2 the stabilised log-domain update
+ *
+ *     f_i <- -eps * LSE_j [ (g_j - C_ij)/eps + log b_j ]
+ *
+ * equals ||x_i||^2 - eps * LSE_j [ (2 x_i.y_j + g_j - ||y_j||^2 + eps log b_j) / eps ],
+ * i.e. the row log-sum-exp of a dot-product score matrix plus a per-column bias.
+ * The g update is the same operation with the two clouds exchanged.  Each half-step
+ * runs as one streaming pass (part 2 of the same section: no n x m matrix in HBM,
+ * online max / sum-exp, row-stationary traversal).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Problem shape (sk_problem): `batch` independent problems, each with n source
+ *    points X[b] (n x d) and m target points Y[b] (m x d), row-major, contiguous:
+ *    X is [batch][n][d], Y is [batch][m][d], element type `dtype` (fp32 or bf16).
+ *    Weights a [batch][n], b [batch][m] and potentials f [batch][n], g [batch][m]
+ *    are fp32.  All of these are DEVICE pointers owned by the caller.
+ *  - Weights must be positive and each row must have at least one positive
+ *    weight; a zero weight removes that point (its log is -inf).  Weights need not
+ *    sum to one (the update is exact for any positive weights).
+ *  - ws / ws_bytes: a caller-owned DEVICE workspace of at least
+ *    sinkhorn_workspace_bytes(p) bytes.  The library never allocates device or
+ *    pinned memory and keeps no state between calls other than what it writes
+ *    into ws.  sinkhorn_init_norms must have run on the same ws (same X, Y, a, b)
+ *    before half-steps or the marginal error are called.
+ *  - stream: a HIP stream; every call only enqueues work on it and returns
+ *    without synchronising.  The caller synchronises before reading outputs.
+ *    Concurrent calls that share one ws race.
+ *  - Errors: arguments are validated on the host before anything is enqueued;
+ *    on failure nothing is launched, a status code is returned and
+ *    sinkhorn_last_error() describes it.  A failed launch returns SK_EHIP.
+ *    NaN or inf inside the data is not checked and propagates.
+ *  - eps: positive and finite.  Log base is natural everywhere in the outputs.
+ */
+#ifndef SINKHORN_MI355X_H
+#define SINKHORN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SK_OK = 0,
+    SK_EINVAL = 1,       /* bad argument: NULL pointer, eps <= 0 or non-finite, iters < 0 ... */
+    SK_ESHAPE = 2,       /* batch, n, m or d out of range */
+    SK_EDTYPE = 3,       /* unknown dtype */
+    SK_EHIP = 4,         /* a HIP launch or runtime call failed */
+    SK_EUNSUPPORTED = 5, /* valid but not supported by this build (d too large) */
+    SK_EWORKSPACE = 6    /* workspace missing or smaller than sinkhorn_workspace_bytes */
+} sk_status;
+
+typedef enum { SK_FP32 = 0, SK_BF16 = 1 } sk_dtype; /* element type of X and Y */
+
+/* Largest supported point dimension: bf16 inputs up to SK_MAX_D, fp32 inputs up
+ * to SK_MAX_D_FP32 (their operands carry seven remainder products per coordinate
+ * that must stay in registers).  Larger d returns SK_EUNSUPPORTED. */
+#define SK_MAX_D 128
+#define SK_MAX_D_FP32 88
+
+typedef struct {
+    int64_t batch; /* >= 1 independent problems */
+    int64_t n;     /* >= 1 source points per problem */
+    int64_t m;     /* >= 1 target points per problem */
+    int64_t d;     /* 1 .. SK_MAX_D (bf16) or SK_MAX_D_FP32 (fp32) */
+    int32_t dtype; /* sk_dtype of X and Y */
+} sk_problem;
+
+/* Bytes of device workspace needed for problem p (0 if p is invalid; see
+ * sinkhorn_last_error).  Linear in batch*(n+m)*d: the n x m matrix is never stored. */
+size_t sinkhorn_workspace_bytes(const sk_problem* p);
+
+/* Precompute ||x_i||^2, ||y_j||^2, log a_i, log b_j and the kernels' operand
+ * layouts of X and Y into ws (the precomputed biases of Proposition 1).
+ * X, Y: [batch][n|m][d] of dtype p->dtype; a, b: fp32 weights. */
+sk_status sinkhorn_init_norms(const sk_problem* p, const void* X, const void* Y,
+                              const float* a, const float* b, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* One f half-step: f_i = -eps * LSE_j[(g_j - C_ij)/eps + log b_j] for every problem.
+ * g [batch][m] in, f [batch][n] out (f and g must not overlap).  X and Y are the
+ * arrays given to sinkhorn_init_norms. */
+sk_status sinkhorn_half_step_f(const sk_problem* p, const void* X, const void* Y, void* ws,
+                               size_t ws_bytes, const float* g, float eps, float* f, void* stream);
+
+/* One g half-step: g_j = -eps * LSE_i[(f_i - C_ij)/eps + log a_i]: the f step with
+ * the roles of X and Y exchanged, read in the same point-major layout (no transposed
+ * copy).  f [batch][n] in, g [batch][m] out. */
+sk_status sinkhorn_half_step_g(const sk_problem* p, const void* X, const void* Y, void* ws,
+                               size_t ws_bytes, const float* f, float eps, float* g, void* stream);
+
+/* Full solve: init_norms, then `iters` iterations of (f half-step, g half-step).
+ * eps: HOST array of n_eps floats; n_eps == 1 means a constant eps, n_eps == iters
+ * means iteration k uses eps[k] for both half-steps (an annealing schedule).
+ * f and g are in/out: the f half-step runs first, so only the incoming g matters
+ * (pass zeros for a cold start, or a saved g to resume).  iters == 0 only runs
+ * init_norms. */
+sk_status sinkhorn_solve(const sk_problem* p, const void* X, const void* Y, const float* a,
+                         const float* b, const float* eps, int64_t n_eps, int64_t iters,
+                         float* f, float* g, void* ws, size_t ws_bytes, void* stream);
+
+/* L1 marginal errors of the plan P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps):
+ * err[2*k]   = sum_i | sum_j P_ij - a_i |   (rows of problem k)
+ * err[2*k+1] = sum_j | sum_i P_ij - b_j |   (columns of problem k)
+ * computed without forming P (row sums are a_i exp((f_i - T_f(g)_i)/eps)).
+ * err is a DEVICE array of 2*batch floats.  Uses ws scratch (after init_norms). */
+sk_status sinkhorn_marginal_error(const sk_problem* p, const void* X, const void* Y, void* ws,
+                                  size_t ws_bytes, const float* f, const float* g, float eps,
+                                  float* err, void* stream);
+
+/* Text for the last error on the calling thread ("" if none). */
+const char* sinkhorn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINKHORN_MI355X_H */

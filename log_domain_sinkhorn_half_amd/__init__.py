@@ -1,0 +1,12 @@
+"""MI355X-native log-domain Sinkhorn half-steps (squared-Euclidean cost).
+
+The compute lives in libsinkhorn.so (HIP, gfx950), declared in include/sinkhorn.h;
+``binding`` marshals torch tensors into that C ABI.  ``inputs`` holds the seeded
+synthetic workloads.
+"""
+
+from .binding import (SK_BF16, SK_FP32, SinkhornError, alloc_workspace, half_step_f, half_step_g,
+                      init_norms, load_library, marginal_error, problem_of, solve, workspace_bytes)
+
+__all__ = ["SK_BF16", "SK_FP32", "SinkhornError", "alloc_workspace", "half_step_f", "half_step_g",
+           "init_norms", "load_library", "marginal_error", "problem_of", "solve", "workspace_bytes"]

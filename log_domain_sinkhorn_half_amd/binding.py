@@ -1,0 +1,183 @@
+"""Thin Python binding over the C ABI in include/sinkhorn.h (libsinkhorn.so).
+
+Argument marshalling only: every step of every call runs in the HIP kernels of
+libsinkhorn.so.  PyTorch provides device memory and the current HIP stream.
+There is no CPU fallback: if the library is missing, every call raises.
+
+Tensors: X [B, n, d] (or [n, d]), Y [B, m, d] (or [m, d]), float32 or bfloat16,
+contiguous, on a ROCm device; a [B, n], b [B, m], f [B, n], g [B, m] float32.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Union
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsinkhorn.so")
+
+SK_FP32, SK_BF16 = 0, 1
+STATUS = {0: "SK_OK", 1: "SK_EINVAL", 2: "SK_ESHAPE", 3: "SK_EDTYPE", 4: "SK_EHIP",
+          5: "SK_EUNSUPPORTED", 6: "SK_EWORKSPACE"}
+EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_init_norms", "sinkhorn_half_step_f",
+           "sinkhorn_half_step_g", "sinkhorn_solve", "sinkhorn_marginal_error",
+           "sinkhorn_last_error")
+
+
+class SkProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("n", ctypes.c_int64), ("m", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("dtype", ctypes.c_int32)]
+
+
+class SinkhornError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libsinkhorn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m log_domain_sinkhorn_half_amd.build` "
+                           "(there is no CPU fallback)")
+    lib = ctypes.CDLL(p)
+    vp, sz, f32p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p
+    P = ctypes.POINTER(SkProblem)
+    lib.sinkhorn_workspace_bytes.argtypes = [P]
+    lib.sinkhorn_workspace_bytes.restype = sz
+    lib.sinkhorn_init_norms.argtypes = [P, vp, vp, f32p, f32p, vp, sz, vp]
+    lib.sinkhorn_init_norms.restype = ctypes.c_int
+    lib.sinkhorn_half_step_f.argtypes = [P, vp, vp, vp, sz, f32p, ctypes.c_float, f32p, vp]
+    lib.sinkhorn_half_step_f.restype = ctypes.c_int
+    lib.sinkhorn_half_step_g.argtypes = [P, vp, vp, vp, sz, f32p, ctypes.c_float, f32p, vp]
+    lib.sinkhorn_half_step_g.restype = ctypes.c_int
+    lib.sinkhorn_solve.argtypes = [P, vp, vp, f32p, f32p, ctypes.POINTER(ctypes.c_float), ctypes.c_int64,
+                                   ctypes.c_int64, f32p, f32p, vp, sz, vp]
+    lib.sinkhorn_solve.restype = ctypes.c_int
+    lib.sinkhorn_marginal_error.argtypes = [P, vp, vp, vp, sz, f32p, f32p, ctypes.c_float, f32p, vp]
+    lib.sinkhorn_marginal_error.restype = ctypes.c_int
+    lib.sinkhorn_last_error.argtypes = []
+    lib.sinkhorn_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load_library().sinkhorn_last_error().decode(errors="replace")
+        raise SinkhornError(status, msg)
+
+
+def _as3(t: torch.Tensor) -> torch.Tensor:
+    return t if t.dim() == 3 else t.unsqueeze(0)
+
+
+def _as2(t: torch.Tensor) -> torch.Tensor:
+    return t if t.dim() == 2 else t.unsqueeze(0)
+
+
+def problem_of(X: torch.Tensor, Y: torch.Tensor) -> SkProblem:
+    X3, Y3 = _as3(X), _as3(Y)
+    if X3.dim() != 3 or Y3.dim() != 3 or X3.shape[0] != Y3.shape[0] or X3.shape[2] != Y3.shape[2]:
+        raise ValueError(f"X {tuple(X.shape)} and Y {tuple(Y.shape)} must be [B,n,d] and [B,m,d]")
+    if X.dtype != Y.dtype or X.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("X and Y must both be float32 or both bfloat16")
+    dt = SK_FP32 if X.dtype == torch.float32 else SK_BF16
+    return SkProblem(X3.shape[0], X3.shape[1], Y3.shape[1], X3.shape[2], dt)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def workspace_bytes(batch: int, n: int, m: int, d: int, dtype: int = SK_FP32) -> int:
+    p = SkProblem(batch, n, m, d, dtype)
+    nb = load_library().sinkhorn_workspace_bytes(ctypes.byref(p))
+    if nb == 0:
+        _check(1)
+    return int(nb)
+
+
+def alloc_workspace(X: torch.Tensor, Y: torch.Tensor) -> torch.Tensor:
+    p = problem_of(X, Y)
+    nb = load_library().sinkhorn_workspace_bytes(ctypes.byref(p))
+    if nb == 0:
+        _check(1)
+    return torch.empty(nb, dtype=torch.uint8, device=X.device)
+
+
+def init_norms(X, Y, a, b, ws):
+    p = problem_of(X, Y)
+    _check(load_library().sinkhorn_init_norms(
+        ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(a, "a", torch.float32),
+        _dev(b, "b", torch.float32), _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream()))
+
+
+def half_step_f(X, Y, ws, g, eps: float, f: Optional[torch.Tensor] = None) -> torch.Tensor:
+    p = problem_of(X, Y)
+    if f is None:
+        f = torch.empty((p.batch, p.n), dtype=torch.float32, device=X.device)
+    _check(load_library().sinkhorn_half_step_f(
+        ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(ws, "ws"), ws.numel() * ws.element_size(),
+        _dev(g, "g", torch.float32), float(eps), _dev(f, "f", torch.float32), _stream()))
+    return f
+
+
+def half_step_g(X, Y, ws, f, eps: float, g: Optional[torch.Tensor] = None) -> torch.Tensor:
+    p = problem_of(X, Y)
+    if g is None:
+        g = torch.empty((p.batch, p.m), dtype=torch.float32, device=X.device)
+    _check(load_library().sinkhorn_half_step_g(
+        ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(ws, "ws"), ws.numel() * ws.element_size(),
+        _dev(f, "f", torch.float32), float(eps), _dev(g, "g", torch.float32), _stream()))
+    return g
+
+
+def solve(X, Y, a, b, eps: Union[float, Sequence[float]], iters: int, f=None, g=None, ws=None):
+    """Run sinkhorn_solve; f and g are in/out (zeros if not given).  Returns (f, g)."""
+    p = problem_of(X, Y)
+    if f is None:
+        f = torch.zeros((p.batch, p.n), dtype=torch.float32, device=X.device)
+    if g is None:
+        g = torch.zeros((p.batch, p.m), dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws = alloc_workspace(X, Y)
+    e = [float(eps)] if isinstance(eps, (int, float)) else [float(v) for v in eps]
+    earr = (ctypes.c_float * len(e))(*e)
+    _check(load_library().sinkhorn_solve(
+        ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(a, "a", torch.float32), _dev(b, "b", torch.float32),
+        earr, len(e), int(iters), _dev(f, "f", torch.float32), _dev(g, "g", torch.float32), _dev(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream()))
+    return f, g
+
+
+def marginal_error(X, Y, ws, f, g, eps: float, err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    p = problem_of(X, Y)
+    if err is None:
+        err = torch.empty((p.batch, 2), dtype=torch.float32, device=X.device)
+    _check(load_library().sinkhorn_marginal_error(
+        ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(ws, "ws"), ws.numel() * ws.element_size(),
+        _dev(f, "f", torch.float32), _dev(g, "g", torch.float32), float(eps), _dev(err, "err", torch.float32),
+        _stream()))
+    return err

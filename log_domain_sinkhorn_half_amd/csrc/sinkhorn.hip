@@ -1,0 +1,911 @@
+// Log-domain Sinkhorn half-steps for squared-Euclidean cost on MI355X (gfx950).
+//
+// Method: page "FlashSinkhorn: IO-aware entropic OT on GPU", section
+// "Methodology".  Part 1 (Proposition 1) rewrites the stabilised update
+//   f_i <- -eps LSE_j[(g_j - C_ij)/eps + log b_j],  C_ij = ||x_i - y_j||^2
+// as f_i = ||x_i||^2 - eps * LSE_j[(2 x_i.y_j + beta_j)/eps] with the per-column
+// bias beta_j = g_j - ||y_j||^2 + eps log b_j: a dot-product score matrix with a
+// bias, reduced by a row log-sum-exp.  Part 2 streams it: query tiles stay on
+// chip (row-stationary), key tiles stream past them, the LSE is accumulated
+// online and the n x m scores never reach HBM.  The g update is the same
+// kernel with the clouds exchanged.
+//
+// MI355X design (not the pages' Triton/A100 design):
+//  * Scores come from v_mfma_f32_16x16x32_bf16.  On gfx950 fp32 MFMA shares
+//    issue with the VALU, while bf16 MFMA overlaps partly with the exp/add
+//    stream that bounds small-d problems.  Scores are produced directly in
+//    base-2 units, lambda = log2(e)/eps, so the VALU does only exp2 + add.
+//  * The bf16 MFMA sums each group of 8 products (one lane group) exactly and
+//    adds the group sums to the fp32 accumulator with round-to-nearest.  The
+//    fp32 path uses that: every coordinate of x and of v = 2*lambda*y is split
+//    into a "grid" part (a multiple of a power-of-two quantum, at most 8 bits)
+//    plus two bf16 remainder parts.  Grid products, the grid part of the bias
+//    lambda*beta_j and the running row offset -m_i are all multiples of one
+//    quantum Q, so their sum is exact in fp32 in any order; they occupy the
+//    first K slots.  The seven remainder products per coordinate (and the bias
+//    remainder) are small and come after, so the only rounding happens at the
+//    magnitude of the final exponent.  Scores are then accurate far below the
+//    fp32 rounding of the output potential.
+//  * bf16 inputs: raw bf16 values (products are exact in fp32); the half bias
+//    beta_j/2 goes in through the accumulator and one FMA per element applies
+//    the 2*lambda scale and the offset.
+//  * Online LSE with a lazy offset: the running offset m is only moved when a
+//    chunk's partial sums exceed 2^112 (rare), so the hot loop has no max or
+//    rescale.  Such a chunk is recomputed with its exact maximum; offsets are
+//    integers, so rescaling is an exact power of two.
+//  * Key chunks are staged through LDS (double buffered) and shared by the
+//    four waves of a workgroup; each wave keeps its own query tiles in VGPRs.
+//  * Key ranges are split across workgroups when rows alone cannot fill the
+//    256 CUs; the partial (max, sum) pairs are merged by a small kernel.
+//  * Norms, log-weights, the bias and the final potential are formed in fp64.
+
+#include <hip/hip_runtime.h>
+
+#include <float.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <utility>
+
+#include "sinkhorn.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+namespace {
+
+constexpr int MODE_SPLIT = 0;  // fp32 inputs
+constexpr int MODE_BF16 = 1;   // bf16 inputs
+constexpr int ROW_PAD = 512;   // operand buffers are padded to a multiple of this many rows
+constexpr int KS_MAX = 64;     // most key splits per half-step
+constexpr int SLACK = 256;     // slack rows after operand buffers (>= one chunk)
+constexpr float NEG_BIG = -1e30f;
+constexpr double LOG2E = 1.4426950408889634;
+// Largest partial sum a lane may carry past a chunk check.  Kept well below
+// FLT_MAX so that merging 4 lanes and up to KS_MAX key splits cannot overflow.
+constexpr float SUM_LIMIT = 0x1p112f;
+
+// ---------------------------------------------------------------------------
+// K-slot layout of the fp32 path for point dimension d.
+//   slots 0,1      query: -m (two bf16 parts, set in registers)    key: 1, 1
+//   slots 2,3,4    query: 1, 1, 1                                   key: grid bias in 3 parts
+//   slots 5..5+d-1 query: x_g[t]                                    key: v_g[t]
+//   (pad to the correction start)
+//   cb+7t+0..6     query: x_g x_g x_1 x_2 x_1 x_1 x_2               key: v_1 v_2 v_g v_g v_1 v_2 v_1
+//   cb+7d, +1      query: 1, 1                                      key: bias remainder in 2 parts
+// The grid section is exact in fp32; for d <= 3 it fills lane group 0 and the
+// corrections fill groups 1-3 of a single MFMA; otherwise each section starts
+// on an MFMA (32-slot) boundary so the grid sum is complete before any
+// correction is added.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int split_grid_slots(int d) { return d + 5; }
+__host__ __device__ constexpr int split_corr_slots(int d) { return 7 * d + 2; }
+__host__ __device__ constexpr bool split_single(int d) { return split_grid_slots(d) <= 8 && split_corr_slots(d) <= 24; }
+__host__ __device__ constexpr int split_corr_begin(int d) {
+  return split_single(d) ? 8 : (split_grid_slots(d) + 31) / 32 * 32;
+}
+__host__ __device__ constexpr int split_nch(int d) {
+  return split_single(d) ? 1 : (split_corr_begin(d) + split_corr_slots(d) + 31) / 32;
+}
+constexpr int MAX_NCH_SPLIT = split_nch(SK_MAX_D_FP32);
+constexpr int MAX_NCH_BF16 = (SK_MAX_D + 31) / 32;
+
+thread_local char g_err[512] = "";
+
+void set_err(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void set_err(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 helpers (round to nearest even on the bit pattern)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u16 bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (u16)(u >> 16);
+}
+__device__ __forceinline__ float bf16_f(u16 h) { return __uint_as_float(((uint32_t)h) << 16); }
+__device__ __forceinline__ u16 bf16_of(double v) { return bf16_rne((float)v); }
+
+constexpr u16 BF16_ONE = 0x3F80;
+
+// Smallest power of two q with |v| / q <= 255 (1 when v == 0).
+__device__ __forceinline__ double grid_quantum(double vmax) {
+  if (!(vmax > 0.0)) return 1.0;
+  double q = exp2(ceil(log2(vmax / 255.0)));
+  while (vmax / q > 255.0) q *= 2.0;
+  return q;
+}
+
+// Grid part and two bf16 remainder parts of v: v ~ g + r1 + r2 with g a
+// multiple of q, |v - g| <= q/2 and a residual below 2^-18 q.
+struct Parts {
+  u16 g, r1, r2;
+};
+__device__ __forceinline__ Parts grid_split(double v, double q) {
+  const double g = rint(v / q) * q;
+  double r = v - g;
+  Parts p;
+  p.g = bf16_of(g);
+  p.r1 = bf16_of(r);
+  r -= (double)bf16_f(p.r1);
+  p.r2 = bf16_of(r);
+  return p;
+}
+
+// s * 2^(m_old - m_new) for integer offsets m_old <= m_new.  Done with ldexp, not
+// exp2: v_exp_f32 flushes results below 2^-126 to zero, which would drop a large
+// partial sum whenever the offset jumps by more than 126.
+__device__ __forceinline__ float rescale(float s, float m_old, float m_new) {
+  const float d = m_old - m_new;
+  return d < -300.f ? 0.f : ldexpf(s, (int)d);
+}
+
+// ---------------------------------------------------------------------------
+// Set-up kernels
+// ---------------------------------------------------------------------------
+// Largest |coordinate| of each problem's X (side 0) and Y (side 1).
+__global__ __launch_bounds__(256) void k_maxabs(const void* __restrict__ X, const void* __restrict__ Y, int mode,
+                                                long long nx, long long ny, float* __restrict__ maxabs,
+                                                int batch) {
+  __shared__ float red[256];
+  const int b = blockIdx.x, side = blockIdx.y;
+  const long long cnt = side == 0 ? nx : ny;
+  const void* P = side == 0 ? X : Y;
+  float mx = 0.f;
+  for (long long i = threadIdx.x; i < cnt; i += 256) {
+    const long long k = (long long)b * cnt + i;
+    const float v = mode == MODE_SPLIT ? static_cast<const float*>(P)[k] : bf16_f(static_cast<const u16*>(P)[k]);
+    mx = fmaxf(mx, fabsf(v));
+  }
+  red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) maxabs[side * batch + b] = red[0];
+}
+
+// Norms (fp64), log-weights (fp64) and operand rows of one cloud: the split
+// query layout (fp32 inputs) or a zero-padded bf16 copy (bf16 inputs).
+template <int MODE>
+__global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, const float* __restrict__ w,
+                                                   int rows, int rows_pad, int d, int KP,
+                                                   const float* __restrict__ maxabs, double* __restrict__ norm,
+                                                   double* __restrict__ logw, u16* __restrict__ opnd) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows_pad) return;
+  u16* dst = opnd + ((size_t)b * rows_pad + i) * KP;
+  if (i >= rows) {
+    for (int k = 0; k < KP; k += 8) *reinterpret_cast<u4*>(dst + k) = u4{0, 0, 0, 0};
+    return;
+  }
+  const size_t r = (size_t)b * rows + i;
+  if (MODE == MODE_BF16) {
+    const u16* src = static_cast<const u16*>(P) + r * d;
+    double nrm = 0.0;
+    for (int t = 0; t < d; ++t) {
+      const double v = bf16_f(src[t]);
+      nrm += v * v;
+    }
+    norm[r] = nrm;
+    logw[r] = log((double)w[r]);
+    for (int k = 0; k < KP; k += 2) {
+      const uint32_t lo = (k < d) ? src[k] : 0, hi = (k + 1 < d) ? src[k + 1] : 0;
+      *reinterpret_cast<uint32_t*>(dst + k) = lo | (hi << 16);
+    }
+    return;
+  }
+  const float* src = static_cast<const float*>(P) + r * d;
+  const double q = grid_quantum(maxabs[b]);
+  double nrm = 0.0;
+  for (int t = 0; t < d; ++t) nrm += (double)src[t] * (double)src[t];
+  norm[r] = nrm;
+  logw[r] = log((double)w[r]);
+  const int cb = split_corr_begin(d);
+  for (int k0 = 0; k0 < KP; k0 += 8) {
+    u16 v[8];
+    for (int e = 0; e < 8; ++e) {
+      const int k = k0 + e;
+      u16 val = 0;
+      if (k >= 2 && k <= 4) {
+        val = BF16_ONE;
+      } else if (k >= 5 && k < 5 + d) {
+        val = grid_split(src[k - 5], q).g;
+      } else if (k >= cb && k < cb + 7 * d) {
+        const Parts pp = grid_split(src[(k - cb) / 7], q);
+        const int s = (k - cb) % 7;
+        val = (s <= 1) ? pp.g : ((s == 3 || s == 6) ? pp.r2 : pp.r1);
+      } else if (k == cb + 7 * d || k == cb + 7 * d + 1) {
+        val = BF16_ONE;
+      }
+      v[e] = val;
+    }
+    *reinterpret_cast<u4*>(dst + k0) = u4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
+                                         (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
+  }
+}
+
+// Key operand rows for one half-step (fp32 inputs): v = 2*lambda*y and the bias
+// lambda*(pot - norm + eps*logw) in grid + remainder parts; writes the grid
+// quantum Q = q_query * q_key of each problem to qgrid.
+__global__ __launch_bounds__(256) void k_prep_keys(const float* __restrict__ P, const float* __restrict__ pot,
+                                                   const double* __restrict__ norm, const double* __restrict__ logw,
+                                                   int keys, int keys_pad, int d, int KP, float lam, float eps,
+                                                   const float* __restrict__ qmax, const float* __restrict__ kmax,
+                                                   float* __restrict__ qgrid, u16* __restrict__ kb) {
+  const int b = blockIdx.y;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= keys_pad) return;
+  const double lam2 = 2.0 * (double)lam;
+  const double qq = grid_quantum(qmax[b]);
+  const double qk = grid_quantum(lam2 * (double)kmax[b]);
+  const double Q = qq * qk;
+  if (j == 0) qgrid[b] = (float)Q;
+  double bias = (double)NEG_BIG;
+  const float* src = nullptr;
+  if (j < keys) {
+    const size_t r = (size_t)b * keys + j;
+    src = P + r * d;
+    bias = (double)lam * ((double)pot[r] - norm[r] + (double)eps * logw[r]);
+    if (!(bias >= (double)NEG_BIG)) bias = (double)NEG_BIG;  // zero weight (-inf) or underflow
+  }
+  u16 b1, b2, b3, br1, br2;
+  if (bias <= (double)NEG_BIG) {
+    b1 = bf16_of(bias);
+    b2 = b3 = br1 = br2 = 0;
+  } else {
+    const double bg = rint(bias / Q) * Q;
+    b1 = bf16_of(bg);
+    b2 = bf16_of(bg - (double)bf16_f(b1));
+    b3 = bf16_of(bg - (double)bf16_f(b1) - (double)bf16_f(b2));
+    const double br = bias - bg;
+    br1 = bf16_of(br);
+    br2 = bf16_of(br - (double)bf16_f(br1));
+  }
+  const int cb = split_corr_begin(d);
+  const int dd = src ? d : 0;
+  u16* dst = kb + ((size_t)b * keys_pad + j) * KP;
+  for (int k0 = 0; k0 < KP; k0 += 8) {
+    u16 v[8];
+    for (int e = 0; e < 8; ++e) {
+      const int k = k0 + e;
+      u16 val = 0;
+      if (k <= 1) {
+        val = BF16_ONE;
+      } else if (k <= 4) {
+        val = k == 2 ? b1 : (k == 3 ? b2 : b3);
+      } else if (k < 5 + dd) {
+        val = grid_split(lam2 * (double)src[k - 5], qk).g;
+      } else if (k >= cb && k < cb + 7 * dd) {
+        const Parts pp = grid_split(lam2 * (double)src[(k - cb) / 7], qk);
+        const int s = (k - cb) % 7;
+        val = (s == 2 || s == 3) ? pp.g : ((s == 1 || s == 5) ? pp.r2 : pp.r1);
+      } else if (k == cb + 7 * d) {
+        val = br1;
+      } else if (k == cb + 7 * d + 1) {
+        val = br2;
+      }
+      v[e] = val;
+    }
+    *reinterpret_cast<u4*>(dst + k0) = u4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
+                                         (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
+  }
+}
+
+// Half bias (pot - norm + eps*logw)/2 per key (bf16 inputs); padding -> -1e30.
+__global__ __launch_bounds__(256) void k_prep_bias(const float* __restrict__ pot, const double* __restrict__ norm,
+                                                   const double* __restrict__ logw, int keys, int keys_pad,
+                                                   float eps, float* __restrict__ hb) {
+  const int b = blockIdx.y;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= keys_pad) return;
+  float v = NEG_BIG;
+  if (j < keys) {
+    const size_t r = (size_t)b * keys + j;
+    v = (float)(0.5 * ((double)pot[r] - norm[r] + (double)eps * logw[r]));
+    if (!(v >= NEG_BIG)) v = NEG_BIG;
+  }
+  hb[(size_t)b * keys_pad + j] = v;
+}
+
+// ---------------------------------------------------------------------------
+// The streaming half-step kernel
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bf16x8 as_bf16x8(u4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Offset slots (query side, chunk 0, lane group 0, elements 0..1) <- -m as two bf16 parts.
+__device__ __forceinline__ void set_offset(u4& q, float off, bool owner) {
+  if (!(off <= 1e30f)) off = 1e30f;
+  if (!(off >= -1e30f)) off = -1e30f;
+  const u16 h = bf16_rne(off);
+  const u16 l = bf16_rne(off - bf16_f(h));
+  if (owner) q.x = (uint32_t)h | ((uint32_t)l << 16);
+}
+
+// New offset from a chunk maximum: an integer that two bf16 parts hold exactly
+// and, on the fp32 path, a multiple of the grid quantum Q.
+__device__ __forceinline__ float offset_from_max(float mx, float Q) {
+  float mq = floorf(mx);
+  if (!(fabsf(mq) < 1e30f)) return mq;
+  float quantum = fmaxf(Q, 1.f);
+  if (fabsf(mq) >= 65536.f) quantum = fmaxf(quantum, ldexpf(1.f, ilogbf(mq) - 15));
+  return floorf(mq / quantum) * quantum;
+}
+
+template <int MODE, int NCH, int R, int TC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == MODE_SPLIT && NCH <= 3 ? 4 : 2))) void k_lse(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb,
+    const float* __restrict__ qgrid, const double* __restrict__ qnorm, float* __restrict__ out,
+    float2* __restrict__ part, int rows, int rows_pad, int keys, int keys_pad, int chunks_per_split, int batch,
+    float lam2, double inv_lam) {
+  constexpr int KP = NCH * 32;
+  constexpr int LROW = KP + 8;  // LDS row stride in elements (16-byte pad against bank conflicts)
+  constexpr int CK = TC * 16;   // keys per chunk
+  constexpr int VPR = KP / 8;   // 16-byte vectors per key row
+  constexpr int NVEC = CK * VPR;
+  constexpr int NLD = (NVEC + 255) / 256;
+  // One spare row per buffer takes the stores of threads past the end of a chunk.
+  __shared__ __attribute__((aligned(16))) u16 lds[2][(CK + 1) * LROW];
+  __shared__ __attribute__((aligned(16))) float ldsb[2][CK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
+  const int b = blockIdx.z;
+  const int qbase = blockIdx.x * (64 * R) + wave * (16 * R);
+  const u16* Qb = Q + (size_t)b * rows_pad * KP;
+  const u16* Kb = K + (size_t)b * keys_pad * KP;
+  const float* hbb = (MODE == MODE_BF16) ? hb + (size_t)b * keys_pad : nullptr;
+  const float qg = (MODE == MODE_SPLIT) ? qgrid[b] : 1.f;
+
+  u4 bq[R][NCH];
+#pragma unroll
+  for (int c = 0; c < R; ++c)
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+      bq[c][ch] = *reinterpret_cast<const u4*>(Qb + (size_t)(qbase + 16 * c + col) * KP + ch * 32 + grp * 8);
+
+  const int total_chunks = (keys + CK - 1) / CK;
+  const int c0 = blockIdx.y * chunks_per_split;
+  const int c1 = min(total_chunks, c0 + chunks_per_split);
+
+  float m[R], s[R];
+#pragma unroll
+  for (int c = 0; c < R; ++c) {
+    m[c] = -FLT_MAX;
+    s[c] = 0.f;
+  }
+
+  u4 pre[NLD];
+  f4 preb = {0.f, 0.f, 0.f, 0.f};
+  // Loads past the end of a chunk land in the slack rows that follow every
+  // operand buffer, so they need no guard; their LDS stores go to a spare row.
+  auto gload = [&](int chunk) {
+    const u16* src = Kb + (size_t)chunk * CK * KP;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) pre[i] = *reinterpret_cast<const u4*>(src + (size_t)(tid + 256 * i) * 8);
+    if (MODE == MODE_BF16) preb = *reinterpret_cast<const f4*>(hbb + (size_t)chunk * CK + (tid & 15) * 4);
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int v = min(tid + 256 * i, NVEC);  // NVEC maps to the spare row
+      *reinterpret_cast<u4*>(&lds[buf][(v / VPR) * LROW + (v % VPR) * 8]) = pre[i];
+    }
+    if (MODE == MODE_BF16 && tid < CK / 4) *reinterpret_cast<f4*>(&ldsb[buf][tid * 4]) = preb;
+  };
+  // Scores of key tile t of the chunk in buffer buf against the R query tiles.
+  auto tile = [&](int buf, int t, f4 (&acc)[R]) {
+    f4 cinit = {0.f, 0.f, 0.f, 0.f};
+    if (MODE == MODE_BF16) cinit = *reinterpret_cast<const f4*>(&ldsb[buf][t * 16 + grp * 4]);
+#pragma unroll
+    for (int c = 0; c < R; ++c) acc[c] = cinit;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const u4 ka = *reinterpret_cast<const u4*>(&lds[buf][(t * 16 + col) * LROW + ch * 32 + grp * 8]);
+#pragma unroll
+      for (int c = 0; c < R; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(bq[c][ch]), acc[c], 0, 0, 0);
+    }
+  };
+  // Base-2 exponent of a score relative to the current offset.
+  auto expo = [&](float v, int c) -> float {
+    if (MODE == MODE_BF16) return fmaf(v, lam2, -m[c]);
+    return v;
+  };
+  auto raw = [&](float v) -> float {
+    if (MODE == MODE_BF16) return v * lam2;
+    return v;
+  };
+
+  if (c0 < c1) {
+    gload(c0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int ci = c0; ci < c1; ++ci) {
+    const int buf = (ci - c0) & 1;
+    if (ci + 1 < c1) gload(ci + 1);
+
+    float ssave[R];
+#pragma unroll
+    for (int c = 0; c < R; ++c) ssave[c] = s[c];
+
+    bool redo = (ci == c0);
+    if (!redo) {
+#pragma unroll 1
+      for (int t = 0; t < TC; ++t) {
+        f4 acc[R];
+        tile(buf, t, acc);
+#pragma unroll
+        for (int c = 0; c < R; ++c) {
+          const float e0 = __builtin_amdgcn_exp2f(expo(acc[c][0], c));
+          const float e1 = __builtin_amdgcn_exp2f(expo(acc[c][1], c));
+          const float e2 = __builtin_amdgcn_exp2f(expo(acc[c][2], c));
+          const float e3 = __builtin_amdgcn_exp2f(expo(acc[c][3], c));
+          s[c] += (e0 + e1) + (e2 + e3);
+        }
+      }
+      int bad = 0;
+#pragma unroll
+      for (int c = 0; c < R; ++c) bad |= !(s[c] <= SUM_LIMIT);
+      redo = __any(bad);
+    }
+    if (redo) {
+      // Exact chunk maximum of the raw scores (offset slots zeroed), a new
+      // offset from it, then the chunk again through the normal path.
+#pragma unroll
+      for (int c = 0; c < R; ++c) s[c] = ssave[c];
+      if (MODE == MODE_SPLIT) {
+#pragma unroll
+        for (int c = 0; c < R; ++c) set_offset(bq[c][0], 0.f, grp == 0);
+      }
+      float mx[R];
+#pragma unroll
+      for (int c = 0; c < R; ++c) mx[c] = -INFINITY;
+#pragma unroll 1
+      for (int t = 0; t < TC; ++t) {
+        f4 acc[R];
+        tile(buf, t, acc);
+#pragma unroll
+        for (int c = 0; c < R; ++c)
+          mx[c] = fmaxf(fmaxf(fmaxf(mx[c], raw(acc[c][0])), fmaxf(raw(acc[c][1]), raw(acc[c][2]))), raw(acc[c][3]));
+      }
+#pragma unroll
+      for (int c = 0; c < R; ++c) {
+        mx[c] = fmaxf(mx[c], __shfl_xor(mx[c], 16));
+        mx[c] = fmaxf(mx[c], __shfl_xor(mx[c], 32));
+        const float mn = fmaxf(m[c], offset_from_max(mx[c], qg));
+        s[c] = rescale(s[c], m[c], mn);
+        m[c] = mn;
+        if (MODE == MODE_SPLIT) set_offset(bq[c][0], -m[c], grp == 0);
+      }
+#pragma unroll 1
+      for (int t = 0; t < TC; ++t) {
+        f4 acc[R];
+        tile(buf, t, acc);
+#pragma unroll
+        for (int c = 0; c < R; ++c) {
+          const float e0 = __builtin_amdgcn_exp2f(expo(acc[c][0], c));
+          const float e1 = __builtin_amdgcn_exp2f(expo(acc[c][1], c));
+          const float e2 = __builtin_amdgcn_exp2f(expo(acc[c][2], c));
+          const float e3 = __builtin_amdgcn_exp2f(expo(acc[c][3], c));
+          s[c] += (e0 + e1) + (e2 + e3);
+        }
+      }
+    }
+    if (ci + 1 < c1) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int c = 0; c < R; ++c) {
+    float st = s[c] + __shfl_xor(s[c], 16);
+    st += __shfl_xor(st, 32);
+    const int q = qbase + 16 * c + col;
+    if (grp == 0 && q < rows) {
+      const size_t r = (size_t)b * rows + q;
+      if (part != nullptr) {
+        part[(size_t)blockIdx.y * batch * rows + r] = make_float2(m[c], st);
+      } else {
+        out[r] = (float)(qnorm[r] - ((double)m[c] + log2((double)st)) * inv_lam);
+      }
+    }
+  }
+}
+
+// Merge the (max, sum) pairs of the key splits and write the potential.
+__global__ __launch_bounds__(256) void k_finalize(const float2* __restrict__ part, int ks, int total,
+                                                  const double* __restrict__ qnorm, float* __restrict__ out,
+                                                  double inv_lam) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  float M = -FLT_MAX;
+  for (int k = 0; k < ks; ++k) M = fmaxf(M, part[(size_t)k * total + i].x);
+  float S = 0.f;
+  for (int k = 0; k < ks; ++k) {
+    const float2 v = part[(size_t)k * total + i];
+    S += rescale(v.y, v.x, M);
+  }
+  out[i] = (float)(qnorm[i] - ((double)M + log2((double)S)) * inv_lam);
+}
+
+// sum_i exp(logw_i) * |expm1((pot_i - tilde_i)/eps)|, one workgroup per problem, fixed order.
+__global__ __launch_bounds__(256) void k_marginal(const float* __restrict__ pot, const float* __restrict__ tilde,
+                                                  const double* __restrict__ logw, int rows, float inv_eps,
+                                                  float* __restrict__ err, int which) {
+  __shared__ float red[256];
+  const int b = blockIdx.x;
+  float acc = 0.f;
+  for (int i = threadIdx.x; i < rows; i += 256) {
+    const size_t r = (size_t)b * rows + i;
+    acc += (float)exp(logw[r]) * fabsf(expm1f((pot[r] - tilde[r]) * inv_eps));
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) err[2 * b + which] = red[0];
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+struct Layout {
+  int mode, KP, n_pad, m_pad, max_pad;
+  size_t xn, yn, la, lb, maxabs, qgrid, qx, qy, kb, hb, part, scratch, total;
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int kp_for(int mode, int64_t d) {
+  if (mode == MODE_SPLIT) return split_nch((int)d) * 32;
+  return (int)align_up((size_t)d, 32);
+}
+
+sk_status check_problem(const sk_problem* p) {
+  if (p == nullptr) {
+    set_err("problem descriptor is NULL");
+    return SK_EINVAL;
+  }
+  if (p->dtype != SK_FP32 && p->dtype != SK_BF16) {
+    set_err("unknown dtype %d (expected SK_FP32=0 or SK_BF16=1)", (int)p->dtype);
+    return SK_EDTYPE;
+  }
+  if (p->batch < 1 || p->n < 1 || p->m < 1 || p->d < 1) {
+    set_err("batch, n, m and d must be >= 1 (got %lld, %lld, %lld, %lld)", (long long)p->batch,
+            (long long)p->n, (long long)p->m, (long long)p->d);
+    return SK_ESHAPE;
+  }
+  if (p->d > SK_MAX_D) {
+    set_err("d = %lld exceeds SK_MAX_D = %d", (long long)p->d, SK_MAX_D);
+    return SK_EUNSUPPORTED;
+  }
+  if (p->dtype == SK_FP32 && p->d > SK_MAX_D_FP32) {
+    set_err("d = %lld exceeds SK_MAX_D_FP32 = %d for fp32 inputs", (long long)p->d, SK_MAX_D_FP32);
+    return SK_EUNSUPPORTED;
+  }
+  const int64_t lim = (int64_t)1 << 30;
+  if (p->n >= lim || p->m >= lim || p->batch >= 65536 || p->batch * std::max(p->n, p->m) >= ((int64_t)1 << 31)) {
+    set_err("problem too large (batch*max(n,m) must stay below 2^31, batch < 65536)");
+    return SK_ESHAPE;
+  }
+  return SK_OK;
+}
+
+Layout layout_of(const sk_problem* p) {
+  Layout L{};
+  L.mode = (p->dtype == SK_BF16) ? MODE_BF16 : MODE_SPLIT;
+  L.KP = kp_for(L.mode, p->d);
+  L.n_pad = (int)align_up((size_t)p->n, ROW_PAD);
+  L.m_pad = (int)align_up((size_t)p->m, ROW_PAD);
+  L.max_pad = std::max(L.n_pad, L.m_pad);
+  const size_t B = (size_t)p->batch, n = (size_t)p->n, m = (size_t)p->m, mx = std::max(n, m);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  L.xn = take(8 * B * n);
+  L.yn = take(8 * B * m);
+  L.la = take(8 * B * n);
+  L.lb = take(8 * B * m);
+  L.maxabs = take(4 * 2 * B);
+  L.qgrid = take(4 * B);
+  // SLACK extra rows after each operand buffer absorb the kernels' unguarded
+  // over-reads at the end of the last chunk.
+  L.qx = take(2 * (B * L.n_pad + SLACK) * L.KP);
+  L.qy = take(2 * (B * L.m_pad + SLACK) * L.KP);
+  L.kb = (L.mode == MODE_SPLIT) ? take(2 * (B * L.max_pad + SLACK) * L.KP) : 0;
+  L.hb = (L.mode == MODE_BF16) ? take(4 * (B * L.max_pad + SLACK)) : 0;
+  L.part = take(8 * (size_t)KS_MAX * B * mx);
+  L.scratch = take(4 * B * mx);
+  L.total = off;
+  return L;
+}
+
+// Query tiles per wave (R) and key tiles per LDS chunk (TC) for NCH K-chunks of 32:
+// small K keeps many query tiles in VGPRs; large K trades them for operand registers.
+constexpr int cfg_R(int nch) { return nch == 1 ? 8 : (nch <= 4 ? 4 : (nch <= 8 ? 2 : 1)); }
+constexpr int cfg_TC(int nch) { return nch == 1 ? 4 : (nch == 2 ? 2 : 1); }
+
+using LseFn = void (*)(const u16*, const u16*, const float*, const float*, const double*, float*, float2*, int, int,
+                       int, int, int, int, float, double);
+
+template <int MODE, int NCH>
+LseFn lse_fn() {
+  if constexpr ((MODE == MODE_SPLIT && NCH <= MAX_NCH_SPLIT) || (MODE == MODE_BF16 && NCH <= MAX_NCH_BF16))
+    return &k_lse<MODE, NCH, cfg_R(NCH), cfg_TC(NCH)>;
+  else
+    return nullptr;
+}
+
+template <int MODE, int... N>
+LseFn lse_lookup_impl(int nch, std::integer_sequence<int, N...>) {
+  LseFn fn = nullptr;
+  ((nch == N + 1 ? (fn = lse_fn<MODE, N + 1>(), 0) : 0), ...);
+  return fn;
+}
+
+template <int MODE>
+LseFn lse_lookup(int nch) {
+  constexpr int MAXN = MODE == MODE_SPLIT ? MAX_NCH_SPLIT : MAX_NCH_BF16;
+  return lse_lookup_impl<MODE>(nch, std::make_integer_sequence<int, MAXN>{});
+}
+
+sk_status hip_check(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_err("%s: %s", what, hipGetErrorString(e));
+    return SK_EHIP;
+  }
+  return SK_OK;
+}
+
+sk_status check_ws(const sk_problem* p, void* ws, size_t ws_bytes, Layout* L) {
+  sk_status st = check_problem(p);
+  if (st != SK_OK) return st;
+  *L = layout_of(p);
+  if (ws == nullptr || ws_bytes < L->total) {
+    set_err("workspace %s: need %zu bytes, got %zu", ws == nullptr ? "is NULL" : "too small", L->total,
+            ws_bytes);
+    return SK_EWORKSPACE;
+  }
+  return SK_OK;
+}
+
+bool eps_ok(float eps) { return eps > 0.f && isfinite(eps) && isfinite((float)(LOG2E / eps)); }
+
+// One half-step.  side 0: f from g (queries X, keys Y); side 1: g from f.
+sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws, const Layout& L,
+                    const float* pot_in, float eps, float* pot_out, int side, hipStream_t stream) {
+  char* w = static_cast<char*>(ws);
+  const int B = (int)p->batch;
+  const int rows = (int)(side == 0 ? p->n : p->m);
+  const int keys = (int)(side == 0 ? p->m : p->n);
+  const int rows_pad = side == 0 ? L.n_pad : L.m_pad;
+  const int keys_pad = side == 0 ? L.m_pad : L.n_pad;
+  const double* qnorm = reinterpret_cast<const double*>(w + (side == 0 ? L.xn : L.yn));
+  const double* knorm = reinterpret_cast<const double*>(w + (side == 0 ? L.yn : L.xn));
+  const double* klogw = reinterpret_cast<const double*>(w + (side == 0 ? L.lb : L.la));
+  const float* maxabs = reinterpret_cast<const float*>(w + L.maxabs);
+  float* qgrid = reinterpret_cast<float*>(w + L.qgrid);
+  const u16* Qop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qx : L.qy));
+  const void* Kraw = side == 0 ? Y : X;
+  const int nch = L.KP / 32;
+  const int cfR = cfg_R(nch), cfTC = cfg_TC(nch);
+  const float lam = (float)(LOG2E / (double)eps);
+
+  const u16* Kop;
+  const float* hb = nullptr;
+  const dim3 pgrid((keys_pad + 255) / 256, B);
+  if (L.mode == MODE_SPLIT) {
+    u16* kb = reinterpret_cast<u16*>(w + L.kb);
+    hipLaunchKernelGGL(k_prep_keys, pgrid, dim3(256), 0, stream, static_cast<const float*>(Kraw), pot_in, knorm,
+                       klogw, keys, keys_pad, (int)p->d, L.KP, lam, eps, maxabs + (side == 0 ? 0 : B),
+                       maxabs + (side == 0 ? B : 0), qgrid, kb);
+    Kop = kb;
+  } else {
+    float* hbw = reinterpret_cast<float*>(w + L.hb);
+    hipLaunchKernelGGL(k_prep_bias, pgrid, dim3(256), 0, stream, pot_in, knorm, klogw, keys, keys_pad, eps, hbw);
+    hb = hbw;
+    Kop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qy : L.qx));
+  }
+  sk_status st = hip_check("key preparation launch");
+  if (st != SK_OK) return st;
+
+  const int wg_x = (rows + 64 * cfR - 1) / (64 * cfR);
+  const int CK = cfTC * 16;
+  const int total_chunks = (keys + CK - 1) / CK;
+  const int target = 2048;
+  int ks = (target + wg_x * B - 1) / (wg_x * B);
+  ks = std::max(1, std::min(ks, std::min(KS_MAX, total_chunks / 2)));
+  const int cps = (total_chunks + ks - 1) / ks;
+  ks = (total_chunks + cps - 1) / cps;
+
+  LseFn fn = (L.mode == MODE_SPLIT) ? lse_lookup<MODE_SPLIT>(nch) : lse_lookup<MODE_BF16>(nch);
+  if (fn == nullptr) {
+    set_err("no kernel for %d K chunks", nch);
+    return SK_EUNSUPPORTED;
+  }
+  float2* part = ks > 1 ? reinterpret_cast<float2*>(w + L.part) : nullptr;
+  const double inv_lam = 1.0 / (double)lam;
+  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, qgrid, qnorm, pot_out, part, rows,
+                     rows_pad, keys, keys_pad, cps, B, 2.f * lam, inv_lam);
+  st = hip_check("half-step kernel launch");
+  if (st != SK_OK) return st;
+  if (ks > 1) {
+    const int total = B * rows;
+    hipLaunchKernelGGL(k_finalize, dim3((total + 255) / 256), dim3(256), 0, stream, part, ks, total, qnorm,
+                       pot_out, inv_lam);
+    st = hip_check("merge kernel launch");
+  }
+  return st;
+}
+
+sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const float* a, const float* b, void* ws,
+                    const Layout& L, hipStream_t stream) {
+  char* w = static_cast<char*>(ws);
+  const int B = (int)p->batch;
+  float* maxabs = reinterpret_cast<float*>(w + L.maxabs);
+  hipLaunchKernelGGL(k_maxabs, dim3(B, 2), dim3(256), 0, stream, X, Y, L.mode, (long long)(p->n * p->d),
+                     (long long)(p->m * p->d), maxabs, B);
+  auto side = [&](const void* P, const float* wt, int rows, int rows_pad, const float* mabs, size_t norm,
+                  size_t logw, size_t op) {
+    const dim3 grid((rows_pad + 255) / 256, B);
+    if (L.mode == MODE_SPLIT)
+      hipLaunchKernelGGL(k_init_side<MODE_SPLIT>, grid, dim3(256), 0, stream, P, wt, rows, rows_pad, (int)p->d,
+                         L.KP, mabs, reinterpret_cast<double*>(w + norm), reinterpret_cast<double*>(w + logw),
+                         reinterpret_cast<u16*>(w + op));
+    else
+      hipLaunchKernelGGL(k_init_side<MODE_BF16>, grid, dim3(256), 0, stream, P, wt, rows, rows_pad, (int)p->d,
+                         L.KP, mabs, reinterpret_cast<double*>(w + norm), reinterpret_cast<double*>(w + logw),
+                         reinterpret_cast<u16*>(w + op));
+  };
+  side(X, a, (int)p->n, L.n_pad, maxabs, L.xn, L.la, L.qx);
+  side(Y, b, (int)p->m, L.m_pad, maxabs + B, L.yn, L.lb, L.qy);
+  return hip_check("init kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sinkhorn_workspace_bytes(const sk_problem* p) {
+  if (check_problem(p) != SK_OK) return 0;
+  return layout_of(p).total;
+}
+
+const char* sinkhorn_last_error(void) { return g_err; }
+
+sk_status sinkhorn_init_norms(const sk_problem* p, const void* X, const void* Y, const float* a, const float* b,
+                              void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  Layout L;
+  sk_status st = check_ws(p, ws, ws_bytes, &L);
+  if (st != SK_OK) return st;
+  if (!X || !Y || !a || !b) {
+    set_err("X, Y, a and b must be non-NULL device pointers");
+    return SK_EINVAL;
+  }
+  return init_impl(p, X, Y, a, b, ws, L, static_cast<hipStream_t>(stream));
+}
+
+sk_status sinkhorn_half_step_f(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
+                               const float* g, float eps, float* f, void* stream) {
+  g_err[0] = 0;
+  Layout L;
+  sk_status st = check_ws(p, ws, ws_bytes, &L);
+  if (st != SK_OK) return st;
+  if (!X || !Y || !g || !f) {
+    set_err("X, Y, g and f must be non-NULL device pointers");
+    return SK_EINVAL;
+  }
+  if (!eps_ok(eps)) {
+    set_err("eps must be positive and finite (got %g)", (double)eps);
+    return SK_EINVAL;
+  }
+  return half_step(p, X, Y, ws, L, g, eps, f, 0, static_cast<hipStream_t>(stream));
+}
+
+sk_status sinkhorn_half_step_g(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
+                               const float* f, float eps, float* g, void* stream) {
+  g_err[0] = 0;
+  Layout L;
+  sk_status st = check_ws(p, ws, ws_bytes, &L);
+  if (st != SK_OK) return st;
+  if (!X || !Y || !g || !f) {
+    set_err("X, Y, f and g must be non-NULL device pointers");
+    return SK_EINVAL;
+  }
+  if (!eps_ok(eps)) {
+    set_err("eps must be positive and finite (got %g)", (double)eps);
+    return SK_EINVAL;
+  }
+  return half_step(p, X, Y, ws, L, f, eps, g, 1, static_cast<hipStream_t>(stream));
+}
+
+sk_status sinkhorn_solve(const sk_problem* p, const void* X, const void* Y, const float* a, const float* b,
+                         const float* eps, int64_t n_eps, int64_t iters, float* f, float* g, void* ws,
+                         size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  Layout L;
+  sk_status st = check_ws(p, ws, ws_bytes, &L);
+  if (st != SK_OK) return st;
+  if (!X || !Y || !a || !b || !f || !g) {
+    set_err("X, Y, a, b, f and g must be non-NULL device pointers");
+    return SK_EINVAL;
+  }
+  if (iters < 0) {
+    set_err("iters must be >= 0 (got %lld)", (long long)iters);
+    return SK_EINVAL;
+  }
+  if (eps == nullptr || !(n_eps == 1 || (n_eps == iters && iters > 0))) {
+    set_err("eps must be a host array of 1 or iters values (n_eps = %lld, iters = %lld)", (long long)n_eps,
+            (long long)iters);
+    return SK_EINVAL;
+  }
+  for (int64_t k = 0; k < n_eps; ++k)
+    if (!eps_ok(eps[k])) {
+      set_err("eps[%lld] must be positive and finite (got %g)", (long long)k, (double)eps[k]);
+      return SK_EINVAL;
+    }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = init_impl(p, X, Y, a, b, ws, L, s);
+  for (int64_t k = 0; k < iters && st == SK_OK; ++k) {
+    const float e = eps[n_eps == 1 ? 0 : k];
+    st = half_step(p, X, Y, ws, L, g, e, f, 0, s);
+    if (st == SK_OK) st = half_step(p, X, Y, ws, L, f, e, g, 1, s);
+  }
+  return st;
+}
+
+sk_status sinkhorn_marginal_error(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
+                                  const float* f, const float* g, float eps, float* err, void* stream) {
+  g_err[0] = 0;
+  Layout L;
+  sk_status st = check_ws(p, ws, ws_bytes, &L);
+  if (st != SK_OK) return st;
+  if (!X || !Y || !f || !g || !err) {
+    set_err("X, Y, f, g and err must be non-NULL device pointers");
+    return SK_EINVAL;
+  }
+  if (!eps_ok(eps)) {
+    set_err("eps must be positive and finite (got %g)", (double)eps);
+    return SK_EINVAL;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  float* tilde = reinterpret_cast<float*>(w + L.scratch);
+  const int B = (int)p->batch;
+  // rows: sum_j P_ij = a_i exp((f_i - T_f(g)_i)/eps)
+  st = half_step(p, X, Y, ws, L, g, eps, tilde, 0, s);
+  if (st != SK_OK) return st;
+  hipLaunchKernelGGL(k_marginal, dim3(B), dim3(256), 0, s, f, tilde, reinterpret_cast<const double*>(w + L.la),
+                     (int)p->n, 1.f / eps, err, 0);
+  st = hip_check("marginal reduction launch");
+  if (st != SK_OK) return st;
+  // columns: sum_i P_ij = b_j exp((g_j - T_g(f)_j)/eps)
+  st = half_step(p, X, Y, ws, L, f, eps, tilde, 1, s);
+  if (st != SK_OK) return st;
+  hipLaunchKernelGGL(k_marginal, dim3(B), dim3(256), 0, s, g, tilde, reinterpret_cast<const double*>(w + L.lb),
+                     (int)p->m, 1.f / eps, err, 1);
+  return hip_check("marginal reduction launch");
+}
+
+}  // extern "C"

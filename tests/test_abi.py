@@ -1,0 +1,113 @@
+"""Host-only checks of the C ABI library (no GPU needed).
+
+The library must load, export every function declared in include/sinkhorn.h,
+size its workspace linearly in (n+m)*d, and reject invalid arguments on the
+host before anything touches a device.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from log_domain_sinkhorn_half_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sinkhorn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sinkhorn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libsinkhorn.so is not built (run __graft_entry__.build())")
+    return binding.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("sinkhorn_init_norms", "sinkhorn_half_step_f", "sinkhorn_half_step_g", "sinkhorn_solve",
+              "sinkhorn_marginal_error", "sinkhorn_workspace_bytes", "sinkhorn_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (sinkhorn_\w+)", out))
+    for n in _declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert set(binding.EXPORTS) <= exported
+
+
+def test_library_has_gfx950_code_object():
+    # the offload bundle embedded by hipcc names its target
+    data = open(binding.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in data
+
+
+def _prob(batch=1, n=10, m=12, d=3, dtype=0):
+    return binding.SkProblem(batch, n, m, d, dtype)
+
+
+def test_workspace_is_linear_not_quadratic(lib):
+    small = lib.sinkhorn_workspace_bytes(ctypes.byref(_prob(1, 70000, 70000, 3)))
+    big = lib.sinkhorn_workspace_bytes(ctypes.byref(_prob(1, 140000, 140000, 3)))
+    assert 0 < small < 200 * 2 ** 20
+    assert big < 2.2 * small  # O((n+m)d), never O(nm)
+    assert lib.sinkhorn_workspace_bytes(ctypes.byref(_prob(1, 65536, 32768, 128, 1))) > 0
+    assert lib.sinkhorn_workspace_bytes(ctypes.byref(_prob(1, 100, 100, 88, 0))) > 0
+
+
+@pytest.mark.parametrize("p,status", [
+    (None, 1),
+    (_prob(n=0), 2),
+    (_prob(m=-3), 2),
+    (_prob(batch=0), 2),
+    (_prob(d=0), 2),
+    (_prob(d=129), 5),
+    (_prob(d=89), 5),
+    (_prob(d=129, dtype=1), 5),
+    (_prob(dtype=7), 3),
+])
+def test_invalid_problem_rejected_before_launch(lib, p, status):
+    ptr = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    arg = ctypes.byref(p) if p is not None else None
+    st = lib.sinkhorn_half_step_f(arg, ptr, ptr, ptr, 1 << 40, ptr, 0.1, ptr, None)
+    assert st == status
+    assert lib.sinkhorn_last_error()
+    if p is not None:
+        assert lib.sinkhorn_workspace_bytes(arg) == 0
+
+
+def test_other_argument_errors(lib):
+    p = _prob()
+    need = lib.sinkhorn_workspace_bytes(ctypes.byref(p))
+    ptr = ctypes.c_void_p(0x1000)
+    bp = ctypes.byref(p)
+    # workspace too small / missing
+    assert lib.sinkhorn_half_step_f(bp, ptr, ptr, ptr, need - 1, ptr, 0.1, ptr, None) == 6
+    assert lib.sinkhorn_half_step_g(bp, ptr, ptr, None, need, ptr, 0.1, ptr, None) == 6
+    # NULL data pointers
+    assert lib.sinkhorn_half_step_f(bp, None, ptr, ptr, need, ptr, 0.1, ptr, None) == 1
+    assert lib.sinkhorn_init_norms(bp, ptr, ptr, None, ptr, ptr, need, None) == 1
+    # bad eps
+    for e in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.sinkhorn_half_step_f(bp, ptr, ptr, ptr, need, ptr, e, ptr, None) == 1
+        assert lib.sinkhorn_marginal_error(bp, ptr, ptr, ptr, need, ptr, ptr, e, ptr, None) == 1
+    # solve: iters < 0, wrong n_eps, bad schedule entry
+    E = (ctypes.c_float * 3)(0.1, 0.2, 0.3)
+    assert lib.sinkhorn_solve(bp, ptr, ptr, ptr, ptr, E, 1, -1, ptr, ptr, ptr, need, None) == 1
+    assert lib.sinkhorn_solve(bp, ptr, ptr, ptr, ptr, E, 2, 3, ptr, ptr, ptr, need, None) == 1
+    assert lib.sinkhorn_solve(bp, ptr, ptr, ptr, ptr, None, 1, 3, ptr, ptr, ptr, need, None) == 1
+    Ebad = (ctypes.c_float * 3)(0.1, 0.0, 0.3)
+    assert lib.sinkhorn_solve(bp, ptr, ptr, ptr, ptr, Ebad, 3, 3, ptr, ptr, ptr, need, None) == 1
+    assert b"eps[1]" in lib.sinkhorn_last_error()

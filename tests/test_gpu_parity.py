@@ -1,0 +1,272 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Acceptance bound (per half-step output and per trajectory):
+  fp32 inputs: max|pot_gpu - pot_ref| <= 1e-3*eps + 1e-5*max|pot_ref|
+  bf16 inputs: max|pot_gpu - pot_ref| <= 2e-2*eps   (eps = the last eps used)
+Both sides read identical seeded inputs (bf16 problems: the exact bf16 values).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from log_domain_sinkhorn_half_amd import binding as sk
+from log_domain_sinkhorn_half_amd.inputs import make_case, make_config, random_potential
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sk.load_library()  # raises loudly if the HIP library is missing
+
+
+def dev(p):
+    if p.dtype == "bf16":
+        X = torch.from_numpy(p.X_bits.view(np.int16)).cuda().view(torch.bfloat16)
+        Y = torch.from_numpy(p.Y_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        X = torch.from_numpy(p.X).cuda()
+        Y = torch.from_numpy(p.Y).cuda()
+    return X, Y, torch.from_numpy(p.a).cuda(), torch.from_numpy(p.b).cuda()
+
+
+def tol(p, eps, ref):
+    if p.dtype == "bf16":
+        return 2e-2 * eps
+    return 1e-3 * eps + 1e-5 * float(np.max(np.abs(ref)))
+
+
+def check(gpu, ref, bound, what):
+    gpu = np.asarray(gpu, np.float64)
+    err = np.max(np.abs(gpu - ref))
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    assert err <= bound, f"{what}: max err {err:.3e} > bound {bound:.3e}"
+    return err
+
+
+def half_steps(p, eps, seed, rows=None, scale=0.3):
+    """GPU f and g half-steps from seeded potentials vs oracle (optionally on sampled rows)."""
+    X, Y, a, b = dev(p)
+    ws = sk.alloc_workspace(X, Y)
+    sk.init_norms(X, Y, a, b, ws)
+    g = random_potential((p.batch, p.m), seed, scale)
+    f_in = random_potential((p.batch, p.n), seed + 1, scale)
+    f = sk.half_step_f(X, Y, ws, torch.from_numpy(g).cuda(), eps)
+    gg = sk.half_step_g(X, Y, ws, torch.from_numpy(f_in).cuda(), eps)
+    torch.cuda.synchronize()
+    f, gg = f.cpu().numpy(), gg.cpu().numpy()
+    for k in range(p.batch):
+        rf = None if rows is None else rows[0]
+        rg = None if rows is None else rows[1]
+        ref_f = oracle.half_step_f(p.X[k], p.Y[k], p.b[k], g[k], eps, rows=rf)
+        ref_g = oracle.half_step_g(p.X[k], p.Y[k], p.a[k], f_in[k], eps, rows=rg)
+        got_f = f[k] if rf is None else f[k][rf]
+        got_g = gg[k] if rg is None else gg[k][rg]
+        check(got_f, ref_f, tol(p, eps, ref_f), f"f half-step problem {k}")
+        check(got_g, ref_g, tol(p, eps, ref_g), f"g half-step problem {k}")
+
+
+# ---------------------------------------------------------------------------
+# half-steps on ragged shapes spanning several tiles, every supported K width
+# ---------------------------------------------------------------------------
+SHAPES = [
+    (1, 1, 3), (1, 7, 3), (7, 1, 2), (63, 65, 3), (65, 63, 4), (1000, 777, 3), (777, 1000, 1),
+    (300, 513, 5), (513, 300, 9), (257, 1029, 17), (1030, 255, 32), (129, 700, 64), (700, 129, 88),
+    (200, 333, 80), (150, 140, 4), (140, 150, 12),
+]
+
+
+@pytest.mark.parametrize("n,m,d", SHAPES)
+def test_half_steps_fp32_ragged(n, m, d):
+    p = make_case(n, m, d, seed=n + m + d, weights="softmax", scale=1.0 / np.sqrt(d))
+    for eps in (0.5, 0.05):
+        half_steps(p, eps, seed=d)
+
+
+@pytest.mark.parametrize("n,m,d", [(1, 5, 8), (63, 65, 8), (1000, 777, 32), (300, 1100, 64),
+                                   (333, 200, 128), (129, 515, 96), (77, 90, 40)])
+def test_half_steps_bf16_ragged(n, m, d):
+    p = make_case(n, m, d, seed=7 * n + m, weights="softmax", dtype="bf16", scale=1.0 / np.sqrt(d))
+    for eps in (1.0, 0.1, 0.01):
+        half_steps(p, eps, seed=d)
+
+
+def test_half_steps_batched_small():
+    p = make_case(70, 90, 6, batch=5, seed=3, weights="softmax")
+    half_steps(p, 0.2, seed=3)
+
+
+# ---------------------------------------------------------------------------
+# full trajectories
+# ---------------------------------------------------------------------------
+def gpu_solve(p, iters=None):
+    X, Y, a, b = dev(p)
+    it = p.iters if iters is None else iters
+    eps = p.eps.tolist() if p.eps.size > 1 else float(p.eps[0])
+    f, g = sk.solve(X, Y, a, b, eps, it)
+    torch.cuda.synchronize()
+    return f.cpu().numpy(), g.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,m,d,eps,iters", [(1000, 777, 3, 0.05, 20), (513, 1000, 16, 0.1, 15),
+                                             (600, 450, 64, 0.2, 10)])
+def test_trajectory_small(n, m, d, eps, iters):
+    p = make_case(n, m, d, eps=eps, iters=iters, seed=n, weights="softmax", scale=1.0 / np.sqrt(d))
+    f, g = gpu_solve(p)
+    rf, rg = oracle.solve(p.X[0], p.Y[0], p.a[0], p.b[0], eps, iters)
+    check(f[0], rf, tol(p, eps, rf), "f")
+    check(g[0], rg, tol(p, eps, rg), "g")
+
+
+def test_config1_full_trajectory():
+    p = make_config(1)
+    f, g = gpu_solve(p)
+    rf, rg = oracle.solve(p.X, p.Y, p.a, p.b, float(p.eps[0]), p.iters)
+    e = float(p.eps[0])
+    check(f, rf, tol(p, e, rf), "C1 f")
+    check(g, rg, tol(p, e, rg), "C1 g")
+
+
+def test_config5_batched_trajectory_sampled_problems():
+    p = make_config(5)
+    f, g = gpu_solve(p)
+    e = float(p.eps[0])
+    for k in (0, 37, 63):
+        rf, rg = oracle.solve(p.X[k], p.Y[k], p.a[k], p.b[k], e, p.iters)
+        check(f[k], rf, tol(p, e, rf), f"C5 f problem {k}")
+        check(g[k], rg, tol(p, e, rg), f"C5 g problem {k}")
+
+
+def test_config5_half_steps_all_rows_sampled_problems():
+    # Launch shape of the batched workload (2 key splits, 64 chunks per split): the
+    # running offset must jump by more than 126 while partial sums are ~2^100+.
+    p = make_config(5)
+    X, Y, a, b = dev(p)
+    ws = sk.alloc_workspace(X, Y)
+    sk.init_norms(X, Y, a, b, ws)
+    e = float(p.eps[0])
+    for seed, scale in ((None, 0.0), (5, 3.0)):
+        g = np.zeros((p.batch, p.m), np.float32) if seed is None else random_potential((p.batch, p.m), seed, scale)
+        f = sk.half_step_f(X, Y, ws, torch.from_numpy(g).cuda(), e)
+        torch.cuda.synchronize()
+        f = f.cpu().numpy()
+        for k in (0, 21, 63):
+            ref = oracle.half_step_f(p.X[k], p.Y[k], p.b[k], g[k], e)
+            check(f[k], ref, tol(p, e, ref), f"C5 f half-step problem {k}")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: one half-step each way on sampled rows
+# ---------------------------------------------------------------------------
+def _rows(n, k, seed):
+    rng = np.random.default_rng(seed)
+    r = rng.choice(n, size=min(k, n), replace=False)
+    return np.sort(np.concatenate([r, [0, n - 1]]))
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_full_size_half_steps_sampled(cfg):
+    p = make_config(cfg)
+    eps = float(p.eps[-1])
+    half_steps(p, eps, seed=cfg, rows=(_rows(p.n, 256, cfg), _rows(p.m, 256, cfg + 1)), scale=0.1)
+
+
+@pytest.mark.parametrize("eps", [1.0, 0.1, 0.01])
+def test_full_size_bf16_half_steps_sampled(eps):
+    p = make_config(4)
+    half_steps(p, eps, seed=4, rows=(_rows(p.n, 128, 4), _rows(p.m, 128, 5)), scale=0.1)
+
+
+# ---------------------------------------------------------------------------
+# properties: determinism, symmetry, resume, batching, marginals
+# ---------------------------------------------------------------------------
+def test_bitwise_determinism_and_role_swap():
+    p = make_case(900, 1300, 3, seed=5, weights="softmax")
+    X, Y, a, b = dev(p)
+    ws = sk.alloc_workspace(X, Y)
+    sk.init_norms(X, Y, a, b, ws)
+    g = torch.from_numpy(random_potential((1, p.m), 5)).cuda()
+    f1 = sk.half_step_f(X, Y, ws, g, 0.07).clone()
+    f2 = sk.half_step_f(X, Y, ws, g, 0.07).clone()
+    # g half-step of the swapped problem (Y as sources) == f half-step of the original
+    ws2 = sk.alloc_workspace(Y, X)
+    sk.init_norms(Y, X, b, a, ws2)
+    f3 = sk.half_step_g(Y, X, ws2, g, 0.07)
+    torch.cuda.synchronize()
+    assert torch.equal(f1, f2)
+    assert torch.equal(f1, f3)
+
+
+def test_resume_equals_uninterrupted():
+    p = make_case(800, 700, 3, seed=6, weights="softmax")
+    X, Y, a, b = dev(p)
+    f, g = sk.solve(X, Y, a, b, 0.05, 30)
+    f2, g2 = sk.solve(X, Y, a, b, 0.05, 18)
+    f2, g2 = sk.solve(X, Y, a, b, 0.05, 12, f=f2, g=g2)
+    torch.cuda.synchronize()
+    assert torch.equal(f, f2) and torch.equal(g, g2)
+
+
+def test_batched_equals_single_problems():
+    p = make_case(500, 600, 8, batch=6, seed=7)
+    X, Y, a, b = dev(p)
+    f, g = sk.solve(X, Y, a, b, 0.1, 8)
+    for k in range(6):
+        fk, gk = sk.solve(X[k:k + 1].contiguous(), Y[k:k + 1].contiguous(), a[k:k + 1].contiguous(),
+                          b[k:k + 1].contiguous(), 0.1, 8)
+        torch.cuda.synchronize()
+        ref = oracle.solve(p.X[k], p.Y[k], p.a[k], p.b[k], 0.1, 8)
+        check(fk[0].cpu().numpy(), f[k].cpu().numpy().astype(np.float64), tol(p, 0.1, ref[0]), "batched f")
+        check(gk[0].cpu().numpy(), g[k].cpu().numpy().astype(np.float64), tol(p, 0.1, ref[1]), "batched g")
+
+
+def test_annealed_schedule_matches_oracle():
+    p = make_case(700, 500, 3, seed=8, weights="softmax")
+    sched = (1.0 * (0.02 / 1.0) ** (np.arange(12) / 11)).astype(np.float32)
+    X, Y, a, b = dev(p)
+    f, g = sk.solve(X, Y, a, b, sched.tolist(), 12)
+    torch.cuda.synchronize()
+    rf, rg = oracle.solve(p.X[0], p.Y[0], p.a[0], p.b[0], sched.astype(np.float64), 12)
+    check(f[0].cpu().numpy(), rf, tol(p, float(sched[-1]), rf), "annealed f")
+    check(g[0].cpu().numpy(), rg, tol(p, float(sched[-1]), rg), "annealed g")
+
+
+def test_marginal_error_matches_oracle_plan():
+    p = make_case(400, 300, 3, seed=9, weights="softmax")
+    eps = 0.1
+    X, Y, a, b = dev(p)
+    ws = sk.alloc_workspace(X, Y)
+    f, g = sk.solve(X, Y, a, b, eps, 5, ws=ws)
+    err = sk.marginal_error(X, Y, ws, f, g, eps)
+    torch.cuda.synchronize()
+    fn, gn = f[0].cpu().numpy().astype(np.float64), g[0].cpu().numpy().astype(np.float64)
+    ra, cb = oracle.marginal_error(p.X[0], p.Y[0], p.a[0], p.b[0], fn, gn, eps)
+    e = err.cpu().numpy()[0]
+    # after a g half-step the columns match b up to fp32 rounding; rows carry the real error
+    assert abs(e[0] - ra) <= 1e-3 * ra + 2e-5, (e, ra)
+    assert e[1] <= 2e-5 and cb <= 1e-5, (e, cb)
+
+
+def test_zero_weight_point_is_removed():
+    p = make_case(300, 200, 3, seed=10, weights="softmax")
+    b = p.b.copy()
+    b[0, 17] = 0.0
+    X, Y, a, _ = dev(p)
+    bt = torch.from_numpy(b).cuda()
+    ws = sk.alloc_workspace(X, Y)
+    sk.init_norms(X, Y, a, bt, ws)
+    g = random_potential((1, 200), 10)
+    f = sk.half_step_f(X, Y, ws, torch.from_numpy(g).cuda(), 0.05)
+    torch.cuda.synchronize()
+    ref = oracle.half_step_f(p.X[0], p.Y[0], b[0], g[0], 0.05)
+    check(f[0].cpu().numpy(), ref, tol(p, 0.05, ref), "zero-weight f")
+
+
+def test_large_dynamic_range_forces_offset_moves():
+    # scores spanning thousands of base-2 units: the lazy offset must move many times
+    p = make_case(333, 2000, 2, seed=11, weights="softmax", dist="cube", scale=8.0)
+    half_steps(p, 0.01, seed=11, scale=5.0)
