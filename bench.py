@@ -1,0 +1,245 @@
+"""Benchmark: Sinkhorn iterations/s on one MI355X, with roofline and CPU-baseline legs.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+
+A step is one full Sinkhorn iteration (f half-step then g half-step) over the
+workload, inputs resident in HBM.  The default workload is n = m = 70000,
+d = 3, fp32, eps = 0.01 (X uniform in the unit cube, Y an 8-Gaussian
+mixture), the scale the FlashSinkhorn summary calls the pain point (page
+"FlashSinkhorn: IO-aware entropic OT on GPU", Problem statement).
+
+Prints ONE JSON line.  `roofline` covers the dominant kernel (the streaming
+half-step kernel k_lse): its launch duration is measured with HIP events on
+the stream the library launches on, around each half-step call (the window
+also holds the small key-preparation and split-merge kernels; the rocprofv3
+summary under profiles/ separates them).  `cpu_baseline` times the fp64 CPU
+oracle on a bounded row slice of the same workload on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Sinkhorn iters/sec & effective TFLOP/s at n=m=70000, fraction of roofline"
+
+# MI355X peaks (AMD published figures; exp rate derived from unit counts and clock)
+CLOCK_HZ = 2.4e9
+N_CU = 256
+PEAK_EXP_PER_S = N_CU * 4 * 8 * CLOCK_HZ       # 8 transcendental lanes/clk per SIMD, 4 SIMDs per CU
+PEAK_MFMA = {"bf16": 2516.6e12, "fp32": 157.3e12}
+PEAK_HBM = 8.0e12
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: n=m=70000, d=3)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0, help="target wall time of the CPU leg")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB mebibytes (scales rocprofv3 byte counters)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    src = os.path.join(ROOT, "log_domain_sinkhorn_half_amd", "csrc", "sinkhorn.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """Measured HBM bytes per launch from the committed rocprofv3 --pmc summary, or None
+    if there is none or it was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        line = line.strip().lstrip("-* ")
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+              "the multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
+        return
+
+    from log_domain_sinkhorn_half_amd import binding as sk
+    from log_domain_sinkhorn_half_amd.inputs import make_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    sk.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    p = make_config(args.config)
+    B, n, m, d = p.batch, p.n, p.m, p.d
+    if p.dtype == "bf16":
+        X = torch.from_numpy(p.X_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        Y = torch.from_numpy(p.Y_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        X = torch.from_numpy(p.X).to(dev)
+        Y = torch.from_numpy(p.Y).to(dev)
+    a = torch.from_numpy(p.a).to(dev)
+    b = torch.from_numpy(p.b).to(dev)
+    ws = sk.alloc_workspace(X, Y)
+    f = torch.zeros((B, n), dtype=torch.float32, device=dev)
+    g = torch.zeros((B, m), dtype=torch.float32, device=dev)
+    eps_sched = [float(e) for e in p.eps]
+
+    def eps_at(k):
+        return eps_sched[k % len(eps_sched)] if len(eps_sched) > 1 else eps_sched[0]
+
+    sk.init_norms(X, Y, a, b, ws)
+    for k in range(args.warmup):
+        sk.half_step_f(X, Y, ws, g, eps_at(k), f=f)
+        sk.half_step_g(X, Y, ws, f, eps_at(k), g=g)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for k in range(K):
+        e = eps_at(args.warmup + k)
+        sk.half_step_f(X, Y, ws, g, e, f=f)
+        ev[2 * k + 1].record(stream)
+        sk.half_step_g(X, Y, ws, f, e, g=g)
+        ev[2 * k + 2].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    half_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(2 * K)])
+    f_ms, g_ms = half_ms[0::2], half_ms[1::2]
+    assert torch.isfinite(f).all() and torch.isfinite(g).all(), "non-finite potentials"
+
+    iters_per_s = K / elapsed
+    ms_per_step = 1e3 * elapsed / K
+    elems_iter = 2.0 * B * n * m                      # score elements (= exps) per iteration
+    eff_ops_iter = 4.0 * B * n * m * d + 2.0 * B * n * m
+    eff_tflops = eff_ops_iter * iters_per_s / 1e12
+    contraction = "bf16" if p.dtype == "bf16" else "fp32"
+    t_exp = elems_iter / PEAK_EXP_PER_S
+    t_mfma = 4.0 * B * n * m * d / PEAK_MFMA[contraction]
+    bound = "alu" if t_exp >= t_mfma else "mfma"
+    t_roof = max(t_exp, t_mfma)
+    frac_iter = t_roof / (elapsed / K)
+
+    # dominant kernel: one half-step launch processes B*n*m (f) or B*m*n (g) score elements
+    launch_s = float(np.mean(half_ms)) / 1e3
+    elems_launch = B * n * m
+    workload = f"C{args.config}"
+    traffic = read_traffic("k_lse", workload)
+    if bound == "alu":
+        achieved = elems_launch / launch_s / 1e9
+        roof = {"bound": "alu", "achieved": round(achieved, 1), "peak": round(PEAK_EXP_PER_S / 1e9, 1),
+                "unit": "Gexp/s", "frac": round(achieved * 1e9 / PEAK_EXP_PER_S, 4)}
+    else:
+        achieved = 2.0 * d * elems_launch / launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA[contraction] / 1e12,
+                "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_MFMA[contraction], 4)}
+    roof["traffic"] = traffic
+    roof["launch_ms"] = round(launch_s * 1e3, 4)
+
+    out = {
+        "metric": METRIC,
+        "value": round(iters_per_s, 2),
+        "unit": "iters/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if p.dtype == "fp32" else "bf16",
+        "data": "synthetic (seeded, see DESIGN.md input recipe)",
+        "config": {"workload": f"C{args.config}: {p.name} batch={B} n={n} m={m} d={d} {p.dtype} "
+                               f"eps={eps_sched[0] if len(eps_sched) == 1 else 'schedule'}",
+                   "batch": B, "n": n, "m": m, "d": d, "parallelism": "single GPU"},
+        "effective_tflops": round(eff_tflops, 3),
+        "roofline_frac_per_iteration": round(frac_iter, 4),
+        "half_step_ms": {"f": round(float(np.mean(f_ms)), 4), "g": round(float(np.mean(g_ms)), 4)},
+        "roofline": roof,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(p, target_s: float):
+    """fp64 oracle (as it stands) on a row slice: f half-step for r rows of X against all
+    of Y, then g half-step for r rows of Y against all of X (problem 0), extrapolated to a
+    full iteration of the whole workload."""
+    import numpy as np
+
+    import oracle
+    from log_domain_sinkhorn_half_amd.inputs import random_potential
+
+    threads = len(os.sched_getaffinity(0))
+    used = oracle.threads_used(threads)
+    X, Y, a, b = (np.asarray(v[0], np.float64) for v in (p.X, p.Y, p.a, p.b))
+    g = random_potential(p.m, 99, 0.1).astype(np.float64)
+    f = random_potential(p.n, 98, 0.1).astype(np.float64)
+    eps = float(p.eps[-1])
+
+    def run(r):
+        rows_x = np.arange(min(r, p.n))
+        rows_y = np.arange(min(r, p.m))
+        t = time.perf_counter()
+        oracle.half_step_f(X, Y, b, g, eps, rows=rows_x, threads=used)
+        oracle.half_step_g(X, Y, a, f, eps, rows=rows_y, threads=used)
+        return time.perf_counter() - t, rows_x.size, rows_y.size
+
+    r = 256
+    dt, rx, ry = run(r)
+    while dt < 0.25 * target_s and (rx < p.n or ry < p.m):
+        r = int(min(max(p.n, p.m), r * max(2.0, 0.5 * target_s / max(dt, 1e-3))))
+        dt, rx, ry = run(r)
+    # work-proportional: the slice evaluated rx*m + ry*n cost terms, a full
+    # iteration of every problem evaluates 2*n*m per problem
+    t_iter = p.batch * dt * (2.0 * p.n * p.m) / (rx * p.m + ry * p.n)
+    return {"value": round(1.0 / t_iter, 6), "unit": "iters/s", "cores": used, "kind": "oracle",
+            "sample": f"one f half-step over {rx} rows of X and one g half-step over {ry} rows of Y "
+                      f"(problem 0, all {p.m}/{p.n} points on the other side), {dt:.2f} s wall, "
+                      f"extrapolated linearly to {p.batch} x ({p.n}+{p.m}) rows"}
+
+
+if __name__ == "__main__":
+    main()

@@ -49,6 +49,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 #include <utility>
 
 #include "sinkhorn.h"
@@ -122,18 +124,19 @@ constexpr u16 BF16_ONE = 0x3F80;
 // Smallest power of two q with |v| / q <= 255 (1 when v == 0).
 __device__ __forceinline__ double grid_quantum(double vmax) {
   if (!(vmax > 0.0)) return 1.0;
-  double q = exp2(ceil(log2(vmax / 255.0)));
-  while (vmax / q > 255.0) q *= 2.0;
-  return q;
+  int e;
+  const double mant = frexp(vmax / 255.0, &e);  // vmax/255 = mant * 2^e, mant in [0.5, 1)
+  return ldexp(1.0, mant == 0.5 ? e - 1 : e);
 }
 
 // Grid part and two bf16 remainder parts of v: v ~ g + r1 + r2 with g a
-// multiple of q, |v - g| <= q/2 and a residual below 2^-18 q.
+// multiple of q, |v - g| <= q/2 and a residual below 2^-18 q.  inv_q = 1/q
+// exactly (q is a power of two).
 struct Parts {
   u16 g, r1, r2;
 };
-__device__ __forceinline__ Parts grid_split(double v, double q) {
-  const double g = rint(v / q) * q;
+__device__ __forceinline__ Parts grid_split(double v, double q, double inv_q) {
+  const double g = rint(v * inv_q) * q;
   double r = v - g;
   Parts p;
   p.g = bf16_of(g);
@@ -154,16 +157,18 @@ __device__ __forceinline__ float rescale(float s, float m_old, float m_new) {
 // ---------------------------------------------------------------------------
 // Set-up kernels
 // ---------------------------------------------------------------------------
-// Largest |coordinate| of each problem's X (side 0) and Y (side 1).
+// Largest |coordinate| of each problem's X (side 0) and Y (side 1): a strided
+// block reduction, then atomicMax on the float bits (values are >= 0, so the
+// unsigned order is the float order).  maxabs must be zero beforehand.
 __global__ __launch_bounds__(256) void k_maxabs(const void* __restrict__ X, const void* __restrict__ Y, int mode,
-                                                long long nx, long long ny, float* __restrict__ maxabs,
+                                                long long nx, long long ny, unsigned* __restrict__ maxabs,
                                                 int batch) {
   __shared__ float red[256];
-  const int b = blockIdx.x, side = blockIdx.y;
+  const int b = blockIdx.y, side = blockIdx.z;
   const long long cnt = side == 0 ? nx : ny;
   const void* P = side == 0 ? X : Y;
   float mx = 0.f;
-  for (long long i = threadIdx.x; i < cnt; i += 256) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < cnt; i += (long long)gridDim.x * 256) {
     const long long k = (long long)b * cnt + i;
     const float v = mode == MODE_SPLIT ? static_cast<const float*>(P)[k] : bf16_f(static_cast<const u16*>(P)[k]);
     mx = fmaxf(mx, fabsf(v));
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(256) void k_maxabs(const void* __restrict__ X, cons
     if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
     __syncthreads();
   }
-  if (threadIdx.x == 0) maxabs[side * batch + b] = red[0];
+  if (threadIdx.x == 0) atomicMax(&maxabs[side * batch + b], __float_as_uint(red[0]));
 }
 
 // Norms (fp64), log-weights (fp64) and operand rows of one cloud: the split
@@ -210,6 +215,7 @@ __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, c
   }
   const float* src = static_cast<const float*>(P) + r * d;
   const double q = grid_quantum(maxabs[b]);
+  const double iq = 1.0 / q;
   double nrm = 0.0;
   for (int t = 0; t < d; ++t) nrm += (double)src[t] * (double)src[t];
   norm[r] = nrm;
@@ -223,9 +229,9 @@ __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, c
       if (k >= 2 && k <= 4) {
         val = BF16_ONE;
       } else if (k >= 5 && k < 5 + d) {
-        val = grid_split(src[k - 5], q).g;
+        val = grid_split(src[k - 5], q, iq).g;
       } else if (k >= cb && k < cb + 7 * d) {
-        const Parts pp = grid_split(src[(k - cb) / 7], q);
+        const Parts pp = grid_split(src[(k - cb) / 7], q, iq);
         const int s = (k - cb) % 7;
         val = (s <= 1) ? pp.g : ((s == 3 || s == 6) ? pp.r2 : pp.r1);
       } else if (k == cb + 7 * d || k == cb + 7 * d + 1) {
@@ -240,69 +246,93 @@ __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, c
 
 // Key operand rows for one half-step (fp32 inputs): v = 2*lambda*y and the bias
 // lambda*(pot - norm + eps*logw) in grid + remainder parts; writes the grid
-// quantum Q = q_query * q_key of each problem to qgrid.
+// quantum Q = q_query * q_key of each problem to qgrid.  One thread per 16-byte
+// segment of a row, so the stores are coalesced.
 __global__ __launch_bounds__(256) void k_prep_keys(const float* __restrict__ P, const float* __restrict__ pot,
                                                    const double* __restrict__ norm, const double* __restrict__ logw,
                                                    int keys, int keys_pad, int d, int KP, float lam, float eps,
                                                    const float* __restrict__ qmax, const float* __restrict__ kmax,
                                                    float* __restrict__ qgrid, u16* __restrict__ kb) {
   const int b = blockIdx.y;
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= keys_pad) return;
+  const int vpr = KP / 8;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)keys_pad * vpr) return;
+  const int j = (int)(idx / vpr), k0 = (int)(idx % vpr) * 8;
   const double lam2 = 2.0 * (double)lam;
   const double qq = grid_quantum(qmax[b]);
   const double qk = grid_quantum(lam2 * (double)kmax[b]);
   const double Q = qq * qk;
-  if (j == 0) qgrid[b] = (float)Q;
-  double bias = (double)NEG_BIG;
-  const float* src = nullptr;
-  if (j < keys) {
-    const size_t r = (size_t)b * keys + j;
-    src = P + r * d;
-    bias = (double)lam * ((double)pot[r] - norm[r] + (double)eps * logw[r]);
-    if (!(bias >= (double)NEG_BIG)) bias = (double)NEG_BIG;  // zero weight (-inf) or underflow
-  }
-  u16 b1, b2, b3, br1, br2;
-  if (bias <= (double)NEG_BIG) {
-    b1 = bf16_of(bias);
-    b2 = b3 = br1 = br2 = 0;
-  } else {
-    const double bg = rint(bias / Q) * Q;
-    b1 = bf16_of(bg);
-    b2 = bf16_of(bg - (double)bf16_f(b1));
-    b3 = bf16_of(bg - (double)bf16_f(b1) - (double)bf16_f(b2));
-    const double br = bias - bg;
-    br1 = bf16_of(br);
-    br2 = bf16_of(br - (double)bf16_f(br1));
-  }
+  const double iqk = 1.0 / qk, iQ = 1.0 / Q;
+  if (idx == 0) qgrid[b] = (float)Q;
   const int cb = split_corr_begin(d);
-  const int dd = src ? d : 0;
-  u16* dst = kb + ((size_t)b * keys_pad + j) * KP;
-  for (int k0 = 0; k0 < KP; k0 += 8) {
-    u16 v[8];
-    for (int e = 0; e < 8; ++e) {
-      const int k = k0 + e;
-      u16 val = 0;
-      if (k <= 1) {
-        val = BF16_ONE;
-      } else if (k <= 4) {
-        val = k == 2 ? b1 : (k == 3 ? b2 : b3);
-      } else if (k < 5 + dd) {
-        val = grid_split(lam2 * (double)src[k - 5], qk).g;
-      } else if (k >= cb && k < cb + 7 * dd) {
-        const Parts pp = grid_split(lam2 * (double)src[(k - cb) / 7], qk);
-        const int s = (k - cb) % 7;
-        val = (s == 2 || s == 3) ? pp.g : ((s == 1 || s == 5) ? pp.r2 : pp.r1);
-      } else if (k == cb + 7 * d) {
-        val = br1;
-      } else if (k == cb + 7 * d + 1) {
-        val = br2;
-      }
-      v[e] = val;
+  const bool real = j < keys;
+  const size_t r = (size_t)b * keys + j;
+  const float* src = P + r * d;
+  // bias parts (only for the segments that hold them)
+  u16 bp[5] = {0, 0, 0, 0, 0};
+  if ((k0 <= 4) || (k0 + 8 > cb + 7 * d && k0 <= cb + 7 * d + 1)) {
+    double bias = (double)NEG_BIG;
+    if (real) {
+      bias = (double)lam * ((double)pot[r] - norm[r] + (double)eps * logw[r]);
+      if (!(bias >= (double)NEG_BIG)) bias = (double)NEG_BIG;  // zero weight (-inf) or underflow
     }
-    *reinterpret_cast<u4*>(dst + k0) = u4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
-                                         (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
+    if (bias <= (double)NEG_BIG) {
+      bp[0] = bf16_of(bias);
+    } else {
+      const double bg = rint(bias * iQ) * Q;
+      bp[0] = bf16_of(bg);
+      bp[1] = bf16_of(bg - (double)bf16_f(bp[0]));
+      bp[2] = bf16_of(bg - (double)bf16_f(bp[0]) - (double)bf16_f(bp[1]));
+      const double br = bias - bg;
+      bp[3] = bf16_of(br);
+      bp[4] = bf16_of(br - (double)bf16_f(bp[3]));
+    }
   }
+  int tc = -1;  // coordinate whose parts are cached
+  Parts pc{0, 0, 0};
+  u16 v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = k0 + e;
+    u16 val = 0;
+    if (k <= 1) {
+      val = BF16_ONE;
+    } else if (k <= 4) {
+      val = bp[k - 2];
+    } else if (k < 5 + d) {
+      if (real) {
+        if (tc != k - 5) {
+          tc = k - 5;
+          pc = grid_split(lam2 * (double)src[tc], qk, iqk);
+        }
+        val = pc.g;
+      }
+    } else if (k >= cb && k < cb + 7 * d) {
+      if (real) {
+        const int t = (k - cb) / 7, sl = (k - cb) % 7;
+        if (tc != t) {
+          tc = t;
+          pc = grid_split(lam2 * (double)src[t], qk, iqk);
+        }
+        // key side of the corrections: v_1 v_2 v_g v_g v_1 v_2 v_1
+        val = (sl == 2 || sl == 3) ? pc.g : ((sl == 1 || sl == 5) ? pc.r2 : pc.r1);
+      }
+    } else if (k == cb + 7 * d) {
+      val = bp[3];
+    } else if (k == cb + 7 * d + 1) {
+      val = bp[4];
+    }
+    v[e] = val;
+  }
+  *reinterpret_cast<u4*>(kb + ((size_t)b * keys_pad + j) * KP + k0) =
+      u4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
+         (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
+}
+
+// Zero-fill n 16-byte words (used instead of a memset so callers may capture it).
+__global__ __launch_bounds__(256) void k_zero(u4* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = u4{0, 0, 0, 0};
 }
 
 // Half bias (pot - norm + eps*logw)/2 per key (bf16 inputs); padding -> -1e30.
@@ -324,9 +354,37 @@ __global__ __launch_bounds__(256) void k_prep_bias(const float* __restrict__ pot
 // ---------------------------------------------------------------------------
 // The streaming half-step kernel
 // ---------------------------------------------------------------------------
+typedef float f16v __attribute__((ext_vector_type(16)));
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Offset slots (query side, chunk 0, lane group 0, elements 0..1) <- -m as two bf16 parts.
+// MFMA tile shapes.  A = key operand (rows = keys), B = query operand (columns =
+// queries), D[key][query].  Every lane holds 8 consecutive K slots of one key
+// (A) or one query (B): lane = col + MW * grp holds slots [8*grp, 8*grp+8) of the
+// instruction's KI slots for row/column `col`.  Output element `o` of a lane is
+// D[key_of(o, grp)][col].
+template <int MW>
+struct Tile;
+template <>
+struct Tile<16> {  // v_mfma_f32_16x16x32_bf16
+  static constexpr int KI = 32, NOUT = 4;
+  using Acc = f4;
+  static __device__ __forceinline__ Acc mma(u4 a, u4 b, Acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int key_of(int o, int grp) { return 4 * grp + o; }
+};
+template <>
+struct Tile<32> {  // v_mfma_f32_32x32x16_bf16
+  static constexpr int KI = 16, NOUT = 16;
+  using Acc = f16v;
+  static __device__ __forceinline__ Acc mma(u4 a, u4 b, Acc c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int key_of(int o, int grp) { return 8 * (o / 4) + 4 * grp + (o % 4); }
+};
+
+// Offset slots (query side, instruction 0, lane group 0, elements 0..1) <- -m as two bf16 parts.
 __device__ __forceinline__ void set_offset(u4& q, float off, bool owner) {
   if (!(off <= 1e30f)) off = 1e30f;
   if (!(off >= -1e30f)) off = -1e30f;
@@ -345,36 +403,55 @@ __device__ __forceinline__ float offset_from_max(float mx, float Q) {
   return floorf(mq / quantum) * quantum;
 }
 
-template <int MODE, int NCH, int R, int TC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == MODE_SPLIT && NCH <= 3 ? 4 : 2))) void k_lse(
+// Launch shape per (path, K chunks of 32 slots): tile width MW, query tiles per
+// wave R, key tiles per LDS chunk TC.  Wide 32x32 tiles halve the MFMA count per
+// score for small K; large K keeps 16x16 tiles so the query operand fits in VGPRs.
+__host__ __device__ constexpr int cfg_MW(int mode, int nch) { return (mode == MODE_BF16 || nch <= 2) ? 32 : 16; }
+__host__ __device__ constexpr int cfg_R(int mode, int nch) {
+  return cfg_MW(mode, nch) == 32 ? (nch == 1 ? 4 : 2) : (nch <= 4 ? 4 : (nch <= 8 ? 2 : 1));
+}
+__host__ __device__ constexpr int cfg_TC(int mode, int nch) {
+  return cfg_MW(mode, nch) == 32 ? (nch <= 2 ? 2 : 1) : 1;
+}
+__host__ __device__ constexpr int cfg_waves(int mode, int nch) { return (mode == MODE_SPLIT && nch == 1) ? 3 : 2; }
+
+template <int MODE, int NCH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(MODE, NCH)))) void k_lse(
     const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb,
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, float* __restrict__ out,
     float2* __restrict__ part, int rows, int rows_pad, int keys, int keys_pad, int chunks_per_split, int batch,
     float lam2, double inv_lam) {
+  constexpr int MW = cfg_MW(MODE, NCH), R = cfg_R(MODE, NCH), TC = cfg_TC(MODE, NCH);
+  using T = Tile<MW>;
+  using Acc = typename T::Acc;
   constexpr int KP = NCH * 32;
-  constexpr int LROW = KP + 8;  // LDS row stride in elements (16-byte pad against bank conflicts)
-  constexpr int CK = TC * 16;   // keys per chunk
-  constexpr int VPR = KP / 8;   // 16-byte vectors per key row
+  constexpr int NI = KP / T::KI;   // MFMA instructions per tile
+  constexpr int NO = T::NOUT;      // outputs per lane per tile
+  constexpr int LROW = KP + 8;     // LDS row stride in elements (16-byte pad against bank conflicts)
+  constexpr int CK = TC * MW;      // keys per chunk
+  constexpr int VPR = KP / 8;      // 16-byte vectors per key row
   constexpr int NVEC = CK * VPR;
   constexpr int NLD = (NVEC + 255) / 256;
+  constexpr int QPW = R * MW;      // queries per wave
   // One spare row per buffer takes the stores of threads past the end of a chunk.
   __shared__ __attribute__((aligned(16))) u16 lds[2][(CK + 1) * LROW];
   __shared__ __attribute__((aligned(16))) float ldsb[2][CK];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane / MW, col = lane % MW;
   const int b = blockIdx.z;
-  const int qbase = blockIdx.x * (64 * R) + wave * (16 * R);
+  const int qbase = blockIdx.x * (4 * QPW) + wave * QPW;
   const u16* Qb = Q + (size_t)b * rows_pad * KP;
   const u16* Kb = K + (size_t)b * keys_pad * KP;
   const float* hbb = (MODE == MODE_BF16) ? hb + (size_t)b * keys_pad : nullptr;
   const float qg = (MODE == MODE_SPLIT) ? qgrid[b] : 1.f;
 
-  u4 bq[R][NCH];
+  u4 bq[R][NI];
 #pragma unroll
   for (int c = 0; c < R; ++c)
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch)
-      bq[c][ch] = *reinterpret_cast<const u4*>(Qb + (size_t)(qbase + 16 * c + col) * KP + ch * 32 + grp * 8);
+    for (int i = 0; i < NI; ++i)
+      bq[c][i] = *reinterpret_cast<const u4*>(Qb + (size_t)(qbase + MW * c + col) * KP + i * T::KI + grp * 8);
 
   const int total_chunks = (keys + CK - 1) / CK;
   const int c0 = blockIdx.y * chunks_per_split;
@@ -406,17 +483,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == MOD
     if (MODE == MODE_BF16 && tid < CK / 4) *reinterpret_cast<f4*>(&ldsb[buf][tid * 4]) = preb;
   };
   // Scores of key tile t of the chunk in buffer buf against the R query tiles.
-  auto tile = [&](int buf, int t, f4 (&acc)[R]) {
-    f4 cinit = {0.f, 0.f, 0.f, 0.f};
-    if (MODE == MODE_BF16) cinit = *reinterpret_cast<const f4*>(&ldsb[buf][t * 16 + grp * 4]);
+  auto tile = [&](int buf, int t, Acc (&acc)[R]) {
+    Acc cinit;
+#pragma unroll
+    for (int o = 0; o < NO; ++o) cinit[o] = 0.f;
+    if (MODE == MODE_BF16) {
+#pragma unroll
+      for (int o = 0; o < NO; o += 4) {
+        const f4 v = *reinterpret_cast<const f4*>(&ldsb[buf][t * MW + T::key_of(o, grp)]);
+        cinit[o] = v[0];
+        cinit[o + 1] = v[1];
+        cinit[o + 2] = v[2];
+        cinit[o + 3] = v[3];
+      }
+    }
 #pragma unroll
     for (int c = 0; c < R; ++c) acc[c] = cinit;
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      const u4 ka = *reinterpret_cast<const u4*>(&lds[buf][(t * 16 + col) * LROW + ch * 32 + grp * 8]);
+    for (int i = 0; i < NI; ++i) {
+      const u4 ka = *reinterpret_cast<const u4*>(&lds[buf][(t * MW + col) * LROW + i * T::KI + grp * 8]);
 #pragma unroll
-      for (int c = 0; c < R; ++c)
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(bq[c][ch]), acc[c], 0, 0, 0);
+      for (int c = 0; c < R; ++c) acc[c] = T::mma(ka, bq[c][i], acc[c]);
     }
   };
   // Base-2 exponent of a score relative to the current offset.
@@ -428,11 +515,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == MOD
     if (MODE == MODE_BF16) return v * lam2;
     return v;
   };
+  auto accumulate = [&](const Acc (&acc)[R]) {
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+      for (int o = 0; o < NO; o += 4) {
+        t0 += __builtin_amdgcn_exp2f(expo(acc[c][o], c)) + __builtin_amdgcn_exp2f(expo(acc[c][o + 1], c));
+        t1 += __builtin_amdgcn_exp2f(expo(acc[c][o + 2], c)) + __builtin_amdgcn_exp2f(expo(acc[c][o + 3], c));
+      }
+      s[c] += t0 + t1;
+    }
+  };
+  // combine a value over the lanes that hold the same query
+  auto lanes_max = [&](float v) {
+#pragma unroll
+    for (int w = MW; w < 64; w *= 2) v = fmaxf(v, __shfl_xor(v, w));
+    return v;
+  };
+  auto lanes_sum = [&](float v) {
+#pragma unroll
+    for (int w = MW; w < 64; w *= 2) v += __shfl_xor(v, w);
+    return v;
+  };
 
   if (c0 < c1) {
-    gload(c0);
-    lstore(0);
-  }
+  gload(c0);
+  lstore(0);
+  __builtin_amdgcn_s_waitcnt(0);  // query operands and the first chunk have landed
   __syncthreads();
 
   for (int ci = c0; ci < c1; ++ci) {
@@ -447,16 +557,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == MOD
     if (!redo) {
 #pragma unroll 1
       for (int t = 0; t < TC; ++t) {
-        f4 acc[R];
+        Acc acc[R];
         tile(buf, t, acc);
-#pragma unroll
-        for (int c = 0; c < R; ++c) {
-          const float e0 = __builtin_amdgcn_exp2f(expo(acc[c][0], c));
-          const float e1 = __builtin_amdgcn_exp2f(expo(acc[c][1], c));
-          const float e2 = __builtin_amdgcn_exp2f(expo(acc[c][2], c));
-          const float e3 = __builtin_amdgcn_exp2f(expo(acc[c][3], c));
-          s[c] += (e0 + e1) + (e2 + e3);
-        }
+        accumulate(acc);
       }
       int bad = 0;
 #pragma unroll
@@ -477,16 +580,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == MOD
       for (int c = 0; c < R; ++c) mx[c] = -INFINITY;
 #pragma unroll 1
       for (int t = 0; t < TC; ++t) {
-        f4 acc[R];
+        Acc acc[R];
         tile(buf, t, acc);
 #pragma unroll
         for (int c = 0; c < R; ++c)
-          mx[c] = fmaxf(fmaxf(fmaxf(mx[c], raw(acc[c][0])), fmaxf(raw(acc[c][1]), raw(acc[c][2]))), raw(acc[c][3]));
+#pragma unroll
+          for (int o = 0; o < NO; ++o) mx[c] = fmaxf(mx[c], raw(acc[c][o]));
       }
 #pragma unroll
       for (int c = 0; c < R; ++c) {
-        mx[c] = fmaxf(mx[c], __shfl_xor(mx[c], 16));
-        mx[c] = fmaxf(mx[c], __shfl_xor(mx[c], 32));
+        mx[c] = lanes_max(mx[c]);
         const float mn = fmaxf(m[c], offset_from_max(mx[c], qg));
         s[c] = rescale(s[c], m[c], mn);
         m[c] = mn;
@@ -494,27 +597,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == MOD
       }
 #pragma unroll 1
       for (int t = 0; t < TC; ++t) {
-        f4 acc[R];
+        Acc acc[R];
         tile(buf, t, acc);
-#pragma unroll
-        for (int c = 0; c < R; ++c) {
-          const float e0 = __builtin_amdgcn_exp2f(expo(acc[c][0], c));
-          const float e1 = __builtin_amdgcn_exp2f(expo(acc[c][1], c));
-          const float e2 = __builtin_amdgcn_exp2f(expo(acc[c][2], c));
-          const float e3 = __builtin_amdgcn_exp2f(expo(acc[c][3], c));
-          s[c] += (e0 + e1) + (e2 + e3);
-        }
+        accumulate(acc);
       }
     }
     if (ci + 1 < c1) lstore(buf ^ 1);
     __syncthreads();
   }
 
+  }  // c0 < c1 (an empty key range leaves m = -FLT_MAX, s = 0: a neutral partial)
+
 #pragma unroll
   for (int c = 0; c < R; ++c) {
-    float st = s[c] + __shfl_xor(s[c], 16);
-    st += __shfl_xor(st, 32);
-    const int q = qbase + 16 * c + col;
+    const float st = lanes_sum(s[c]);
+    const int q = qbase + MW * c + col;
     if (grp == 0 && q < rows) {
       const size_t r = (size_t)b * rows + q;
       if (part != nullptr) {
@@ -526,18 +623,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == MOD
   }
 }
 
-// Merge the (max, sum) pairs of the key splits and write the potential.
-__global__ __launch_bounds__(256) void k_finalize(const float2* __restrict__ part, int ks, int total,
-                                                  const double* __restrict__ qnorm, float* __restrict__ out,
-                                                  double inv_lam) {
+// Merge the (max, sum) pairs of the key splits (one pass, exact power-of-two
+// rescaling) and write the potential.
+__global__ __launch_bounds__(256) void k_merge(const float2* __restrict__ part, int ks, int total,
+                                               const double* __restrict__ qnorm, float* __restrict__ out,
+                                               double inv_lam) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
-  float M = -FLT_MAX;
-  for (int k = 0; k < ks; ++k) M = fmaxf(M, part[(size_t)k * total + i].x);
-  float S = 0.f;
+  float M = -FLT_MAX, S = 0.f;
   for (int k = 0; k < ks; ++k) {
     const float2 v = part[(size_t)k * total + i];
-    S += rescale(v.y, v.x, M);
+    if (v.x > M) {
+      S = rescale(S, M, v.x) + v.y;
+      M = v.x;
+    } else {
+      S += rescale(v.y, v.x, M);
+    }
   }
   out[i] = (float)(qnorm[i] - ((double)M + log2((double)S)) * inv_lam);
 }
@@ -625,7 +726,7 @@ Layout layout_of(const sk_problem* p) {
   L.yn = take(8 * B * m);
   L.la = take(8 * B * n);
   L.lb = take(8 * B * m);
-  L.maxabs = take(4 * 2 * B);
+  L.maxabs = take(align_up(4 * 2 * B, 16));
   L.qgrid = take(4 * B);
   // SLACK extra rows after each operand buffer absorb the kernels' unguarded
   // over-reads at the end of the last chunk.
@@ -639,18 +740,13 @@ Layout layout_of(const sk_problem* p) {
   return L;
 }
 
-// Query tiles per wave (R) and key tiles per LDS chunk (TC) for NCH K-chunks of 32:
-// small K keeps many query tiles in VGPRs; large K trades them for operand registers.
-constexpr int cfg_R(int nch) { return nch == 1 ? 8 : (nch <= 4 ? 4 : (nch <= 8 ? 2 : 1)); }
-constexpr int cfg_TC(int nch) { return nch == 1 ? 4 : (nch == 2 ? 2 : 1); }
-
 using LseFn = void (*)(const u16*, const u16*, const float*, const float*, const double*, float*, float2*, int, int,
                        int, int, int, int, float, double);
 
 template <int MODE, int NCH>
 LseFn lse_fn() {
   if constexpr ((MODE == MODE_SPLIT && NCH <= MAX_NCH_SPLIT) || (MODE == MODE_BF16 && NCH <= MAX_NCH_BF16))
-    return &k_lse<MODE, NCH, cfg_R(NCH), cfg_TC(NCH)>;
+    return &k_lse<MODE, NCH>;
   else
     return nullptr;
 }
@@ -689,6 +785,61 @@ sk_status check_ws(const sk_problem* p, void* ws, size_t ws_bytes, Layout* L) {
   return SK_OK;
 }
 
+// Workgroups of `fn` that the current device holds at once (CUs x WGs per CU).
+sk_status resident_capacity(LseFn fn, int* out) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    set_err("hipGetDevice failed");
+    return SK_EHIP;
+  }
+  const auto key = std::make_pair(dev, reinterpret_cast<const void*>(fn));
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) {
+    *out = it->second;
+    return SK_OK;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), 256, 0) !=
+          hipSuccess) {
+    set_err("occupancy query failed");
+    return SK_EHIP;
+  }
+  *out = cache[key] = std::max(1, cus * std::max(1, per_cu));
+  return SK_OK;
+}
+
+// Number of key splits ks (and chunks per split) for `rowgroups` row-block
+// workgroups: every split does nearly the same work, and rowgroups*ks is chosen
+// to fill whole waves of the `capacity` resident slots, so no round of
+// workgroups runs nearly empty at the end of the kernel.
+int choose_key_splits(int rowgroups, int total_chunks, int capacity, int* cps_out) {
+  const int kmax = std::max(1, std::min(KS_MAX, total_chunks / 2));
+  // busy fraction of the resident slots x balance of the split sizes; the
+  // fewest splits within 2% of the best (each split adds merge traffic)
+  auto score = [&](int ks) {
+    const int cps = (total_chunks + ks - 1) / ks;
+    const int ks_eff = (total_chunks + cps - 1) / cps;
+    const double wgs = (double)rowgroups * ks_eff;
+    const double rounds = std::ceil(wgs / capacity);
+    return (wgs / (rounds * capacity)) * ((double)total_chunks / ((double)ks_eff * cps));
+  };
+  double best_score = 0.0;
+  for (int ks = 1; ks <= kmax; ++ks) best_score = std::max(best_score, score(ks));
+  int best = kmax;
+  for (int ks = 1; ks <= kmax; ++ks)
+    if (score(ks) >= 0.98 * best_score) {
+      best = ks;
+      break;
+    }
+  const int cps = (total_chunks + best - 1) / best;
+  *cps_out = cps;
+  return (total_chunks + cps - 1) / cps;
+}
+
 bool eps_ok(float eps) { return eps > 0.f && isfinite(eps) && isfinite((float)(LOG2E / eps)); }
 
 // One half-step.  side 0: f from g (queries X, keys Y); side 1: g from f.
@@ -708,15 +859,17 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   const u16* Qop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qx : L.qy));
   const void* Kraw = side == 0 ? Y : X;
   const int nch = L.KP / 32;
-  const int cfR = cfg_R(nch), cfTC = cfg_TC(nch);
+  const int cfMW = cfg_MW(L.mode, nch), cfR = cfg_R(L.mode, nch), cfTC = cfg_TC(L.mode, nch);
   const float lam = (float)(LOG2E / (double)eps);
 
+  sk_status st = SK_OK;
   const u16* Kop;
   const float* hb = nullptr;
   const dim3 pgrid((keys_pad + 255) / 256, B);
   if (L.mode == MODE_SPLIT) {
     u16* kb = reinterpret_cast<u16*>(w + L.kb);
-    hipLaunchKernelGGL(k_prep_keys, pgrid, dim3(256), 0, stream, static_cast<const float*>(Kraw), pot_in, knorm,
+    const dim3 kgrid((unsigned)(((long long)keys_pad * (L.KP / 8) + 255) / 256), B);
+    hipLaunchKernelGGL(k_prep_keys, kgrid, dim3(256), 0, stream, static_cast<const float*>(Kraw), pot_in, knorm,
                        klogw, keys, keys_pad, (int)p->d, L.KP, lam, eps, maxabs + (side == 0 ? 0 : B),
                        maxabs + (side == 0 ? B : 0), qgrid, kb);
     Kop = kb;
@@ -726,36 +879,32 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
     hb = hbw;
     Kop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qy : L.qx));
   }
-  sk_status st = hip_check("key preparation launch");
+  st = hip_check("key preparation launch");
   if (st != SK_OK) return st;
-
-  const int wg_x = (rows + 64 * cfR - 1) / (64 * cfR);
-  const int CK = cfTC * 16;
-  const int total_chunks = (keys + CK - 1) / CK;
-  const int target = 2048;
-  int ks = (target + wg_x * B - 1) / (wg_x * B);
-  ks = std::max(1, std::min(ks, std::min(KS_MAX, total_chunks / 2)));
-  const int cps = (total_chunks + ks - 1) / ks;
-  ks = (total_chunks + cps - 1) / cps;
 
   LseFn fn = (L.mode == MODE_SPLIT) ? lse_lookup<MODE_SPLIT>(nch) : lse_lookup<MODE_BF16>(nch);
   if (fn == nullptr) {
     set_err("no kernel for %d K chunks", nch);
     return SK_EUNSUPPORTED;
   }
+  const int wg_x = (rows + 4 * cfR * cfMW - 1) / (4 * cfR * cfMW);
+  const int CK = cfTC * cfMW;
+  const int total_chunks = (keys + CK - 1) / CK;
+  int capacity = 0;
+  st = resident_capacity(fn, &capacity);
+  if (st != SK_OK) return st;
+  int cps = 0;
+  const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps);
   float2* part = ks > 1 ? reinterpret_cast<float2*>(w + L.part) : nullptr;
   const double inv_lam = 1.0 / (double)lam;
   hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, qgrid, qnorm, pot_out, part, rows,
                      rows_pad, keys, keys_pad, cps, B, 2.f * lam, inv_lam);
   st = hip_check("half-step kernel launch");
-  if (st != SK_OK) return st;
-  if (ks > 1) {
-    const int total = B * rows;
-    hipLaunchKernelGGL(k_finalize, dim3((total + 255) / 256), dim3(256), 0, stream, part, ks, total, qnorm,
-                       pot_out, inv_lam);
-    st = hip_check("merge kernel launch");
-  }
-  return st;
+  if (st != SK_OK || ks == 1) return st;
+  const int total = B * rows;
+  hipLaunchKernelGGL(k_merge, dim3((total + 255) / 256), dim3(256), 0, stream, part, ks, total, qnorm, pot_out,
+                     inv_lam);
+  return hip_check("split merge launch");
 }
 
 sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const float* a, const float* b, void* ws,
@@ -763,8 +912,16 @@ sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const flo
   char* w = static_cast<char*>(ws);
   const int B = (int)p->batch;
   float* maxabs = reinterpret_cast<float*>(w + L.maxabs);
-  hipLaunchKernelGGL(k_maxabs, dim3(B, 2), dim3(256), 0, stream, X, Y, L.mode, (long long)(p->n * p->d),
-                     (long long)(p->m * p->d), maxabs, B);
+  auto zero = [&](size_t off, size_t bytes) {
+    const size_t n16 = bytes / 16;
+    if (n16) hipLaunchKernelGGL(k_zero, dim3((unsigned)std::min<size_t>((n16 + 255) / 256, 4096)), dim3(256), 0,
+                                stream, reinterpret_cast<u4*>(w + off), n16);
+  };
+  zero(L.maxabs, align_up(8 * (size_t)B, 16));
+  const long long most = std::max(p->n, p->m) * p->d;
+  const unsigned mblocks = (unsigned)std::min<long long>((most + 255) / 256, 64);
+  hipLaunchKernelGGL(k_maxabs, dim3(mblocks, B, 2), dim3(256), 0, stream, X, Y, L.mode, (long long)(p->n * p->d),
+                     (long long)(p->m * p->d), reinterpret_cast<unsigned*>(maxabs), B);
   auto side = [&](const void* P, const float* wt, int rows, int rows_pad, const float* mabs, size_t norm,
                   size_t logw, size_t op) {
     const dim3 grid((rows_pad + 255) / 256, B);

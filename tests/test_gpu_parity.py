@@ -270,3 +270,32 @@ def test_large_dynamic_range_forces_offset_moves():
     # scores spanning thousands of base-2 units: the lazy offset must move many times
     p = make_case(333, 2000, 2, seed=11, weights="softmax", dist="cube", scale=8.0)
     half_steps(p, 0.01, seed=11, scale=5.0)
+
+
+# ---------------------------------------------------------------------------
+# full-size trajectories at sampled indices (fixtures written by
+# tests/golden/make_golden.py from the oracle alone)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_full_trajectory_against_golden_samples(cfg):
+    import hashlib
+    import json
+    import os
+
+    path = os.path.join(os.path.dirname(__file__), "golden", f"trajectory_config{cfg}.json")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated (python tests/golden/make_golden.py {cfg})")
+    gold = json.load(open(path))
+    p = make_config(cfg)
+    h = hashlib.sha256()
+    for arr in (p.X, p.Y, p.a, p.b, p.eps):
+        h.update(np.ascontiguousarray(arr).tobytes())
+    assert h.hexdigest()[:16] == gold["inputs_sha256_16"], "inputs changed since the fixture was written"
+    f, g = gpu_solve(p)
+    e = float(p.eps[-1])
+    rf = np.array(gold["f"])
+    rg = np.array(gold["g"])
+    bf = 1e-3 * e + 1e-5 * gold["f_absmax"]
+    bg = 1e-3 * e + 1e-5 * gold["g_absmax"]
+    check(f[0][gold["f_index"]], rf, bf, f"C{cfg} f trajectory")
+    check(g[0][gold["g_index"]], rg, bg, f"C{cfg} g trajectory")
