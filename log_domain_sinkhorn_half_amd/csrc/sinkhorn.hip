@@ -406,12 +406,17 @@ __device__ __forceinline__ float offset_from_max(float mx, float Q) {
 // Launch shape per (path, K chunks of 32 slots): tile width MW, query tiles per
 // wave R, key tiles per LDS chunk TC.  Wide 32x32 tiles halve the MFMA count per
 // score for small K; large K keeps 16x16 tiles so the query operand fits in VGPRs.
+// For 12..19 chunks two query tiles per wave and two key tiles per chunk halve
+// the LDS operand reads per score while two workgroups still fit a CU's LDS.
+__host__ __device__ constexpr bool cfg_wide_k(int mode, int nch) { return mode == MODE_SPLIT && nch >= 12 && nch <= 19; }
 __host__ __device__ constexpr int cfg_MW(int mode, int nch) { return (mode == MODE_BF16 || nch <= 2) ? 32 : 16; }
 __host__ __device__ constexpr int cfg_R(int mode, int nch) {
-  return cfg_MW(mode, nch) == 32 ? (nch == 1 ? 4 : 2) : (nch <= 4 ? 4 : (nch <= 8 ? 2 : 1));
+  return cfg_MW(mode, nch) == 32 ? (nch == 1 ? 4 : 2)
+                                 : (nch <= 4 ? 4 : (nch <= 8 ? 2 : (cfg_wide_k(mode, nch) ? 2 : 1)));
 }
 __host__ __device__ constexpr int cfg_TC(int mode, int nch) {
-  return cfg_MW(mode, nch) == 32 ? (nch <= 2 ? 2 : 1) : 1;
+  return (mode == MODE_SPLIT && nch == 1) ? 4
+                                          : (cfg_MW(mode, nch) == 32 ? (nch <= 2 ? 2 : 1) : (cfg_wide_k(mode, nch) ? 2 : 1));
 }
 __host__ __device__ constexpr int cfg_waves(int mode, int nch) { return (mode == MODE_SPLIT && nch == 1) ? 3 : 2; }
 
@@ -433,6 +438,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
   constexpr int NVEC = CK * VPR;
   constexpr int NLD = (NVEC + 255) / 256;
   constexpr int QPW = R * MW;      // queries per wave
+  static_assert(CK % 4 == 0 && CK / 4 <= 256, "one 4-key bias vector per thread");
   // One spare row per buffer takes the stores of threads past the end of a chunk.
   __shared__ __attribute__((aligned(16))) u16 lds[2][(CK + 1) * LROW];
   __shared__ __attribute__((aligned(16))) float ldsb[2][CK];
@@ -472,7 +478,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
     const u16* src = Kb + (size_t)chunk * CK * KP;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) pre[i] = *reinterpret_cast<const u4*>(src + (size_t)(tid + 256 * i) * 8);
-    if (MODE == MODE_BF16) preb = *reinterpret_cast<const f4*>(hbb + (size_t)chunk * CK + (tid & 15) * 4);
+    if (MODE == MODE_BF16) preb = *reinterpret_cast<const f4*>(hbb + (size_t)chunk * CK + (tid % (CK / 4)) * 4);
   };
   auto lstore = [&](int buf) {
 #pragma unroll
@@ -515,16 +521,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
     if (MODE == MODE_BF16) return v * lam2;
     return v;
   };
+  // s += sum of exp2 over a lane's outputs: NO exps and NO adds (pairwise tree).
   auto accumulate = [&](const Acc (&acc)[R]) {
 #pragma unroll
     for (int c = 0; c < R; ++c) {
-      float t0 = 0.f, t1 = 0.f;
+      float e[NO];
 #pragma unroll
-      for (int o = 0; o < NO; o += 4) {
-        t0 += __builtin_amdgcn_exp2f(expo(acc[c][o], c)) + __builtin_amdgcn_exp2f(expo(acc[c][o + 1], c));
-        t1 += __builtin_amdgcn_exp2f(expo(acc[c][o + 2], c)) + __builtin_amdgcn_exp2f(expo(acc[c][o + 3], c));
-      }
-      s[c] += t0 + t1;
+      for (int o = 0; o < NO; ++o) e[o] = __builtin_amdgcn_exp2f(expo(acc[c][o], c));
+#pragma unroll
+      for (int w = 1; w < NO; w *= 2)
+#pragma unroll
+        for (int o = 0; o + w < NO; o += 2 * w) e[o] += e[o + w];
+      s[c] += e[0];
     }
   };
   // combine a value over the lanes that hold the same query
