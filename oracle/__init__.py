@@ -19,6 +19,10 @@ Parity status of each function:
   solve            : pinned (gauge shift, dual ascent, eps->0 assignment limit,
                      invariances, fixed points of the closed forms)
   plan_marginals   : pinned (closed forms; numpy brute force in the tests)
+  transport / transport_x / transport_y : pinned (m=1 closed form, large-eps
+      weighted mean, eps->0 assignment limit, finite differences of the
+      converged dual value, translation balance of the two gradients,
+      numpy brute force on tiny inputs)
 """
 
 from __future__ import annotations
@@ -67,6 +71,10 @@ def _load():
     lib.oracle_plan_marginals.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _D, _D,
                                           _D, _D, _D, _D, ctypes.c_double, _D, _D, ctypes.c_int]
     lib.oracle_plan_marginals.restype = None
+    lib.oracle_transport.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _D, _D, _D, _D,
+                                     _D, _D, ctypes.c_double, _I64, ctypes.c_int64, _D, _D, _D,
+                                     ctypes.c_int]
+    lib.oracle_transport.restype = None
     _lib = lib
     return lib
 
@@ -160,3 +168,43 @@ def marginal_error(X, Y, a, b, f, g, eps: float, threads: Optional[int] = None):
     """L1 deviations (sum_i |row_i - a_i|, sum_j |col_j - b_j|) of the plan's marginals."""
     row, col = plan_marginals(X, Y, a, b, f, g, eps, threads=threads)
     return float(np.abs(row - _f64(a)).sum()), float(np.abs(col - _f64(b)).sum())
+
+
+def transport(P, Q, wp, wq, hp, hq, eps: float, rows=None, threads: Optional[int] = None):
+    """Barycentric projection, gradient and row mass of the plan
+    pi_rj = wp_r wq_j exp((hp_r + hq_j - ||P_r - Q_j||^2)/eps) for the rows of P.
+
+    Returns (bary [k,d], grad [k,d], mass [k]) for the selected rows (all by default):
+    bary_r = sum_j pi_rj Q_j / sum_j pi_rj, grad_r = sum_j pi_rj 2 (P_r - Q_j),
+    mass_r = sum_j pi_rj.
+    """
+    lib = _load()
+    P, Q, wp, wq, hp, hq = (_f64(v) for v in (P, Q, wp, wq, hp, hq))
+    np_, d = P.shape
+    nq = Q.shape[0]
+    assert Q.shape[1] == d and wp.shape == (np_,) and hp.shape == (np_,)
+    assert wq.shape == (nq,) and hq.shape == (nq,)
+    if rows is None:
+        k, rp = np_, None
+    else:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        assert rows.ndim == 1 and (rows.size == 0 or (rows.min() >= 0 and rows.max() < np_))
+        k, rp = rows.size, rows.ctypes.data_as(_I64)
+    bary = np.empty((k, d), dtype=np.float64)
+    grad = np.empty((k, d), dtype=np.float64)
+    mass = np.empty(k, dtype=np.float64)
+    lib.oracle_transport(np_, nq, d, _ptr(P), _ptr(Q), _ptr(wp), _ptr(wq), _ptr(hp), _ptr(hq),
+                         float(eps), rp, k, _ptr(bary), _ptr(grad), _ptr(mass), int(threads or 0))
+    return bary, grad, mass
+
+
+def transport_x(X, Y, a, b, f, g, eps: float, rows=None, threads=None):
+    """Transport application for the points of X: bary_i = (P Y)_i / (P 1)_i,
+    grad_i = sum_j P_ij 2 (x_i - y_j), mass_i = (P 1)_i, P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps)."""
+    return transport(X, Y, a, b, f, g, eps, rows=rows, threads=threads)
+
+
+def transport_y(X, Y, a, b, f, g, eps: float, rows=None, threads=None):
+    """Transport application for the points of Y (the same plan read by columns):
+    bary_j = (P^T X)_j / (P^T 1)_j, grad_j = sum_i P_ij 2 (y_j - x_i), mass_j = (P^T 1)_j."""
+    return transport(Y, X, b, a, g, f, eps, rows=rows, threads=threads)

@@ -155,3 +155,62 @@ void oracle_plan_marginals(int64_t n, int64_t m, int64_t d, const double* X, con
     }
     (void)nt;
 }
+
+/*
+ * Transport application for the rows of P (page "FlashSinkhorn: IO-aware
+ * entropic OT on GPU", section "Differentiation and second-order
+ * optimisation": the barycentric projection and the gradient are weighted
+ * averages over the transport plan, evaluated without forming the plan).
+ *
+ * With the plan entries pi_rj = wp_r wq_j exp((hp_r + hq_j - C_rj)/eps):
+ *   mass[r]        = sum_j pi_rj
+ *   bary[r*d + t]  = sum_j pi_rj Q_jt / mass[r]       (barycentric projection of P_r)
+ *   grad[r*d + t]  = sum_j pi_rj * 2 (P_rt - Q_jt)    (derivative of sum_j pi_rj C_rj in P_rt,
+ *                                                      the plan held fixed)
+ * The row's largest exponent is factored out of every pi_rj (exact in exact
+ * arithmetic); each output is then the plain sum over j written above.
+ * rows: optional list of nsel row indices (NULL = all np rows).  grad and mass
+ * may be NULL.
+ */
+void oracle_transport(int64_t np_, int64_t nq, int64_t d, const double* P, const double* Q,
+                      const double* wp, const double* wq, const double* hp, const double* hq,
+                      double eps, const int64_t* rows, int64_t nsel, double* bary, double* grad,
+                      double* mass, int nthreads) {
+    if (rows == NULL) nsel = np_;
+    int nt = oracle_threads(nthreads);
+#ifdef _OPENMP
+#pragma omp parallel num_threads(nt)
+#endif
+    {
+        double* v = (double*)malloc(sizeof(double) * (size_t)(nq > 0 ? nq : 1));
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+        for (int64_t r = 0; r < nsel; ++r) {
+            int64_t i = rows ? rows[r] : r;
+            const double* p = P + i * d;
+            /* log pi_ij = log wp_i + hp_i/eps + v_j with v_j = (hq_j - C_ij)/eps + log wq_j */
+            double vmax = -INFINITY;
+            for (int64_t j = 0; j < nq; ++j) {
+                v[j] = (hq[j] - sq_dist(p, Q + j * d, d)) / eps + log(wq[j]);
+                if (v[j] > vmax) vmax = v[j];
+            }
+            double lead = log(wp[i]) + hp[i] / eps + vmax; /* pi_ij = exp(lead) * exp(v_j - vmax) */
+            double s = 0.0;
+            for (int64_t j = 0; j < nq; ++j) s += exp(v[j] - vmax);
+            for (int64_t t = 0; t < d; ++t) {
+                double num = 0.0, gr = 0.0;
+                for (int64_t j = 0; j < nq; ++j) {
+                    double pij = exp(lead + v[j] - vmax);
+                    num += exp(v[j] - vmax) * Q[j * d + t];
+                    gr += pij * 2.0 * (p[t] - Q[j * d + t]);
+                }
+                bary[r * d + t] = num / s;
+                if (grad) grad[r * d + t] = gr;
+            }
+            if (mass) mass[r] = exp(lead) * s;
+        }
+        free(v);
+    }
+    (void)nt;
+}
