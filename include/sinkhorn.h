@@ -115,6 +115,40 @@ sk_status sinkhorn_marginal_error(const sk_problem* p, const void* X, const void
                                   size_t ws_bytes, const float* f, const float* g, float eps,
                                   float* err, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Transport application (page "FlashSinkhorn: IO-aware entropic OT on GPU",
+ * section "Differentiation and second-order optimisation": the barycentric
+ * projection and the gradient are weighted averages over the transport plan,
+ * computed by the same streaming pass without forming the plan).
+ *
+ * For the plan P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps) of potentials f, g:
+ *   sinkhorn_barycentric_x:  bary_i = sum_j P_ij y_j / sum_j P_ij        [batch][n][d]
+ *                            grad_i = sum_j P_ij 2 (x_i - y_j)           [batch][n][d]
+ *                                   = 2 r_i (x_i - bary_i),  r_i = sum_j P_ij
+ *   sinkhorn_barycentric_y:  the same for the points of Y (columns of P):
+ *                            bary_j = sum_i P_ij x_i / sum_i P_ij,
+ *                            grad_j = sum_i P_ij 2 (y_j - x_i)            [batch][m][d]
+ * grad is the gradient of <P, C> in the points with the plan held fixed, which
+ * at converged potentials is the gradient of the entropic OT value (envelope
+ * theorem).  bary does not depend on the potential of its own side.
+ * bary and grad are fp32 DEVICE arrays owned by the caller; grad may be NULL.
+ * These calls need a workspace of sinkhorn_transport_workspace_bytes(p) (a
+ * superset of the solver's; every other call accepts it too) on which
+ * sinkhorn_init_norms has run.  They run one half-step internally (into
+ * workspace scratch) to fix each row's offset, then one pass over the keys.
+ * --------------------------------------------------------------------------- */
+
+/* Workspace bytes for the transport calls (0 if p is invalid). */
+size_t sinkhorn_transport_workspace_bytes(const sk_problem* p);
+
+sk_status sinkhorn_barycentric_x(const sk_problem* p, const void* X, const void* Y, void* ws,
+                                 size_t ws_bytes, const float* f, const float* g, float eps,
+                                 float* bary, float* grad, void* stream);
+
+sk_status sinkhorn_barycentric_y(const sk_problem* p, const void* X, const void* Y, void* ws,
+                                 size_t ws_bytes, const float* f, const float* g, float eps,
+                                 float* bary, float* grad, void* stream);
+
 /* Text for the last error on the calling thread ("" if none). */
 const char* sinkhorn_last_error(void);
 

@@ -24,6 +24,7 @@ STATUS = {0: "SK_OK", 1: "SK_EINVAL", 2: "SK_ESHAPE", 3: "SK_EDTYPE", 4: "SK_EHI
           5: "SK_EUNSUPPORTED", 6: "SK_EWORKSPACE"}
 EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_init_norms", "sinkhorn_half_step_f",
            "sinkhorn_half_step_g", "sinkhorn_solve", "sinkhorn_marginal_error",
+           "sinkhorn_transport_workspace_bytes", "sinkhorn_barycentric_x", "sinkhorn_barycentric_y",
            "sinkhorn_last_error")
 
 
@@ -66,6 +67,12 @@ def load_library(path: Optional[str] = None):
     lib.sinkhorn_solve.restype = ctypes.c_int
     lib.sinkhorn_marginal_error.argtypes = [P, vp, vp, vp, sz, f32p, f32p, ctypes.c_float, f32p, vp]
     lib.sinkhorn_marginal_error.restype = ctypes.c_int
+    lib.sinkhorn_transport_workspace_bytes.argtypes = [P]
+    lib.sinkhorn_transport_workspace_bytes.restype = sz
+    for name in ("sinkhorn_barycentric_x", "sinkhorn_barycentric_y"):
+        fn = getattr(lib, name)
+        fn.argtypes = [P, vp, vp, vp, sz, f32p, f32p, ctypes.c_float, f32p, f32p, vp]
+        fn.restype = ctypes.c_int
     lib.sinkhorn_last_error.argtypes = []
     lib.sinkhorn_last_error.restype = ctypes.c_char_p
     if path is None:
@@ -119,9 +126,11 @@ def workspace_bytes(batch: int, n: int, m: int, d: int, dtype: int = SK_FP32) ->
     return int(nb)
 
 
-def alloc_workspace(X: torch.Tensor, Y: torch.Tensor) -> torch.Tensor:
+def alloc_workspace(X: torch.Tensor, Y: torch.Tensor, transport: bool = False) -> torch.Tensor:
+    """Device workspace for the solver (transport=True: also for the barycentric calls)."""
     p = problem_of(X, Y)
-    nb = load_library().sinkhorn_workspace_bytes(ctypes.byref(p))
+    lib = load_library()
+    nb = (lib.sinkhorn_transport_workspace_bytes if transport else lib.sinkhorn_workspace_bytes)(ctypes.byref(p))
     if nb == 0:
         _check(1)
     return torch.empty(nb, dtype=torch.uint8, device=X.device)
@@ -181,3 +190,29 @@ def marginal_error(X, Y, ws, f, g, eps: float, err: Optional[torch.Tensor] = Non
         _dev(f, "f", torch.float32), _dev(g, "g", torch.float32), float(eps), _dev(err, "err", torch.float32),
         _stream()))
     return err
+
+
+def _barycentric(name, X, Y, ws, f, g, eps, rows, bary, grad, with_grad):
+    p = problem_of(X, Y)
+    shape = (p.batch, rows(p), p.d)
+    if bary is None:
+        bary = torch.empty(shape, dtype=torch.float32, device=X.device)
+    if grad is None and with_grad:
+        grad = torch.empty(shape, dtype=torch.float32, device=X.device)
+    _check(getattr(load_library(), name)(
+        ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(ws, "ws"), ws.numel() * ws.element_size(),
+        _dev(f, "f", torch.float32), _dev(g, "g", torch.float32), float(eps), _dev(bary, "bary", torch.float32),
+        None if grad is None else _dev(grad, "grad", torch.float32), _stream()))
+    return bary, grad
+
+
+def barycentric_x(X, Y, ws, f, g, eps: float, bary=None, grad=None, with_grad: bool = True):
+    """Barycentric projection of the points of X under the plan of (f, g), and the
+    gradient sum_j P_ij 2 (x_i - y_j).  ws must come from alloc_workspace(..., transport=True)."""
+    return _barycentric("sinkhorn_barycentric_x", X, Y, ws, f, g, eps, lambda p: p.n, bary, grad, with_grad)
+
+
+def barycentric_y(X, Y, ws, f, g, eps: float, bary=None, grad=None, with_grad: bool = True):
+    """Barycentric projection of the points of Y (columns of the plan) and the
+    gradient sum_i P_ij 2 (y_j - x_i)."""
+    return _barycentric("sinkhorn_barycentric_y", X, Y, ws, f, g, eps, lambda p: p.m, bary, grad, with_grad)

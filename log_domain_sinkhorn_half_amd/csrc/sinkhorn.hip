@@ -672,11 +672,315 @@ __global__ __launch_bounds__(256) void k_marginal(const float* __restrict__ pot,
 }
 
 // ---------------------------------------------------------------------------
+// Transport application (page "FlashSinkhorn: IO-aware entropic OT on GPU",
+// section "Differentiation and second-order optimisation"): the barycentric
+// projection bary_i = sum_j P_ij y_j / sum_j P_ij and the gradient
+// sum_j P_ij 2 (x_i - y_j) = 2 r_i (x_i - bary_i), r_i = sum_j P_ij, are
+// softmax-weighted averages of the other cloud: an attention-style P.V product
+// streamed over the same key chunks as the half-step, with V = the other
+// cloud's coordinates and the plan never formed.
+//
+// MI355X design:
+//  * The row offset is fixed before the pass: it is the row log-sum-exp that a
+//    half-step computes first, so every weight is at most about 1, no running
+//    maximum is kept and the partial sums of key splits simply add.
+//  * The weights leave the score MFMA in its accumulator layout and enter the
+//    P.V MFMA (16x16x32) as its A operand straight from registers: the keys of
+//    V are read in the matching permuted order, so no shuffle or LDS round
+//    trip is needed.  Two 16-key score tiles feed one 32-key P.V step.
+//  * Each weight is split into two bf16 parts (16 significant bits) and each
+//    fp32 coordinate into three bf16 parts (exact); bf16 coordinates are one
+//    part.  The products are exact and accumulate in fp32; the final sums and
+//    the division run in fp64.
+// ---------------------------------------------------------------------------
+constexpr int VK = 32;  // keys per value block: one 16x16x32 K step, two 16-key score tiles
+
+__host__ __device__ constexpr int val_parts(int mode) { return mode == MODE_SPLIT ? 3 : 1; }
+__host__ __device__ constexpr int val_tiles(int mode, int d) { return (val_parts(mode) * d + 15) / 16; }
+// query tiles of 16 rows per wave, and waves per SIMD, of the transport kernel
+__host__ __device__ constexpr int bary_R(int nch) { return nch == 1 ? 4 : (nch <= 8 ? 2 : 1); }
+__host__ __device__ constexpr int bary_waves(int nch) { return nch >= 12 ? 1 : 2; }
+
+__device__ __forceinline__ u4 pack8(const u16 (&v)[8]) {
+  return u4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
+            (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
+}
+
+// Value operand of one cloud: per problem and 32-key block a [ncols][32] bf16
+// tile, col = part*d + t (the LDS image of the block).  Padding keys and
+// columns are zero.  One thread per 8 keys of one column.
+__global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, int mode, int keys, int keys_pad, int d,
+                                                   int ncols, u16* __restrict__ vt) {
+  const int b = blockIdx.y;
+  const long long per_blk = (long long)ncols * (VK / 8);
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)(keys_pad / VK) * per_blk) return;
+  const int blk = (int)(idx / per_blk);
+  const int rem = (int)(idx % per_blk);
+  const int c = rem / (VK / 8), k0 = (rem % (VK / 8)) * 8;
+  const int part = c / d, t = c % d;
+  u16 v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int j = blk * VK + k0 + e;
+    u16 val = 0;
+    if (j < keys && part < val_parts(mode)) {
+      const size_t r = ((size_t)b * keys + j) * d + t;
+      if (mode == MODE_BF16) {
+        val = static_cast<const u16*>(P)[r];
+      } else {
+        // x = h0 + h1 + h2 exactly: each remainder is exact in fp32
+        const float x = static_cast<const float*>(P)[r];
+        const u16 h0 = bf16_rne(x);
+        const float r1 = x - bf16_f(h0);
+        const u16 h1 = bf16_rne(r1);
+        val = part == 0 ? h0 : (part == 1 ? h1 : bf16_rne(r1 - bf16_f(h1)));
+      }
+    }
+    v[e] = val;
+  }
+  *reinterpret_cast<u4*>(vt + (((size_t)b * (keys_pad / VK) + blk) * ncols + c) * VK + k0) = pack8(v);
+}
+
+// Two packed bf16 parts of a weight pair: hi = rne(e), lo = rne(e - hi).
+// Returns (hi, lo) packed pairs.
+__device__ __forceinline__ uint2 split_pair(float a, float b) {
+  const u16 ha = bf16_rne(a), hb = bf16_rne(b);
+  return make_uint2((uint32_t)ha | ((uint32_t)hb << 16),
+                    (uint32_t)bf16_rne(a - bf16_f(ha)) | ((uint32_t)bf16_rne(b - bf16_f(hb)) << 16));
+}
+
+// One pass of P.V over a key range for 4 waves x R query tiles of 16 rows.
+// Writes the partial weighted sums pv_out[split][b][row][NCT*16] (columns
+// part*d + t) and the partial weight sums s_out[split][b][row].
+template <int MODE, int NCH, int NCT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(NCH)))) void k_bary(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb, const u16* __restrict__ V,
+    const float* __restrict__ qgrid, const double* __restrict__ qnorm, const float* __restrict__ lse,
+    float* __restrict__ pv_out, float* __restrict__ s_out, int rows, int rows_pad, int keys, int keys_pad,
+    int chunks_per_split, int batch, float lam, float lam2) {
+  constexpr int MW = 16, R = bary_R(NCH);
+  using T = Tile<16>;
+  constexpr int KP = NCH * 32;
+  constexpr int NI = KP / T::KI;
+  constexpr int LROW = KP + 8;
+  constexpr int CK = VK;
+  constexpr int VPR = KP / 8;
+  constexpr int NVEC = CK * VPR;
+  constexpr int NLD = (NVEC + 255) / 256;
+  constexpr int NC = NCT * 16;        // value columns
+  constexpr int VROW = VK + 8;        // LDS row stride of the value tile (elements)
+  constexpr int NVV = NC * (VK / 8);  // 16-byte vectors per value block
+  constexpr int NLV = (NVV + 255) / 256;
+  constexpr int QPW = R * MW;
+  __shared__ __attribute__((aligned(16))) u16 lds[2][(CK + 1) * LROW];
+  __shared__ __attribute__((aligned(16))) u16 ldv[2][(NC + 1) * VROW];
+  __shared__ __attribute__((aligned(16))) float ldsb[2][CK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane / MW, col = lane % MW;
+  const int b = blockIdx.z;
+  const int qbase = blockIdx.x * (4 * QPW) + wave * QPW;
+  const u16* Qb = Q + (size_t)b * rows_pad * KP;
+  const u16* Kb = K + (size_t)b * keys_pad * KP;
+  const u16* Vb = V + (size_t)b * keys_pad * NC;
+  const float* hbb = (MODE == MODE_BF16) ? hb + (size_t)b * keys_pad : nullptr;
+  const float qg = (MODE == MODE_SPLIT) ? qgrid[b] : 1.f;
+
+  u4 bq[R][NI];
+#pragma unroll
+  for (int c = 0; c < R; ++c)
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      bq[c][i] = *reinterpret_cast<const u4*>(Qb + (size_t)(qbase + MW * c + col) * KP + i * T::KI + grp * 8);
+
+  // Fixed row offsets.  M = lam (||p||^2 - lse) is log2 of the row's sum of
+  // 2^score, so every weight 2^(score - M) is at most about 1.  The fp32 path
+  // carries the grid-aligned part of M in the query operand and subtracts the
+  // rest on the VALU.
+  float sub[R];
+#pragma unroll
+  for (int c = 0; c < R; ++c) {
+    const int q = qbase + MW * c + col;
+    double M = 0.0;
+    if (q < rows) {
+      const size_t r = (size_t)b * rows + q;
+      M = (double)lam * (qnorm[r] - (double)lse[r]);
+    }
+    if (!(fabs(M) < 1e30)) M = 0.0;
+    if (MODE == MODE_SPLIT) {
+      const float mo = offset_from_max((float)M, qg);
+      set_offset(bq[c][0], -mo, grp == 0);
+      sub[c] = (float)(M - (double)mo);
+    } else {
+      sub[c] = (float)M;
+    }
+  }
+
+  const int total_chunks = (keys + CK - 1) / CK;
+  const int c0 = blockIdx.y * chunks_per_split;
+  const int c1 = min(total_chunks, c0 + chunks_per_split);
+
+  float s[R];
+  f4 pv[R][NCT];
+#pragma unroll
+  for (int c = 0; c < R; ++c) {
+    s[c] = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) pv[c][ct] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  u4 pre[NLD];
+  u4 prev[NLV];
+  f4 preb = {0.f, 0.f, 0.f, 0.f};
+  // Key rows past the end of a chunk land in the operand buffers' slack rows;
+  // value vectors are clamped to the block; both store surplus to a spare row.
+  auto gload = [&](int chunk) {
+    const u16* src = Kb + (size_t)chunk * CK * KP;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) pre[i] = *reinterpret_cast<const u4*>(src + (size_t)(tid + 256 * i) * 8);
+    const u16* vsrc = Vb + (size_t)chunk * NC * VK;
+#pragma unroll
+    for (int i = 0; i < NLV; ++i) prev[i] = *reinterpret_cast<const u4*>(vsrc + (size_t)min(tid + 256 * i, NVV - 1) * 8);
+    if (MODE == MODE_BF16) preb = *reinterpret_cast<const f4*>(hbb + (size_t)chunk * CK + (tid % (CK / 4)) * 4);
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int v = min(tid + 256 * i, NVEC);
+      *reinterpret_cast<u4*>(&lds[buf][(v / VPR) * LROW + (v % VPR) * 8]) = pre[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NLV; ++i) {
+      const int v = min(tid + 256 * i, NVV);
+      *reinterpret_cast<u4*>(&ldv[buf][(v / (VK / 8)) * VROW + (v % (VK / 8)) * 8]) = prev[i];
+    }
+    if (MODE == MODE_BF16 && tid < CK / 4) *reinterpret_cast<f4*>(&ldsb[buf][tid * 4]) = preb;
+  };
+  // Scores of the 16-key tile t of the chunk against the R query tiles.
+  auto score = [&](int buf, int t, f4 (&acc)[R]) {
+    f4 cinit = {0.f, 0.f, 0.f, 0.f};
+    if (MODE == MODE_BF16) cinit = *reinterpret_cast<const f4*>(&ldsb[buf][t * MW + 4 * grp]);
+#pragma unroll
+    for (int c = 0; c < R; ++c) acc[c] = cinit;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const u4 ka = *reinterpret_cast<const u4*>(&lds[buf][(t * MW + col) * LROW + i * T::KI + grp * 8]);
+#pragma unroll
+      for (int c = 0; c < R; ++c) acc[c] = T::mma(ka, bq[c][i], acc[c]);
+    }
+  };
+  auto weight = [&](float v, int c) -> float {
+    if (MODE == MODE_BF16) return __builtin_amdgcn_exp2f(fmaf(v, lam2, -sub[c]));
+    return __builtin_amdgcn_exp2f(v - sub[c]);
+  };
+
+  if (c0 < c1) {
+    gload(c0);
+    lstore(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int ci = c0; ci < c1; ++ci) {
+      const int buf = (ci - c0) & 1;
+      if (ci + 1 < c1) gload(ci + 1);
+      f4 a0[R], a1[R];
+      score(buf, 0, a0);
+      score(buf, 1, a1);
+      // A operand of the P.V step: lane (query col, group grp) holds the
+      // weights of keys 4grp..4grp+3 of tile 0 and of tile 1, in that order.
+      u4 ehi[R], elo[R];
+#pragma unroll
+      for (int c = 0; c < R; ++c) {
+        float e[8];
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+          e[o] = weight(a0[c][o], c);
+          e[4 + o] = weight(a1[c][o], c);
+        }
+        s[c] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        const uint2 p0 = split_pair(e[0], e[1]), p1 = split_pair(e[2], e[3]);
+        const uint2 p2 = split_pair(e[4], e[5]), p3 = split_pair(e[6], e[7]);
+        ehi[c] = u4{p0.x, p1.x, p2.x, p3.x};
+        elo[c] = u4{p0.y, p1.y, p2.y, p3.y};
+      }
+      // B operand: lane (column col, group grp) reads the same keys of V.
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const u16* vr = &ldv[buf][(ct * 16 + col) * VROW];
+        const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * grp);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * grp);
+        const u4 vb = u4{v0.x, v0.y, v1.x, v1.y};
+#pragma unroll
+        for (int c = 0; c < R; ++c) {
+          pv[c][ct] = T::mma(ehi[c], vb, pv[c][ct]);
+          pv[c][ct] = T::mma(elo[c], vb, pv[c][ct]);
+        }
+      }
+      if (ci + 1 < c1) lstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  const size_t split_base = (size_t)blockIdx.y * batch * rows + (size_t)b * rows;
+#pragma unroll
+  for (int c = 0; c < R; ++c) {
+    float st = s[c];
+#pragma unroll
+    for (int w = MW; w < 64; w *= 2) st += __shfl_xor(st, w);
+    const int q = qbase + MW * c + col;
+    if (grp == 0 && q < rows) s_out[split_base + q] = st;
+    // P.V output: lane (column col, group grp), element r = query 4grp + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qr = qbase + MW * c + 4 * grp + r;
+      if (qr < rows) {
+        float* dst = pv_out + (split_base + qr) * NC + col;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) dst[ct * 16] = pv[c][ct][r];
+      }
+    }
+  }
+}
+
+// Barycentric projection and gradient from the split partials, one thread per
+// (problem, row, coordinate): bary = sum_parts sum_splits pv / sum_splits s,
+// grad = 2 r (p - bary) with the row mass r = w exp((pot - lse)/eps).
+__global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv, const float* __restrict__ sp, int ks,
+                                                    int batch, int rows, int d, int ncols, int parts,
+                                                    const void* __restrict__ P, int mode,
+                                                    const float* __restrict__ pot, const float* __restrict__ lse,
+                                                    const double* __restrict__ logw, double eps,
+                                                    float* __restrict__ bary, float* __restrict__ grad) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)batch * rows * d) return;
+  const int t = (int)(idx % d);
+  const long long rr = idx / d;  // b * rows + row
+  double S = 0.0, num = 0.0;
+  for (int k = 0; k < ks; ++k) {
+    const size_t base = (size_t)k * batch * rows + (size_t)rr;
+    S += (double)sp[base];
+    for (int part = 0; part < parts; ++part) num += (double)pv[base * ncols + part * d + t];
+  }
+  const double bc = num / S;
+  bary[idx] = (float)bc;
+  if (grad != nullptr) {
+    const double x = mode == MODE_SPLIT ? (double)static_cast<const float*>(P)[idx]
+                                        : (double)bf16_f(static_cast<const u16*>(P)[idx]);
+    const double mass = exp(logw[rr] + ((double)pot[rr] - (double)lse[rr]) / eps);
+    grad[idx] = (float)(2.0 * mass * (x - bc));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 struct Layout {
   int mode, KP, n_pad, m_pad, max_pad;
   size_t xn, yn, la, lb, maxabs, qgrid, qx, qy, kb, hb, part, scratch, total;
+  // transport application (after `total`; only its entry points need them)
+  int ncols, ksb;
+  size_t vt, bpv, bs, ttotal;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -745,6 +1049,14 @@ Layout layout_of(const sk_problem* p) {
   L.part = take(8 * (size_t)KS_MAX * B * mx);
   L.scratch = take(4 * B * mx);
   L.total = off;
+  // Transport: the value operand and the split partials of the P.V pass, at
+  // most 128 MiB of partials (and at most 16 splits).
+  L.ncols = val_tiles(L.mode, (int)p->d) * 16;
+  L.ksb = (int)std::min<size_t>(16, std::max<size_t>(1, (size_t(128) << 20) / (4 * B * mx * (size_t)L.ncols)));
+  L.vt = take(2 * B * (size_t)L.max_pad * L.ncols);
+  L.bpv = take(4 * (size_t)L.ksb * B * mx * L.ncols);
+  L.bs = take(4 * (size_t)L.ksb * B * mx);
+  L.ttotal = off;
   return L;
 }
 
@@ -781,20 +1093,21 @@ sk_status hip_check(const char* what) {
   return SK_OK;
 }
 
-sk_status check_ws(const sk_problem* p, void* ws, size_t ws_bytes, Layout* L) {
+sk_status check_ws(const sk_problem* p, void* ws, size_t ws_bytes, Layout* L, bool transport = false) {
   sk_status st = check_problem(p);
   if (st != SK_OK) return st;
   *L = layout_of(p);
-  if (ws == nullptr || ws_bytes < L->total) {
-    set_err("workspace %s: need %zu bytes, got %zu", ws == nullptr ? "is NULL" : "too small", L->total,
-            ws_bytes);
+  const size_t need = transport ? L->ttotal : L->total;
+  if (ws == nullptr || ws_bytes < need) {
+    set_err("workspace %s: need %zu bytes, got %zu%s", ws == nullptr ? "is NULL" : "too small", need, ws_bytes,
+            transport ? " (transport calls need sinkhorn_transport_workspace_bytes)" : "");
     return SK_EWORKSPACE;
   }
   return SK_OK;
 }
 
 // Workgroups of `fn` that the current device holds at once (CUs x WGs per CU).
-sk_status resident_capacity(LseFn fn, int* out) {
+sk_status resident_capacity(const void* fn, int* out) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, int> cache;
   int dev = 0;
@@ -802,7 +1115,7 @@ sk_status resident_capacity(LseFn fn, int* out) {
     set_err("hipGetDevice failed");
     return SK_EHIP;
   }
-  const auto key = std::make_pair(dev, reinterpret_cast<const void*>(fn));
+  const auto key = std::make_pair(dev, fn);
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(key);
   if (it != cache.end()) {
@@ -811,7 +1124,7 @@ sk_status resident_capacity(LseFn fn, int* out) {
   }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), 256, 0) !=
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) !=
           hipSuccess) {
     set_err("occupancy query failed");
     return SK_EHIP;
@@ -824,8 +1137,8 @@ sk_status resident_capacity(LseFn fn, int* out) {
 // workgroups: every split does nearly the same work, and rowgroups*ks is chosen
 // to fill whole waves of the `capacity` resident slots, so no round of
 // workgroups runs nearly empty at the end of the kernel.
-int choose_key_splits(int rowgroups, int total_chunks, int capacity, int* cps_out) {
-  const int kmax = std::max(1, std::min(KS_MAX, total_chunks / 2));
+int choose_key_splits(int rowgroups, int total_chunks, int capacity, int* cps_out, int ks_cap = KS_MAX) {
+  const int kmax = std::max(1, std::min(ks_cap, total_chunks / 2));
   // busy fraction of the resident slots x balance of the split sizes; the
   // fewest splits within 2% of the best (each split adds merge traffic)
   auto score = [&](int ks) {
@@ -899,7 +1212,7 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   const int CK = cfTC * cfMW;
   const int total_chunks = (keys + CK - 1) / CK;
   int capacity = 0;
-  st = resident_capacity(fn, &capacity);
+  st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity);
   if (st != SK_OK) return st;
   int cps = 0;
   const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps);
@@ -913,6 +1226,92 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   hipLaunchKernelGGL(k_merge, dim3((total + 255) / 256), dim3(256), 0, stream, part, ks, total, qnorm, pot_out,
                      inv_lam);
   return hip_check("split merge launch");
+}
+
+using BaryFn = void (*)(const u16*, const u16*, const float*, const u16*, const float*, const double*, const float*,
+                        float*, float*, int, int, int, int, int, int, float, float);
+
+template <int MODE, int D>
+BaryFn bary_fn_d() {
+  constexpr int NCH = MODE == MODE_SPLIT ? split_nch(D) : (D + 31) / 32;
+  return &k_bary<MODE, NCH, val_tiles(MODE, D)>;
+}
+
+template <int MODE, int... N>
+BaryFn bary_lookup_impl(int d, std::integer_sequence<int, N...>) {
+  BaryFn fn = nullptr;
+  ((d == N + 1 ? (fn = bary_fn_d<MODE, N + 1>(), 0) : 0), ...);
+  return fn;
+}
+
+BaryFn bary_lookup(int mode, int d) {
+  if (mode == MODE_SPLIT) return bary_lookup_impl<MODE_SPLIT>(d, std::make_integer_sequence<int, SK_MAX_D_FP32>{});
+  return bary_lookup_impl<MODE_BF16>(d, std::make_integer_sequence<int, SK_MAX_D>{});
+}
+
+// Barycentric projection (and gradient) of the rows of one side: side 0 the
+// points of X against Y, side 1 the points of Y against X.
+sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws, const Layout& L, const float* f,
+                    const float* g, float eps, float* bary, float* grad, int side, hipStream_t stream) {
+  char* w = static_cast<char*>(ws);
+  const int B = (int)p->batch, d = (int)p->d;
+  const int rows = (int)(side == 0 ? p->n : p->m);
+  const int keys = (int)(side == 0 ? p->m : p->n);
+  const int rows_pad = side == 0 ? L.n_pad : L.m_pad;
+  const int keys_pad = side == 0 ? L.m_pad : L.n_pad;
+  const double* qnorm = reinterpret_cast<const double*>(w + (side == 0 ? L.xn : L.yn));
+  const double* qlogw = reinterpret_cast<const double*>(w + (side == 0 ? L.la : L.lb));
+  const float* qgrid = reinterpret_cast<const float*>(w + L.qgrid);
+  const u16* Qop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qx : L.qy));
+  const void* Praw = side == 0 ? X : Y;
+  const void* Kraw = side == 0 ? Y : X;
+  const float* pot_row = side == 0 ? f : g;
+  float* lse = reinterpret_cast<float*>(w + L.scratch);
+
+  // 1. The row log-sum-exp (the half-step's output); this also prepares the
+  //    key operand of this side for the current potential and eps.
+  sk_status st = half_step(p, X, Y, ws, L, side == 0 ? g : f, eps, lse, side, stream);
+  if (st != SK_OK) return st;
+
+  // 2. Value operand from the other cloud's coordinates.
+  u16* vt = reinterpret_cast<u16*>(w + L.vt);
+  const long long nvec = (long long)(keys_pad / VK) * L.ncols * (VK / 8);
+  hipLaunchKernelGGL(k_prep_vals, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, Kraw, L.mode, keys,
+                     keys_pad, d, L.ncols, vt);
+  st = hip_check("value preparation launch");
+  if (st != SK_OK) return st;
+
+  // 3. The P.V pass, split over keys when rows alone do not fill the GPU.
+  BaryFn fn = bary_lookup(L.mode, d);
+  if (fn == nullptr) {
+    set_err("no transport kernel for d = %d", d);
+    return SK_EUNSUPPORTED;
+  }
+  const int nch = L.KP / 32;
+  const int R = bary_R(nch);
+  const int wg_x = (rows + 4 * R * 16 - 1) / (4 * R * 16);
+  const int total_chunks = (keys + VK - 1) / VK;
+  int capacity = 0;
+  st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity);
+  if (st != SK_OK) return st;
+  int cps = 0;
+  const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps, L.ksb);
+  const u16* Kop = (L.mode == MODE_SPLIT) ? reinterpret_cast<const u16*>(w + L.kb)
+                                          : reinterpret_cast<const u16*>(w + (side == 0 ? L.qy : L.qx));
+  const float* hb = (L.mode == MODE_BF16) ? reinterpret_cast<const float*>(w + L.hb) : nullptr;
+  float* bpv = reinterpret_cast<float*>(w + L.bpv);
+  float* bs = reinterpret_cast<float*>(w + L.bs);
+  const float lam = (float)(LOG2E / (double)eps);
+  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, lse, bpv, bs, rows,
+                     rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam);
+  st = hip_check("transport kernel launch");
+  if (st != SK_OK) return st;
+
+  // 4. Merge the splits, divide, form the gradient.
+  const long long total = (long long)B * rows * d;
+  hipLaunchKernelGGL(k_bary_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, bs, ks, B, rows,
+                     d, L.ncols, val_parts(L.mode), Praw, L.mode, pot_row, lse, qlogw, (double)eps, bary, grad);
+  return hip_check("transport merge launch");
 }
 
 sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const float* a, const float* b, void* ws,
@@ -1071,6 +1470,39 @@ sk_status sinkhorn_marginal_error(const sk_problem* p, const void* X, const void
   hipLaunchKernelGGL(k_marginal, dim3(B), dim3(256), 0, s, g, tilde, reinterpret_cast<const double*>(w + L.lb),
                      (int)p->m, 1.f / eps, err, 1);
   return hip_check("marginal reduction launch");
+}
+
+size_t sinkhorn_transport_workspace_bytes(const sk_problem* p) {
+  if (check_problem(p) != SK_OK) return 0;
+  return layout_of(p).ttotal;
+}
+
+static sk_status transport_entry(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
+                                 const float* f, const float* g, float eps, float* bary, float* grad, void* stream,
+                                 int side) {
+  g_err[0] = 0;
+  Layout L;
+  sk_status st = check_ws(p, ws, ws_bytes, &L, true);
+  if (st != SK_OK) return st;
+  if (!X || !Y || !f || !g || !bary) {
+    set_err("X, Y, f, g and bary must be non-NULL device pointers");
+    return SK_EINVAL;
+  }
+  if (!eps_ok(eps)) {
+    set_err("eps must be positive and finite (got %g)", (double)eps);
+    return SK_EINVAL;
+  }
+  return transport(p, X, Y, ws, L, f, g, eps, bary, grad, side, static_cast<hipStream_t>(stream));
+}
+
+sk_status sinkhorn_barycentric_x(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
+                                 const float* f, const float* g, float eps, float* bary, float* grad, void* stream) {
+  return transport_entry(p, X, Y, ws, ws_bytes, f, g, eps, bary, grad, stream, 0);
+}
+
+sk_status sinkhorn_barycentric_y(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
+                                 const float* f, const float* g, float eps, float* bary, float* grad, void* stream) {
+  return transport_entry(p, X, Y, ws, ws_bytes, f, g, eps, bary, grad, stream, 1);
 }
 
 }  // extern "C"

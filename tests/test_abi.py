@@ -34,7 +34,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("sinkhorn_init_norms", "sinkhorn_half_step_f", "sinkhorn_half_step_g", "sinkhorn_solve",
-              "sinkhorn_marginal_error", "sinkhorn_workspace_bytes", "sinkhorn_last_error"):
+              "sinkhorn_marginal_error", "sinkhorn_workspace_bytes", "sinkhorn_last_error",
+              "sinkhorn_transport_workspace_bytes", "sinkhorn_barycentric_x", "sinkhorn_barycentric_y"):
         assert n in names
 
 
@@ -111,3 +112,25 @@ def test_other_argument_errors(lib):
     Ebad = (ctypes.c_float * 3)(0.1, 0.0, 0.3)
     assert lib.sinkhorn_solve(bp, ptr, ptr, ptr, ptr, Ebad, 3, 3, ptr, ptr, ptr, need, None) == 1
     assert b"eps[1]" in lib.sinkhorn_last_error()
+
+
+def test_transport_workspace_and_argument_errors(lib):
+    p = _prob(1, 700, 500, 3)
+    bp = ctypes.byref(p)
+    base = lib.sinkhorn_workspace_bytes(bp)
+    full = lib.sinkhorn_transport_workspace_bytes(bp)
+    assert full > base > 0
+    # linear in (n+m)d and bounded at the large workloads
+    assert lib.sinkhorn_transport_workspace_bytes(ctypes.byref(_prob(1, 65536, 32768, 128, 1))) < 2 ** 30
+    assert lib.sinkhorn_transport_workspace_bytes(ctypes.byref(_prob(1, 100, 100, 88, 0))) > 0
+    assert lib.sinkhorn_transport_workspace_bytes(ctypes.byref(_prob(d=129))) == 0
+    ptr = ctypes.c_void_p(0x1000)
+    for fn in (lib.sinkhorn_barycentric_x, lib.sinkhorn_barycentric_y):
+        # the solver-sized workspace is too small for the transport calls
+        assert fn(bp, ptr, ptr, ptr, base, ptr, ptr, 0.1, ptr, None, None) == 6
+        assert b"sinkhorn_transport_workspace_bytes" in lib.sinkhorn_last_error()
+        # bary is required, grad is optional (NULL passes validation up to the launch)
+        assert fn(bp, ptr, ptr, ptr, full, ptr, ptr, 0.1, None, ptr, None) == 1
+        assert fn(bp, ptr, ptr, ptr, full, None, ptr, 0.1, ptr, ptr, None) == 1
+        assert fn(bp, ptr, ptr, ptr, full, ptr, ptr, 0.0, ptr, ptr, None) == 1
+        assert fn(ctypes.byref(_prob(d=89)), ptr, ptr, ptr, full, ptr, ptr, 0.1, ptr, ptr, None) == 5
