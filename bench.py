@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: n=m=70000, d=3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-transport", action="store_true", help="skip the transport-application leg")
     ap.add_argument("--cpu-seconds", type=float, default=6.0, help="target wall time of the CPU leg")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes (scales rocprofv3 byte counters)")
@@ -198,9 +199,49 @@ def main():
         "roofline": roof,
     }
 
+    if not args.no_transport:
+        out["transport"] = transport_leg(sk, X, Y, a, b, f, g, eps_sched[-1], p, contraction)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def transport_leg(sk, X, Y, a, b, f, g, eps, p, contraction, reps=10):
+    """Time the transport application (barycentric projection + gradient) of each
+    side at the final potentials.  One call = a half-step (row log-sum-exp) plus
+    the P.V pass: 2 exps and 6d algorithmic flops (two score contractions and
+    P.V) per score element."""
+    import numpy as np
+    import torch
+
+    ws = sk.alloc_workspace(X, Y, transport=True)
+    sk.init_norms(X, Y, a, b, ws)
+    bx, gx = sk.barycentric_x(X, Y, ws, f, g, eps)
+    by, gy = sk.barycentric_y(X, Y, ws, f, g, eps)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ms = {}
+    for side, call, outs in (("x", sk.barycentric_x, (bx, gx)), ("y", sk.barycentric_y, (by, gy))):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for r in range(reps):
+            call(X, Y, ws, f, g, eps, bary=outs[0], grad=outs[1])
+            ev[r + 1].record(stream)
+        torch.cuda.synchronize()
+        ms[side] = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+    assert all(torch.isfinite(t).all() for t in (bx, gx, by, gy)), "non-finite transport outputs"
+    elems = p.batch * p.n * p.m
+    t_call = 0.5 * (ms["x"] + ms["y"]) / 1e3
+    t_exp = 2.0 * elems / PEAK_EXP_PER_S
+    t_mfma = 6.0 * elems * p.d / PEAK_MFMA[contraction]
+    if t_exp >= t_mfma:
+        roof = {"bound": "alu", "achieved": round(2.0 * elems / t_call / 1e9, 1),
+                "peak": round(PEAK_EXP_PER_S / 1e9, 1), "unit": "Gexp/s", "frac": round(t_exp / t_call, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(6.0 * elems * p.d / t_call / 1e12, 2),
+                "peak": PEAK_MFMA[contraction] / 1e12, "unit": "TFLOP/s", "frac": round(t_mfma / t_call, 4)}
+    return {"what": "barycentric projection + gradient of every point (one call per side)",
+            "ms_per_call": {"x": round(ms["x"], 4), "y": round(ms["y"], 4)}, "reps": reps, "roofline": roof}
 
 
 def cpu_baseline(p, target_s: float):

@@ -51,6 +51,7 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <type_traits>
 #include <utility>
 
 #include "sinkhorn.h"
@@ -697,6 +698,8 @@ constexpr int VK = 32;  // keys per value block: one 16x16x32 K step, two 16-key
 
 __host__ __device__ constexpr int val_parts(int mode) { return mode == MODE_SPLIT ? 3 : 1; }
 __host__ __device__ constexpr int val_tiles(int mode, int d) { return (val_parts(mode) * d + 15) / 16; }
+// A spare value column holds ones, so the P.V product also yields the sum of the weights.
+__host__ __device__ constexpr bool val_sumcol(int mode, int d) { return val_parts(mode) * d < val_tiles(mode, d) * 16; }
 // query tiles of 16 rows per wave, and waves per SIMD, of the transport kernel
 __host__ __device__ constexpr int bary_R(int nch) { return nch == 1 ? 4 : (nch <= 8 ? 2 : 1); }
 __host__ __device__ constexpr int bary_waves(int nch) { return nch >= 12 ? 1 : 2; }
@@ -707,10 +710,11 @@ __device__ __forceinline__ u4 pack8(const u16 (&v)[8]) {
 }
 
 // Value operand of one cloud: per problem and 32-key block a [ncols][32] bf16
-// tile, col = part*d + t (the LDS image of the block).  Padding keys and
-// columns are zero.  One thread per 8 keys of one column.
+// tile, col = part*d + t (the LDS image of the block), and ones in the last
+// column when it is spare (sumcol).  Padding keys and other columns are zero.
+// One thread per 8 keys of one column.
 __global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, int mode, int keys, int keys_pad, int d,
-                                                   int ncols, u16* __restrict__ vt) {
+                                                   int ncols, int sumcol, u16* __restrict__ vt) {
   const int b = blockIdx.y;
   const long long per_blk = (long long)ncols * (VK / 8);
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -724,7 +728,9 @@ __global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, i
   for (int e = 0; e < 8; ++e) {
     const int j = blk * VK + k0 + e;
     u16 val = 0;
-    if (j < keys && part < val_parts(mode)) {
+    if (j < keys && sumcol && c == ncols - 1) {
+      val = BF16_ONE;
+    } else if (j < keys && part < val_parts(mode)) {
       const size_t r = ((size_t)b * keys + j) * d + t;
       if (mode == MODE_BF16) {
         val = static_cast<const u16*>(P)[r];
@@ -742,18 +748,22 @@ __global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, i
   *reinterpret_cast<u4*>(vt + (((size_t)b * (keys_pad / VK) + blk) * ncols + c) * VK + k0) = pack8(v);
 }
 
-// Two packed bf16 parts of a weight pair: hi = rne(e), lo = rne(e - hi).
-// Returns (hi, lo) packed pairs.
+// Two packed bf16 parts of a weight pair: hi = e truncated to bf16 (its upper
+// half), lo = rne(e - hi), where e - hi is exact; together 16 significant bits.
+// Returns (hi pair, lo pair).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 split_pair(float a, float b) {
-  const u16 ha = bf16_rne(a), hb = bf16_rne(b);
-  return make_uint2((uint32_t)ha | ((uint32_t)hb << 16),
-                    (uint32_t)bf16_rne(a - bf16_f(ha)) | ((uint32_t)bf16_rne(b - bf16_f(hb)) << 16));
+  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  const uint32_t hi = (ua >> 16) | (ub & 0xFFFF0000u);
+  const bf16x2 l = {(__bf16)(a - __uint_as_float(ua & 0xFFFF0000u)), (__bf16)(b - __uint_as_float(ub & 0xFFFF0000u))};
+  return make_uint2(hi, __builtin_bit_cast(uint32_t, l));
 }
 
 // One pass of P.V over a key range for 4 waves x R query tiles of 16 rows.
 // Writes the partial weighted sums pv_out[split][b][row][NCT*16] (columns
-// part*d + t) and the partial weight sums s_out[split][b][row].
-template <int MODE, int NCH, int NCT>
+// part*d + t, and the weight sums in the last column if SUMCOL) or, without
+// SUMCOL, the partial weight sums to s_out[split][b][row].
+template <int MODE, int NCH, int NCT, bool SUMCOL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(NCH)))) void k_bary(
     const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb, const u16* __restrict__ V,
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, const float* __restrict__ lse,
@@ -796,8 +806,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
 
   // Fixed row offsets.  M = lam (||p||^2 - lse) is log2 of the row's sum of
   // 2^score, so every weight 2^(score - M) is at most about 1.  The fp32 path
-  // carries the grid-aligned part of M in the query operand and subtracts the
-  // rest on the VALU.
+  // carries the grid-aligned part of M in the query operand; the rest (below
+  // the grid quantum) only scales a row's weights uniformly, which the
+  // normalisation cancels, so it is subtracted on the VALU only when it could
+  // be large enough to overflow the sums.
   float sub[R];
 #pragma unroll
   for (int c = 0; c < R; ++c) {
@@ -870,12 +882,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
       for (int c = 0; c < R; ++c) acc[c] = T::mma(ka, bq[c][i], acc[c]);
     }
   };
-  auto weight = [&](float v, int c) -> float {
-    if (MODE == MODE_BF16) return __builtin_amdgcn_exp2f(fmaf(v, lam2, -sub[c]));
-    return __builtin_amdgcn_exp2f(v - sub[c]);
-  };
+  float sub_max = 0.f;
+#pragma unroll
+  for (int c = 0; c < R; ++c) sub_max = fmaxf(sub_max, sub[c]);
+  const bool fine = (MODE == MODE_BF16) || __any(!(sub_max <= 32.f));
 
-  if (c0 < c1) {
+  auto pass = [&](auto fine_c) {
+    constexpr bool FINE = decltype(fine_c)::value;
+    auto weight = [&](float v, int c) -> float {
+      if (MODE == MODE_BF16) return __builtin_amdgcn_exp2f(fmaf(v, lam2, -sub[c]));
+      return __builtin_amdgcn_exp2f(FINE ? v - sub[c] : v);
+    };
     gload(c0);
     lstore(0);
     __builtin_amdgcn_s_waitcnt(0);
@@ -898,7 +915,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
           e[o] = weight(a0[c][o], c);
           e[4 + o] = weight(a1[c][o], c);
         }
-        s[c] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        if (!SUMCOL) s[c] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
         const uint2 p0 = split_pair(e[0], e[1]), p1 = split_pair(e[2], e[3]);
         const uint2 p2 = split_pair(e[4], e[5]), p3 = split_pair(e[6], e[7]);
         ehi[c] = u4{p0.x, p1.x, p2.x, p3.x};
@@ -920,6 +937,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
       if (ci + 1 < c1) lstore(buf ^ 1);
       __syncthreads();
     }
+  };
+  if (c0 < c1) {
+    if (fine)
+      pass(std::true_type{});
+    else
+      pass(std::false_type{});
   }
 
   const size_t split_base = (size_t)blockIdx.y * batch * rows + (size_t)b * rows;
@@ -929,7 +952,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
 #pragma unroll
     for (int w = MW; w < 64; w *= 2) st += __shfl_xor(st, w);
     const int q = qbase + MW * c + col;
-    if (grp == 0 && q < rows) s_out[split_base + q] = st;
+    if (!SUMCOL && grp == 0 && q < rows) s_out[split_base + q] = st;
     // P.V output: lane (column col, group grp), element r = query 4grp + r
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -947,7 +970,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
 // (problem, row, coordinate): bary = sum_parts sum_splits pv / sum_splits s,
 // grad = 2 r (p - bary) with the row mass r = w exp((pot - lse)/eps).
 __global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv, const float* __restrict__ sp, int ks,
-                                                    int batch, int rows, int d, int ncols, int parts,
+                                                    int batch, int rows, int d, int ncols, int parts, int sumcol,
                                                     const void* __restrict__ P, int mode,
                                                     const float* __restrict__ pot, const float* __restrict__ lse,
                                                     const double* __restrict__ logw, double eps,
@@ -959,7 +982,7 @@ __global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv
   double S = 0.0, num = 0.0;
   for (int k = 0; k < ks; ++k) {
     const size_t base = (size_t)k * batch * rows + (size_t)rr;
-    S += (double)sp[base];
+    S += sumcol ? (double)pv[base * ncols + ncols - 1] : (double)sp[base];
     for (int part = 0; part < parts; ++part) num += (double)pv[base * ncols + part * d + t];
   }
   const double bc = num / S;
@@ -1234,7 +1257,7 @@ using BaryFn = void (*)(const u16*, const u16*, const float*, const u16*, const 
 template <int MODE, int D>
 BaryFn bary_fn_d() {
   constexpr int NCH = MODE == MODE_SPLIT ? split_nch(D) : (D + 31) / 32;
-  return &k_bary<MODE, NCH, val_tiles(MODE, D)>;
+  return &k_bary<MODE, NCH, val_tiles(MODE, D), val_sumcol(MODE, D)>;
 }
 
 template <int MODE, int... N>
@@ -1276,8 +1299,9 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   // 2. Value operand from the other cloud's coordinates.
   u16* vt = reinterpret_cast<u16*>(w + L.vt);
   const long long nvec = (long long)(keys_pad / VK) * L.ncols * (VK / 8);
+  const int sumcol = val_sumcol(L.mode, d) ? 1 : 0;
   hipLaunchKernelGGL(k_prep_vals, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, Kraw, L.mode, keys,
-                     keys_pad, d, L.ncols, vt);
+                     keys_pad, d, L.ncols, sumcol, vt);
   st = hip_check("value preparation launch");
   if (st != SK_OK) return st;
 
@@ -1310,7 +1334,8 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   // 4. Merge the splits, divide, form the gradient.
   const long long total = (long long)B * rows * d;
   hipLaunchKernelGGL(k_bary_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, bs, ks, B, rows,
-                     d, L.ncols, val_parts(L.mode), Praw, L.mode, pot_row, lse, qlogw, (double)eps, bary, grad);
+                     d, L.ncols, val_parts(L.mode), sumcol, Praw, L.mode, pot_row, lse, qlogw, (double)eps, bary,
+                     grad);
   return hip_check("transport merge launch");
 }
 
