@@ -23,6 +23,10 @@ Parity status of each function:
       weighted mean, eps->0 assignment limit, finite differences of the
       converged dual value, translation balance of the two gradients,
       numpy brute force on tiny inputs)
+  normalize / cosine_grad : pinned (cost = 2 - 2 cos of the angle in closed
+      form for d = 2, invariance of the potentials under positive rescaling of
+      points, finite differences of the converged dual value in the raw points,
+      gradient orthogonal to its point)
 """
 
 from __future__ import annotations
@@ -208,3 +212,30 @@ def transport_y(X, Y, a, b, f, g, eps: float, rows=None, threads=None):
     """Transport application for the points of Y (the same plan read by columns):
     bary_j = (P^T X)_j / (P^T 1)_j, grad_j = sum_i P_ij 2 (y_j - x_i), mass_j = (P^T 1)_j."""
     return transport(Y, X, b, a, g, f, eps, rows=rows, threads=threads)
+
+
+# ---------------------------------------------------------------------------
+# Cosine cost (page "FlashSinkhorn: IO-aware entropic OT on GPU", closing
+# remarks: the method covers squared-Euclidean cost and the cosine distance
+# after normalisation).  C_ij = ||x_i/|x_i| - y_j/|y_j|||^2 = 2 - 2 cos(x_i, y_j);
+# a zero point stays zero.  Every routine above applies unchanged to the
+# normalised clouds; only the gradient in the raw points needs the chain rule.
+# ---------------------------------------------------------------------------
+def normalize(P) -> np.ndarray:
+    """Rows of P divided by their Euclidean norm (fp64); zero rows stay zero."""
+    P = _f64(P)
+    nrm = np.sqrt((P * P).sum(-1, keepdims=True))
+    return np.divide(P, nrm, out=np.zeros_like(P), where=nrm > 0)
+
+
+def cosine_grad(P, grad_hat) -> np.ndarray:
+    """Gradient in the raw points from the gradient in the normalised points:
+    d(p/|p|)/dp = (I - p_hat p_hat^T)/|p|, applied row by row (zero rows: 0)."""
+    P, G = _f64(P), _f64(grad_hat)
+    out = np.zeros_like(P)
+    for i in range(P.shape[0]):
+        nrm = float(np.sqrt(P[i] @ P[i]))
+        if nrm > 0:
+            ph = P[i] / nrm
+            out[i] = (G[i] - (ph @ G[i]) * ph) / nrm
+    return out
