@@ -49,7 +49,7 @@ extern "C" {
 
 typedef enum {
     SK_OK = 0,
-    SK_EINVAL = 1,       /* bad argument: NULL pointer, eps <= 0 or non-finite, iters < 0 ... */
+    SK_EINVAL = 1,       /* bad argument: NULL pointer, eps <= 0 or non-finite, iters < 0, unknown cost ... */
     SK_ESHAPE = 2,       /* batch, n, m or d out of range */
     SK_EDTYPE = 3,       /* unknown dtype */
     SK_EHIP = 4,         /* a HIP launch or runtime call failed */
@@ -65,12 +65,22 @@ typedef enum { SK_FP32 = 0, SK_BF16 = 1 } sk_dtype; /* element type of X and Y *
 #define SK_MAX_D 128
 #define SK_MAX_D_FP32 88
 
+/* Ground cost.  SK_COST_SQEUCLID: C_ij = ||x_i - y_j||^2 (the pages' cost).
+ * SK_COST_COSINE: the cosine distance after normalisation (page "FlashSinkhorn:
+ * IO-aware entropic OT on GPU", closing remarks), taken as the squared distance
+ * between the normalised points, C_ij = ||x_i/|x_i| - y_j/|y_j|||^2
+ * = 2 - 2 cos(x_i, y_j); a zero point stays zero (cost 1 to any other point).
+ * The cosine cost runs on the split fp32 layout, so d <= SK_MAX_D_FP32 for
+ * either dtype. */
+typedef enum { SK_COST_SQEUCLID = 0, SK_COST_COSINE = 1 } sk_cost;
+
 typedef struct {
     int64_t batch; /* >= 1 independent problems */
     int64_t n;     /* >= 1 source points per problem */
     int64_t m;     /* >= 1 target points per problem */
-    int64_t d;     /* 1 .. SK_MAX_D (bf16) or SK_MAX_D_FP32 (fp32) */
+    int64_t d;     /* 1 .. SK_MAX_D (bf16) or SK_MAX_D_FP32 (fp32, or cosine cost) */
     int32_t dtype; /* sk_dtype of X and Y */
+    int32_t cost;  /* sk_cost; 0 = squared Euclidean */
 } sk_problem;
 
 /* Bytes of device workspace needed for problem p (0 if p is invalid; see
@@ -131,6 +141,9 @@ sk_status sinkhorn_marginal_error(const sk_problem* p, const void* X, const void
  * grad is the gradient of <P, C> in the points with the plan held fixed, which
  * at converged potentials is the gradient of the entropic OT value (envelope
  * theorem).  bary does not depend on the potential of its own side.
+ * Under the cosine cost, bary is the projection among the normalised points of
+ * the other cloud, and grad is taken in the raw points (through the
+ * normalisation: it is orthogonal to its point).
  * bary and grad are fp32 DEVICE arrays owned by the caller; grad may be NULL.
  * These calls need a workspace of sinkhorn_transport_workspace_bytes(p) (a
  * superset of the solver's; every other call accepts it too) on which

@@ -5,10 +5,10 @@ The compute lives in libsinkhorn.so (HIP, gfx950), declared in include/sinkhorn.
 synthetic workloads.
 """
 
-from .binding import (SK_BF16, SK_FP32, SinkhornError, alloc_workspace, barycentric_x, barycentric_y,
+from .binding import (SK_BF16, SK_COSINE, SK_FP32, SK_SQEUCLID, SinkhornError, alloc_workspace, barycentric_x, barycentric_y,
                       half_step_f, half_step_g, init_norms, load_library, marginal_error, problem_of, solve,
                       workspace_bytes)
 
-__all__ = ["SK_BF16", "SK_FP32", "SinkhornError", "alloc_workspace", "barycentric_x", "barycentric_y",
+__all__ = ["SK_BF16", "SK_COSINE", "SK_FP32", "SK_SQEUCLID", "SinkhornError", "alloc_workspace", "barycentric_x", "barycentric_y",
            "half_step_f", "half_step_g", "init_norms", "load_library", "marginal_error", "problem_of", "solve",
            "workspace_bytes"]

@@ -6,6 +6,8 @@ There is no CPU fallback: if the library is missing, every call raises.
 
 Tensors: X [B, n, d] (or [n, d]), Y [B, m, d] (or [m, d]), float32 or bfloat16,
 contiguous, on a ROCm device; a [B, n], b [B, m], f [B, n], g [B, m] float32.
+Every call takes `cost` (SK_SQEUCLID or SK_COSINE); it must be the same for
+all calls on one workspace.
 """
 
 from __future__ import annotations
@@ -20,6 +22,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsinkhorn.so")
 
 SK_FP32, SK_BF16 = 0, 1
+SK_SQEUCLID, SK_COSINE = 0, 1  # ground cost: ||x - y||^2, or the same between normalised points
 STATUS = {0: "SK_OK", 1: "SK_EINVAL", 2: "SK_ESHAPE", 3: "SK_EDTYPE", 4: "SK_EHIP",
           5: "SK_EUNSUPPORTED", 6: "SK_EWORKSPACE"}
 EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_init_norms", "sinkhorn_half_step_f",
@@ -30,7 +33,7 @@ EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_init_norms", "sinkhorn_half_ste
 
 class SkProblem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("n", ctypes.c_int64), ("m", ctypes.c_int64),
-                ("d", ctypes.c_int64), ("dtype", ctypes.c_int32)]
+                ("d", ctypes.c_int64), ("dtype", ctypes.c_int32), ("cost", ctypes.c_int32)]
 
 
 class SinkhornError(RuntimeError):
@@ -94,14 +97,14 @@ def _as2(t: torch.Tensor) -> torch.Tensor:
     return t if t.dim() == 2 else t.unsqueeze(0)
 
 
-def problem_of(X: torch.Tensor, Y: torch.Tensor) -> SkProblem:
+def problem_of(X: torch.Tensor, Y: torch.Tensor, cost: int = SK_SQEUCLID) -> SkProblem:
     X3, Y3 = _as3(X), _as3(Y)
     if X3.dim() != 3 or Y3.dim() != 3 or X3.shape[0] != Y3.shape[0] or X3.shape[2] != Y3.shape[2]:
         raise ValueError(f"X {tuple(X.shape)} and Y {tuple(Y.shape)} must be [B,n,d] and [B,m,d]")
     if X.dtype != Y.dtype or X.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("X and Y must both be float32 or both bfloat16")
     dt = SK_FP32 if X.dtype == torch.float32 else SK_BF16
-    return SkProblem(X3.shape[0], X3.shape[1], Y3.shape[1], X3.shape[2], dt)
+    return SkProblem(X3.shape[0], X3.shape[1], Y3.shape[1], X3.shape[2], dt, int(cost))
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
@@ -118,17 +121,17 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def workspace_bytes(batch: int, n: int, m: int, d: int, dtype: int = SK_FP32) -> int:
-    p = SkProblem(batch, n, m, d, dtype)
+def workspace_bytes(batch: int, n: int, m: int, d: int, dtype: int = SK_FP32, cost: int = SK_SQEUCLID) -> int:
+    p = SkProblem(batch, n, m, d, dtype, cost)
     nb = load_library().sinkhorn_workspace_bytes(ctypes.byref(p))
     if nb == 0:
         _check(1)
     return int(nb)
 
 
-def alloc_workspace(X: torch.Tensor, Y: torch.Tensor, transport: bool = False) -> torch.Tensor:
+def alloc_workspace(X: torch.Tensor, Y: torch.Tensor, transport: bool = False, cost: int = SK_SQEUCLID) -> torch.Tensor:
     """Device workspace for the solver (transport=True: also for the barycentric calls)."""
-    p = problem_of(X, Y)
+    p = problem_of(X, Y, cost)
     lib = load_library()
     nb = (lib.sinkhorn_transport_workspace_bytes if transport else lib.sinkhorn_workspace_bytes)(ctypes.byref(p))
     if nb == 0:
@@ -136,15 +139,15 @@ def alloc_workspace(X: torch.Tensor, Y: torch.Tensor, transport: bool = False) -
     return torch.empty(nb, dtype=torch.uint8, device=X.device)
 
 
-def init_norms(X, Y, a, b, ws):
-    p = problem_of(X, Y)
+def init_norms(X, Y, a, b, ws, cost: int = SK_SQEUCLID):
+    p = problem_of(X, Y, cost)
     _check(load_library().sinkhorn_init_norms(
         ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(a, "a", torch.float32),
         _dev(b, "b", torch.float32), _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream()))
 
 
-def half_step_f(X, Y, ws, g, eps: float, f: Optional[torch.Tensor] = None) -> torch.Tensor:
-    p = problem_of(X, Y)
+def half_step_f(X, Y, ws, g, eps: float, f: Optional[torch.Tensor] = None, cost: int = SK_SQEUCLID) -> torch.Tensor:
+    p = problem_of(X, Y, cost)
     if f is None:
         f = torch.empty((p.batch, p.n), dtype=torch.float32, device=X.device)
     _check(load_library().sinkhorn_half_step_f(
@@ -153,8 +156,8 @@ def half_step_f(X, Y, ws, g, eps: float, f: Optional[torch.Tensor] = None) -> to
     return f
 
 
-def half_step_g(X, Y, ws, f, eps: float, g: Optional[torch.Tensor] = None) -> torch.Tensor:
-    p = problem_of(X, Y)
+def half_step_g(X, Y, ws, f, eps: float, g: Optional[torch.Tensor] = None, cost: int = SK_SQEUCLID) -> torch.Tensor:
+    p = problem_of(X, Y, cost)
     if g is None:
         g = torch.empty((p.batch, p.m), dtype=torch.float32, device=X.device)
     _check(load_library().sinkhorn_half_step_g(
@@ -163,15 +166,16 @@ def half_step_g(X, Y, ws, f, eps: float, g: Optional[torch.Tensor] = None) -> to
     return g
 
 
-def solve(X, Y, a, b, eps: Union[float, Sequence[float]], iters: int, f=None, g=None, ws=None):
+def solve(X, Y, a, b, eps: Union[float, Sequence[float]], iters: int, f=None, g=None, ws=None,
+          cost: int = SK_SQEUCLID):
     """Run sinkhorn_solve; f and g are in/out (zeros if not given).  Returns (f, g)."""
-    p = problem_of(X, Y)
+    p = problem_of(X, Y, cost)
     if f is None:
         f = torch.zeros((p.batch, p.n), dtype=torch.float32, device=X.device)
     if g is None:
         g = torch.zeros((p.batch, p.m), dtype=torch.float32, device=X.device)
     if ws is None:
-        ws = alloc_workspace(X, Y)
+        ws = alloc_workspace(X, Y, cost=cost)
     e = [float(eps)] if isinstance(eps, (int, float)) else [float(v) for v in eps]
     earr = (ctypes.c_float * len(e))(*e)
     _check(load_library().sinkhorn_solve(
@@ -181,8 +185,9 @@ def solve(X, Y, a, b, eps: Union[float, Sequence[float]], iters: int, f=None, g=
     return f, g
 
 
-def marginal_error(X, Y, ws, f, g, eps: float, err: Optional[torch.Tensor] = None) -> torch.Tensor:
-    p = problem_of(X, Y)
+def marginal_error(X, Y, ws, f, g, eps: float, err: Optional[torch.Tensor] = None,
+                   cost: int = SK_SQEUCLID) -> torch.Tensor:
+    p = problem_of(X, Y, cost)
     if err is None:
         err = torch.empty((p.batch, 2), dtype=torch.float32, device=X.device)
     _check(load_library().sinkhorn_marginal_error(
@@ -192,8 +197,8 @@ def marginal_error(X, Y, ws, f, g, eps: float, err: Optional[torch.Tensor] = Non
     return err
 
 
-def _barycentric(name, X, Y, ws, f, g, eps, rows, bary, grad, with_grad):
-    p = problem_of(X, Y)
+def _barycentric(name, X, Y, ws, f, g, eps, rows, bary, grad, with_grad, cost):
+    p = problem_of(X, Y, cost)
     shape = (p.batch, rows(p), p.d)
     if bary is None:
         bary = torch.empty(shape, dtype=torch.float32, device=X.device)
@@ -206,13 +211,15 @@ def _barycentric(name, X, Y, ws, f, g, eps, rows, bary, grad, with_grad):
     return bary, grad
 
 
-def barycentric_x(X, Y, ws, f, g, eps: float, bary=None, grad=None, with_grad: bool = True):
+def barycentric_x(X, Y, ws, f, g, eps: float, bary=None, grad=None, with_grad: bool = True,
+                  cost: int = SK_SQEUCLID):
     """Barycentric projection of the points of X under the plan of (f, g), and the
     gradient sum_j P_ij 2 (x_i - y_j).  ws must come from alloc_workspace(..., transport=True)."""
-    return _barycentric("sinkhorn_barycentric_x", X, Y, ws, f, g, eps, lambda p: p.n, bary, grad, with_grad)
+    return _barycentric("sinkhorn_barycentric_x", X, Y, ws, f, g, eps, lambda p: p.n, bary, grad, with_grad, cost)
 
 
-def barycentric_y(X, Y, ws, f, g, eps: float, bary=None, grad=None, with_grad: bool = True):
+def barycentric_y(X, Y, ws, f, g, eps: float, bary=None, grad=None, with_grad: bool = True,
+                  cost: int = SK_SQEUCLID):
     """Barycentric projection of the points of Y (columns of the plan) and the
     gradient sum_i P_ij 2 (y_j - x_i)."""
-    return _barycentric("sinkhorn_barycentric_y", X, Y, ws, f, g, eps, lambda p: p.m, bary, grad, with_grad)
+    return _barycentric("sinkhorn_barycentric_y", X, Y, ws, f, g, eps, lambda p: p.m, bary, grad, with_grad, cost)

@@ -155,13 +155,18 @@ __device__ __forceinline__ float rescale(float s, float m_old, float m_new) {
   return d < -300.f ? 0.f : ldexpf(s, (int)d);
 }
 
+// Coordinate k of a point cloud stored as fp32 or bf16.
+__device__ __forceinline__ float coord(const void* P, size_t k, int in_bf16) {
+  return in_bf16 ? bf16_f(static_cast<const u16*>(P)[k]) : static_cast<const float*>(P)[k];
+}
+
 // ---------------------------------------------------------------------------
 // Set-up kernels
 // ---------------------------------------------------------------------------
 // Largest |coordinate| of each problem's X (side 0) and Y (side 1): a strided
 // block reduction, then atomicMax on the float bits (values are >= 0, so the
 // unsigned order is the float order).  maxabs must be zero beforehand.
-__global__ __launch_bounds__(256) void k_maxabs(const void* __restrict__ X, const void* __restrict__ Y, int mode,
+__global__ __launch_bounds__(256) void k_maxabs(const void* __restrict__ X, const void* __restrict__ Y, int in_bf16,
                                                 long long nx, long long ny, unsigned* __restrict__ maxabs,
                                                 int batch) {
   __shared__ float red[256];
@@ -171,8 +176,7 @@ __global__ __launch_bounds__(256) void k_maxabs(const void* __restrict__ X, cons
   float mx = 0.f;
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < cnt; i += (long long)gridDim.x * 256) {
     const long long k = (long long)b * cnt + i;
-    const float v = mode == MODE_SPLIT ? static_cast<const float*>(P)[k] : bf16_f(static_cast<const u16*>(P)[k]);
-    mx = fmaxf(mx, fabsf(v));
+    mx = fmaxf(mx, fabsf(coord(P, (size_t)k, in_bf16)));
   }
   red[threadIdx.x] = mx;
   __syncthreads();
@@ -183,13 +187,16 @@ __global__ __launch_bounds__(256) void k_maxabs(const void* __restrict__ X, cons
   if (threadIdx.x == 0) atomicMax(&maxabs[side * batch + b], __float_as_uint(red[0]));
 }
 
-// Norms (fp64), log-weights (fp64) and operand rows of one cloud: the split
-// query layout (fp32 inputs) or a zero-padded bf16 copy (bf16 inputs).
+// Norms (fp64), log-weights (fp64), inverse norms and operand rows of one
+// cloud: the split query layout (fp32 inputs, or any input under the cosine
+// cost, whose points are first divided by their norm) or a zero-padded bf16
+// copy (bf16 inputs, squared-Euclidean cost).
 template <int MODE>
 __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, const float* __restrict__ w,
-                                                   int rows, int rows_pad, int d, int KP,
+                                                   int rows, int rows_pad, int d, int KP, int in_bf16, int cosine,
                                                    const float* __restrict__ maxabs, double* __restrict__ norm,
-                                                   double* __restrict__ logw, u16* __restrict__ opnd) {
+                                                   double* __restrict__ logw, double* __restrict__ rnorm,
+                                                   u16* __restrict__ opnd) {
   const int b = blockIdx.y;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= rows_pad) return;
@@ -207,6 +214,7 @@ __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, c
       nrm += v * v;
     }
     norm[r] = nrm;
+    rnorm[r] = 1.0;
     logw[r] = log((double)w[r]);
     for (int k = 0; k < KP; k += 2) {
       const uint32_t lo = (k < d) ? src[k] : 0, hi = (k + 1 < d) ? src[k + 1] : 0;
@@ -214,31 +222,41 @@ __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, c
     }
     return;
   }
-  const float* src = static_cast<const float*>(P) + r * d;
   const double q = grid_quantum(maxabs[b]);
   const double iq = 1.0 / q;
+  double rn = 1.0;
+  if (cosine) {
+    double raw = 0.0;
+    for (int t = 0; t < d; ++t) {
+      const double v = coord(P, r * d + t, in_bf16);
+      raw += v * v;
+    }
+    rn = raw > 0.0 ? 1.0 / sqrt(raw) : 0.0;  // a zero point stays zero
+  }
+  auto val = [&](int t) { return (double)coord(P, r * d + t, in_bf16) * rn; };
   double nrm = 0.0;
-  for (int t = 0; t < d; ++t) nrm += (double)src[t] * (double)src[t];
+  for (int t = 0; t < d; ++t) nrm += val(t) * val(t);
   norm[r] = nrm;
+  rnorm[r] = rn;
   logw[r] = log((double)w[r]);
   const int cb = split_corr_begin(d);
   for (int k0 = 0; k0 < KP; k0 += 8) {
     u16 v[8];
     for (int e = 0; e < 8; ++e) {
       const int k = k0 + e;
-      u16 val = 0;
+      u16 v_ = 0;
       if (k >= 2 && k <= 4) {
-        val = BF16_ONE;
+        v_ = BF16_ONE;
       } else if (k >= 5 && k < 5 + d) {
-        val = grid_split(src[k - 5], q, iq).g;
+        v_ = grid_split(val(k - 5), q, iq).g;
       } else if (k >= cb && k < cb + 7 * d) {
-        const Parts pp = grid_split(src[(k - cb) / 7], q, iq);
+        const Parts pp = grid_split(val((k - cb) / 7), q, iq);
         const int s = (k - cb) % 7;
-        val = (s <= 1) ? pp.g : ((s == 3 || s == 6) ? pp.r2 : pp.r1);
+        v_ = (s <= 1) ? pp.g : ((s == 3 || s == 6) ? pp.r2 : pp.r1);
       } else if (k == cb + 7 * d || k == cb + 7 * d + 1) {
-        val = BF16_ONE;
+        v_ = BF16_ONE;
       }
-      v[e] = val;
+      v[e] = v_;
     }
     *reinterpret_cast<u4*>(dst + k0) = u4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
                                          (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
@@ -249,7 +267,8 @@ __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, c
 // lambda*(pot - norm + eps*logw) in grid + remainder parts; writes the grid
 // quantum Q = q_query * q_key of each problem to qgrid.  One thread per 16-byte
 // segment of a row, so the stores are coalesced.
-__global__ __launch_bounds__(256) void k_prep_keys(const float* __restrict__ P, const float* __restrict__ pot,
+__global__ __launch_bounds__(256) void k_prep_keys(const void* __restrict__ P, int in_bf16,
+                                                   const double* __restrict__ rnorm, const float* __restrict__ pot,
                                                    const double* __restrict__ norm, const double* __restrict__ logw,
                                                    int keys, int keys_pad, int d, int KP, float lam, float eps,
                                                    const float* __restrict__ qmax, const float* __restrict__ kmax,
@@ -268,7 +287,8 @@ __global__ __launch_bounds__(256) void k_prep_keys(const float* __restrict__ P, 
   const int cb = split_corr_begin(d);
   const bool real = j < keys;
   const size_t r = (size_t)b * keys + j;
-  const float* src = P + r * d;
+  const double rn = real ? rnorm[r] : 1.0;
+  auto src = [&](int t) { return (double)coord(P, r * d + t, in_bf16) * rn; };
   // bias parts (only for the segments that hold them)
   u16 bp[5] = {0, 0, 0, 0, 0};
   if ((k0 <= 4) || (k0 + 8 > cb + 7 * d && k0 <= cb + 7 * d + 1)) {
@@ -304,7 +324,7 @@ __global__ __launch_bounds__(256) void k_prep_keys(const float* __restrict__ P, 
       if (real) {
         if (tc != k - 5) {
           tc = k - 5;
-          pc = grid_split(lam2 * (double)src[tc], qk, iqk);
+          pc = grid_split(lam2 * src(tc), qk, iqk);
         }
         val = pc.g;
       }
@@ -313,7 +333,7 @@ __global__ __launch_bounds__(256) void k_prep_keys(const float* __restrict__ P, 
         const int t = (k - cb) / 7, sl = (k - cb) % 7;
         if (tc != t) {
           tc = t;
-          pc = grid_split(lam2 * (double)src[t], qk, iqk);
+          pc = grid_split(lam2 * src(t), qk, iqk);
         }
         // key side of the corrections: v_1 v_2 v_g v_g v_1 v_2 v_1
         val = (sl == 2 || sl == 3) ? pc.g : ((sl == 1 || sl == 5) ? pc.r2 : pc.r1);
@@ -328,6 +348,12 @@ __global__ __launch_bounds__(256) void k_prep_keys(const float* __restrict__ P, 
   *reinterpret_cast<u4*>(kb + ((size_t)b * keys_pad + j) * KP + k0) =
       u4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
          (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
+}
+
+// Fill n floats with v.
+__global__ __launch_bounds__(256) void k_fill_f32(float* __restrict__ p, int n, float v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
 }
 
 // Zero-fill n 16-byte words (used instead of a memset so callers may capture it).
@@ -713,7 +739,8 @@ __device__ __forceinline__ u4 pack8(const u16 (&v)[8]) {
 // tile, col = part*d + t (the LDS image of the block), and ones in the last
 // column when it is spare (sumcol).  Padding keys and other columns are zero.
 // One thread per 8 keys of one column.
-__global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, int mode, int keys, int keys_pad, int d,
+__global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, int mode, int in_bf16,
+                                                   const double* __restrict__ rnorm, int keys, int keys_pad, int d,
                                                    int ncols, int sumcol, u16* __restrict__ vt) {
   const int b = blockIdx.y;
   const long long per_blk = (long long)ncols * (VK / 8);
@@ -736,7 +763,7 @@ __global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, i
         val = static_cast<const u16*>(P)[r];
       } else {
         // x = h0 + h1 + h2 exactly: each remainder is exact in fp32
-        const float x = static_cast<const float*>(P)[r];
+        const float x = (float)((double)coord(P, r, in_bf16) * rnorm[(size_t)b * keys + j]);
         const u16 h0 = bf16_rne(x);
         const float r1 = x - bf16_f(h0);
         const u16 h1 = bf16_rne(r1);
@@ -971,7 +998,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
 // grad = 2 r (p - bary) with the row mass r = w exp((pot - lse)/eps).
 __global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv, const float* __restrict__ sp, int ks,
                                                     int batch, int rows, int d, int ncols, int parts, int sumcol,
-                                                    const void* __restrict__ P, int mode,
+                                                    const void* __restrict__ P, int in_bf16,
                                                     const float* __restrict__ pot, const float* __restrict__ lse,
                                                     const double* __restrict__ logw, double eps,
                                                     float* __restrict__ bary, float* __restrict__ grad) {
@@ -988,10 +1015,34 @@ __global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv
   const double bc = num / S;
   bary[idx] = (float)bc;
   if (grad != nullptr) {
-    const double x = mode == MODE_SPLIT ? (double)static_cast<const float*>(P)[idx]
-                                        : (double)bf16_f(static_cast<const u16*>(P)[idx]);
+    const double x = coord(P, (size_t)idx, in_bf16);
     const double mass = exp(logw[rr] + ((double)pot[rr] - (double)lse[rr]) / eps);
     grad[idx] = (float)(2.0 * mass * (x - bc));
+  }
+}
+
+// Cosine cost: the gradient in the raw point p from the barycentric projection
+// of p_hat = p/|p| among the normalised points, by the chain rule through the
+// normalisation: grad = (I - p_hat p_hat^T) 2 r (p_hat - bary) / |p|.  One
+// thread per (problem, row); a zero point gets a zero gradient.
+__global__ __launch_bounds__(256) void k_cosine_grad(const float* __restrict__ bary, const void* __restrict__ P,
+                                                     int in_bf16, const double* __restrict__ rnorm,
+                                                     const float* __restrict__ pot, const float* __restrict__ lse,
+                                                     const double* __restrict__ logw, double eps, long long total,
+                                                     int d, float* __restrict__ grad) {
+  const long long rr = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (rr >= total) return;
+  const double rn = rnorm[rr];
+  const double mass = exp(logw[rr] + ((double)pot[rr] - (double)lse[rr]) / eps);
+  double radial = 0.0;  // p_hat . (p_hat - bary)
+  for (int t = 0; t < d; ++t) {
+    const double ph = (double)coord(P, (size_t)rr * d + t, in_bf16) * rn;
+    radial += ph * (ph - (double)bary[rr * d + t]);
+  }
+  for (int t = 0; t < d; ++t) {
+    const double ph = (double)coord(P, (size_t)rr * d + t, in_bf16) * rn;
+    const double gh = 2.0 * mass * (ph - (double)bary[rr * d + t]);
+    grad[rr * d + t] = (float)((gh - radial * 2.0 * mass * ph) * rn);
   }
 }
 
@@ -1000,7 +1051,8 @@ __global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv
 // ---------------------------------------------------------------------------
 struct Layout {
   int mode, KP, n_pad, m_pad, max_pad;
-  size_t xn, yn, la, lb, maxabs, qgrid, qx, qy, kb, hb, part, scratch, total;
+  int in_bf16, cosine;
+  size_t xn, yn, la, lb, rx, ry, maxabs, qgrid, qx, qy, kb, hb, part, scratch, total;
   // transport application (after `total`; only its entry points need them)
   int ncols, ksb;
   size_t vt, bpv, bs, ttotal;
@@ -1031,8 +1083,13 @@ sk_status check_problem(const sk_problem* p) {
     set_err("d = %lld exceeds SK_MAX_D = %d", (long long)p->d, SK_MAX_D);
     return SK_EUNSUPPORTED;
   }
-  if (p->dtype == SK_FP32 && p->d > SK_MAX_D_FP32) {
-    set_err("d = %lld exceeds SK_MAX_D_FP32 = %d for fp32 inputs", (long long)p->d, SK_MAX_D_FP32);
+  if (p->cost != SK_COST_SQEUCLID && p->cost != SK_COST_COSINE) {
+    set_err("unknown cost %d (expected SK_COST_SQEUCLID=0 or SK_COST_COSINE=1)", (int)p->cost);
+    return SK_EINVAL;
+  }
+  if ((p->dtype == SK_FP32 || p->cost == SK_COST_COSINE) && p->d > SK_MAX_D_FP32) {
+    set_err("d = %lld exceeds SK_MAX_D_FP32 = %d for fp32 inputs and the cosine cost", (long long)p->d,
+            SK_MAX_D_FP32);
     return SK_EUNSUPPORTED;
   }
   const int64_t lim = (int64_t)1 << 30;
@@ -1045,7 +1102,10 @@ sk_status check_problem(const sk_problem* p) {
 
 Layout layout_of(const sk_problem* p) {
   Layout L{};
-  L.mode = (p->dtype == SK_BF16) ? MODE_BF16 : MODE_SPLIT;
+  L.in_bf16 = p->dtype == SK_BF16;
+  L.cosine = p->cost == SK_COST_COSINE;
+  // bf16 operands are used as they are; fp32 inputs and normalised points take the split layout
+  L.mode = (L.in_bf16 && !L.cosine) ? MODE_BF16 : MODE_SPLIT;
   L.KP = kp_for(L.mode, p->d);
   L.n_pad = (int)align_up((size_t)p->n, ROW_PAD);
   L.m_pad = (int)align_up((size_t)p->m, ROW_PAD);
@@ -1061,6 +1121,8 @@ Layout layout_of(const sk_problem* p) {
   L.yn = take(8 * B * m);
   L.la = take(8 * B * n);
   L.lb = take(8 * B * m);
+  L.rx = take(8 * B * n);
+  L.ry = take(8 * B * m);
   L.maxabs = take(align_up(4 * 2 * B, 16));
   L.qgrid = take(4 * B);
   // SLACK extra rows after each operand buffer absorb the kernels' unguarded
@@ -1213,7 +1275,8 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   if (L.mode == MODE_SPLIT) {
     u16* kb = reinterpret_cast<u16*>(w + L.kb);
     const dim3 kgrid((unsigned)(((long long)keys_pad * (L.KP / 8) + 255) / 256), B);
-    hipLaunchKernelGGL(k_prep_keys, kgrid, dim3(256), 0, stream, static_cast<const float*>(Kraw), pot_in, knorm,
+    const double* krn = reinterpret_cast<const double*>(w + (side == 0 ? L.ry : L.rx));
+    hipLaunchKernelGGL(k_prep_keys, kgrid, dim3(256), 0, stream, Kraw, L.in_bf16, krn, pot_in, knorm,
                        klogw, keys, keys_pad, (int)p->d, L.KP, lam, eps, maxabs + (side == 0 ? 0 : B),
                        maxabs + (side == 0 ? B : 0), qgrid, kb);
     Kop = kb;
@@ -1300,8 +1363,9 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   u16* vt = reinterpret_cast<u16*>(w + L.vt);
   const long long nvec = (long long)(keys_pad / VK) * L.ncols * (VK / 8);
   const int sumcol = val_sumcol(L.mode, d) ? 1 : 0;
-  hipLaunchKernelGGL(k_prep_vals, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, Kraw, L.mode, keys,
-                     keys_pad, d, L.ncols, sumcol, vt);
+  const double* krn = reinterpret_cast<const double*>(w + (side == 0 ? L.ry : L.rx));
+  hipLaunchKernelGGL(k_prep_vals, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, Kraw, L.mode,
+                     L.in_bf16, krn, keys, keys_pad, d, L.ncols, sumcol, vt);
   st = hip_check("value preparation launch");
   if (st != SK_OK) return st;
 
@@ -1334,9 +1398,15 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   // 4. Merge the splits, divide, form the gradient.
   const long long total = (long long)B * rows * d;
   hipLaunchKernelGGL(k_bary_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, bs, ks, B, rows,
-                     d, L.ncols, val_parts(L.mode), sumcol, Praw, L.mode, pot_row, lse, qlogw, (double)eps, bary,
-                     grad);
-  return hip_check("transport merge launch");
+                     d, L.ncols, val_parts(L.mode), sumcol, Praw, L.in_bf16, pot_row, lse, qlogw, (double)eps, bary,
+                     L.cosine ? nullptr : grad);
+  st = hip_check("transport merge launch");
+  if (st != SK_OK || !L.cosine || grad == nullptr) return st;
+  const double* qrn = reinterpret_cast<const double*>(w + (side == 0 ? L.rx : L.ry));
+  const long long nrows = (long long)B * rows;
+  hipLaunchKernelGGL(k_cosine_grad, dim3((unsigned)((nrows + 255) / 256)), dim3(256), 0, stream, bary, Praw,
+                     L.in_bf16, qrn, pot_row, lse, qlogw, (double)eps, nrows, d, grad);
+  return hip_check("cosine gradient launch");
 }
 
 sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const float* a, const float* b, void* ws,
@@ -1349,25 +1419,32 @@ sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const flo
     if (n16) hipLaunchKernelGGL(k_zero, dim3((unsigned)std::min<size_t>((n16 + 255) / 256, 4096)), dim3(256), 0,
                                 stream, reinterpret_cast<u4*>(w + off), n16);
   };
-  zero(L.maxabs, align_up(8 * (size_t)B, 16));
-  const long long most = std::max(p->n, p->m) * p->d;
-  const unsigned mblocks = (unsigned)std::min<long long>((most + 255) / 256, 64);
-  hipLaunchKernelGGL(k_maxabs, dim3(mblocks, B, 2), dim3(256), 0, stream, X, Y, L.mode, (long long)(p->n * p->d),
-                     (long long)(p->m * p->d), reinterpret_cast<unsigned*>(maxabs), B);
+  if (L.cosine) {
+    // normalised points: every coordinate is at most 1 in magnitude
+    hipLaunchKernelGGL(k_fill_f32, dim3((2 * B + 255) / 256), dim3(256), 0, stream, maxabs, 2 * B, 1.f);
+  } else {
+    zero(L.maxabs, align_up(8 * (size_t)B, 16));
+    const long long most = std::max(p->n, p->m) * p->d;
+    const unsigned mblocks = (unsigned)std::min<long long>((most + 255) / 256, 64);
+    hipLaunchKernelGGL(k_maxabs, dim3(mblocks, B, 2), dim3(256), 0, stream, X, Y, L.in_bf16,
+                       (long long)(p->n * p->d), (long long)(p->m * p->d), reinterpret_cast<unsigned*>(maxabs), B);
+  }
   auto side = [&](const void* P, const float* wt, int rows, int rows_pad, const float* mabs, size_t norm,
-                  size_t logw, size_t op) {
+                  size_t logw, size_t rnorm, size_t op) {
     const dim3 grid((rows_pad + 255) / 256, B);
     if (L.mode == MODE_SPLIT)
       hipLaunchKernelGGL(k_init_side<MODE_SPLIT>, grid, dim3(256), 0, stream, P, wt, rows, rows_pad, (int)p->d,
-                         L.KP, mabs, reinterpret_cast<double*>(w + norm), reinterpret_cast<double*>(w + logw),
+                         L.KP, L.in_bf16, L.cosine, mabs, reinterpret_cast<double*>(w + norm),
+                         reinterpret_cast<double*>(w + logw), reinterpret_cast<double*>(w + rnorm),
                          reinterpret_cast<u16*>(w + op));
     else
       hipLaunchKernelGGL(k_init_side<MODE_BF16>, grid, dim3(256), 0, stream, P, wt, rows, rows_pad, (int)p->d,
-                         L.KP, mabs, reinterpret_cast<double*>(w + norm), reinterpret_cast<double*>(w + logw),
+                         L.KP, L.in_bf16, L.cosine, mabs, reinterpret_cast<double*>(w + norm),
+                         reinterpret_cast<double*>(w + logw), reinterpret_cast<double*>(w + rnorm),
                          reinterpret_cast<u16*>(w + op));
   };
-  side(X, a, (int)p->n, L.n_pad, maxabs, L.xn, L.la, L.qx);
-  side(Y, b, (int)p->m, L.m_pad, maxabs + B, L.yn, L.lb, L.qy);
+  side(X, a, (int)p->n, L.n_pad, maxabs, L.xn, L.la, L.rx, L.qx);
+  side(Y, b, (int)p->m, L.m_pad, maxabs + B, L.yn, L.lb, L.ry, L.qy);
   return hip_check("init kernel launch");
 }
 

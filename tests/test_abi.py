@@ -134,3 +134,19 @@ def test_transport_workspace_and_argument_errors(lib):
         assert fn(bp, ptr, ptr, ptr, full, None, ptr, 0.1, ptr, ptr, None) == 1
         assert fn(bp, ptr, ptr, ptr, full, ptr, ptr, 0.0, ptr, ptr, None) == 1
         assert fn(ctypes.byref(_prob(d=89)), ptr, ptr, ptr, full, ptr, ptr, 0.1, ptr, ptr, None) == 5
+
+
+def test_cost_field_validation(lib):
+    ptr = ctypes.c_void_p(0x1000)
+    bad = binding.SkProblem(1, 10, 12, 3, 0, 7)
+    assert lib.sinkhorn_workspace_bytes(ctypes.byref(bad)) == 0
+    assert lib.sinkhorn_half_step_f(ctypes.byref(bad), ptr, ptr, ptr, 1 << 40, ptr, 0.1, ptr, None) == 1
+    assert b"cost" in lib.sinkhorn_last_error()
+    # the cosine cost uses the split layout: bf16 inputs are limited like fp32 ones
+    assert lib.sinkhorn_workspace_bytes(ctypes.byref(binding.SkProblem(1, 10, 12, 100, 1, 1))) == 0
+    assert lib.sinkhorn_workspace_bytes(ctypes.byref(binding.SkProblem(1, 10, 12, 100, 1, 0))) > 0
+    sq = lib.sinkhorn_workspace_bytes(ctypes.byref(binding.SkProblem(1, 1000, 1000, 64, 1, 0)))
+    cos = lib.sinkhorn_workspace_bytes(ctypes.byref(binding.SkProblem(1, 1000, 1000, 64, 1, 1)))
+    assert cos > sq > 0
+    text = open(HEADER).read()
+    assert "SK_COST_SQEUCLID = 0" in text and "SK_COST_COSINE = 1" in text
