@@ -23,6 +23,11 @@ Parity status of each function:
       weighted mean, eps->0 assignment limit, finite differences of the
       converged dual value, translation balance of the two gradients,
       numpy brute force on tiny inputs)
+  apply_plan_x / apply_plan_y : pinned (dense numpy plan; equals mass * bary
+      for V = the other cloud)
+  hvp_x            : pinned (central finite differences of the converged
+      gradient along the direction; symmetry of the Hessian; zero for a common
+      translation of both clouds in the joint form)
   normalize / cosine_grad : pinned (cost = 2 - 2 cos of the angle in closed
       form for d = 2, invariance of the potentials under positive rescaling of
       points, finite differences of the converged dual value in the raw points,
@@ -79,6 +84,10 @@ def _load():
                                      _D, _D, ctypes.c_double, _I64, ctypes.c_int64, _D, _D, _D,
                                      ctypes.c_int]
     lib.oracle_transport.restype = None
+    lib.oracle_apply_plan.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _D, _D, _D, _D,
+                                      _D, _D, ctypes.c_double, _D, ctypes.c_int64, _I64, ctypes.c_int64,
+                                      _D, ctypes.c_int]
+    lib.oracle_apply_plan.restype = None
     _lib = lib
     return lib
 
@@ -239,3 +248,66 @@ def cosine_grad(P, grad_hat) -> np.ndarray:
             ph = P[i] / nrm
             out[i] = (G[i] - (ph @ G[i]) * ph) / nrm
     return out
+
+
+def apply_plan(P, Q, wp, wq, hp, hq, eps: float, V, rows=None, threads: Optional[int] = None) -> np.ndarray:
+    """out_r = sum_j pi_rj V_j with pi_rj = wp_r wq_j exp((hp_r + hq_j - ||P_r - Q_j||^2)/eps)."""
+    lib = _load()
+    P, Q, wp, wq, hp, hq = (_f64(v) for v in (P, Q, wp, wq, hp, hq))
+    V = _f64(V)
+    squeeze = V.ndim == 1
+    if squeeze:
+        V = V[:, None].copy()
+    np_, d = P.shape
+    nq, c = V.shape
+    assert Q.shape == (nq, d)
+    if rows is None:
+        k, rp = np_, None
+    else:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        k, rp = rows.size, rows.ctypes.data_as(_I64)
+    out = np.empty((k, c), dtype=np.float64)
+    lib.oracle_apply_plan(np_, nq, d, _ptr(P), _ptr(Q), _ptr(wp), _ptr(wq), _ptr(hp), _ptr(hq), float(eps),
+                          _ptr(V), c, rp, k, _ptr(out), int(threads or 0))
+    return out[:, 0] if squeeze else out
+
+
+def apply_plan_x(X, Y, a, b, f, g, eps: float, V, rows=None, threads=None):
+    """(P V)_i = sum_j P_ij V_j, V: [m] or [m, c]."""
+    return apply_plan(X, Y, a, b, f, g, eps, V, rows=rows, threads=threads)
+
+
+def apply_plan_y(X, Y, a, b, f, g, eps: float, U, rows=None, threads=None):
+    """(P^T U)_j = sum_i P_ij U_i, U: [n] or [n, c]."""
+    return apply_plan(Y, X, b, a, g, f, eps, U, rows=rows, threads=threads)
+
+
+def hvp_x(X, Y, a, b, f, g, eps: float, V) -> np.ndarray:
+    """Hessian of the entropic OT value in the points X, applied to the direction V
+    (page "FlashSinkhorn: IO-aware entropic OT on GPU", section "Differentiation and
+    second-order optimisation": Hessian-vector products without the Hessian).
+
+    Plain dense definition for small problems, at potentials (f, g) taken as optimal:
+    the gradient is G_i = sum_j P_ij 2 (x_i - y_j).  Moving X along V moves the cost by
+    dC_ij = 2 (x_i - y_j) . v_i and the potentials by (df, dg), which keep the plan's
+    marginals fixed:  sum_j P_ij (df_i + dg_j - dC_ij) = 0 for every i and
+    sum_i P_ij (df_i + dg_j - dC_ij) = 0 for every j  (solved here by least squares on
+    the full (n+m) system; its null direction (1, -1) does not change the plan).  Then
+    dP = P * (df + dg - dC)/eps and  H V = sum_j dP_ij 2 (x_i - y_j) + 2 (sum_j P_ij) v_i.
+    """
+    X, Y, a, b, f, g, V = (_f64(v) for v in (X, Y, a, b, f, g, V))
+    n, m = X.shape[0], Y.shape[0]
+    D = X[:, None, :] - Y[None, :, :]                      # x_i - y_j
+    C = (D * D).sum(-1)
+    P = a[:, None] * b[None, :] * np.exp((f[:, None] + g[None, :] - C) / eps)
+    dC = 2.0 * (D * V[:, None, :]).sum(-1)
+    A = np.zeros((n + m, n + m))
+    A[:n, :n] = np.diag(P.sum(1))
+    A[:n, n:] = P
+    A[n:, :n] = P.T
+    A[n:, n:] = np.diag(P.sum(0))
+    rhs = np.concatenate([(P * dC).sum(1), (P * dC).sum(0)])
+    sol = np.linalg.lstsq(A, rhs, rcond=None)[0]
+    df, dg = sol[:n], sol[n:]
+    dP = P * (df[:, None] + dg[None, :] - dC) / eps
+    return 2.0 * (dP[:, :, None] * D).sum(1) + 2.0 * P.sum(1)[:, None] * V

@@ -214,3 +214,31 @@ void oracle_transport(int64_t np_, int64_t nq, int64_t d, const double* P, const
     }
     (void)nt;
 }
+
+/*
+ * Plan applied to a matrix (page "FlashSinkhorn: IO-aware entropic OT on GPU",
+ * section "Differentiation and second-order optimisation": vector- and
+ * matrix-transport products):
+ *   out[r*c + k] = sum_j pi_rj V[j*c + k],  pi_rj = wp_r wq_j exp((hp_r + hq_j - C_rj)/eps)
+ * for the selected rows r of P (rows NULL = all).  V is [nq, c].
+ */
+void oracle_apply_plan(int64_t np_, int64_t nq, int64_t d, const double* P, const double* Q,
+                       const double* wp, const double* wq, const double* hp, const double* hq,
+                       double eps, const double* V, int64_t c, const int64_t* rows, int64_t nsel,
+                       double* out, int nthreads) {
+    if (rows == NULL) nsel = np_;
+    int nt = oracle_threads(nthreads);
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(nt)
+#endif
+    for (int64_t r = 0; r < nsel; ++r) {
+        int64_t i = rows ? rows[r] : r;
+        const double* p = P + i * d;
+        for (int64_t k = 0; k < c; ++k) out[r * c + k] = 0.0;
+        for (int64_t j = 0; j < nq; ++j) {
+            double pij = wp[i] * wq[j] * exp((hp[i] + hq[j] - sq_dist(p, Q + j * d, d)) / eps);
+            for (int64_t k = 0; k < c; ++k) out[r * c + k] += pij * V[j * c + k];
+        }
+    }
+    (void)nt;
+}
