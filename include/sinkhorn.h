@@ -162,6 +162,49 @@ sk_status sinkhorn_barycentric_y(const sk_problem* p, const void* X, const void*
                                  size_t ws_bytes, const float* f, const float* g, float eps,
                                  float* bary, float* grad, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Plan application: vector- and matrix-transport products (page "FlashSinkhorn:
+ * IO-aware entropic OT on GPU", section "Differentiation and second-order
+ * optimisation"), streamed like the transport calls, the plan never formed:
+ *   sinkhorn_apply_plan_x:  out[b][i][k] = sum_j P_ij V[b][j][k]   V [batch][m][c] -> out [batch][n][c]
+ *   sinkhorn_apply_plan_y:  out[b][j][k] = sum_i P_ij U[b][i][k]   U [batch][n][c] -> out [batch][m][c]
+ * fp32 DEVICE arrays; c >= 1 columns (processed in passes of 64).  Each value is
+ * carried as three exact bf16 parts.  Workspace: sinkhorn_transport_workspace_bytes.
+ * --------------------------------------------------------------------------- */
+sk_status sinkhorn_apply_plan_x(const sk_problem* p, const void* X, const void* Y, void* ws,
+                                size_t ws_bytes, const float* f, const float* g, float eps,
+                                const float* V, int64_t c, float* out, void* stream);
+
+sk_status sinkhorn_apply_plan_y(const sk_problem* p, const void* X, const void* Y, void* ws,
+                                size_t ws_bytes, const float* f, const float* g, float eps,
+                                const float* U, int64_t c, float* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Hessian-vector products of the entropic OT value in the points (same page and
+ * section: the HVP decomposes into transport products, with no Hessian and no
+ * plan in memory; working memory O((n+m) d)).
+ *   sinkhorn_hvp_x:  out = (d^2 OT / dX^2) V,  V and out [batch][n][d]
+ *   sinkhorn_hvp_y:  out = (d^2 OT / dY^2) V,  V and out [batch][m][d]
+ * at potentials (f, g) taken as optimal (pass the result of a converged solve).
+ * Moving the points along V moves the potentials by (df, dg) that keep the plan's
+ * marginals; df is eliminated and dg solves the Schur system
+ * (diag(c) - P^T diag(1/r) P) dg = rhs by conjugate gradients (Jacobi
+ * preconditioned, at most cg_iters iterations, stopped per problem when the
+ * preconditioned residual falls below cg_tol relative to its start), each
+ * iteration two one-column plan applications.  Squared-Euclidean cost only
+ * (SK_EUNSUPPORTED for the cosine cost).  Workspace: sinkhorn_hvp_workspace_bytes
+ * (a superset of the transport workspace), after sinkhorn_init_norms.
+ * --------------------------------------------------------------------------- */
+size_t sinkhorn_hvp_workspace_bytes(const sk_problem* p);
+
+sk_status sinkhorn_hvp_x(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
+                         const float* f, const float* g, float eps, const float* V, int64_t cg_iters,
+                         float cg_tol, float* out, void* stream);
+
+sk_status sinkhorn_hvp_y(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
+                         const float* f, const float* g, float eps, const float* V, int64_t cg_iters,
+                         float cg_tol, float* out, void* stream);
+
 /* Text for the last error on the calling thread ("" if none). */
 const char* sinkhorn_last_error(void);
 

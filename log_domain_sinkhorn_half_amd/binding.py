@@ -28,7 +28,8 @@ STATUS = {0: "SK_OK", 1: "SK_EINVAL", 2: "SK_ESHAPE", 3: "SK_EDTYPE", 4: "SK_EHI
 EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_init_norms", "sinkhorn_half_step_f",
            "sinkhorn_half_step_g", "sinkhorn_solve", "sinkhorn_marginal_error",
            "sinkhorn_transport_workspace_bytes", "sinkhorn_barycentric_x", "sinkhorn_barycentric_y",
-           "sinkhorn_last_error")
+           "sinkhorn_apply_plan_x", "sinkhorn_apply_plan_y", "sinkhorn_hvp_workspace_bytes",
+           "sinkhorn_hvp_x", "sinkhorn_hvp_y", "sinkhorn_last_error")
 
 
 class SkProblem(ctypes.Structure):
@@ -75,6 +76,17 @@ def load_library(path: Optional[str] = None):
     for name in ("sinkhorn_barycentric_x", "sinkhorn_barycentric_y"):
         fn = getattr(lib, name)
         fn.argtypes = [P, vp, vp, vp, sz, f32p, f32p, ctypes.c_float, f32p, f32p, vp]
+        fn.restype = ctypes.c_int
+    for name in ("sinkhorn_apply_plan_x", "sinkhorn_apply_plan_y"):
+        fn = getattr(lib, name)
+        fn.argtypes = [P, vp, vp, vp, sz, f32p, f32p, ctypes.c_float, f32p, ctypes.c_int64, f32p, vp]
+        fn.restype = ctypes.c_int
+    lib.sinkhorn_hvp_workspace_bytes.argtypes = [P]
+    lib.sinkhorn_hvp_workspace_bytes.restype = sz
+    for name in ("sinkhorn_hvp_x", "sinkhorn_hvp_y"):
+        fn = getattr(lib, name)
+        fn.argtypes = [P, vp, vp, vp, sz, f32p, f32p, ctypes.c_float, f32p, ctypes.c_int64, ctypes.c_float,
+                       f32p, vp]
         fn.restype = ctypes.c_int
     lib.sinkhorn_last_error.argtypes = []
     lib.sinkhorn_last_error.restype = ctypes.c_char_p
@@ -129,11 +141,15 @@ def workspace_bytes(batch: int, n: int, m: int, d: int, dtype: int = SK_FP32, co
     return int(nb)
 
 
-def alloc_workspace(X: torch.Tensor, Y: torch.Tensor, transport: bool = False, cost: int = SK_SQEUCLID) -> torch.Tensor:
-    """Device workspace for the solver (transport=True: also for the barycentric calls)."""
+def alloc_workspace(X: torch.Tensor, Y: torch.Tensor, transport: bool = False, cost: int = SK_SQEUCLID,
+                    hvp: bool = False) -> torch.Tensor:
+    """Device workspace for the solver (transport=True: also for the barycentric and
+    plan-application calls; hvp=True: also for the Hessian-vector products)."""
     p = problem_of(X, Y, cost)
     lib = load_library()
-    nb = (lib.sinkhorn_transport_workspace_bytes if transport else lib.sinkhorn_workspace_bytes)(ctypes.byref(p))
+    size_fn = (lib.sinkhorn_hvp_workspace_bytes if hvp else
+               lib.sinkhorn_transport_workspace_bytes if transport else lib.sinkhorn_workspace_bytes)
+    nb = size_fn(ctypes.byref(p))
     if nb == 0:
         _check(1)
     return torch.empty(nb, dtype=torch.uint8, device=X.device)
@@ -223,3 +239,49 @@ def barycentric_y(X, Y, ws, f, g, eps: float, bary=None, grad=None, with_grad: b
     """Barycentric projection of the points of Y (columns of the plan) and the
     gradient sum_i P_ij 2 (y_j - x_i)."""
     return _barycentric("sinkhorn_barycentric_y", X, Y, ws, f, g, eps, lambda p: p.m, bary, grad, with_grad, cost)
+
+
+def _apply(name, X, Y, ws, f, g, eps, M, rows, out, cost):
+    p = problem_of(X, Y, cost)
+    squeeze = M.dim() == 2
+    M3 = M.unsqueeze(-1) if squeeze else M
+    c = M3.shape[-1]
+    if out is None:
+        out = torch.empty((p.batch, rows(p), c), dtype=torch.float32, device=X.device)
+    _check(getattr(load_library(), name)(
+        ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(ws, "ws"), ws.numel() * ws.element_size(),
+        _dev(f, "f", torch.float32), _dev(g, "g", torch.float32), float(eps), _dev(M3, "matrix", torch.float32),
+        int(c), _dev(out, "out", torch.float32), _stream()))
+    return out.squeeze(-1) if squeeze else out
+
+
+def apply_plan_x(X, Y, ws, f, g, eps: float, V, out=None, cost: int = SK_SQEUCLID):
+    """(P V)_i = sum_j P_ij V_j for V [B, m, c] (or [B, m]); ws from alloc_workspace(..., transport=True)."""
+    return _apply("sinkhorn_apply_plan_x", X, Y, ws, f, g, eps, V, lambda p: p.n, out, cost)
+
+
+def apply_plan_y(X, Y, ws, f, g, eps: float, U, out=None, cost: int = SK_SQEUCLID):
+    """(P^T U)_j = sum_i P_ij U_i for U [B, n, c] (or [B, n])."""
+    return _apply("sinkhorn_apply_plan_y", X, Y, ws, f, g, eps, U, lambda p: p.m, out, cost)
+
+
+def _hvp(name, X, Y, ws, f, g, eps, V, cg_iters, cg_tol, out):
+    p = problem_of(X, Y)
+    if out is None:
+        out = torch.empty_like(V, dtype=torch.float32)
+    _check(getattr(load_library(), name)(
+        ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(ws, "ws"), ws.numel() * ws.element_size(),
+        _dev(f, "f", torch.float32), _dev(g, "g", torch.float32), float(eps), _dev(V, "V", torch.float32),
+        int(cg_iters), float(cg_tol), _dev(out, "out", torch.float32), _stream()))
+    return out
+
+
+def hvp_x(X, Y, ws, f, g, eps: float, V, cg_iters: int = 200, cg_tol: float = 1e-6, out=None):
+    """Hessian of the entropic OT value in X applied to V [B, n, d], at optimal (f, g).
+    ws from alloc_workspace(..., hvp=True)."""
+    return _hvp("sinkhorn_hvp_x", X, Y, ws, f, g, eps, V, cg_iters, cg_tol, out)
+
+
+def hvp_y(X, Y, ws, f, g, eps: float, V, cg_iters: int = 200, cg_tol: float = 1e-6, out=None):
+    """Hessian of the entropic OT value in Y applied to V [B, m, d], at optimal (f, g)."""
+    return _hvp("sinkhorn_hvp_y", X, Y, ws, f, g, eps, V, cg_iters, cg_tol, out)

@@ -727,7 +727,10 @@ __host__ __device__ constexpr int val_tiles(int mode, int d) { return (val_parts
 // A spare value column holds ones, so the P.V product also yields the sum of the weights.
 __host__ __device__ constexpr bool val_sumcol(int mode, int d) { return val_parts(mode) * d < val_tiles(mode, d) * 16; }
 // query tiles of 16 rows per wave, and waves per SIMD, of the transport kernel
-__host__ __device__ constexpr int bary_R(int nch) { return nch == 1 ? 4 : (nch <= 8 ? 2 : 1); }
+// (nct value tiles of accumulators per query tile must fit beside the operands)
+__host__ __device__ constexpr int bary_R(int nch, int nct) {
+  return nct >= 9 ? 1 : (nch == 1 ? (nct >= 4 ? 2 : 4) : (nch <= 8 ? 2 : 1));
+}
 __host__ __device__ constexpr int bary_waves(int nch) { return nch >= 12 ? 1 : 2; }
 
 __device__ __forceinline__ u4 pack8(const u16 (&v)[8]) {
@@ -796,7 +799,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, const float* __restrict__ lse,
     float* __restrict__ pv_out, float* __restrict__ s_out, int rows, int rows_pad, int keys, int keys_pad,
     int chunks_per_split, int batch, float lam, float lam2) {
-  constexpr int MW = 16, R = bary_R(NCH);
+  constexpr int MW = 16, R = bary_R(NCH, NCT);
   using T = Tile<16>;
   constexpr int KP = NCH * 32;
   constexpr int NI = KP / T::KI;
@@ -1047,15 +1050,294 @@ __global__ __launch_bounds__(256) void k_cosine_grad(const float* __restrict__ b
 }
 
 // ---------------------------------------------------------------------------
+// Plan application and Hessian-vector products (page "FlashSinkhorn: IO-aware
+// entropic OT on GPU", section "Differentiation and second-order
+// optimisation": the Hessian-vector product decomposes into vector- and
+// matrix-transport products, so neither the Hessian nor the plan is formed).
+// A plan application out_i = sum_j P_ij V_j is the transport pass above with V
+// an arbitrary fp32 matrix, scaled by the row mass.
+// ---------------------------------------------------------------------------
+constexpr int APPLY_COLS = 64;  // matrix columns per pass (3 parts each + the ones column <= 13 tiles)
+
+__host__ __device__ constexpr int apply_tiles(int cb) { return cb <= 5 ? 1 : (cb <= 21 ? 4 : 13); }
+
+// Value operand from columns col0 .. col0+cb-1 of an fp32 matrix M [B][keys][c]:
+// three exact bf16 parts per column (col = part*cb + k) and ones in the last
+// column.  One thread per 8 keys of one column.
+__global__ __launch_bounds__(256) void k_prep_mat(const float* __restrict__ M, int keys, int keys_pad, int c, int col0,
+                                                  int cb, int ncols, u16* __restrict__ vt) {
+  const int b = blockIdx.y;
+  const long long per_blk = (long long)ncols * (VK / 8);
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)(keys_pad / VK) * per_blk) return;
+  const int blk = (int)(idx / per_blk);
+  const int rem = (int)(idx % per_blk);
+  const int cc = rem / (VK / 8), k0 = (rem % (VK / 8)) * 8;
+  u16 v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int j = blk * VK + k0 + e;
+    u16 val = 0;
+    if (j < keys && cc == ncols - 1) {
+      val = BF16_ONE;
+    } else if (j < keys && cc < 3 * cb) {
+      const int part = cc / cb, k = cc % cb;
+      const float x = M[((size_t)b * keys + j) * c + col0 + k];
+      const u16 h0 = bf16_rne(x);
+      const float r1 = x - bf16_f(h0);
+      const u16 h1 = bf16_rne(r1);
+      val = part == 0 ? h0 : (part == 1 ? h1 : bf16_rne(r1 - bf16_f(h1)));
+    }
+    v[e] = val;
+  }
+  *reinterpret_cast<u4*>(vt + (((size_t)b * (keys_pad / VK) + blk) * ncols + cc) * VK + k0) = pack8(v);
+}
+
+// out[b][row][col0+k] = r_row * (weighted sum of column k) / (sum of weights),
+// r_row = w exp((pot - lse)/eps) the row mass.  One thread per (problem, row, k).
+__global__ __launch_bounds__(256) void k_apply_merge(const float* __restrict__ pv, int ks, int batch, int rows, int cb,
+                                                     int ncols, int c, int col0, const double* __restrict__ logw,
+                                                     const float* __restrict__ pot, const float* __restrict__ lse,
+                                                     double eps, float* __restrict__ out) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)batch * rows * cb) return;
+  const int k = (int)(idx % cb);
+  const long long rr = idx / cb;
+  double S = 0.0, num = 0.0;
+  for (int sp = 0; sp < ks; ++sp) {
+    const size_t base = ((size_t)sp * batch * rows + (size_t)rr) * ncols;
+    S += (double)pv[base + ncols - 1];
+    for (int part = 0; part < 3; ++part) num += (double)pv[base + part * cb + k];
+  }
+  const double mass = exp(logw[rr] + ((double)pot[rr] - (double)lse[rr]) / eps);
+  out[rr * c + col0 + k] = (float)(mass > 0.0 ? mass * num / S : 0.0);
+}
+
+// Row masses r = w exp((pot - lse)/eps).
+__global__ __launch_bounds__(256) void k_mass(const double* __restrict__ logw, const float* __restrict__ pot,
+                                              const float* __restrict__ lse, double eps, long long total,
+                                              double* __restrict__ mass) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < total) mass[i] = exp(logw[i] + ((double)pot[i] - (double)lse[i]) / eps);
+}
+
+// HVP set-up per row of the moving cloud (points p, direction v, PY = P Y):
+//   z = p.v,  cr = 2 (r z - v.PY)  (= sum_j P_ij dC_ij),  and the matrix [z, v, cr/r]
+// that the other side's plan application turns into the right-hand side.
+__global__ __launch_bounds__(256) void k_hvp_rows(const void* __restrict__ P, int in_bf16, const float* __restrict__ V,
+                                                  const float* __restrict__ PY, const double* __restrict__ mass,
+                                                  long long total, int d, double* __restrict__ zr,
+                                                  double* __restrict__ cr, float* __restrict__ M) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  double z = 0.0, vpy = 0.0;
+  for (int t = 0; t < d; ++t) {
+    const double v = V[i * d + t];
+    z += (double)coord(P, (size_t)i * d + t, in_bf16) * v;
+    vpy += v * (double)PY[i * d + t];
+  }
+  const double r = mass[i];
+  const double c = 2.0 * (r * z - vpy);
+  zr[i] = z;
+  cr[i] = c;
+  float* row = M + i * (d + 2);
+  row[0] = (float)z;
+  for (int t = 0; t < d; ++t) row[1 + t] = V[i * d + t];
+  row[d + 1] = (float)(r > 0.0 ? c / r : 0.0);
+}
+
+// Right-hand side of the Schur system per row of the fixed cloud (points q):
+//   rhs = 2 (W0 - q.W1) - W2  with W = P^T [z, v, cr/r].
+__global__ __launch_bounds__(256) void k_hvp_rhs(const void* __restrict__ Q, int in_bf16, const float* __restrict__ W,
+                                                 long long total, int d, double* __restrict__ rhs) {
+  const long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= total) return;
+  const float* w = W + j * (d + 2);
+  double qw = 0.0;
+  for (int t = 0; t < d; ++t) qw += (double)coord(Q, (size_t)j * d + t, in_bf16) * (double)w[1 + t];
+  rhs[j] = 2.0 * ((double)w[0] - qw) - (double)w[d + 1];
+}
+
+// Conjugate gradients on the Schur system (diag(c) - P^T diag(1/r) P) dg = rhs,
+// preconditioned by diag(c), for every problem at once.  The system is singular
+// along constants (a common shift of the potentials leaves the plan
+// unchanged); the residual is kept at zero sum.  One workgroup per problem,
+// fixed-order reductions.  State per problem: st[0] = rz, st[1] = rz0, st[2] = done.
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  __syncthreads();
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  return red[0];
+}
+
+__global__ __launch_bounds__(256) void k_cg_init(const double* __restrict__ rhs, const double* __restrict__ cmass,
+                                                 int m, double* __restrict__ dg, double* __restrict__ res,
+                                                 double* __restrict__ pd, float* __restrict__ pdf,
+                                                 double* __restrict__ st) {
+  __shared__ double red[256];
+  const size_t o = (size_t)blockIdx.x * m;
+  double s = 0.0;
+  for (int j = threadIdx.x; j < m; j += 256) s += rhs[o + j];
+  const double mean = block_sum(s, red) / m;
+  double rz = 0.0;
+  for (int j = threadIdx.x; j < m; j += 256) {
+    const double r = rhs[o + j] - mean;
+    const double z = cmass[o + j] > 0.0 ? r / cmass[o + j] : 0.0;
+    res[o + j] = r;
+    pd[o + j] = z;
+    pdf[o + j] = (float)z;
+    dg[o + j] = 0.0;
+    rz += r * z;
+  }
+  rz = block_sum(rz, red);
+  if (threadIdx.x == 0) {
+    st[3 * blockIdx.x] = rz;
+    st[3 * blockIdx.x + 1] = rz;
+    st[3 * blockIdx.x + 2] = rz > 0.0 ? 0.0 : 1.0;
+  }
+}
+
+// t <- t / r (the plan product of the search direction, per row of the moving cloud)
+__global__ __launch_bounds__(256) void k_div_mass(float* __restrict__ t, const double* __restrict__ mass,
+                                                  long long total) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < total) t[i] = (float)(mass[i] > 0.0 ? (double)t[i] / mass[i] : 0.0);
+}
+
+__global__ __launch_bounds__(256) void k_cg_step(const float* __restrict__ q, const double* __restrict__ cmass, int m,
+                                                 double tol2, double* __restrict__ dg, double* __restrict__ res,
+                                                 double* __restrict__ pd, float* __restrict__ pdf,
+                                                 double* __restrict__ st) {
+  __shared__ double red[256];
+  const size_t o = (size_t)blockIdx.x * m;
+  double* s3 = st + 3 * blockIdx.x;
+  const bool done = s3[2] != 0.0;
+  // S p = c p - P^T (P p / r)
+  double pap = 0.0;
+  for (int j = threadIdx.x; j < m; j += 256) pap += pd[o + j] * (cmass[o + j] * pd[o + j] - (double)q[o + j]);
+  pap = block_sum(pap, red);
+  const double rz = s3[0];
+  const double alpha = (done || !(pap > 0.0)) ? 0.0 : rz / pap;
+  double sum = 0.0;
+  for (int j = threadIdx.x; j < m; j += 256) {
+    const double sp = cmass[o + j] * pd[o + j] - (double)q[o + j];
+    dg[o + j] += alpha * pd[o + j];
+    res[o + j] -= alpha * sp;
+    sum += res[o + j];
+  }
+  const double mean = block_sum(sum, red) / m;
+  double rzn = 0.0;
+  for (int j = threadIdx.x; j < m; j += 256) {
+    res[o + j] -= mean;
+    const double z = cmass[o + j] > 0.0 ? res[o + j] / cmass[o + j] : 0.0;
+    rzn += res[o + j] * z;
+  }
+  rzn = block_sum(rzn, red);
+  const bool stop = done || alpha == 0.0 || rzn <= tol2 * s3[1];
+  const double beta = stop ? 0.0 : rzn / rz;
+  for (int j = threadIdx.x; j < m; j += 256) {
+    const double z = cmass[o + j] > 0.0 ? res[o + j] / cmass[o + j] : 0.0;
+    const double p = stop ? 0.0 : z + beta * pd[o + j];
+    pd[o + j] = p;
+    pdf[o + j] = (float)p;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    s3[0] = rzn;
+    s3[2] = stop ? 1.0 : 0.0;
+  }
+}
+
+// Matrix [dg, dg * q] per row of the fixed cloud (points q).
+__global__ __launch_bounds__(256) void k_hvp_gmat(const void* __restrict__ Q, int in_bf16,
+                                                  const double* __restrict__ dg, long long total, int d,
+                                                  float* __restrict__ M) {
+  const long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= total) return;
+  float* row = M + j * (d + 1);
+  row[0] = (float)dg[j];
+  for (int t = 0; t < d; ++t) row[1 + t] = (float)(dg[j] * (double)coord(Q, (size_t)j * d + t, in_bf16));
+}
+
+// Matrix [q_t * q for t in t0 .. t0+nt-1] per row of the fixed cloud.
+__global__ __launch_bounds__(256) void k_hvp_qqmat(const void* __restrict__ Q, int in_bf16, long long total, int d,
+                                                   int t0, int nt, float* __restrict__ M) {
+  const long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= total) return;
+  float* row = M + j * (nt * d);
+  for (int u = 0; u < nt; ++u) {
+    const double qt = coord(Q, (size_t)j * d + t0 + u, in_bf16);
+    for (int t = 0; t < d; ++t) row[u * d + t] = (float)(qt * (double)coord(Q, (size_t)j * d + t, in_bf16));
+  }
+}
+
+// quad_i += sum_{u < nt} v_i[t0+u] * A_i[u*d .. u*d+d)   (A = P [q_t q])
+__global__ __launch_bounds__(256) void k_hvp_quad(const float* __restrict__ V, const float* __restrict__ A,
+                                                  long long total, int d, int t0, int nt,
+                                                  double* __restrict__ quad) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  for (int t = 0; t < d; ++t) {
+    double acc = quad[i * d + t];
+    for (int u = 0; u < nt; ++u) acc += (double)V[i * d + t0 + u] * (double)A[i * (nt * d) + u * d + t];
+    quad[i * d + t] = acc;
+  }
+}
+
+// Coordinates of a cloud as an fp32 matrix.
+__global__ __launch_bounds__(256) void k_coords(const void* __restrict__ P, int in_bf16, long long total,
+                                                float* __restrict__ M) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < total) M[i] = coord(P, (size_t)i, in_bf16);
+}
+
+// HV_i = 2 r v + (2/eps) [ df (r p - PY) + p (P dg) - P(dg q) - 2 (z (r p - PY) - (v.PY) p + quad) ]
+// with df = (cr - P dg)/r; G = P [dg, dg q].
+__global__ __launch_bounds__(256) void k_hvp_final(const void* __restrict__ P, int in_bf16,
+                                                   const float* __restrict__ V, const float* __restrict__ PY,
+                                                   const double* __restrict__ mass, const double* __restrict__ zr,
+                                                   const double* __restrict__ cr, const float* __restrict__ G,
+                                                   const double* __restrict__ quad, long long total, int d,
+                                                   double eps, float* __restrict__ out) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const double r = mass[i];
+  if (!(r > 0.0)) {
+    for (int t = 0; t < d; ++t) out[i * d + t] = 0.f;
+    return;
+  }
+  const float* g = G + i * (d + 1);
+  const double df = (cr[i] - (double)g[0]) / r;
+  double vpy = 0.0;
+  for (int t = 0; t < d; ++t) vpy += (double)V[i * d + t] * (double)PY[i * d + t];
+  const double z = zr[i];
+  for (int t = 0; t < d; ++t) {
+    const double pt = coord(P, (size_t)i * d + t, in_bf16);
+    const double grad_half = r * pt - (double)PY[i * d + t];
+    const double K = 2.0 * (z * grad_half - vpy * pt + quad[i * d + t]);
+    const double inner = df * grad_half + pt * (double)g[0] - (double)g[1 + t] - K;
+    out[i * d + t] = (float)(2.0 * r * (double)V[i * d + t] + (2.0 / eps) * inner);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 struct Layout {
   int mode, KP, n_pad, m_pad, max_pad;
   int in_bf16, cosine;
   size_t xn, yn, la, lb, rx, ry, maxabs, qgrid, qx, qy, kb, hb, part, scratch, total;
-  // transport application (after `total`; only its entry points need them)
-  int ncols, ksb;
+  // transport application and plan products (after `total`; only their entry points need them)
+  int ncols;             // widest value operand (columns) of any transport pass
+  size_t bpv_bytes;      // bytes of the split-partials region
   size_t vt, bpv, bs, ttotal;
+  // Hessian-vector products (after `ttotal`)
+  size_t h_lse_r, h_lse_k, h_mr, h_mk, h_py, h_mat, h_w, h_g, h_quad, h_tmp, h_zr, h_cr, h_rhs, h_dg, h_res,
+      h_pd, h_pdf, h_t, h_q, h_st, htotal;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -1134,14 +1416,38 @@ Layout layout_of(const sk_problem* p) {
   L.part = take(8 * (size_t)KS_MAX * B * mx);
   L.scratch = take(4 * B * mx);
   L.total = off;
-  // Transport: the value operand and the split partials of the P.V pass, at
-  // most 128 MiB of partials (and at most 16 splits).
-  L.ncols = val_tiles(L.mode, (int)p->d) * 16;
-  L.ksb = (int)std::min<size_t>(16, std::max<size_t>(1, (size_t(128) << 20) / (4 * B * mx * (size_t)L.ncols)));
+  // Transport: the value operand and the split partials of the P.V pass: room
+  // for 16 splits of a one-tile pass or one split of the widest pass.
+  const size_t d = (size_t)p->d;
+  L.ncols = std::max(val_tiles(L.mode, (int)p->d), apply_tiles(APPLY_COLS)) * 16;
+  L.bpv_bytes = std::max<size_t>(4 * 16 * 16 * B * mx, 4 * B * mx * (size_t)L.ncols);
   L.vt = take(2 * B * (size_t)L.max_pad * L.ncols);
-  L.bpv = take(4 * (size_t)L.ksb * B * mx * L.ncols);
-  L.bs = take(4 * (size_t)L.ksb * B * mx);
+  L.bpv = take(L.bpv_bytes);
+  L.bs = take(4 * 16 * B * mx);
   L.ttotal = off;
+  // Hessian-vector products: per-row vectors and small matrices, O((n+m) d)
+  const size_t bm = B * mx;
+  L.h_lse_r = take(4 * bm);
+  L.h_lse_k = take(4 * bm);
+  L.h_mr = take(8 * bm);
+  L.h_mk = take(8 * bm);
+  L.h_py = take(4 * bm * d);
+  L.h_mat = take(4 * bm * std::max<size_t>(d + 2, std::max<size_t>((size_t)APPLY_COLS, d)));
+  L.h_w = take(4 * bm * (d + 2));
+  L.h_g = take(4 * bm * (d + 1));
+  L.h_quad = take(8 * bm * d);
+  L.h_tmp = take(4 * bm * std::max<size_t>((size_t)APPLY_COLS, d));
+  L.h_zr = take(8 * bm);
+  L.h_cr = take(8 * bm);
+  L.h_rhs = take(8 * bm);
+  L.h_dg = take(8 * bm);
+  L.h_res = take(8 * bm);
+  L.h_pd = take(8 * bm);
+  L.h_pdf = take(4 * bm);
+  L.h_t = take(4 * bm);
+  L.h_q = take(4 * bm);
+  L.h_st = take(8 * 3 * (size_t)B);
+  L.htotal = off;
   return L;
 }
 
@@ -1178,14 +1484,16 @@ sk_status hip_check(const char* what) {
   return SK_OK;
 }
 
-sk_status check_ws(const sk_problem* p, void* ws, size_t ws_bytes, Layout* L, bool transport = false) {
+// need: 0 solver, 1 transport and plan products, 2 Hessian-vector products
+sk_status check_ws(const sk_problem* p, void* ws, size_t ws_bytes, Layout* L, int need_kind = 0) {
   sk_status st = check_problem(p);
   if (st != SK_OK) return st;
   *L = layout_of(p);
-  const size_t need = transport ? L->ttotal : L->total;
+  const size_t need = need_kind == 2 ? L->htotal : (need_kind == 1 ? L->ttotal : L->total);
   if (ws == nullptr || ws_bytes < need) {
     set_err("workspace %s: need %zu bytes, got %zu%s", ws == nullptr ? "is NULL" : "too small", need, ws_bytes,
-            transport ? " (transport calls need sinkhorn_transport_workspace_bytes)" : "");
+            need_kind == 2 ? " (HVP calls need sinkhorn_hvp_workspace_bytes)"
+                           : (need_kind == 1 ? " (transport calls need sinkhorn_transport_workspace_bytes)" : ""));
     return SK_EWORKSPACE;
   }
   return SK_OK;
@@ -1248,6 +1556,38 @@ int choose_key_splits(int rowgroups, int total_chunks, int capacity, int* cps_ou
 
 bool eps_ok(float eps) { return eps > 0.f && isfinite(eps) && isfinite((float)(LOG2E / eps)); }
 
+// Key operand of one side for the potential pot_in and eps: the split key rows
+// (fp32 path) or the half bias (bf16 path).  Returns the key operand and bias.
+sk_status prep_keys(const sk_problem* p, const void* X, const void* Y, char* w, const Layout& L, const float* pot_in,
+                    float eps, int side, hipStream_t stream, const u16** Kop, const float** hb) {
+  const int B = (int)p->batch;
+  const int keys = (int)(side == 0 ? p->m : p->n);
+  const int keys_pad = side == 0 ? L.m_pad : L.n_pad;
+  const double* knorm = reinterpret_cast<const double*>(w + (side == 0 ? L.yn : L.xn));
+  const double* klogw = reinterpret_cast<const double*>(w + (side == 0 ? L.lb : L.la));
+  const float* maxabs = reinterpret_cast<const float*>(w + L.maxabs);
+  float* qgrid = reinterpret_cast<float*>(w + L.qgrid);
+  const void* Kraw = side == 0 ? Y : X;
+  const float lam = (float)(LOG2E / (double)eps);
+  *hb = nullptr;
+  if (L.mode == MODE_SPLIT) {
+    u16* kb = reinterpret_cast<u16*>(w + L.kb);
+    const dim3 kgrid((unsigned)(((long long)keys_pad * (L.KP / 8) + 255) / 256), B);
+    const double* krn = reinterpret_cast<const double*>(w + (side == 0 ? L.ry : L.rx));
+    hipLaunchKernelGGL(k_prep_keys, kgrid, dim3(256), 0, stream, Kraw, L.in_bf16, krn, pot_in, knorm,
+                       klogw, keys, keys_pad, (int)p->d, L.KP, lam, eps, maxabs + (side == 0 ? 0 : B),
+                       maxabs + (side == 0 ? B : 0), qgrid, kb);
+    *Kop = kb;
+  } else {
+    float* hbw = reinterpret_cast<float*>(w + L.hb);
+    const dim3 pgrid((keys_pad + 255) / 256, B);
+    hipLaunchKernelGGL(k_prep_bias, pgrid, dim3(256), 0, stream, pot_in, knorm, klogw, keys, keys_pad, eps, hbw);
+    *hb = hbw;
+    *Kop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qy : L.qx));
+  }
+  return hip_check("key preparation launch");
+}
+
 // One half-step.  side 0: f from g (queries X, keys Y); side 1: g from f.
 sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws, const Layout& L,
                     const float* pot_in, float eps, float* pot_out, int side, hipStream_t stream) {
@@ -1258,35 +1598,15 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   const int rows_pad = side == 0 ? L.n_pad : L.m_pad;
   const int keys_pad = side == 0 ? L.m_pad : L.n_pad;
   const double* qnorm = reinterpret_cast<const double*>(w + (side == 0 ? L.xn : L.yn));
-  const double* knorm = reinterpret_cast<const double*>(w + (side == 0 ? L.yn : L.xn));
-  const double* klogw = reinterpret_cast<const double*>(w + (side == 0 ? L.lb : L.la));
-  const float* maxabs = reinterpret_cast<const float*>(w + L.maxabs);
-  float* qgrid = reinterpret_cast<float*>(w + L.qgrid);
+  const float* qgrid = reinterpret_cast<const float*>(w + L.qgrid);
   const u16* Qop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qx : L.qy));
-  const void* Kraw = side == 0 ? Y : X;
   const int nch = L.KP / 32;
   const int cfMW = cfg_MW(L.mode, nch), cfR = cfg_R(L.mode, nch), cfTC = cfg_TC(L.mode, nch);
   const float lam = (float)(LOG2E / (double)eps);
 
-  sk_status st = SK_OK;
-  const u16* Kop;
+  const u16* Kop = nullptr;
   const float* hb = nullptr;
-  const dim3 pgrid((keys_pad + 255) / 256, B);
-  if (L.mode == MODE_SPLIT) {
-    u16* kb = reinterpret_cast<u16*>(w + L.kb);
-    const dim3 kgrid((unsigned)(((long long)keys_pad * (L.KP / 8) + 255) / 256), B);
-    const double* krn = reinterpret_cast<const double*>(w + (side == 0 ? L.ry : L.rx));
-    hipLaunchKernelGGL(k_prep_keys, kgrid, dim3(256), 0, stream, Kraw, L.in_bf16, krn, pot_in, knorm,
-                       klogw, keys, keys_pad, (int)p->d, L.KP, lam, eps, maxabs + (side == 0 ? 0 : B),
-                       maxabs + (side == 0 ? B : 0), qgrid, kb);
-    Kop = kb;
-  } else {
-    float* hbw = reinterpret_cast<float*>(w + L.hb);
-    hipLaunchKernelGGL(k_prep_bias, pgrid, dim3(256), 0, stream, pot_in, knorm, klogw, keys, keys_pad, eps, hbw);
-    hb = hbw;
-    Kop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qy : L.qx));
-  }
-  st = hip_check("key preparation launch");
+  sk_status st = prep_keys(p, X, Y, w, L, pot_in, eps, side, stream, &Kop, &hb);
   if (st != SK_OK) return st;
 
   LseFn fn = (L.mode == MODE_SPLIT) ? lse_lookup<MODE_SPLIT>(nch) : lse_lookup<MODE_BF16>(nch);
@@ -1361,11 +1681,12 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
 
   // 2. Value operand from the other cloud's coordinates.
   u16* vt = reinterpret_cast<u16*>(w + L.vt);
-  const long long nvec = (long long)(keys_pad / VK) * L.ncols * (VK / 8);
+  const int nc = val_tiles(L.mode, d) * 16;
+  const long long nvec = (long long)(keys_pad / VK) * nc * (VK / 8);
   const int sumcol = val_sumcol(L.mode, d) ? 1 : 0;
   const double* krn = reinterpret_cast<const double*>(w + (side == 0 ? L.ry : L.rx));
   hipLaunchKernelGGL(k_prep_vals, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, Kraw, L.mode,
-                     L.in_bf16, krn, keys, keys_pad, d, L.ncols, sumcol, vt);
+                     L.in_bf16, krn, keys, keys_pad, d, nc, sumcol, vt);
   st = hip_check("value preparation launch");
   if (st != SK_OK) return st;
 
@@ -1376,14 +1697,15 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
     return SK_EUNSUPPORTED;
   }
   const int nch = L.KP / 32;
-  const int R = bary_R(nch);
+  const int R = bary_R(nch, val_tiles(L.mode, d));
   const int wg_x = (rows + 4 * R * 16 - 1) / (4 * R * 16);
   const int total_chunks = (keys + VK - 1) / VK;
   int capacity = 0;
   st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity);
   if (st != SK_OK) return st;
   int cps = 0;
-  const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps, L.ksb);
+  const int ks_cap = (int)std::min<size_t>(16, std::max<size_t>(1, L.bpv_bytes / (4 * (size_t)B * rows * nc)));
+  const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps, ks_cap);
   const u16* Kop = (L.mode == MODE_SPLIT) ? reinterpret_cast<const u16*>(w + L.kb)
                                           : reinterpret_cast<const u16*>(w + (side == 0 ? L.qy : L.qx));
   const float* hb = (L.mode == MODE_BF16) ? reinterpret_cast<const float*>(w + L.hb) : nullptr;
@@ -1398,7 +1720,7 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   // 4. Merge the splits, divide, form the gradient.
   const long long total = (long long)B * rows * d;
   hipLaunchKernelGGL(k_bary_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, bs, ks, B, rows,
-                     d, L.ncols, val_parts(L.mode), sumcol, Praw, L.in_bf16, pot_row, lse, qlogw, (double)eps, bary,
+                     d, nc, val_parts(L.mode), sumcol, Praw, L.in_bf16, pot_row, lse, qlogw, (double)eps, bary,
                      L.cosine ? nullptr : grad);
   st = hip_check("transport merge launch");
   if (st != SK_OK || !L.cosine || grad == nullptr) return st;
@@ -1407,6 +1729,187 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   hipLaunchKernelGGL(k_cosine_grad, dim3((unsigned)((nrows + 255) / 256)), dim3(256), 0, stream, bary, Praw,
                      L.in_bf16, qrn, pot_row, lse, qlogw, (double)eps, nrows, d, grad);
   return hip_check("cosine gradient launch");
+}
+
+// ---------------------------------------------------------------------------
+// Plan application (vector- and matrix-transport products) and HVP drivers
+// ---------------------------------------------------------------------------
+template <int MODE, int D>
+BaryFn apply_fn_d(int nct) {
+  constexpr int NCH = MODE == MODE_SPLIT ? split_nch(D) : (D + 31) / 32;
+  if (nct == 1) return &k_bary<MODE, NCH, 1, true>;
+  if (nct == 4) return &k_bary<MODE, NCH, 4, true>;
+  return &k_bary<MODE, NCH, 13, true>;
+}
+
+template <int MODE, int... N>
+BaryFn apply_lookup_impl(int d, int nct, std::integer_sequence<int, N...>) {
+  BaryFn fn = nullptr;
+  ((d == N + 1 ? (fn = apply_fn_d<MODE, N + 1>(nct), 0) : 0), ...);
+  return fn;
+}
+
+BaryFn apply_lookup(int mode, int d, int nct) {
+  if (mode == MODE_SPLIT)
+    return apply_lookup_impl<MODE_SPLIT>(d, nct, std::make_integer_sequence<int, SK_MAX_D_FP32>{});
+  return apply_lookup_impl<MODE_BF16>(d, nct, std::make_integer_sequence<int, SK_MAX_D>{});
+}
+
+// out[b][row][k] = sum_j P_ij M[b][j][k] (k < c) for one side (side 0: rows are
+// the points of X, keys those of Y), at potentials pot_row / pot_key whose
+// half-step values for the rows are lse.  Columns go in passes of APPLY_COLS.
+sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w, const Layout& L,
+                     const float* pot_row, const float* pot_key, const float* lse, float eps, int side,
+                     const float* M, int c, float* out, hipStream_t stream) {
+  const int B = (int)p->batch, d = (int)p->d;
+  const int rows = (int)(side == 0 ? p->n : p->m);
+  const int keys = (int)(side == 0 ? p->m : p->n);
+  const int rows_pad = side == 0 ? L.n_pad : L.m_pad;
+  const int keys_pad = side == 0 ? L.m_pad : L.n_pad;
+  const double* qnorm = reinterpret_cast<const double*>(w + (side == 0 ? L.xn : L.yn));
+  const double* qlogw = reinterpret_cast<const double*>(w + (side == 0 ? L.la : L.lb));
+  const float* qgrid = reinterpret_cast<const float*>(w + L.qgrid);
+  const u16* Qop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qx : L.qy));
+  const u16* Kop = nullptr;
+  const float* hb = nullptr;
+  sk_status st = prep_keys(p, X, Y, w, L, pot_key, eps, side, stream, &Kop, &hb);
+  if (st != SK_OK) return st;
+  u16* vt = reinterpret_cast<u16*>(w + L.vt);
+  float* bpv = reinterpret_cast<float*>(w + L.bpv);
+  float* bs = reinterpret_cast<float*>(w + L.bs);
+  const float lam = (float)(LOG2E / (double)eps);
+  const int nch = L.KP / 32;
+  const int total_chunks = (keys + VK - 1) / VK;
+  for (int col0 = 0; col0 < c; col0 += APPLY_COLS) {
+    const int cb = std::min(APPLY_COLS, c - col0);
+    const int nct = apply_tiles(cb), nc = nct * 16;
+    const int R = bary_R(nch, nct);
+    const int wg_x = (rows + 4 * R * 16 - 1) / (4 * R * 16);
+    const long long nvec = (long long)(keys_pad / VK) * nc * (VK / 8);
+    hipLaunchKernelGGL(k_prep_mat, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, M, keys, keys_pad,
+                       c, col0, cb, nc, vt);
+    st = hip_check("matrix preparation launch");
+    if (st != SK_OK) return st;
+    BaryFn fn = apply_lookup(L.mode, d, nct);
+    if (fn == nullptr) {
+      set_err("no plan-application kernel for d = %d", d);
+      return SK_EUNSUPPORTED;
+    }
+    int capacity = 0;
+    st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity);
+    if (st != SK_OK) return st;
+    const int ks_cap = (int)std::min<size_t>(16, std::max<size_t>(1, L.bpv_bytes / (4 * (size_t)B * rows * nc)));
+    int cps = 0;
+    const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps, ks_cap);
+    hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, lse, bpv, bs,
+                       rows, rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam);
+    st = hip_check("plan-application kernel launch");
+    if (st != SK_OK) return st;
+    const long long total = (long long)B * rows * cb;
+    hipLaunchKernelGGL(k_apply_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, ks, B, rows,
+                       cb, nc, c, col0, qlogw, pot_row, lse, (double)eps, out);
+    st = hip_check("plan-application merge launch");
+    if (st != SK_OK) return st;
+  }
+  return SK_OK;
+}
+
+unsigned blocks_for(long long n) { return (unsigned)((n + 255) / 256); }
+
+// Hessian of the entropic OT value in the points of one cloud (side 0: X,
+// side 1: Y) applied to V, at potentials (f, g) taken as optimal.  Moving the
+// points along V changes the costs by dC and the potentials by (df, dg) that
+// keep the plan's marginals; eliminating df leaves the Schur system in dg,
+// solved by conjugate gradients whose products are plan applications.
+sk_status hvp(const sk_problem* p, const void* X, const void* Y, char* w, const Layout& L, const float* f,
+              const float* g, float eps, const float* V, int64_t cg_iters, float cg_tol, float* out, int side,
+              hipStream_t s) {
+  const int B = (int)p->batch, d = (int)p->d;
+  const int rows = (int)(side == 0 ? p->n : p->m);
+  const int keys = (int)(side == 0 ? p->m : p->n);
+  const void* Praw = side == 0 ? X : Y;
+  const void* Qraw = side == 0 ? Y : X;
+  const float* pot_r = side == 0 ? f : g;
+  const float* pot_k = side == 0 ? g : f;
+  const double* logw_r = reinterpret_cast<const double*>(w + (side == 0 ? L.la : L.lb));
+  const double* logw_k = reinterpret_cast<const double*>(w + (side == 0 ? L.lb : L.la));
+  float* lse_r = reinterpret_cast<float*>(w + L.h_lse_r);
+  float* lse_k = reinterpret_cast<float*>(w + L.h_lse_k);
+  double* mr = reinterpret_cast<double*>(w + L.h_mr);
+  double* mk = reinterpret_cast<double*>(w + L.h_mk);
+  float* py = reinterpret_cast<float*>(w + L.h_py);
+  float* mat = reinterpret_cast<float*>(w + L.h_mat);
+  float* wk = reinterpret_cast<float*>(w + L.h_w);
+  float* gm = reinterpret_cast<float*>(w + L.h_g);
+  double* quad = reinterpret_cast<double*>(w + L.h_quad);
+  float* tmp = reinterpret_cast<float*>(w + L.h_tmp);
+  double* zr = reinterpret_cast<double*>(w + L.h_zr);
+  double* cr = reinterpret_cast<double*>(w + L.h_cr);
+  double* rhs = reinterpret_cast<double*>(w + L.h_rhs);
+  double* dg = reinterpret_cast<double*>(w + L.h_dg);
+  double* res = reinterpret_cast<double*>(w + L.h_res);
+  double* pd = reinterpret_cast<double*>(w + L.h_pd);
+  float* pdf = reinterpret_cast<float*>(w + L.h_pdf);
+  float* tv = reinterpret_cast<float*>(w + L.h_t);
+  float* qv = reinterpret_cast<float*>(w + L.h_q);
+  double* stt = reinterpret_cast<double*>(w + L.h_st);
+  const long long nr = (long long)B * rows, nk = (long long)B * keys;
+  const int in16 = L.in_bf16;
+  void* vw = static_cast<void*>(w);
+
+  // 1. both sides' row log-sum-exps (fixed offsets of every plan pass) and masses
+  sk_status st = half_step(p, X, Y, vw, L, pot_k, eps, lse_r, side, s);
+  if (st == SK_OK) st = half_step(p, X, Y, vw, L, pot_r, eps, lse_k, 1 - side, s);
+  if (st != SK_OK) return st;
+  hipLaunchKernelGGL(k_mass, dim3(blocks_for(nr)), dim3(256), 0, s, logw_r, pot_r, lse_r, (double)eps, nr, mr);
+  hipLaunchKernelGGL(k_mass, dim3(blocks_for(nk)), dim3(256), 0, s, logw_k, pot_k, lse_k, (double)eps, nk, mk);
+  // 2. P Q (the plan applied to the fixed cloud's coordinates)
+  hipLaunchKernelGGL(k_coords, dim3(blocks_for(nk * d)), dim3(256), 0, s, Qraw, in16, nk * d, mat);
+  st = hip_check("HVP set-up launch");
+  if (st == SK_OK) st = apply_plan(p, X, Y, w, L, pot_r, pot_k, lse_r, eps, side, mat, d, py, s);
+  if (st != SK_OK) return st;
+  // 3. right-hand side: cr per moving row, then P^T [z, v, cr/r] per fixed row
+  hipLaunchKernelGGL(k_hvp_rows, dim3(blocks_for(nr)), dim3(256), 0, s, Praw, in16, V, py, mr, nr, d, zr, cr, mat);
+  st = hip_check("HVP rows launch");
+  if (st == SK_OK) st = apply_plan(p, X, Y, w, L, pot_k, pot_r, lse_k, eps, 1 - side, mat, d + 2, wk, s);
+  if (st != SK_OK) return st;
+  hipLaunchKernelGGL(k_hvp_rhs, dim3(blocks_for(nk)), dim3(256), 0, s, Qraw, in16, wk, nk, d, rhs);
+  // 4. conjugate gradients on the Schur system in dg
+  hipLaunchKernelGGL(k_cg_init, dim3(B), dim3(256), 0, s, rhs, mk, keys, dg, res, pd, pdf, stt);
+  st = hip_check("CG set-up launch");
+  if (st != SK_OK) return st;
+  const double tol2 = (double)cg_tol * (double)cg_tol;
+  for (int64_t it = 0; it < cg_iters; ++it) {
+    st = apply_plan(p, X, Y, w, L, pot_r, pot_k, lse_r, eps, side, pdf, 1, tv, s);
+    if (st != SK_OK) return st;
+    hipLaunchKernelGGL(k_div_mass, dim3(blocks_for(nr)), dim3(256), 0, s, tv, mr, nr);
+    st = apply_plan(p, X, Y, w, L, pot_k, pot_r, lse_k, eps, 1 - side, tv, 1, qv, s);
+    if (st != SK_OK) return st;
+    hipLaunchKernelGGL(k_cg_step, dim3(B), dim3(256), 0, s, qv, mk, keys, tol2, dg, res, pd, pdf, stt);
+    st = hip_check("CG step launch");
+    if (st != SK_OK) return st;
+  }
+  // 5. P [dg, dg q]
+  hipLaunchKernelGGL(k_hvp_gmat, dim3(blocks_for(nk)), dim3(256), 0, s, Qraw, in16, dg, nk, d, mat);
+  st = hip_check("HVP matrix launch");
+  if (st == SK_OK) st = apply_plan(p, X, Y, w, L, pot_r, pot_k, lse_r, eps, side, mat, d + 1, gm, s);
+  if (st != SK_OK) return st;
+  // 6. sum_j P_ij (q_j . v_i) q_j = sum_t v_i[t] (P [q_t q])_i, a few coordinates t per pass
+  hipLaunchKernelGGL(k_fill_f32, dim3(blocks_for(2 * nr * d)), dim3(256), 0, s, reinterpret_cast<float*>(quad),
+                     (int)(2 * nr * d), 0.f);
+  const int per = std::max(1, APPLY_COLS / d);
+  for (int t0 = 0; t0 < d; t0 += per) {
+    const int nt = std::min(per, d - t0);
+    hipLaunchKernelGGL(k_hvp_qqmat, dim3(blocks_for(nk)), dim3(256), 0, s, Qraw, in16, nk, d, t0, nt, mat);
+    st = hip_check("HVP matrix launch");
+    if (st == SK_OK) st = apply_plan(p, X, Y, w, L, pot_r, pot_k, lse_r, eps, side, mat, nt * d, tmp, s);
+    if (st != SK_OK) return st;
+    hipLaunchKernelGGL(k_hvp_quad, dim3(blocks_for(nr)), dim3(256), 0, s, V, tmp, nr, d, t0, nt, quad);
+  }
+  // 7. assemble
+  hipLaunchKernelGGL(k_hvp_final, dim3(blocks_for(nr)), dim3(256), 0, s, Praw, in16, V, py, mr, zr, cr, gm, quad, nr,
+                     d, (double)eps, out);
+  return hip_check("HVP assembly launch");
 }
 
 sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const float* a, const float* b, void* ws,
@@ -1584,7 +2087,7 @@ static sk_status transport_entry(const sk_problem* p, const void* X, const void*
                                  int side) {
   g_err[0] = 0;
   Layout L;
-  sk_status st = check_ws(p, ws, ws_bytes, &L, true);
+  sk_status st = check_ws(p, ws, ws_bytes, &L, 1);
   if (st != SK_OK) return st;
   if (!X || !Y || !f || !g || !bary) {
     set_err("X, Y, f, g and bary must be non-NULL device pointers");
@@ -1605,6 +2108,90 @@ sk_status sinkhorn_barycentric_x(const sk_problem* p, const void* X, const void*
 sk_status sinkhorn_barycentric_y(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
                                  const float* f, const float* g, float eps, float* bary, float* grad, void* stream) {
   return transport_entry(p, X, Y, ws, ws_bytes, f, g, eps, bary, grad, stream, 1);
+}
+
+static sk_status apply_entry(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
+                             const float* f, const float* g, float eps, const float* M, int64_t c, float* out,
+                             void* stream, int side) {
+  g_err[0] = 0;
+  Layout L;
+  sk_status st = check_ws(p, ws, ws_bytes, &L, 1);
+  if (st != SK_OK) return st;
+  if (!X || !Y || !f || !g || !M || !out) {
+    set_err("X, Y, f, g, the matrix and out must be non-NULL device pointers");
+    return SK_EINVAL;
+  }
+  if (c < 1 || c > (int64_t)1 << 20) {
+    set_err("columns c = %lld must be in 1 .. 2^20", (long long)c);
+    return SK_EINVAL;
+  }
+  if (!eps_ok(eps)) {
+    set_err("eps must be positive and finite (got %g)", (double)eps);
+    return SK_EINVAL;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  float* lse = reinterpret_cast<float*>(w + L.scratch);
+  st = half_step(p, X, Y, ws, L, side == 0 ? g : f, eps, lse, side, s);
+  if (st != SK_OK) return st;
+  return apply_plan(p, X, Y, w, L, side == 0 ? f : g, side == 0 ? g : f, lse, eps, side, M, (int)c, out, s);
+}
+
+sk_status sinkhorn_apply_plan_x(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
+                                const float* f, const float* g, float eps, const float* V, int64_t c, float* out,
+                                void* stream) {
+  return apply_entry(p, X, Y, ws, ws_bytes, f, g, eps, V, c, out, stream, 0);
+}
+
+sk_status sinkhorn_apply_plan_y(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
+                                const float* f, const float* g, float eps, const float* U, int64_t c, float* out,
+                                void* stream) {
+  return apply_entry(p, X, Y, ws, ws_bytes, f, g, eps, U, c, out, stream, 1);
+}
+
+size_t sinkhorn_hvp_workspace_bytes(const sk_problem* p) {
+  if (check_problem(p) != SK_OK) return 0;
+  return layout_of(p).htotal;
+}
+
+static sk_status hvp_entry(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
+                           const float* f, const float* g, float eps, const float* V, int64_t cg_iters, float cg_tol,
+                           float* out, void* stream, int side) {
+  g_err[0] = 0;
+  Layout L;
+  sk_status st = check_ws(p, ws, ws_bytes, &L, 2);
+  if (st != SK_OK) return st;
+  if (!X || !Y || !f || !g || !V || !out) {
+    set_err("X, Y, f, g, V and out must be non-NULL device pointers");
+    return SK_EINVAL;
+  }
+  if (!eps_ok(eps)) {
+    set_err("eps must be positive and finite (got %g)", (double)eps);
+    return SK_EINVAL;
+  }
+  if (cg_iters < 0 || cg_iters > 100000 || !(cg_tol >= 0.f) || !isfinite(cg_tol)) {
+    set_err("cg_iters must be in 0 .. 100000 and cg_tol >= 0 finite (got %lld, %g)", (long long)cg_iters,
+            (double)cg_tol);
+    return SK_EINVAL;
+  }
+  if (L.cosine) {
+    set_err("Hessian-vector products support the squared-Euclidean cost only");
+    return SK_EUNSUPPORTED;
+  }
+  return hvp(p, X, Y, static_cast<char*>(ws), L, f, g, eps, V, cg_iters, cg_tol, out, side,
+             static_cast<hipStream_t>(stream));
+}
+
+sk_status sinkhorn_hvp_x(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
+                         const float* f, const float* g, float eps, const float* V, int64_t cg_iters, float cg_tol,
+                         float* out, void* stream) {
+  return hvp_entry(p, X, Y, ws, ws_bytes, f, g, eps, V, cg_iters, cg_tol, out, stream, 0);
+}
+
+sk_status sinkhorn_hvp_y(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
+                         const float* f, const float* g, float eps, const float* V, int64_t cg_iters, float cg_tol,
+                         float* out, void* stream) {
+  return hvp_entry(p, X, Y, ws, ws_bytes, f, g, eps, V, cg_iters, cg_tol, out, stream, 1);
 }
 
 }  // extern "C"

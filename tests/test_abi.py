@@ -150,3 +150,27 @@ def test_cost_field_validation(lib):
     assert cos > sq > 0
     text = open(HEADER).read()
     assert "SK_COST_SQEUCLID = 0" in text and "SK_COST_COSINE = 1" in text
+
+
+def test_plan_and_hvp_entry_points_validate(lib):
+    p = _prob(1, 300, 200, 3)
+    bp = ctypes.byref(p)
+    t = lib.sinkhorn_transport_workspace_bytes(bp)
+    h = lib.sinkhorn_hvp_workspace_bytes(bp)
+    assert h > t > lib.sinkhorn_workspace_bytes(bp) > 0
+    assert lib.sinkhorn_hvp_workspace_bytes(ctypes.byref(_prob(1, 65536, 32768, 128, 1))) < 2 ** 31
+    ptr = ctypes.c_void_p(0x1000)
+    for fn in (lib.sinkhorn_apply_plan_x, lib.sinkhorn_apply_plan_y):
+        assert fn(bp, ptr, ptr, ptr, t - 1, ptr, ptr, 0.1, ptr, 3, ptr, None) == 6
+        assert fn(bp, ptr, ptr, ptr, t, ptr, ptr, 0.1, ptr, 0, ptr, None) == 1       # no columns
+        assert fn(bp, ptr, ptr, ptr, t, ptr, ptr, 0.1, None, 3, ptr, None) == 1      # no matrix
+        assert fn(bp, ptr, ptr, ptr, t, ptr, ptr, -1.0, ptr, 3, ptr, None) == 1
+    for fn in (lib.sinkhorn_hvp_x, lib.sinkhorn_hvp_y):
+        assert fn(bp, ptr, ptr, ptr, t, ptr, ptr, 0.1, ptr, 10, 1e-6, ptr, None) == 6  # transport size is too small
+        assert b"sinkhorn_hvp_workspace_bytes" in lib.sinkhorn_last_error()
+        assert fn(bp, ptr, ptr, ptr, h, ptr, ptr, 0.1, ptr, -1, 1e-6, ptr, None) == 1
+        assert fn(bp, ptr, ptr, ptr, h, ptr, ptr, 0.1, ptr, 10, float("nan"), ptr, None) == 1
+        assert fn(bp, ptr, ptr, ptr, h, ptr, ptr, 0.1, None, 10, 1e-6, ptr, None) == 1
+        cos = binding.SkProblem(1, 300, 200, 3, 0, 1)
+        hc = lib.sinkhorn_hvp_workspace_bytes(ctypes.byref(cos))
+        assert fn(ctypes.byref(cos), ptr, ptr, ptr, hc, ptr, ptr, 0.1, ptr, 10, 1e-6, ptr, None) == 5

@@ -1,0 +1,154 @@
+"""GPU parity of the plan application (vector- and matrix-transport products) and
+the Hessian-vector product (page "FlashSinkhorn: IO-aware entropic OT on GPU",
+section "Differentiation and second-order optimisation") against the oracle.
+
+Bounds:
+  apply_plan: |d(PV)_ik| <= r_i (rel * max|V_k| (1 + dm) + |avg_ik| dm) with rel = 2e-5
+    (fp32) / 5e-4 (bf16) the transport bound of a weighted average, avg = PV/r, and
+    dm = expm1(tol_T/eps) the row-mass bound from the half-step.
+  hvp: max|dHV| <= tau * max|HV_ref|, tau = 5e-4 (fp32), 5e-3 (bf16).  The HVP
+    combines several plan products with weight 2/eps; running the same algorithm in
+    fp64 with every plan product perturbed by random relative errors of 1e-6 (1e-5)
+    moves the result by 7e-5 (9e-4) relative at eps = 0.1, growing like 1/eps.  The
+    plan products carry about 1e-6 (fp32 operands) to 1e-5 (bf16 operands).
+Potentials come from converged oracle solves (never from the GPU).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from log_domain_sinkhorn_half_amd import binding as sk
+from log_domain_sinkhorn_half_amd.inputs import make_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sk.load_library()
+
+
+def dev(p):
+    if p.dtype == "bf16":
+        X = torch.from_numpy(p.X_bits.view(np.int16)).cuda().view(torch.bfloat16)
+        Y = torch.from_numpy(p.Y_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        X = torch.from_numpy(p.X).cuda()
+        Y = torch.from_numpy(p.Y).cuda()
+    return X, Y, torch.from_numpy(p.a).cuda(), torch.from_numpy(p.b).cuda()
+
+
+def potentials(p, eps, iters):
+    f, g = oracle.solve(p.X, p.Y, p.a, p.b, eps, iters)
+    return f.astype(np.float32), g.astype(np.float32)
+
+
+def check_apply(p, eps, f, g, side, M, got):
+    for k in range(p.batch):
+        X, Y, a, b = (np.asarray(v[k], np.float64) for v in (p.X, p.Y, p.a, p.b))
+        if side == "x":
+            ref = oracle.apply_plan_x(X, Y, a, b, f[k], g[k], eps, M[k])
+            mass = oracle.apply_plan_x(X, Y, a, b, f[k], g[k], eps, np.ones(p.m))
+            T = oracle.half_step_f(X, Y, b, g[k], eps)
+        else:
+            ref = oracle.apply_plan_y(X, Y, a, b, f[k], g[k], eps, M[k])
+            mass = oracle.apply_plan_y(X, Y, a, b, f[k], g[k], eps, np.ones(p.n))
+            T = oracle.half_step_g(X, Y, a, f[k], eps)
+        rel = 5e-4 if p.dtype == "bf16" else 2e-5
+        tT = 2e-2 * eps if p.dtype == "bf16" else 1e-3 * eps + 1e-5 * float(np.max(np.abs(T)))
+        dm = np.expm1(tT / eps)
+        avg = np.divide(ref, mass[:, None], out=np.zeros_like(ref), where=mass[:, None] > 0)
+        tol = mass[:, None] * (rel * np.max(np.abs(M[k]), axis=0)[None, :] * (1 + dm) + np.abs(avg) * dm)
+        err = np.abs(got[k] - ref)
+        assert np.all(np.isfinite(got[k]))
+        assert np.all(err <= tol), f"apply_{side} problem {k}: worst err {err.max():.3e}, excess {(err - tol).max():.3e}"
+
+
+@pytest.mark.parametrize("n,m,d,dtype,c", [(300, 200, 3, "fp32", 1), (129, 257, 16, "fp32", 5),
+                                           (200, 333, 64, "fp32", 21), (150, 140, 4, "fp32", 70),
+                                           (100, 90, 128, "bf16", 7), (63, 65, 8, "bf16", 64)])
+def test_apply_plan(n, m, d, dtype, c):
+    p = make_case(n, m, d, seed=17 * n + c, weights="softmax", dtype=dtype, scale=1.0 / np.sqrt(d))
+    eps = 0.1
+    f, g = potentials(p, eps, 3)
+    rng = np.random.default_rng(c)
+    Vx = rng.standard_normal((1, m, c)).astype(np.float32)
+    Uy = rng.standard_normal((1, n, c)).astype(np.float32)
+    X, Y, a, b = dev(p)
+    ws = sk.alloc_workspace(X, Y, transport=True)
+    sk.init_norms(X, Y, a, b, ws)
+    ft, gt = torch.from_numpy(f).cuda(), torch.from_numpy(g).cuda()
+    ox = sk.apply_plan_x(X, Y, ws, ft, gt, eps, torch.from_numpy(Vx).cuda()).cpu().numpy()
+    oy = sk.apply_plan_y(X, Y, ws, ft, gt, eps, torch.from_numpy(Uy).cuda()).cpu().numpy()
+    check_apply(p, eps, f.astype(np.float64), g.astype(np.float64), "x", Vx.astype(np.float64), ox)
+    check_apply(p, eps, f.astype(np.float64), g.astype(np.float64), "y", Uy.astype(np.float64), oy)
+
+
+def test_apply_plan_batched_vector():
+    p = make_case(70, 90, 6, batch=3, seed=9, weights="softmax")
+    eps = 0.2
+    f, g = potentials(p, eps, 3)
+    V = np.random.default_rng(4).standard_normal((3, 90)).astype(np.float32)
+    X, Y, a, b = dev(p)
+    ws = sk.alloc_workspace(X, Y, transport=True)
+    sk.init_norms(X, Y, a, b, ws)
+    out = sk.apply_plan_x(X, Y, ws, torch.from_numpy(f).cuda(), torch.from_numpy(g).cuda(), eps,
+                          torch.from_numpy(V).cuda()).cpu().numpy()
+    check_apply(p, eps, f.astype(np.float64), g.astype(np.float64), "x", V[..., None].astype(np.float64),
+                out[..., None])
+
+
+def run_hvp(p, eps, f, g, V, side, iters=400, tol=1e-7):
+    X, Y, a, b = dev(p)
+    ws = sk.alloc_workspace(X, Y, hvp=True)
+    sk.init_norms(X, Y, a, b, ws)
+    ft, gt = torch.from_numpy(f).cuda(), torch.from_numpy(g).cuda()
+    fn = sk.hvp_x if side == "x" else sk.hvp_y
+    out = fn(X, Y, ws, ft, gt, eps, torch.from_numpy(V).cuda(), cg_iters=iters, cg_tol=tol)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,m,d,eps,dtype", [(64, 48, 2, 0.5, "fp32"), (200, 150, 3, 0.1, "fp32"),
+                                             (120, 140, 16, 0.2, "fp32"), (100, 90, 32, 0.5, "bf16")])
+def test_hvp_against_oracle(n, m, d, eps, dtype):
+    p = make_case(n, m, d, seed=23 * n + d, weights="softmax", dtype=dtype, scale=1.0 / np.sqrt(d))
+    f, g = potentials(p, eps, 2000)
+    rng = np.random.default_rng(d)
+    Vx = rng.standard_normal((1, n, d)).astype(np.float32)
+    Vy = rng.standard_normal((1, m, d)).astype(np.float32)
+    X, Y, a, b = (np.asarray(v[0], np.float64) for v in (p.X, p.Y, p.a, p.b))
+    tau = 5e-3 if dtype == "bf16" else 5e-4
+    hx = run_hvp(p, eps, f, g, Vx, "x")[0]
+    ref_x = oracle.hvp_x(X, Y, a, b, f[0], g[0], eps, Vx[0])
+    assert np.max(np.abs(hx - ref_x)) <= tau * np.max(np.abs(ref_x)), np.max(np.abs(hx - ref_x)) / np.max(np.abs(ref_x))
+    hy = run_hvp(p, eps, f, g, Vy, "y")[0]
+    ref_y = oracle.hvp_x(Y, X, b, a, g[0], f[0], eps, Vy[0])
+    assert np.max(np.abs(hy - ref_y)) <= tau * np.max(np.abs(ref_y)), np.max(np.abs(hy - ref_y)) / np.max(np.abs(ref_y))
+
+
+def test_hvp_symmetric_and_linear_at_larger_size():
+    """A property that holds at any size: <U, H V> = <V, H U>, and H is linear."""
+    p = make_case(3000, 2500, 3, seed=77, weights="uniform")
+    eps = 0.1
+    X, Y, a, b = dev(p)
+    f, g = sk.solve(X, Y, a, b, eps, 300)
+    rng = np.random.default_rng(5)
+    U = rng.standard_normal((1, 3000, 3)).astype(np.float32)
+    V = rng.standard_normal((1, 3000, 3)).astype(np.float32)
+    ws = sk.alloc_workspace(X, Y, hvp=True)
+    sk.init_norms(X, Y, a, b, ws)
+    hU = sk.hvp_x(X, Y, ws, f, g, eps, torch.from_numpy(U).cuda(), cg_iters=400, cg_tol=1e-7).cpu().numpy()
+    hV = sk.hvp_x(X, Y, ws, f, g, eps, torch.from_numpy(V).cuda(), cg_iters=400, cg_tol=1e-7).cpu().numpy()
+    W = (2.0 * U - 0.5 * V).astype(np.float32)
+    hW = sk.hvp_x(X, Y, ws, f, g, eps, torch.from_numpy(W).cuda(), cg_iters=400, cg_tol=1e-7).cpu().numpy()
+    lhs = float((U.astype(np.float64) * hV).sum())
+    rhs = float((V.astype(np.float64) * hU).sum())
+    scale = float(np.abs(U * hV).sum() + np.abs(V * hU).sum())
+    assert abs(lhs - rhs) <= 5e-4 * scale
+    lin = 2.0 * hU - 0.5 * hV
+    assert np.max(np.abs(hW - lin)) <= 5e-4 * np.max(np.abs(lin))
