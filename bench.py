@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: n=m=70000, d=3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-transport", action="store_true", help="skip the transport-application leg")
+    ap.add_argument("--no-hvp", action="store_true", help="skip the Hessian-vector-product leg")
+    ap.add_argument("--hvp-cg", type=int, default=50, help="CG iterations of the timed HVP")
     ap.add_argument("--cpu-seconds", type=float, default=6.0, help="target wall time of the CPU leg")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes (scales rocprofv3 byte counters)")
@@ -201,6 +203,8 @@ def main():
 
     if not args.no_transport:
         out["transport"] = transport_leg(sk, X, Y, a, b, f, g, eps_sched[-1], p, contraction)
+    if not args.no_hvp:
+        out["hvp"] = hvp_leg(sk, X, Y, a, b, f, g, eps_sched[-1], p, args.hvp_cg)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(out), flush=True)
@@ -242,6 +246,42 @@ def transport_leg(sk, X, Y, a, b, f, g, eps, p, contraction, reps=10):
                 "peak": PEAK_MFMA[contraction] / 1e12, "unit": "TFLOP/s", "frac": round(t_mfma / t_call, 4)}
     return {"what": "barycentric projection + gradient of every point (one call per side)",
             "ms_per_call": {"x": round(ms["x"], 4), "y": round(ms["y"], 4)}, "reps": reps, "roofline": roof}
+
+
+def hvp_leg(sk, X, Y, a, b, f, g, eps, p, cg_iters, reps=3):
+    """Time one Hessian-vector product in X (fixed CG iteration count, no early stop).
+    Every plan pass evaluates each of the B*n*m scores once: 2 half-steps, the plan
+    applied to Y, P^T [z, v, cr/r], 2 passes per CG iteration, P [dg, dg y] and
+    ceil(d / floor(64/d)) passes for the quadratic term."""
+    import math
+
+    import numpy as np
+    import torch
+
+    ws = sk.alloc_workspace(X, Y, hvp=True)
+    sk.init_norms(X, Y, a, b, ws)
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    V = torch.randn((p.batch, p.n, p.d), device="cuda", generator=gen)
+    out = sk.hvp_x(X, Y, ws, f, g, eps, V, cg_iters=cg_iters, cg_tol=0.0)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for r in range(reps):
+        sk.hvp_x(X, Y, ws, f, g, eps, V, cg_iters=cg_iters, cg_tol=0.0, out=out)
+        ev[r + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+    assert torch.isfinite(out).all(), "non-finite HVP"
+    per = max(1, 64 // p.d)
+    passes = 2 + 1 + 1 + 2 * cg_iters + 1 + math.ceil(p.d / per)
+    exps = passes * p.batch * p.n * p.m
+    achieved = exps / (ms / 1e3)
+    return {"what": f"one Hessian-vector product in X, {cg_iters} CG iterations ({passes} plan passes)",
+            "ms_per_call": round(ms, 3), "reps": reps,
+            "roofline": {"bound": "alu", "achieved": round(achieved / 1e9, 1),
+                         "peak": round(PEAK_EXP_PER_S / 1e9, 1), "unit": "Gexp/s",
+                         "frac": round(achieved / PEAK_EXP_PER_S, 4)}}
 
 
 def cpu_baseline(p, target_s: float):
