@@ -1161,8 +1161,14 @@ __global__ __launch_bounds__(256) void k_hvp_rhs(const void* __restrict__ Q, int
 // Conjugate gradients on the Schur system (diag(c) - P^T diag(1/r) P) dg = rhs,
 // preconditioned by diag(c), for every problem at once.  The system is singular
 // along constants (a common shift of the potentials leaves the plan
-// unchanged); the residual is kept at zero sum.  One workgroup per problem,
-// fixed-order reductions.  State per problem: st[0] = rz, st[1] = rz0, st[2] = done.
+// unchanged); the residual is kept at zero sum.  Each vector is split into
+// CG_BLK-element blocks, one workgroup each; every reduction writes one partial
+// per block and the next kernel adds the partials in block order (identical in
+// every workgroup, so the result is deterministic).  Scalars per problem live
+// in st[b][0..3] = (rz, rz0, done, pAp); rz is double buffered (st_in/st_out)
+// because the kernel that computes the new value also reads the old one.
+constexpr int CG_BLK = 2048;
+
 __device__ __forceinline__ double block_sum(double v, double* red) {
   __syncthreads();
   red[threadIdx.x] = v;
@@ -1174,30 +1180,63 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
   return red[0];
 }
 
-__global__ __launch_bounds__(256) void k_cg_init(const double* __restrict__ rhs, const double* __restrict__ cmass,
-                                                 int m, double* __restrict__ dg, double* __restrict__ res,
-                                                 double* __restrict__ pd, float* __restrict__ pdf,
-                                                 double* __restrict__ st) {
+// Sum of the nblk partials of problem b, in order.
+__device__ __forceinline__ double sum_partials(const double* part, int nblk, double* red) {
+  double v = 0.0;
+  for (int k = threadIdx.x; k < nblk; k += 256) v += part[k];
+  return block_sum(v, red);
+}
+
+// res = rhs, partial sums of res
+__global__ __launch_bounds__(256) void k_cg_init1(const double* __restrict__ rhs, int m, int nblk,
+                                                  double* __restrict__ res, double* __restrict__ part) {
   __shared__ double red[256];
-  const size_t o = (size_t)blockIdx.x * m;
-  double s = 0.0;
-  for (int j = threadIdx.x; j < m; j += 256) s += rhs[o + j];
-  const double mean = block_sum(s, red) / m;
-  double rz = 0.0;
-  for (int j = threadIdx.x; j < m; j += 256) {
-    const double r = rhs[o + j] - mean;
+  const int b = blockIdx.y;
+  const size_t o = (size_t)b * m;
+  const int j0 = blockIdx.x * CG_BLK, j1 = min(m, j0 + CG_BLK);
+  double v = 0.0;
+  for (int j = j0 + threadIdx.x; j < j1; j += 256) {
+    res[o + j] = rhs[o + j];
+    v += rhs[o + j];
+  }
+  v = block_sum(v, red);
+  if (threadIdx.x == 0) part[(size_t)b * nblk + blockIdx.x] = v;
+}
+
+// res -= mean, z = res/c, pd = z, dg = 0, partials of res.z
+__global__ __launch_bounds__(256) void k_cg_init2(const double* __restrict__ cmass, int m, int nblk,
+                                                  const double* __restrict__ psum, double* __restrict__ dg,
+                                                  double* __restrict__ res, double* __restrict__ pd,
+                                                  float* __restrict__ pdf, double* __restrict__ part) {
+  __shared__ double red[256];
+  const int b = blockIdx.y;
+  const size_t o = (size_t)b * m;
+  const double mean = sum_partials(psum + (size_t)b * nblk, nblk, red) / m;
+  const int j0 = blockIdx.x * CG_BLK, j1 = min(m, j0 + CG_BLK);
+  double v = 0.0;
+  for (int j = j0 + threadIdx.x; j < j1; j += 256) {
+    const double r = res[o + j] - mean;
     const double z = cmass[o + j] > 0.0 ? r / cmass[o + j] : 0.0;
     res[o + j] = r;
     pd[o + j] = z;
     pdf[o + j] = (float)z;
     dg[o + j] = 0.0;
-    rz += r * z;
+    v += r * z;
   }
-  rz = block_sum(rz, red);
+  v = block_sum(v, red);
+  if (threadIdx.x == 0) part[(size_t)b * nblk + blockIdx.x] = v;
+}
+
+// rz0 = rz = sum of the partials; done if zero
+__global__ __launch_bounds__(256) void k_cg_init3(int nblk, const double* __restrict__ prz,
+                                                  double* __restrict__ st) {
+  __shared__ double red[256];
+  const int b = blockIdx.x;
+  const double rz = sum_partials(prz + (size_t)b * nblk, nblk, red);
   if (threadIdx.x == 0) {
-    st[3 * blockIdx.x] = rz;
-    st[3 * blockIdx.x + 1] = rz;
-    st[3 * blockIdx.x + 2] = rz > 0.0 ? 0.0 : 1.0;
+    st[4 * b] = rz;
+    st[4 * b + 1] = rz;
+    st[4 * b + 2] = rz > 0.0 ? 0.0 : 1.0;
   }
 }
 
@@ -1208,47 +1247,89 @@ __global__ __launch_bounds__(256) void k_div_mass(float* __restrict__ t, const d
   if (i < total) t[i] = (float)(mass[i] > 0.0 ? (double)t[i] / mass[i] : 0.0);
 }
 
-__global__ __launch_bounds__(256) void k_cg_step(const float* __restrict__ q, const double* __restrict__ cmass, int m,
-                                                 double tol2, double* __restrict__ dg, double* __restrict__ res,
-                                                 double* __restrict__ pd, float* __restrict__ pdf,
-                                                 double* __restrict__ st) {
+// partials of pd . S pd, S pd = c pd - q  (q = P^T (P pd / r))
+__global__ __launch_bounds__(256) void k_cg_a(const float* __restrict__ q, const double* __restrict__ cmass, int m,
+                                              int nblk, const double* __restrict__ pd, double* __restrict__ part) {
   __shared__ double red[256];
-  const size_t o = (size_t)blockIdx.x * m;
-  double* s3 = st + 3 * blockIdx.x;
-  const bool done = s3[2] != 0.0;
-  // S p = c p - P^T (P p / r)
-  double pap = 0.0;
-  for (int j = threadIdx.x; j < m; j += 256) pap += pd[o + j] * (cmass[o + j] * pd[o + j] - (double)q[o + j]);
-  pap = block_sum(pap, red);
-  const double rz = s3[0];
-  const double alpha = (done || !(pap > 0.0)) ? 0.0 : rz / pap;
-  double sum = 0.0;
-  for (int j = threadIdx.x; j < m; j += 256) {
+  const int b = blockIdx.y;
+  const size_t o = (size_t)b * m;
+  const int j0 = blockIdx.x * CG_BLK, j1 = min(m, j0 + CG_BLK);
+  double v = 0.0;
+  for (int j = j0 + threadIdx.x; j < j1; j += 256) v += pd[o + j] * (cmass[o + j] * pd[o + j] - (double)q[o + j]);
+  v = block_sum(v, red);
+  if (threadIdx.x == 0) part[(size_t)b * nblk + blockIdx.x] = v;
+}
+
+// alpha = rz / pAp; dg += alpha pd; res -= alpha S pd; partial sums of res
+__global__ __launch_bounds__(256) void k_cg_b(const float* __restrict__ q, const double* __restrict__ cmass, int m,
+                                              int nblk, const double* __restrict__ ppap,
+                                              const double* __restrict__ st, double* __restrict__ dg,
+                                              double* __restrict__ res, const double* __restrict__ pd,
+                                              double* __restrict__ part) {
+  __shared__ double red[256];
+  const int b = blockIdx.y;
+  const size_t o = (size_t)b * m;
+  const double pap = sum_partials(ppap + (size_t)b * nblk, nblk, red);
+  const double* s4 = st + 4 * b;
+  const double alpha = (s4[2] != 0.0 || !(pap > 0.0)) ? 0.0 : s4[0] / pap;
+  const int j0 = blockIdx.x * CG_BLK, j1 = min(m, j0 + CG_BLK);
+  double v = 0.0;
+  for (int j = j0 + threadIdx.x; j < j1; j += 256) {
     const double sp = cmass[o + j] * pd[o + j] - (double)q[o + j];
     dg[o + j] += alpha * pd[o + j];
     res[o + j] -= alpha * sp;
-    sum += res[o + j];
+    v += res[o + j];
   }
-  const double mean = block_sum(sum, red) / m;
-  double rzn = 0.0;
-  for (int j = threadIdx.x; j < m; j += 256) {
-    res[o + j] -= mean;
-    const double z = cmass[o + j] > 0.0 ? res[o + j] / cmass[o + j] : 0.0;
-    rzn += res[o + j] * z;
+  v = block_sum(v, red);
+  if (threadIdx.x == 0) part[(size_t)b * nblk + blockIdx.x] = v;
+}
+
+// res -= mean; partials of res . z, z = res / c
+__global__ __launch_bounds__(256) void k_cg_c(const double* __restrict__ cmass, int m, int nblk,
+                                              const double* __restrict__ psum, double* __restrict__ res,
+                                              double* __restrict__ part) {
+  __shared__ double red[256];
+  const int b = blockIdx.y;
+  const size_t o = (size_t)b * m;
+  const double mean = sum_partials(psum + (size_t)b * nblk, nblk, red) / m;
+  const int j0 = blockIdx.x * CG_BLK, j1 = min(m, j0 + CG_BLK);
+  double v = 0.0;
+  for (int j = j0 + threadIdx.x; j < j1; j += 256) {
+    const double r = res[o + j] - mean;
+    res[o + j] = r;
+    v += r * (cmass[o + j] > 0.0 ? r / cmass[o + j] : 0.0);
   }
-  rzn = block_sum(rzn, red);
-  const bool stop = done || alpha == 0.0 || rzn <= tol2 * s3[1];
-  const double beta = stop ? 0.0 : rzn / rz;
-  for (int j = threadIdx.x; j < m; j += 256) {
+  v = block_sum(v, red);
+  if (threadIdx.x == 0) part[(size_t)b * nblk + blockIdx.x] = v;
+}
+
+// rz_new from the partials; stop test; pd = z + beta pd.  Reads st_in, writes st_out.
+__global__ __launch_bounds__(256) void k_cg_d(const double* __restrict__ cmass, int m, int nblk,
+                                              const double* __restrict__ prz, const double* __restrict__ ppap,
+                                              double tol2, const double* __restrict__ st_in,
+                                              double* __restrict__ st_out, const double* __restrict__ res,
+                                              double* __restrict__ pd, float* __restrict__ pdf) {
+  __shared__ double red[256];
+  const int b = blockIdx.y;
+  const size_t o = (size_t)b * m;
+  const double rzn = sum_partials(prz + (size_t)b * nblk, nblk, red);
+  const double pap = sum_partials(ppap + (size_t)b * nblk, nblk, red);
+  const double* si = st_in + 4 * b;
+  const bool stalled = !(pap > 0.0);
+  const bool stop = si[2] != 0.0 || stalled || rzn <= tol2 * si[1];
+  const double beta = stop ? 0.0 : rzn / si[0];
+  const int j0 = blockIdx.x * CG_BLK, j1 = min(m, j0 + CG_BLK);
+  for (int j = j0 + threadIdx.x; j < j1; j += 256) {
     const double z = cmass[o + j] > 0.0 ? res[o + j] / cmass[o + j] : 0.0;
     const double p = stop ? 0.0 : z + beta * pd[o + j];
     pd[o + j] = p;
     pdf[o + j] = (float)p;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    s3[0] = rzn;
-    s3[2] = stop ? 1.0 : 0.0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    double* so = st_out + 4 * b;
+    so[0] = si[2] != 0.0 ? si[0] : rzn;
+    so[1] = si[1];
+    so[2] = stop ? 1.0 : 0.0;
   }
 }
 
@@ -1337,7 +1418,7 @@ struct Layout {
   size_t vt, bpv, bs, ttotal;
   // Hessian-vector products (after `ttotal`)
   size_t h_lse_r, h_lse_k, h_mr, h_mk, h_py, h_mat, h_w, h_g, h_quad, h_tmp, h_zr, h_cr, h_rhs, h_dg, h_res,
-      h_pd, h_pdf, h_t, h_q, h_st, htotal;
+      h_pd, h_pdf, h_t, h_q, h_st, h_part, htotal;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -1446,7 +1527,8 @@ Layout layout_of(const sk_problem* p) {
   L.h_pdf = take(4 * bm);
   L.h_t = take(4 * bm);
   L.h_q = take(4 * bm);
-  L.h_st = take(8 * 3 * (size_t)B);
+  L.h_st = take(8 * 8 * (size_t)B);
+  L.h_part = take(8 * 3 * (size_t)B * ((mx + CG_BLK - 1) / CG_BLK));
   L.htotal = off;
   return L;
 }
@@ -1875,7 +1957,15 @@ sk_status hvp(const sk_problem* p, const void* X, const void* Y, char* w, const 
   if (st != SK_OK) return st;
   hipLaunchKernelGGL(k_hvp_rhs, dim3(blocks_for(nk)), dim3(256), 0, s, Qraw, in16, wk, nk, d, rhs);
   // 4. conjugate gradients on the Schur system in dg
-  hipLaunchKernelGGL(k_cg_init, dim3(B), dim3(256), 0, s, rhs, mk, keys, dg, res, pd, pdf, stt);
+  const int nblk = (keys + CG_BLK - 1) / CG_BLK;
+  double* pa = reinterpret_cast<double*>(w + L.h_part);
+  double* pb = pa + (size_t)B * nblk;
+  double* st_a = stt;
+  double* st_b = stt + 4 * (size_t)B;
+  const dim3 vgrid(nblk, B);
+  hipLaunchKernelGGL(k_cg_init1, vgrid, dim3(256), 0, s, rhs, keys, nblk, res, pa);
+  hipLaunchKernelGGL(k_cg_init2, vgrid, dim3(256), 0, s, mk, keys, nblk, pa, dg, res, pd, pdf, pb);
+  hipLaunchKernelGGL(k_cg_init3, dim3(B), dim3(256), 0, s, nblk, pb, st_a);
   st = hip_check("CG set-up launch");
   if (st != SK_OK) return st;
   const double tol2 = (double)cg_tol * (double)cg_tol;
@@ -1885,7 +1975,14 @@ sk_status hvp(const sk_problem* p, const void* X, const void* Y, char* w, const 
     hipLaunchKernelGGL(k_div_mass, dim3(blocks_for(nr)), dim3(256), 0, s, tv, mr, nr);
     st = apply_plan(p, X, Y, w, L, pot_k, pot_r, lse_k, eps, 1 - side, tv, 1, qv, s);
     if (st != SK_OK) return st;
-    hipLaunchKernelGGL(k_cg_step, dim3(B), dim3(256), 0, s, qv, mk, keys, tol2, dg, res, pd, pdf, stt);
+    double* st_in = (it % 2 == 0) ? st_a : st_b;
+    double* st_out = (it % 2 == 0) ? st_b : st_a;
+    hipLaunchKernelGGL(k_cg_a, vgrid, dim3(256), 0, s, qv, mk, keys, nblk, pd, pa);
+    hipLaunchKernelGGL(k_cg_b, vgrid, dim3(256), 0, s, qv, mk, keys, nblk, pa, st_in, dg, res, pd, pb);
+    // pb (sum of res) is consumed by k_cg_c before k_cg_c's own partials go to a third buffer
+    hipLaunchKernelGGL(k_cg_c, vgrid, dim3(256), 0, s, mk, keys, nblk, pb, res, pb + (size_t)B * nblk);
+    hipLaunchKernelGGL(k_cg_d, vgrid, dim3(256), 0, s, mk, keys, nblk, pb + (size_t)B * nblk, pa, tol2, st_in,
+                       st_out, res, pd, pdf);
     st = hip_check("CG step launch");
     if (st != SK_OK) return st;
   }
