@@ -459,7 +459,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
   constexpr int KP = NCH * 32;
   constexpr int NI = KP / T::KI;   // MFMA instructions per tile
   constexpr int NO = T::NOUT;      // outputs per lane per tile
-  constexpr int LROW = KP + 8;     // LDS row stride in elements (16-byte pad against bank conflicts)
+  constexpr int LROW = KP + (MW == 16 ? 16 : 8);  // LDS row stride (elements); the pad avoids bank conflicts
   constexpr int CK = TC * MW;      // keys per chunk
   constexpr int VPR = KP / 8;      // 16-byte vectors per key row
   constexpr int NVEC = CK * VPR;
@@ -803,7 +803,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
   using T = Tile<16>;
   constexpr int KP = NCH * 32;
   constexpr int NI = KP / T::KI;
-  constexpr int LROW = KP + 8;
+  constexpr int LROW = KP + 16;  // 32-byte pad: conflict-free 16-wide operand reads
   constexpr int CK = VK;
   constexpr int VPR = KP / 8;
   constexpr int NVEC = CK * VPR;
