@@ -29,7 +29,8 @@
 //  * bf16 inputs: raw bf16 values (products are exact in fp32); the half bias
 //    beta_j/2 goes in through the accumulator and one FMA per element applies
 //    the 2*lambda scale and the offset.
-//  * Online LSE with a lazy offset: the running offset m is only moved when a
+//  * Online LSE with a lazy offset: a workgroup sets its row offsets from the
+//    first key tile's maximum plus a headroom, and moves them only when a
 //    chunk's partial sums exceed 2^112 (rare), so the hot loop has no max or
 //    rescale.  Such a chunk is recomputed with its exact maximum; offsets are
 //    integers, so rescaling is an exact power of two.
@@ -73,6 +74,11 @@ constexpr double LOG2E = 1.4426950408889634;
 // Largest partial sum a lane may carry past a chunk check.  Kept well below
 // FLT_MAX so that merging 4 lanes and up to KS_MAX key splits cannot overflow.
 constexpr float SUM_LIMIT = 0x1p112f;
+// Offsets sit this far (base 2) above the largest score seen when they are set:
+// terms more than HEADROOM + 126 below it flush to zero (relative size below
+// 2^-62 of that score's term), and scores may grow by HEADROOM + 112 before a
+// chunk must be redone.
+constexpr float HEADROOM = 64.f;
 
 // ---------------------------------------------------------------------------
 // K-slot layout of the fp32 path for point dimension d.
@@ -442,7 +448,7 @@ __host__ __device__ constexpr int cfg_R(int mode, int nch) {
                                  : (nch <= 4 ? 4 : (nch <= 8 ? 2 : (cfg_wide_k(mode, nch) ? 2 : 1)));
 }
 __host__ __device__ constexpr int cfg_TC(int mode, int nch) {
-  return (mode == MODE_SPLIT && nch == 1) ? 4
+  return (mode == MODE_SPLIT && nch == 1) ? 8
                                           : (cfg_MW(mode, nch) == 32 ? (nch <= 2 ? 2 : 1) : (cfg_wide_k(mode, nch) ? 2 : 1));
 }
 __host__ __device__ constexpr int cfg_waves(int mode, int nch) { return (mode == MODE_SPLIT && nch == 1) ? 3 : 2; }
@@ -588,19 +594,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
 #pragma unroll
     for (int c = 0; c < R; ++c) ssave[c] = s[c];
 
-    bool redo = (ci == c0);
-    if (!redo) {
-#pragma unroll 1
-      for (int t = 0; t < TC; ++t) {
-        Acc acc[R];
-        tile(buf, t, acc);
-        accumulate(acc);
-      }
-      int bad = 0;
+    if (ci == c0) {
+      // First offsets: the maximum raw score of the chunk's first key tile plus
+      // HEADROOM, so later keys may score up to HEADROOM + 112 higher before a
+      // chunk has to be redone.
+      if (MODE == MODE_SPLIT) {
 #pragma unroll
-      for (int c = 0; c < R; ++c) bad |= !(s[c] <= SUM_LIMIT);
-      redo = __any(bad);
+        for (int c = 0; c < R; ++c) set_offset(bq[c][0], 0.f, grp == 0);
+      }
+      Acc acc[R];
+      tile(buf, 0, acc);
+#pragma unroll
+      for (int c = 0; c < R; ++c) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int o = 0; o < NO; ++o) mx = fmaxf(mx, raw(acc[c][o]));
+        m[c] = offset_from_max(lanes_max(mx) + HEADROOM, qg);
+        if (MODE == MODE_SPLIT) set_offset(bq[c][0], -m[c], grp == 0);
+      }
     }
+#pragma unroll 1
+    for (int t = 0; t < TC; ++t) {
+      Acc acc[R];
+      tile(buf, t, acc);
+      accumulate(acc);
+    }
+    int bad = 0;
+#pragma unroll
+    for (int c = 0; c < R; ++c) bad |= !(s[c] <= SUM_LIMIT);
+    const bool redo = __any(bad);
     if (redo) {
       // Exact chunk maximum of the raw scores (offset slots zeroed), a new
       // offset from it, then the chunk again through the normal path.
@@ -625,7 +647,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
 #pragma unroll
       for (int c = 0; c < R; ++c) {
         mx[c] = lanes_max(mx[c]);
-        const float mn = fmaxf(m[c], offset_from_max(mx[c], qg));
+        const float mn = fmaxf(m[c], offset_from_max(mx[c] + HEADROOM, qg));
         s[c] = rescale(s[c], m[c], mn);
         m[c] = mn;
         if (MODE == MODE_SPLIT) set_offset(bq[c][0], -m[c], grp == 0);
