@@ -79,6 +79,9 @@ constexpr float SUM_LIMIT = 0x1p112f;
 // 2^-62 of that score's term), and scores may grow by HEADROOM + 112 before a
 // chunk must be redone.
 constexpr float HEADROOM = 64.f;
+// Below this many keys the d <= 3 half-step uses SMALL_TC key tiles per chunk.
+constexpr int SMALL_KEYS = 16384;
+constexpr int SMALL_TC = 4;
 
 // ---------------------------------------------------------------------------
 // K-slot layout of the fp32 path for point dimension d.
@@ -453,13 +456,14 @@ __host__ __device__ constexpr int cfg_TC(int mode, int nch) {
 }
 __host__ __device__ constexpr int cfg_waves(int mode, int nch) { return (mode == MODE_SPLIT && nch == 1) ? 3 : 2; }
 
-template <int MODE, int NCH>
+// TCX overrides the key tiles per chunk (0: cfg_TC), for small problems.
+template <int MODE, int NCH, int TCX = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(MODE, NCH)))) void k_lse(
     const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb,
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, float* __restrict__ out,
     float2* __restrict__ part, int rows, int rows_pad, int keys, int keys_pad, int chunks_per_split, int batch,
     float lam2, double inv_lam) {
-  constexpr int MW = cfg_MW(MODE, NCH), R = cfg_R(MODE, NCH), TC = cfg_TC(MODE, NCH);
+  constexpr int MW = cfg_MW(MODE, NCH), R = cfg_R(MODE, NCH), TC = TCX ? TCX : cfg_TC(MODE, NCH);
   using T = Tile<MW>;
   using Acc = typename T::Acc;
   constexpr int KP = NCH * 32;
@@ -1714,12 +1718,18 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   if (st != SK_OK) return st;
 
   LseFn fn = (L.mode == MODE_SPLIT) ? lse_lookup<MODE_SPLIT>(nch) : lse_lookup<MODE_BF16>(nch);
+  int tc = cfTC;
+  if (L.mode == MODE_SPLIT && nch == 1 && keys < SMALL_KEYS) {
+    // fewer keys than a few workgroups' worth of 256-key chunks: 128-key chunks fill the GPU better
+    fn = &k_lse<MODE_SPLIT, 1, SMALL_TC>;
+    tc = SMALL_TC;
+  }
   if (fn == nullptr) {
     set_err("no kernel for %d K chunks", nch);
     return SK_EUNSUPPORTED;
   }
   const int wg_x = (rows + 4 * cfR * cfMW - 1) / (4 * cfR * cfMW);
-  const int CK = cfTC * cfMW;
+  const int CK = tc * cfMW;
   const int total_chunks = (keys + CK - 1) / CK;
   int capacity = 0;
   st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity);
