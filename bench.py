@@ -252,7 +252,7 @@ def hvp_leg(sk, X, Y, a, b, f, g, eps, p, cg_iters, reps=3):
     """Time one Hessian-vector product in X (fixed CG iteration count, no early stop).
     Every plan pass evaluates each of the B*n*m scores once: 2 half-steps, the plan
     applied to Y, P^T [z, v, cr/r], 2 passes per CG iteration, P [dg, dg y] and
-    ceil(d / floor(64/d)) passes for the quadratic term."""
+    ceil(d(d+1)/2 / 64) passes for the quadratic term."""
     import math
 
     import numpy as np
@@ -273,8 +273,7 @@ def hvp_leg(sk, X, Y, a, b, f, g, eps, p, cg_iters, reps=3):
     torch.cuda.synchronize()
     ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
     assert torch.isfinite(out).all(), "non-finite HVP"
-    per = max(1, 64 // p.d)
-    passes = 2 + 1 + 1 + 2 * cg_iters + 1 + math.ceil(p.d / per)
+    passes = 2 + 1 + 1 + 2 * cg_iters + 1 + math.ceil(p.d * (p.d + 1) / 2 / 64)
     exps = passes * p.batch * p.n * p.m
     achieved = exps / (ms / 1e3)
     return {"what": f"one Hessian-vector product in X, {cg_iters} CG iterations ({passes} plan passes)",

@@ -1370,28 +1370,48 @@ __global__ __launch_bounds__(256) void k_hvp_gmat(const void* __restrict__ Q, in
   for (int t = 0; t < d; ++t) row[1 + t] = (float)(dg[j] * (double)coord(Q, (size_t)j * d + t, in_bf16));
 }
 
-// Matrix [q_t * q for t in t0 .. t0+nt-1] per row of the fixed cloud.
+// Pairs (t, u), t <= u, of coordinates in the order (0,0) (0,1) .. (0,d-1) (1,1) ..;
+// pair k's coordinates.
+__device__ __forceinline__ void pair_of(int k, int d, int& t, int& u) {
+  t = 0;
+  while (k >= d - t) {
+    k -= d - t;
+    ++t;
+  }
+  u = t + k;
+}
+
+// Matrix [q_t q_u for pairs k0 .. k0+nb-1] per row of the fixed cloud.
 __global__ __launch_bounds__(256) void k_hvp_qqmat(const void* __restrict__ Q, int in_bf16, long long total, int d,
-                                                   int t0, int nt, float* __restrict__ M) {
+                                                   int k0, int nb, float* __restrict__ M) {
   const long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= total) return;
-  float* row = M + j * (nt * d);
-  for (int u = 0; u < nt; ++u) {
-    const double qt = coord(Q, (size_t)j * d + t0 + u, in_bf16);
-    for (int t = 0; t < d; ++t) row[u * d + t] = (float)(qt * (double)coord(Q, (size_t)j * d + t, in_bf16));
+  int t, u;
+  pair_of(k0, d, t, u);
+  float* row = M + j * nb;
+  for (int e = 0; e < nb; ++e) {
+    row[e] = (float)((double)coord(Q, (size_t)j * d + t, in_bf16) * (double)coord(Q, (size_t)j * d + u, in_bf16));
+    if (++u == d) u = ++t;
   }
 }
 
-// quad_i += sum_{u < nt} v_i[t0+u] * A_i[u*d .. u*d+d)   (A = P [q_t q])
+// quad_i += M_i v_i with M_i = sum_j P_ij q_j q_j^T symmetric: a pair (t, u) with
+// A = (P [q_t q_u])_i adds v_i[t] A to component u and, off the diagonal,
+// v_i[u] A to component t.
 __global__ __launch_bounds__(256) void k_hvp_quad(const float* __restrict__ V, const float* __restrict__ A,
-                                                  long long total, int d, int t0, int nt,
+                                                  long long total, int d, int k0, int nb,
                                                   double* __restrict__ quad) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
-  for (int t = 0; t < d; ++t) {
-    double acc = quad[i * d + t];
-    for (int u = 0; u < nt; ++u) acc += (double)V[i * d + t0 + u] * (double)A[i * (nt * d) + u * d + t];
-    quad[i * d + t] = acc;
+  int t, u;
+  pair_of(k0, d, t, u);
+  const float* v = V + i * d;
+  double* q = quad + i * d;
+  for (int e = 0; e < nb; ++e) {
+    const double a = A[i * nb + e];
+    q[u] += (double)v[t] * a;
+    if (t != u) q[t] += (double)v[u] * a;
+    if (++u == d) u = ++t;
   }
 }
 
@@ -2023,17 +2043,18 @@ sk_status hvp(const sk_problem* p, const void* X, const void* Y, char* w, const 
   st = hip_check("HVP matrix launch");
   if (st == SK_OK) st = apply_plan(p, X, Y, w, L, pot_r, pot_k, lse_r, eps, side, mat, d + 1, gm, s);
   if (st != SK_OK) return st;
-  // 6. sum_j P_ij (q_j . v_i) q_j = sum_t v_i[t] (P [q_t q])_i, a few coordinates t per pass
+  // 6. sum_j P_ij (q_j . v_i) q_j = M_i v_i, M_i = sum_j P_ij q_j q_j^T from the plan
+  //    applied to the d(d+1)/2 products q_t q_u, APPLY_COLS pairs per pass
   hipLaunchKernelGGL(k_fill_f32, dim3(blocks_for(2 * nr * d)), dim3(256), 0, s, reinterpret_cast<float*>(quad),
                      (int)(2 * nr * d), 0.f);
-  const int per = std::max(1, APPLY_COLS / d);
-  for (int t0 = 0; t0 < d; t0 += per) {
-    const int nt = std::min(per, d - t0);
-    hipLaunchKernelGGL(k_hvp_qqmat, dim3(blocks_for(nk)), dim3(256), 0, s, Qraw, in16, nk, d, t0, nt, mat);
+  const int npairs = d * (d + 1) / 2;
+  for (int k0 = 0; k0 < npairs; k0 += APPLY_COLS) {
+    const int nb = std::min(APPLY_COLS, npairs - k0);
+    hipLaunchKernelGGL(k_hvp_qqmat, dim3(blocks_for(nk)), dim3(256), 0, s, Qraw, in16, nk, d, k0, nb, mat);
     st = hip_check("HVP matrix launch");
-    if (st == SK_OK) st = apply_plan(p, X, Y, w, L, pot_r, pot_k, lse_r, eps, side, mat, nt * d, tmp, s);
+    if (st == SK_OK) st = apply_plan(p, X, Y, w, L, pot_r, pot_k, lse_r, eps, side, mat, nb, tmp, s);
     if (st != SK_OK) return st;
-    hipLaunchKernelGGL(k_hvp_quad, dim3(blocks_for(nr)), dim3(256), 0, s, V, tmp, nr, d, t0, nt, quad);
+    hipLaunchKernelGGL(k_hvp_quad, dim3(blocks_for(nr)), dim3(256), 0, s, V, tmp, nr, d, k0, nb, quad);
   }
   // 7. assemble
   hipLaunchKernelGGL(k_hvp_final, dim3(blocks_for(nr)), dim3(256), 0, s, Praw, in16, V, py, mr, zr, cr, gm, quad, nr,
