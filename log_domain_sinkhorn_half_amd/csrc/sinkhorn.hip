@@ -758,6 +758,8 @@ __host__ __device__ constexpr int bary_R(int nch, int nct) {
   return nct >= 9 ? 1 : (nch == 1 ? (nct >= 4 ? 2 : 4) : (nch <= 8 ? 2 : 1));
 }
 __host__ __device__ constexpr int bary_waves(int nch) { return nch >= 12 ? 1 : 2; }
+// 32-key value blocks per LDS chunk of the transport kernel (fewer barriers for small operands)
+__host__ __device__ constexpr int bary_TCB(int nch, int nct) { return (nch <= 2 && nct <= 4) ? 4 : 1; }
 
 __device__ __forceinline__ u4 pack8(const u16 (&v)[8]) {
   return u4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
@@ -830,17 +832,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
   constexpr int KP = NCH * 32;
   constexpr int NI = KP / T::KI;
   constexpr int LROW = KP + 16;  // 32-byte pad: conflict-free 16-wide operand reads
-  constexpr int CK = VK;
+  constexpr int TCB = bary_TCB(NCH, NCT);  // value blocks per chunk
+  constexpr int CK = TCB * VK;
   constexpr int VPR = KP / 8;
   constexpr int NVEC = CK * VPR;
   constexpr int NLD = (NVEC + 255) / 256;
   constexpr int NC = NCT * 16;        // value columns
   constexpr int VROW = VK + 8;        // LDS row stride of the value tile (elements)
-  constexpr int NVV = NC * (VK / 8);  // 16-byte vectors per value block
+  constexpr int NVV = TCB * NC * (VK / 8);  // 16-byte vectors per chunk of value blocks
   constexpr int NLV = (NVV + 255) / 256;
   constexpr int QPW = R * MW;
   __shared__ __attribute__((aligned(16))) u16 lds[2][(CK + 1) * LROW];
-  __shared__ __attribute__((aligned(16))) u16 ldv[2][(NC + 1) * VROW];
+  __shared__ __attribute__((aligned(16))) u16 ldv[2][(TCB * NC + 1) * VROW];
   __shared__ __attribute__((aligned(16))) float ldsb[2][CK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -907,7 +910,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
     const u16* src = Kb + (size_t)chunk * CK * KP;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) pre[i] = *reinterpret_cast<const u4*>(src + (size_t)(tid + 256 * i) * 8);
-    const u16* vsrc = Vb + (size_t)chunk * NC * VK;
+    const u16* vsrc = Vb + (size_t)chunk * TCB * NC * VK;
 #pragma unroll
     for (int i = 0; i < NLV; ++i) prev[i] = *reinterpret_cast<const u4*>(vsrc + (size_t)min(tid + 256 * i, NVV - 1) * 8);
     if (MODE == MODE_BF16) preb = *reinterpret_cast<const f4*>(hbb + (size_t)chunk * CK + (tid % (CK / 4)) * 4);
@@ -957,9 +960,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
     for (int ci = c0; ci < c1; ++ci) {
       const int buf = (ci - c0) & 1;
       if (ci + 1 < c1) gload(ci + 1);
+#pragma unroll 1
+      for (int vb = 0; vb < TCB; ++vb) {
       f4 a0[R], a1[R];
-      score(buf, 0, a0);
-      score(buf, 1, a1);
+      score(buf, 2 * vb, a0);
+      score(buf, 2 * vb + 1, a1);
       // A operand of the P.V step: lane (query col, group grp) holds the
       // weights of keys 4grp..4grp+3 of tile 0 and of tile 1, in that order.
       u4 ehi[R], elo[R];
@@ -980,16 +985,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
       // B operand: lane (column col, group grp) reads the same keys of V.
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const u16* vr = &ldv[buf][(ct * 16 + col) * VROW];
+        const u16* vr = &ldv[buf][(vb * NC + ct * 16 + col) * VROW];
         const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * grp);
         const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * grp);
-        const u4 vb = u4{v0.x, v0.y, v1.x, v1.y};
+        const u4 vv = u4{v0.x, v0.y, v1.x, v1.y};
 #pragma unroll
         for (int c = 0; c < R; ++c) {
-          pv[c][ct] = T::mma(ehi[c], vb, pv[c][ct]);
-          pv[c][ct] = T::mma(elo[c], vb, pv[c][ct]);
+          pv[c][ct] = T::mma(ehi[c], vv, pv[c][ct]);
+          pv[c][ct] = T::mma(elo[c], vv, pv[c][ct]);
         }
       }
+      }  // value blocks of the chunk
       if (ci + 1 < c1) lstore(buf ^ 1);
       __syncthreads();
     }
@@ -1833,7 +1839,8 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   const int nch = L.KP / 32;
   const int R = bary_R(nch, val_tiles(L.mode, d));
   const int wg_x = (rows + 4 * R * 16 - 1) / (4 * R * 16);
-  const int total_chunks = (keys + VK - 1) / VK;
+  const int CKb = bary_TCB(nch, val_tiles(L.mode, d)) * VK;
+  const int total_chunks = (keys + CKb - 1) / CKb;
   int capacity = 0;
   st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity);
   if (st != SK_OK) return st;
@@ -1913,11 +1920,12 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
   float* bs = reinterpret_cast<float*>(w + L.bs);
   const float lam = (float)(LOG2E / (double)eps);
   const int nch = L.KP / 32;
-  const int total_chunks = (keys + VK - 1) / VK;
   for (int col0 = 0; col0 < c; col0 += APPLY_COLS) {
     const int cb = std::min(APPLY_COLS, c - col0);
     const int nct = apply_tiles(cb), nc = nct * 16;
     const int R = bary_R(nch, nct);
+    const int CKb = bary_TCB(nch, nct) * VK;
+    const int total_chunks = (keys + CKb - 1) / CKb;
     const int wg_x = (rows + 4 * R * 16 - 1) / (4 * R * 16);
     const long long nvec = (long long)(keys_pad / VK) * nc * (VK / 8);
     hipLaunchKernelGGL(k_prep_mat, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, M, keys, keys_pad,
