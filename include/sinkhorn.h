@@ -61,9 +61,13 @@ typedef enum { SK_FP32 = 0, SK_BF16 = 1 } sk_dtype; /* element type of X and Y *
 
 /* Largest supported point dimension: bf16 inputs up to SK_MAX_D, fp32 inputs up
  * to SK_MAX_D_FP32 (their operands carry seven remainder products per coordinate
- * that must stay in registers).  Larger d returns SK_EUNSUPPORTED. */
-#define SK_MAX_D 128
+ * that must stay in registers).  The transport, plan-product and HVP calls keep
+ * the query operand of their P.V pass in registers too: d <= SK_MAX_D_TRANSPORT
+ * (and <= SK_MAX_D_FP32 for fp32 inputs or the cosine cost).  Larger d returns
+ * SK_EUNSUPPORTED. */
+#define SK_MAX_D 1024
 #define SK_MAX_D_FP32 88
+#define SK_MAX_D_TRANSPORT 256
 
 /* Ground cost.  SK_COST_SQEUCLID: C_ij = ||x_i - y_j||^2 (the pages' cost).
  * SK_COST_COSINE: the cosine distance after normalisation (page "FlashSinkhorn:

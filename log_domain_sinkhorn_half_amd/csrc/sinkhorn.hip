@@ -445,16 +445,22 @@ __device__ __forceinline__ float offset_from_max(float mx, float Q) {
 // For 12..19 chunks two query tiles per wave and two key tiles per chunk halve
 // the LDS operand reads per score while two workgroups still fit a CU's LDS.
 __host__ __device__ constexpr bool cfg_wide_k(int mode, int nch) { return mode == MODE_SPLIT && nch >= 12 && nch <= 19; }
-__host__ __device__ constexpr int cfg_MW(int mode, int nch) { return (mode == MODE_BF16 || nch <= 2) ? 32 : 16; }
+// bf16 operands wider than 256 slots (d > 256) switch to 16x16 tiles with one
+// query tile per wave: the query operand alone then takes up to 128 VGPRs.
+__host__ __device__ constexpr int cfg_MW(int mode, int nch) {
+  return mode == MODE_BF16 ? (nch <= 8 ? 32 : 16) : (nch <= 2 ? 32 : 16);
+}
 __host__ __device__ constexpr int cfg_R(int mode, int nch) {
-  return cfg_MW(mode, nch) == 32 ? (nch == 1 ? 4 : 2)
+  return cfg_MW(mode, nch) == 32 ? (nch == 1 ? 4 : (nch <= 4 ? 2 : 1))
                                  : (nch <= 4 ? 4 : (nch <= 8 ? 2 : (cfg_wide_k(mode, nch) ? 2 : 1)));
 }
 __host__ __device__ constexpr int cfg_TC(int mode, int nch) {
   return (mode == MODE_SPLIT && nch == 1) ? 8
                                           : (cfg_MW(mode, nch) == 32 ? (nch <= 2 ? 2 : 1) : (cfg_wide_k(mode, nch) ? 2 : 1));
 }
-__host__ __device__ constexpr int cfg_waves(int mode, int nch) { return (mode == MODE_SPLIT && nch == 1) ? 3 : 2; }
+__host__ __device__ constexpr int cfg_waves(int mode, int nch) {
+  return (mode == MODE_SPLIT && nch == 1) ? 3 : ((mode == MODE_BF16 && nch > 20) ? 1 : 2);
+}
 
 // TCX overrides the key tiles per chunk (0: cfg_TC), for small problems.
 template <int MODE, int NCH, int TCX = 0>
@@ -1552,7 +1558,7 @@ Layout layout_of(const sk_problem* p) {
   // Transport: the value operand and the split partials of the P.V pass: room
   // for 16 splits of a one-tile pass or one split of the widest pass.
   const size_t d = (size_t)p->d;
-  L.ncols = std::max(val_tiles(L.mode, (int)p->d), apply_tiles(APPLY_COLS)) * 16;
+  L.ncols = std::max(p->d <= SK_MAX_D_TRANSPORT ? val_tiles(L.mode, (int)p->d) : 0, apply_tiles(APPLY_COLS)) * 16;
   L.bpv_bytes = std::max<size_t>(4 * 16 * 16 * B * mx, 4 * B * mx * (size_t)L.ncols);
   L.vt = take(2 * B * (size_t)L.max_pad * L.ncols);
   L.bpv = take(L.bpv_bytes);
@@ -1792,7 +1798,7 @@ BaryFn bary_lookup_impl(int d, std::integer_sequence<int, N...>) {
 
 BaryFn bary_lookup(int mode, int d) {
   if (mode == MODE_SPLIT) return bary_lookup_impl<MODE_SPLIT>(d, std::make_integer_sequence<int, SK_MAX_D_FP32>{});
-  return bary_lookup_impl<MODE_BF16>(d, std::make_integer_sequence<int, SK_MAX_D>{});
+  return bary_lookup_impl<MODE_BF16>(d, std::make_integer_sequence<int, SK_MAX_D_TRANSPORT>{});
 }
 
 // Barycentric projection (and gradient) of the rows of one side: side 0 the
@@ -1893,7 +1899,7 @@ BaryFn apply_lookup_impl(int d, int nct, std::integer_sequence<int, N...>) {
 BaryFn apply_lookup(int mode, int d, int nct) {
   if (mode == MODE_SPLIT)
     return apply_lookup_impl<MODE_SPLIT>(d, nct, std::make_integer_sequence<int, SK_MAX_D_FP32>{});
-  return apply_lookup_impl<MODE_BF16>(d, nct, std::make_integer_sequence<int, SK_MAX_D>{});
+  return apply_lookup_impl<MODE_BF16>(d, nct, std::make_integer_sequence<int, SK_MAX_D_TRANSPORT>{});
 }
 
 // out[b][row][k] = sum_j P_ij M[b][j][k] (k < c) for one side (side 0: rows are
@@ -2240,12 +2246,24 @@ size_t sinkhorn_transport_workspace_bytes(const sk_problem* p) {
   return layout_of(p).ttotal;
 }
 
+// Transport, plan products and HVPs keep the query operand of the P.V kernel in
+// registers: d <= SK_MAX_D_TRANSPORT.
+static sk_status check_transport_d(const sk_problem* p) {
+  if (p->d > SK_MAX_D_TRANSPORT) {
+    set_err("d = %lld exceeds SK_MAX_D_TRANSPORT = %d for transport, plan and HVP calls", (long long)p->d,
+            SK_MAX_D_TRANSPORT);
+    return SK_EUNSUPPORTED;
+  }
+  return SK_OK;
+}
+
 static sk_status transport_entry(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
                                  const float* f, const float* g, float eps, float* bary, float* grad, void* stream,
                                  int side) {
   g_err[0] = 0;
   Layout L;
   sk_status st = check_ws(p, ws, ws_bytes, &L, 1);
+  if (st == SK_OK) st = check_transport_d(p);
   if (st != SK_OK) return st;
   if (!X || !Y || !f || !g || !bary) {
     set_err("X, Y, f, g and bary must be non-NULL device pointers");
@@ -2274,6 +2292,7 @@ static sk_status apply_entry(const sk_problem* p, const void* X, const void* Y, 
   g_err[0] = 0;
   Layout L;
   sk_status st = check_ws(p, ws, ws_bytes, &L, 1);
+  if (st == SK_OK) st = check_transport_d(p);
   if (st != SK_OK) return st;
   if (!X || !Y || !f || !g || !M || !out) {
     set_err("X, Y, f, g, the matrix and out must be non-NULL device pointers");
@@ -2318,6 +2337,7 @@ static sk_status hvp_entry(const sk_problem* p, const void* X, const void* Y, vo
   g_err[0] = 0;
   Layout L;
   sk_status st = check_ws(p, ws, ws_bytes, &L, 2);
+  if (st == SK_OK) st = check_transport_d(p);
   if (st != SK_OK) return st;
   if (!X || !Y || !f || !g || !V || !out) {
     set_err("X, Y, f, g, V and out must be non-NULL device pointers");

@@ -76,7 +76,7 @@ def test_workspace_is_linear_not_quadratic(lib):
     (_prob(d=0), 2),
     (_prob(d=129), 5),
     (_prob(d=89), 5),
-    (_prob(d=129, dtype=1), 5),
+    (_prob(d=1025, dtype=1), 5),
     (_prob(dtype=7), 3),
 ])
 def test_invalid_problem_rejected_before_launch(lib, p, status):
@@ -134,6 +134,11 @@ def test_transport_workspace_and_argument_errors(lib):
         assert fn(bp, ptr, ptr, ptr, full, None, ptr, 0.1, ptr, ptr, None) == 1
         assert fn(bp, ptr, ptr, ptr, full, ptr, ptr, 0.0, ptr, ptr, None) == 1
         assert fn(ctypes.byref(_prob(d=89)), ptr, ptr, ptr, full, ptr, ptr, 0.1, ptr, ptr, None) == 5
+        wide = _prob(1, 300, 200, 300, 1)  # bf16 half-steps go to d = 1024, transport to 256
+        wb = lib.sinkhorn_transport_workspace_bytes(ctypes.byref(wide))
+        assert wb > 0
+        assert fn(ctypes.byref(wide), ptr, ptr, ptr, wb, ptr, ptr, 0.1, ptr, ptr, None) == 5
+        assert b"SK_MAX_D_TRANSPORT" in lib.sinkhorn_last_error()
 
 
 def test_cost_field_validation(lib):

@@ -95,6 +95,24 @@ def test_half_steps_bf16_ragged(n, m, d):
         half_steps(p, eps, seed=d)
 
 
+@pytest.mark.parametrize("n,m,d", [(200, 150, 200), (129, 260, 256), (100, 90, 300), (70, 130, 512),
+                                   (64, 65, 777), (50, 60, 1024)])
+def test_half_steps_bf16_wide(n, m, d):
+    """bf16 operands past 256 slots take 16x16 tiles with one query tile per wave."""
+    p = make_case(n, m, d, seed=3 * n + d, weights="softmax", dtype="bf16", scale=1.0 / np.sqrt(d))
+    for eps in (1.0, 0.05):
+        half_steps(p, eps, seed=d)
+
+
+def test_solve_bf16_wide_trajectory():
+    p = make_case(150, 170, 512, seed=12, weights="softmax", dtype="bf16", scale=1.0 / np.sqrt(512), iters=20)
+    X, Y, a, b = dev(p)
+    f, g = sk.solve(X, Y, a, b, 0.05, p.iters)
+    rf, rg = oracle.solve(p.X[0], p.Y[0], p.a[0], p.b[0], 0.05, p.iters)
+    check(f.cpu().numpy()[0], rf, tol(p, 0.05, rf), "bf16 d=512 f")
+    check(g.cpu().numpy()[0], rg, tol(p, 0.05, rg), "bf16 d=512 g")
+
+
 def test_half_steps_batched_small():
     p = make_case(70, 90, 6, batch=5, seed=3, weights="softmax")
     half_steps(p, 0.2, seed=3)
