@@ -85,7 +85,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
-              "the multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+              "sharding across GPUs is not built", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -191,7 +191,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32" if p.dtype == "fp32" else "bf16",
-        "data": "synthetic (seeded, see DESIGN.md input recipe)",
+        "data": "synthetic (seeded generator log_domain_sinkhorn_half_amd/inputs.py)",
         "config": {"workload": f"C{args.config}: {p.name} batch={B} n={n} m={m} d={d} {p.dtype} "
                                f"eps={eps_sched[0] if len(eps_sched) == 1 else 'schedule'}",
                    "batch": B, "n": n, "m": m, "d": d, "parallelism": "single GPU"},

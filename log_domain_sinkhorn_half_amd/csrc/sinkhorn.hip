@@ -39,6 +39,15 @@
 //  * Key ranges are split across workgroups when rows alone cannot fill the
 //    256 CUs; the partial (max, sum) pairs are merged by a small kernel.
 //  * Norms, log-weights, the bias and the final potential are formed in fp64.
+//
+// Beyond the half-step (same page, section "Differentiation and second-order
+// optimisation"; and the closing remarks on costs):
+//  * transport application: barycentric projection and gradient, and the plan
+//    applied to any matrix, as a P.V pass that reuses the score tiles with the
+//    row offsets fixed by a half-step (k_bary);
+//  * Hessian-vector products of the OT value, from plan products only
+//    (conjugate gradients on a Schur system, then an assembly);
+//  * the cosine cost, as the squared-Euclidean cost between normalised points.
 
 #include <hip/hip_runtime.h>
 
