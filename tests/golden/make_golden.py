@@ -6,8 +6,9 @@ indices (plus the first and last index) as JSON under tests/golden/.  The GPU
 parity tests compare the HIP path's potentials at those indices.
 
 Only `oracle` and the seeded input generator are used: no value here comes from
-the HIP path.  Runtime: workload 2 about a minute, workload 3 about an hour on
-8 cores.
+the HIP path.  Runtime: workload 2 about three minutes, workload 3 about an hour
+on 6 cores, workload 5 (all 64 problems) about a quarter of an hour.  For a
+batched workload the indices run over the problem-major flattened potentials.
 
     python tests/golden/make_golden.py 2 3 [--threads N]
 """
@@ -48,16 +49,22 @@ def sample(n: int, seed: int) -> np.ndarray:
 
 def run(cfg: int, threads: int) -> str:
     p = make_config(cfg)
-    assert p.batch == 1
     eps = p.eps.astype(np.float64)
     t0 = time.time()
-    f, g = oracle.solve(p.X[0], p.Y[0], p.a[0], p.b[0], eps if eps.size > 1 else float(eps[0]),
-                        p.iters, threads=threads)
+    if p.batch == 1:
+        f, g = oracle.solve(p.X[0], p.Y[0], p.a[0], p.b[0], eps if eps.size > 1 else float(eps[0]),
+                            p.iters, threads=threads)
+        fi, gi = sample(p.n, 100 + cfg), sample(p.m, 200 + cfg)
+    else:
+        # batched workload: every problem, a few indices each (flattened problem-major)
+        F, G = oracle.solve(p.X, p.Y, p.a, p.b, eps if eps.size > 1 else float(eps[0]), p.iters, threads=threads)
+        f, g = F.reshape(-1), G.reshape(-1)
+        fi, gi = sample(p.batch * p.n, 100 + cfg), sample(p.batch * p.m, 200 + cfg)
     dt = time.time() - t0
-    fi, gi = sample(p.n, 100 + cfg), sample(p.m, 200 + cfg)
     out = {
         "workload": cfg,
         "name": p.name,
+        "batch": p.batch,
         "iters": p.iters,
         "inputs_sha256_16": digest(p),
         "oracle_seconds": round(dt, 1),

@@ -152,3 +152,32 @@ def test_hvp_symmetric_and_linear_at_larger_size():
     assert abs(lhs - rhs) <= 5e-4 * scale
     lin = 2.0 * hU - 0.5 * hV
     assert np.max(np.abs(hW - lin)) <= 5e-4 * np.max(np.abs(lin))
+
+
+def test_hvp_batched_problems_are_independent():
+    p = make_case(80, 70, 3, batch=3, seed=41, weights="softmax")
+    eps = 0.3
+    f, g = potentials(p, eps, 2000)
+    V = np.random.default_rng(8).standard_normal((3, 80, 3)).astype(np.float32)
+    out = run_hvp(p, eps, f, g, V, "x")
+    for k in range(3):
+        X, Y, a, b = (np.asarray(v[k], np.float64) for v in (p.X, p.Y, p.a, p.b))
+        ref = oracle.hvp_x(X, Y, a, b, f[k], g[k], eps, V[k])
+        assert np.max(np.abs(out[k] - ref)) <= 5e-4 * np.max(np.abs(ref)), k
+
+
+def test_transport_and_hvp_are_deterministic():
+    p = make_case(500, 400, 3, seed=42, weights="softmax")
+    eps = 0.1
+    f, g = potentials(p, eps, 5)
+    V = np.random.default_rng(9).standard_normal((1, 500, 3)).astype(np.float32)
+    h1 = run_hvp(p, eps, f, g, V, "x", iters=30)
+    h2 = run_hvp(p, eps, f, g, V, "x", iters=30)
+    np.testing.assert_array_equal(h1, h2)
+    X, Y, a, b = dev(p)
+    ws = sk.alloc_workspace(X, Y, transport=True)
+    sk.init_norms(X, Y, a, b, ws)
+    ft, gt = torch.from_numpy(f).cuda(), torch.from_numpy(g).cuda()
+    b1, g1 = sk.barycentric_x(X, Y, ws, ft, gt, eps)
+    b2, g2 = sk.barycentric_x(X, Y, ws, ft, gt, eps)
+    assert torch.equal(b1, b2) and torch.equal(g1, g2)

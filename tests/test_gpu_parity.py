@@ -294,7 +294,7 @@ def test_large_dynamic_range_forces_offset_moves():
 # full-size trajectories at sampled indices (fixtures written by
 # tests/golden/make_golden.py from the oracle alone)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("cfg", [2, 3])
+@pytest.mark.parametrize("cfg", [2, 3, 5])
 def test_full_trajectory_against_golden_samples(cfg):
     import hashlib
     import json
@@ -315,5 +315,6 @@ def test_full_trajectory_against_golden_samples(cfg):
     rg = np.array(gold["g"])
     bf = 1e-3 * e + 1e-5 * gold["f_absmax"]
     bg = 1e-3 * e + 1e-5 * gold["g_absmax"]
-    check(f[0][gold["f_index"]], rf, bf, f"C{cfg} f trajectory")
-    check(g[0][gold["g_index"]], rg, bg, f"C{cfg} g trajectory")
+    # indices run over the problem-major flattened potentials (one problem: the rows)
+    check(f.reshape(-1)[gold["f_index"]], rf, bf, f"C{cfg} f trajectory")
+    check(g.reshape(-1)[gold["g_index"]], rg, bg, f"C{cfg} g trajectory")
