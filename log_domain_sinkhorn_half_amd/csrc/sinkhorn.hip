@@ -491,6 +491,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
   constexpr int NLD = (NVEC + 255) / 256;
   constexpr int QPW = R * MW;      // queries per wave
   static_assert(CK % 4 == 0 && CK / 4 <= 256, "one 4-key bias vector per thread");
+  // chunks must tile the padded key range: keys past it (slack rows) are not prepared
+  static_assert(ROW_PAD % CK == 0 && CK <= SLACK, "a key chunk must divide the row padding");
   // One spare row per buffer takes the stores of threads past the end of a chunk.
   __shared__ __attribute__((aligned(16))) u16 lds[2][(CK + 1) * LROW];
   __shared__ __attribute__((aligned(16))) float ldsb[2][CK];
@@ -849,6 +851,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
   constexpr int LROW = KP + 16;  // 32-byte pad: conflict-free 16-wide operand reads
   constexpr int TCB = bary_TCB(NCH, NCT);  // value blocks per chunk
   constexpr int CK = TCB * VK;
+  static_assert(ROW_PAD % CK == 0 && CK <= SLACK, "a key chunk must divide the row padding");
   constexpr int VPR = KP / 8;
   constexpr int NVEC = CK * VPR;
   constexpr int NLD = (NVEC + 255) / 256;
