@@ -91,6 +91,8 @@ constexpr float HEADROOM = 64.f;
 // Below this many keys the d <= 3 half-step uses SMALL_TC key tiles per chunk.
 constexpr int SMALL_KEYS = 16384;
 constexpr int SMALL_TC = 4;
+// Key-operand segments per thread of k_prep_keys when every segment is rebuilt.
+constexpr int PREP_SEGS = 4;
 
 // ---------------------------------------------------------------------------
 // K-slot layout of the fp32 path for point dimension d.
@@ -140,12 +142,13 @@ __device__ __forceinline__ u16 bf16_of(double v) { return bf16_rne((float)v); }
 
 constexpr u16 BF16_ONE = 0x3F80;
 
-// Smallest power of two q with |v| / q <= 255 (1 when v == 0).
-__device__ __forceinline__ double grid_quantum(double vmax) {
-  if (!(vmax > 0.0)) return 1.0;
+// Exponent k of the smallest power of two q = 2^k with |v| / q <= 255 (k = 0
+// when v == 0).  Callers form q and 1/q exactly with ldexp.
+__device__ __forceinline__ int grid_exponent(double vmax) {
+  if (!(vmax > 0.0)) return 0;
   int e;
   const double mant = frexp(vmax / 255.0, &e);  // vmax/255 = mant * 2^e, mant in [0.5, 1)
-  return ldexp(1.0, mant == 0.5 ? e - 1 : e);
+  return mant == 0.5 ? e - 1 : e;
 }
 
 // Grid part and two bf16 remainder parts of v: v ~ g + r1 + r2 with g a
@@ -240,8 +243,8 @@ __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, c
     }
     return;
   }
-  const double q = grid_quantum(maxabs[b]);
-  const double iq = 1.0 / q;
+  const int qe = grid_exponent(maxabs[b]);
+  const double q = ldexp(1.0, qe), iq = ldexp(1.0, -qe);
   double rn = 1.0;
   if (cosine) {
     double raw = 0.0;
@@ -281,91 +284,128 @@ __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, c
   }
 }
 
+// Bias lambda*(pot - norm + eps*logw) of key r in parts: bp[0..2] its multiple
+// of the grid quantum Q (exact in three bf16 parts), bp[3..4] the remainder.
+// Keys of zero weight and padding keys (real == false) take NEG_BIG alone.
+__device__ __forceinline__ void bias_parts(bool real, size_t r, const float* __restrict__ pot,
+                                           const double* __restrict__ norm, const double* __restrict__ logw,
+                                           float lam, float eps, double Q, double iQ, u16 (&bp)[5]) {
+  double bias = (double)NEG_BIG;
+  if (real) {
+    bias = (double)lam * ((double)pot[r] - norm[r] + (double)eps * logw[r]);
+    if (!(bias >= (double)NEG_BIG)) bias = (double)NEG_BIG;  // zero weight (-inf) or underflow
+  }
+  for (int e = 0; e < 5; ++e) bp[e] = 0;
+  if (bias <= (double)NEG_BIG) {
+    bp[0] = bf16_of(bias);
+  } else {
+    const double bg = rint(bias * iQ) * Q;
+    bp[0] = bf16_of(bg);
+    bp[1] = bf16_of(bg - (double)bf16_f(bp[0]));
+    bp[2] = bf16_of(bg - (double)bf16_f(bp[0]) - (double)bf16_f(bp[1]));
+    const double br = bias - bg;
+    bp[3] = bf16_of(br);
+    bp[4] = bf16_of(br - (double)bf16_f(bp[3]));
+  }
+}
+
 // Key operand rows for one half-step (fp32 inputs): v = 2*lambda*y and the bias
 // lambda*(pot - norm + eps*logw) in grid + remainder parts; writes the grid
-// quantum Q = q_query * q_key of each problem to qgrid.  One thread per 16-byte
-// segment of a row, so the stores are coalesced.
+// quantum Q = q_query * q_key of each problem to qgrid.  Work items are 16-byte
+// segments of a row, consecutive across the threads of a stride, so the stores
+// are coalesced.
+//
+// The coordinate parts depend only on the cloud and lambda.  *tag holds the bit
+// pattern of the lambda they were last built for (0: none).  When it equals
+// lam, only the five bias slots of each row are rewritten (one key per thread);
+// otherwise every segment is, and the tag is cleared.  Only the half-step kernel that follows on
+// the stream sets the tag, after every segment of this launch has been written;
+// a clear written during this launch cannot change any thread's decision, since
+// neither the old tag nor 0 equals lam.
 __global__ __launch_bounds__(256) void k_prep_keys(const void* __restrict__ P, int in_bf16,
                                                    const double* __restrict__ rnorm, const float* __restrict__ pot,
                                                    const double* __restrict__ norm, const double* __restrict__ logw,
                                                    int keys, int keys_pad, int d, int KP, float lam, float eps,
                                                    const float* __restrict__ qmax, const float* __restrict__ kmax,
-                                                   float* __restrict__ qgrid, u16* __restrict__ kb) {
+                                                   float* __restrict__ qgrid, unsigned* __restrict__ tag,
+                                                   u16* __restrict__ kb) {
   const int b = blockIdx.y;
   const int vpr = KP / 8;
-  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long long)keys_pad * vpr) return;
-  const int j = (int)(idx / vpr), k0 = (int)(idx % vpr) * 8;
-  const double lam2 = 2.0 * (double)lam;
-  const double qq = grid_quantum(qmax[b]);
-  const double qk = grid_quantum(lam2 * (double)kmax[b]);
-  const double Q = qq * qk;
-  const double iqk = 1.0 / qk, iQ = 1.0 / Q;
-  if (idx == 0) qgrid[b] = (float)Q;
   const int cb = split_corr_begin(d);
-  const bool real = j < keys;
-  const size_t r = (size_t)b * keys + j;
-  const double rn = real ? rnorm[r] : 1.0;
-  auto src = [&](int t) { return (double)coord(P, r * d + t, in_bf16) * rn; };
-  // bias parts (only for the segments that hold them)
-  u16 bp[5] = {0, 0, 0, 0, 0};
-  if ((k0 <= 4) || (k0 + 8 > cb + 7 * d && k0 <= cb + 7 * d + 1)) {
-    double bias = (double)NEG_BIG;
-    if (real) {
-      bias = (double)lam * ((double)pot[r] - norm[r] + (double)eps * logw[r]);
-      if (!(bias >= (double)NEG_BIG)) bias = (double)NEG_BIG;  // zero weight (-inf) or underflow
+  const int sb1 = (cb + 7 * d) / 8, sb2 = (cb + 7 * d + 1) / 8;  // segments of the remainder slots
+  const bool fresh = *tag == __float_as_uint(lam);
+  const long long gtid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  if (!fresh && gtid == 0 && b == 0) *tag = 0u;
+  const double lam2 = 2.0 * (double)lam;
+  const int qqe = grid_exponent(qmax[b]);
+  const int qke = grid_exponent(lam2 * (double)kmax[b]);
+  const double qk = ldexp(1.0, qke), iqk = ldexp(1.0, -qke);
+  const double Q = ldexp(1.0, qqe + qke), iQ = ldexp(1.0, -(qqe + qke));
+  if (gtid == 0) qgrid[b] = (float)Q;
+  if (fresh) {
+    for (long long j = gtid; j < keys_pad; j += stride) {
+      u16 bp[5];
+      bias_parts(j < keys, (size_t)b * keys + j, pot, norm, logw, lam, eps, Q, iQ, bp);
+      u16* row = kb + ((size_t)b * keys_pad + j) * KP;
+      row[2] = bp[0];
+      row[3] = bp[1];
+      row[4] = bp[2];
+      row[cb + 7 * d] = bp[3];
+      row[cb + 7 * d + 1] = bp[4];
     }
-    if (bias <= (double)NEG_BIG) {
-      bp[0] = bf16_of(bias);
-    } else {
-      const double bg = rint(bias * iQ) * Q;
-      bp[0] = bf16_of(bg);
-      bp[1] = bf16_of(bg - (double)bf16_f(bp[0]));
-      bp[2] = bf16_of(bg - (double)bf16_f(bp[0]) - (double)bf16_f(bp[1]));
-      const double br = bias - bg;
-      bp[3] = bf16_of(br);
-      bp[4] = bf16_of(br - (double)bf16_f(bp[3]));
-    }
+    return;
   }
-  int tc = -1;  // coordinate whose parts are cached
-  Parts pc{0, 0, 0};
-  u16 v[8];
+  const long long nwork = (long long)keys_pad * vpr;
+  for (long long wi = gtid; wi < nwork; wi += stride) {
+    const int j = (int)(wi / vpr), seg = (int)(wi % vpr);
+    const int k0 = seg * 8;
+    const bool real = j < keys;
+    const size_t r = (size_t)b * keys + j;
+    const double rn = real ? rnorm[r] : 1.0;
+    auto src = [&](int t) { return (double)coord(P, r * d + t, in_bf16) * rn; };
+    u16 bp[5] = {0, 0, 0, 0, 0};
+    if (seg == 0 || seg == sb1 || seg == sb2) bias_parts(real, r, pot, norm, logw, lam, eps, Q, iQ, bp);
+    int tc = -1;  // coordinate whose parts are cached
+    Parts pc{0, 0, 0};
+    u16 v[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int k = k0 + e;
-    u16 val = 0;
-    if (k <= 1) {
-      val = BF16_ONE;
-    } else if (k <= 4) {
-      val = bp[k - 2];
-    } else if (k < 5 + d) {
-      if (real) {
-        if (tc != k - 5) {
-          tc = k - 5;
-          pc = grid_split(lam2 * src(tc), qk, iqk);
+    for (int e = 0; e < 8; ++e) {
+      const int k = k0 + e;
+      u16 val = 0;
+      if (k <= 1) {
+        val = BF16_ONE;
+      } else if (k <= 4) {
+        val = bp[k - 2];
+      } else if (k < 5 + d) {
+        if (real) {
+          if (tc != k - 5) {
+            tc = k - 5;
+            pc = grid_split(lam2 * src(tc), qk, iqk);
+          }
+          val = pc.g;
         }
-        val = pc.g;
-      }
-    } else if (k >= cb && k < cb + 7 * d) {
-      if (real) {
-        const int t = (k - cb) / 7, sl = (k - cb) % 7;
-        if (tc != t) {
-          tc = t;
-          pc = grid_split(lam2 * src(t), qk, iqk);
+      } else if (k >= cb && k < cb + 7 * d) {
+        if (real) {
+          const int t = (k - cb) / 7, sl = (k - cb) % 7;
+          if (tc != t) {
+            tc = t;
+            pc = grid_split(lam2 * src(t), qk, iqk);
+          }
+          // key side of the corrections: v_1 v_2 v_g v_g v_1 v_2 v_1
+          val = (sl == 2 || sl == 3) ? pc.g : ((sl == 1 || sl == 5) ? pc.r2 : pc.r1);
         }
-        // key side of the corrections: v_1 v_2 v_g v_g v_1 v_2 v_1
-        val = (sl == 2 || sl == 3) ? pc.g : ((sl == 1 || sl == 5) ? pc.r2 : pc.r1);
+      } else if (k == cb + 7 * d) {
+        val = bp[3];
+      } else if (k == cb + 7 * d + 1) {
+        val = bp[4];
       }
-    } else if (k == cb + 7 * d) {
-      val = bp[3];
-    } else if (k == cb + 7 * d + 1) {
-      val = bp[4];
+      v[e] = val;
     }
-    v[e] = val;
+    *reinterpret_cast<u4*>(kb + ((size_t)b * keys_pad + j) * KP + k0) =
+        u4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
+           (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
   }
-  *reinterpret_cast<u4*>(kb + ((size_t)b * keys_pad + j) * KP + k0) =
-      u4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
-         (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
 }
 
 // Fill n floats with v.
@@ -477,7 +517,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
     const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb,
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, float* __restrict__ out,
     float2* __restrict__ part, int rows, int rows_pad, int keys, int keys_pad, int chunks_per_split, int batch,
-    float lam2, double inv_lam) {
+    float lam2, double inv_lam, unsigned* __restrict__ tag, unsigned tag_val) {
   constexpr int MW = cfg_MW(MODE, NCH), R = cfg_R(MODE, NCH), TC = TCX ? TCX : cfg_TC(MODE, NCH);
   using T = Tile<MW>;
   using Acc = typename T::Acc;
@@ -501,6 +541,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
   const int grp = lane / MW, col = lane % MW;
   const int b = blockIdx.z;
   const int qbase = blockIdx.x * (4 * QPW) + wave * QPW;
+  // The key operand's preparation (the previous launch on the stream) is
+  // complete: record the lambda its coordinate parts now hold.
+  if (tag != nullptr && tid == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) *tag = tag_val;
   const u16* Qb = Q + (size_t)b * rows_pad * KP;
   const u16* Kb = K + (size_t)b * keys_pad * KP;
   const float* hbb = (MODE == MODE_BF16) ? hb + (size_t)b * keys_pad : nullptr;
@@ -1481,7 +1524,9 @@ __global__ __launch_bounds__(256) void k_hvp_final(const void* __restrict__ P, i
 struct Layout {
   int mode, KP, n_pad, m_pad, max_pad;
   int in_bf16, cosine;
-  size_t xn, yn, la, lb, rx, ry, maxabs, qgrid, qx, qy, kb, hb, part, scratch, total;
+  size_t xn, yn, la, lb, rx, ry, maxabs, qgrid, ktag, qx, qy, kbx, kby, hb, part, scratch, total;
+  // key operand of the fp32 path for side 0 (Y as keys) or side 1 (X as keys)
+  size_t kb(int side) const { return side == 0 ? kby : kbx; }
   // transport application and plan products (after `total`; only their entry points need them)
   int ncols;             // widest value operand (columns) of any transport pass
   size_t bpv_bytes;      // bytes of the split-partials region
@@ -1558,11 +1603,13 @@ Layout layout_of(const sk_problem* p) {
   L.ry = take(8 * B * m);
   L.maxabs = take(align_up(4 * 2 * B, 16));
   L.qgrid = take(4 * B);
+  L.ktag = take(16);  // lambda tags of the two key operands
   // SLACK extra rows after each operand buffer absorb the kernels' unguarded
   // over-reads at the end of the last chunk.
   L.qx = take(2 * (B * L.n_pad + SLACK) * L.KP);
   L.qy = take(2 * (B * L.m_pad + SLACK) * L.KP);
-  L.kb = (L.mode == MODE_SPLIT) ? take(2 * (B * L.max_pad + SLACK) * L.KP) : 0;
+  L.kbx = (L.mode == MODE_SPLIT) ? take(2 * (B * L.n_pad + SLACK) * L.KP) : 0;
+  L.kby = (L.mode == MODE_SPLIT) ? take(2 * (B * L.m_pad + SLACK) * L.KP) : 0;
   L.hb = (L.mode == MODE_BF16) ? take(4 * (B * L.max_pad + SLACK)) : 0;
   L.part = take(8 * (size_t)KS_MAX * B * mx);
   L.scratch = take(4 * B * mx);
@@ -1604,7 +1651,7 @@ Layout layout_of(const sk_problem* p) {
 }
 
 using LseFn = void (*)(const u16*, const u16*, const float*, const float*, const double*, float*, float2*, int, int,
-                       int, int, int, int, float, double);
+                       int, int, int, int, float, double, unsigned*, unsigned);
 
 template <int MODE, int NCH>
 LseFn lse_fn() {
@@ -1711,7 +1758,8 @@ bool eps_ok(float eps) { return eps > 0.f && isfinite(eps) && isfinite((float)(L
 // Key operand of one side for the potential pot_in and eps: the split key rows
 // (fp32 path) or the half bias (bf16 path).  Returns the key operand and bias.
 sk_status prep_keys(const sk_problem* p, const void* X, const void* Y, char* w, const Layout& L, const float* pot_in,
-                    float eps, int side, hipStream_t stream, const u16** Kop, const float** hb) {
+                    float eps, int side, hipStream_t stream, const u16** Kop, const float** hb,
+                    unsigned** tag_out = nullptr) {
   const int B = (int)p->batch;
   const int keys = (int)(side == 0 ? p->m : p->n);
   const int keys_pad = side == 0 ? L.m_pad : L.n_pad;
@@ -1723,13 +1771,16 @@ sk_status prep_keys(const sk_problem* p, const void* X, const void* Y, char* w, 
   const float lam = (float)(LOG2E / (double)eps);
   *hb = nullptr;
   if (L.mode == MODE_SPLIT) {
-    u16* kb = reinterpret_cast<u16*>(w + L.kb);
-    const dim3 kgrid((unsigned)(((long long)keys_pad * (L.KP / 8) + 255) / 256), B);
+    u16* kb = reinterpret_cast<u16*>(w + L.kb(side));
+    unsigned* tag = reinterpret_cast<unsigned*>(w + L.ktag) + side;
+    // about PREP_SEGS segments per thread when every segment is rebuilt
+    const dim3 kgrid((unsigned)(((long long)keys_pad * (L.KP / 8) + 256 * PREP_SEGS - 1) / (256 * PREP_SEGS)), B);
     const double* krn = reinterpret_cast<const double*>(w + (side == 0 ? L.ry : L.rx));
     hipLaunchKernelGGL(k_prep_keys, kgrid, dim3(256), 0, stream, Kraw, L.in_bf16, krn, pot_in, knorm,
                        klogw, keys, keys_pad, (int)p->d, L.KP, lam, eps, maxabs + (side == 0 ? 0 : B),
-                       maxabs + (side == 0 ? B : 0), qgrid, kb);
+                       maxabs + (side == 0 ? B : 0), qgrid, tag, kb);
     *Kop = kb;
+    if (tag_out != nullptr) *tag_out = tag;
   } else {
     float* hbw = reinterpret_cast<float*>(w + L.hb);
     const dim3 pgrid((keys_pad + 255) / 256, B);
@@ -1758,7 +1809,8 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
 
   const u16* Kop = nullptr;
   const float* hb = nullptr;
-  sk_status st = prep_keys(p, X, Y, w, L, pot_in, eps, side, stream, &Kop, &hb);
+  unsigned* tag = nullptr;
+  sk_status st = prep_keys(p, X, Y, w, L, pot_in, eps, side, stream, &Kop, &hb, &tag);
   if (st != SK_OK) return st;
 
   LseFn fn = (L.mode == MODE_SPLIT) ? lse_lookup<MODE_SPLIT>(nch) : lse_lookup<MODE_BF16>(nch);
@@ -1783,7 +1835,7 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   float2* part = ks > 1 ? reinterpret_cast<float2*>(w + L.part) : nullptr;
   const double inv_lam = 1.0 / (double)lam;
   hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, qgrid, qnorm, pot_out, part, rows,
-                     rows_pad, keys, keys_pad, cps, B, 2.f * lam, inv_lam);
+                     rows_pad, keys, keys_pad, cps, B, 2.f * lam, inv_lam, tag, __builtin_bit_cast(unsigned, lam));
   st = hip_check("half-step kernel launch");
   if (st != SK_OK || ks == 1) return st;
   const int total = B * rows;
@@ -1865,7 +1917,7 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   int cps = 0;
   const int ks_cap = (int)std::min<size_t>(16, std::max<size_t>(1, L.bpv_bytes / (4 * (size_t)B * rows * nc)));
   const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps, ks_cap);
-  const u16* Kop = (L.mode == MODE_SPLIT) ? reinterpret_cast<const u16*>(w + L.kb)
+  const u16* Kop = (L.mode == MODE_SPLIT) ? reinterpret_cast<const u16*>(w + L.kb(side))
                                           : reinterpret_cast<const u16*>(w + (side == 0 ? L.qy : L.qx));
   const float* hb = (L.mode == MODE_BF16) ? reinterpret_cast<const float*>(w + L.hb) : nullptr;
   float* bpv = reinterpret_cast<float*>(w + L.bpv);
@@ -2124,6 +2176,8 @@ sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const flo
   };
   side(X, a, (int)p->n, L.n_pad, maxabs, L.xn, L.la, L.rx, L.qx);
   side(Y, b, (int)p->m, L.m_pad, maxabs + B, L.yn, L.lb, L.ry, L.qy);
+  // new clouds: the key operands hold no coordinate parts yet
+  if (L.mode == MODE_SPLIT) zero(L.ktag, 16);
   return hip_check("init kernel launch");
 }
 

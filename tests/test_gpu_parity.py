@@ -253,6 +253,44 @@ def test_annealed_schedule_matches_oracle():
     check(g[0].cpu().numpy(), rg, tol(p, float(sched[-1]), rg), "annealed g")
 
 
+@pytest.mark.parametrize("d", [3, 32])
+def test_key_operand_reuse_across_eps_and_clouds(d):
+    """The fp32 key operands keep their coordinate parts between half-steps at one
+    eps and rebuild them when eps changes, after a plan product at another eps, and
+    after init_norms with new clouds on the same workspace: every step here is
+    checked against the oracle."""
+    p = make_case(300, 200, d, seed=12 + d, weights="softmax", scale=1.0 / np.sqrt(d))
+    q = make_case(300, 200, d, seed=40 + d, weights="softmax", scale=1.0 / np.sqrt(d))
+    X, Y, a, b = dev(p)
+    ws = sk.alloc_workspace(X, Y, transport=True)
+    sk.init_norms(X, Y, a, b, ws)
+    g1 = random_potential((1, 200), 21, 0.3)
+    g2 = random_potential((1, 200), 22, 0.3)
+    f1 = random_potential((1, 300), 23, 0.3)
+
+    def step_f(Xc, Yc, pc, g, eps, what):
+        out = sk.half_step_f(Xc, Yc, ws, torch.from_numpy(g).cuda(), eps)
+        torch.cuda.synchronize()
+        ref = oracle.half_step_f(pc.X[0], pc.Y[0], pc.b[0], g[0], eps)
+        check(out[0].cpu().numpy(), ref, tol(pc, eps, ref), what)
+
+    step_f(X, Y, p, g1, 0.1, "first build")
+    step_f(X, Y, p, g2, 0.1, "same eps, new potential")
+    gg = sk.half_step_g(X, Y, ws, torch.from_numpy(f1).cuda(), 0.1)  # the other side's operand
+    torch.cuda.synchronize()
+    ref = oracle.half_step_g(p.X[0], p.Y[0], p.a[0], f1[0], 0.1)
+    check(gg[0].cpu().numpy(), ref, tol(p, 0.1, ref), "g side")
+    step_f(X, Y, p, g1, 0.1, "f side again")
+    step_f(X, Y, p, g1, 0.03, "new eps")
+    V = np.random.default_rng(3).standard_normal((1, 200)).astype(np.float32)
+    sk.apply_plan_x(X, Y, ws, torch.from_numpy(f1).cuda(), torch.from_numpy(g2).cuda(), 0.5,
+                    torch.from_numpy(V).cuda())
+    step_f(X, Y, p, g2, 0.03, "after a plan product at another eps")
+    Xq, Yq, aq, bq = dev(q)
+    sk.init_norms(Xq, Yq, aq, bq, ws)
+    step_f(Xq, Yq, q, g2, 0.03, "new clouds, same eps")
+
+
 def test_marginal_error_matches_oracle_plan():
     p = make_case(400, 300, 3, seed=9, weights="softmax")
     eps = 0.1
