@@ -284,6 +284,29 @@ __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, c
   }
 }
 
+// Grid and remainder parts of v = l2*y*rn (l2 = 2*lambda) for the key operand,
+// in fp32: v is carried as vh + vl, exactly when rn == 1 (the product of two
+// fp32 numbers and its fma error term), so the remainder takes one fp32
+// rounding, as in the fp64 split.  q = 2^k and iq = 1/q must be normal floats.
+__device__ __forceinline__ Parts key_split(float y, double rn, float l2, float q, float iq) {
+  float vh, vl;
+  if (rn == 1.0) {
+    vh = l2 * y;
+    vl = fmaf(l2, y, -vh);
+  } else {
+    const double v = (double)l2 * (double)y * rn;
+    vh = (float)v;
+    vl = (float)(v - (double)vh);
+  }
+  const float g = rintf(vh * iq) * q;
+  const float r = (vh - g) + vl;  // vh - g is exact: both are multiples of ulp(vh)
+  Parts p;
+  p.g = bf16_rne(g);
+  p.r1 = bf16_rne(r);
+  p.r2 = bf16_rne(r - bf16_f(p.r1));
+  return p;
+}
+
 // Bias lambda*(pot - norm + eps*logw) of key r in parts: bp[0..2] its multiple
 // of the grid quantum Q (exact in three bf16 parts), bp[3..4] the remainder.
 // Keys of zero weight and padding keys (real == false) take NEG_BIG alone.
@@ -343,6 +366,9 @@ __global__ __launch_bounds__(256) void k_prep_keys(const void* __restrict__ P, i
   const double qk = ldexp(1.0, qke), iqk = ldexp(1.0, -qke);
   const double Q = ldexp(1.0, qqe + qke), iQ = ldexp(1.0, -(qqe + qke));
   if (gtid == 0) qgrid[b] = (float)Q;
+  // fp32 coordinate splits unless the key quantum leaves the normal float range
+  const bool f32 = qke > -100 && qke < 100;
+  const float l2f = 2.f * lam, qkf = ldexpf(1.f, qke), iqkf = ldexpf(1.f, -qke);
   if (fresh) {
     for (long long j = gtid; j < keys_pad; j += stride) {
       u16 bp[5];
@@ -363,44 +389,49 @@ __global__ __launch_bounds__(256) void k_prep_keys(const void* __restrict__ P, i
     const bool real = j < keys;
     const size_t r = (size_t)b * keys + j;
     const double rn = real ? rnorm[r] : 1.0;
-    auto src = [&](int t) { return (double)coord(P, r * d + t, in_bf16) * rn; };
+    auto split = [&](int t) {
+      const float y = coord(P, r * d + t, in_bf16);
+      return f32 ? key_split(y, rn, l2f, qkf, iqkf) : grid_split(lam2 * (double)y * rn, qk, iqk);
+    };
     u16 bp[5] = {0, 0, 0, 0, 0};
     if (seg == 0 || seg == sb1 || seg == sb2) bias_parts(real, r, pot, norm, logw, lam, eps, Q, iQ, bp);
-    int tc = -1;  // coordinate whose parts are cached
-    Parts pc{0, 0, 0};
     u16 v[8];
+    if (k0 < cb) {
+      // grid section: offset slots (ones), bias grid parts, coordinate grid parts
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int k = k0 + e;
-      u16 val = 0;
-      if (k <= 1) {
-        val = BF16_ONE;
-      } else if (k <= 4) {
-        val = bp[k - 2];
-      } else if (k < 5 + d) {
-        if (real) {
-          if (tc != k - 5) {
-            tc = k - 5;
-            pc = grid_split(lam2 * src(tc), qk, iqk);
-          }
-          val = pc.g;
-        }
-      } else if (k >= cb && k < cb + 7 * d) {
-        if (real) {
-          const int t = (k - cb) / 7, sl = (k - cb) % 7;
-          if (tc != t) {
-            tc = t;
-            pc = grid_split(lam2 * src(t), qk, iqk);
-          }
-          // key side of the corrections: v_1 v_2 v_g v_g v_1 v_2 v_1
-          val = (sl == 2 || sl == 3) ? pc.g : ((sl == 1 || sl == 5) ? pc.r2 : pc.r1);
-        }
-      } else if (k == cb + 7 * d) {
-        val = bp[3];
-      } else if (k == cb + 7 * d + 1) {
-        val = bp[4];
+      for (int e = 0; e < 8; ++e) {
+        const int k = k0 + e;
+        u16 val = 0;
+        if (k <= 1)
+          val = BF16_ONE;
+        else if (k <= 4)
+          val = bp[k - 2];
+        else if (k < 5 + d && real)
+          val = split(k - 5).g;
+        v[e] = val;
       }
-      v[e] = val;
+    } else {
+      // corrections (key side v_1 v_2 v_g v_g v_1 v_2 v_1 per coordinate), then the
+      // bias remainder; a segment touches at most two coordinates
+      const int t0 = (k0 - cb) / 7;
+      const Parts zero{0, 0, 0};
+      const Parts p0 = (real && t0 < d) ? split(t0) : zero;
+      const Parts p1 = (real && t0 + 1 < d) ? split(t0 + 1) : zero;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int rel = k0 + e - cb;
+        u16 val = 0;
+        if (rel < 7 * d) {
+          const Parts& pc = rel / 7 == t0 ? p0 : p1;
+          const int sl = rel % 7;
+          val = (sl == 2 || sl == 3) ? pc.g : ((sl == 1 || sl == 5) ? pc.r2 : pc.r1);
+        } else if (rel == 7 * d) {
+          val = bp[3];
+        } else if (rel == 7 * d + 1) {
+          val = bp[4];
+        }
+        v[e] = val;
+      }
     }
     *reinterpret_cast<u4*>(kb + ((size_t)b * keys_pad + j) * KP + k0) =
         u4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
