@@ -27,7 +27,9 @@
  *    sinkhorn_workspace_bytes(p) bytes.  The library never allocates device or
  *    pinned memory and keeps no state between calls other than what it writes
  *    into ws.  sinkhorn_init_norms must have run on the same ws (same X, Y, a, b)
- *    before half-steps or the marginal error are called.
+ *    before half-steps or the marginal error are called, and must run again
+ *    after X, Y, a or b change: ws keeps operand rows derived from them (for fp32
+ *    inputs, per-eps key rows that later calls at the same eps reuse).
  *  - stream: a HIP stream; every call only enqueues work on it and returns
  *    without synchronising.  The caller synchronises before reading outputs.
  *    Concurrent calls that share one ws race.
