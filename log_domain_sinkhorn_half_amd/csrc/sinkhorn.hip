@@ -547,9 +547,9 @@ __host__ __device__ constexpr int cfg_waves(int mode, int nch) {
 // Chunks of key rows in flight ahead of the one being scored: 1 loads chunk
 // c+1 while scoring c; 2 also keeps chunk c+2 in flight (two register sets),
 // which hides a global-load latency longer than one chunk's scoring.  Measured:
-// 2 gains about 2% on the d <= 3 path with 256-key chunks and loses 5-10% on
-// the MFMA-heavy shapes.
-__host__ __device__ constexpr int cfg_PF(int mode, int nch) { return (mode == MODE_SPLIT && nch == 1) ? 2 : 1; }
+// 2 loses 5-10% on the MFMA-heavy shapes and 2% on the d <= 3 path once its
+// tile loop is unrolled, so every shape uses 1.
+__host__ __device__ constexpr int cfg_PF(int mode, int nch) { return 1; }
 
 // Compile-time parity of a chunk within a workgroup's range: selects the LDS
 // buffer and the register set of the prefetch.
@@ -731,11 +731,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
         if (MODE == MODE_SPLIT) set_offset(bq[c][0], -m[c], grp == 0);
       }
     }
+    if constexpr (NCH == 1) {
+      // short K: the unrolled tiles let the scheduler overlap one tile's MFMAs
+      // with the previous tile's exps (about 1% at d <= 3; larger K spills)
+#pragma unroll
+      for (int t = 0; t < TC; ++t) {
+        Acc acc[R];
+        tile(buf, t, acc);
+        accumulate(acc);
+      }
+    } else {
 #pragma unroll 1
-    for (int t = 0; t < TC; ++t) {
-      Acc acc[R];
-      tile(buf, t, acc);
-      accumulate(acc);
+      for (int t = 0; t < TC; ++t) {
+        Acc acc[R];
+        tile(buf, t, acc);
+        accumulate(acc);
+      }
     }
     int bad = 0;
 #pragma unroll
