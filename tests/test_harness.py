@@ -1,0 +1,27 @@
+"""Host-side checks of the rocprof harness: its counter passes stay within the
+per-block limits of one rocprofv3 run, and its operand sizes match the half-step
+kernels the traces name (k_lse<0, NCH, 0> for fp32 inputs: NCH 32-slot chunks)."""
+
+from log_domain_sinkhorn_half_amd import rocprof_harness as h
+
+
+def test_counter_passes_fit_one_run():
+    for p in (h.SQ_PASS, h.LDS_PASS):
+        assert sum(c.startswith("SQ_") for c in p) <= 8
+        assert sum(c.startswith("GRBM_") for c in p) <= 2
+        assert len(set(p)) == len(p)
+
+
+def test_operand_slots_match_kernel_instances():
+    # d = 3 -> k_lse<0, 1>, d = 32 -> k_lse<0, 10>, d = 64 -> k_lse<0, 18>, d = 88 (the fp32 limit) -> 23 chunks
+    assert h.operand_slots(3, False) == 32
+    assert h.operand_slots(32, False) == 320
+    assert h.operand_slots(64, False) == 576
+    assert h.operand_slots(88, False) == 23 * 32
+    assert h.operand_slots(128, True) == 128
+    assert h.operand_slots(300, True) == 320
+
+
+def test_algorithmic_bytes_of_the_headline_workload():
+    # 70000 queries and 70000 keys of 32 bf16 slots, plus 70000 fp32 potentials per launch
+    assert h.algorithmic_bytes(3) == 2 * 70000 * 32 * 2 + 70000 * 4
