@@ -397,15 +397,16 @@ __global__ __launch_bounds__(256) void k_prep_keys(const void* __restrict__ P, i
     if (seg == 0 || seg == sb1 || seg == sb2) bias_parts(real, r, pot, norm, logw, lam, eps, Q, iQ, bp);
     u16 v[8];
     if (k0 < cb) {
-      // grid section: offset slots (ones), bias grid parts, coordinate grid parts
+      // grid section: offset slots (ones), bias grid parts, coordinate grid parts;
+      // segment 0 holds slots 0..7, so its bias slots have fixed positions
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int k = k0 + e;
         u16 val = 0;
-        if (k <= 1)
+        if (seg == 0 && e <= 1)
           val = BF16_ONE;
-        else if (k <= 4)
-          val = bp[k - 2];
+        else if (seg == 0 && e <= 4)
+          val = bp[e - 2];
         else if (k < 5 + d && real)
           val = split(k - 5).g;
         v[e] = val;
@@ -422,9 +423,10 @@ __global__ __launch_bounds__(256) void k_prep_keys(const void* __restrict__ P, i
         const int rel = k0 + e - cb;
         u16 val = 0;
         if (rel < 7 * d) {
-          const Parts& pc = rel / 7 == t0 ? p0 : p1;
+          const bool first = rel / 7 == t0;  // selects values: a reference select would go to scratch
+          const u16 pg = first ? p0.g : p1.g, p1r = first ? p0.r1 : p1.r1, p2r = first ? p0.r2 : p1.r2;
           const int sl = rel % 7;
-          val = (sl == 2 || sl == 3) ? pc.g : ((sl == 1 || sl == 5) ? pc.r2 : pc.r1);
+          val = (sl == 2 || sl == 3) ? pg : ((sl == 1 || sl == 5) ? p2r : p1r);
         } else if (rel == 7 * d) {
           val = bp[3];
         } else if (rel == 7 * d + 1) {
