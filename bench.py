@@ -44,7 +44,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: n=m=70000, d=3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-transport", action="store_true", help="skip the transport-application leg")

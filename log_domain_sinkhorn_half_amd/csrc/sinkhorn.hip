@@ -91,8 +91,9 @@ constexpr float HEADROOM = 64.f;
 // Below this many keys the d <= 3 half-step uses SMALL_TC key tiles per chunk.
 constexpr int SMALL_KEYS = 16384;
 constexpr int SMALL_TC = 4;
-// Key-operand segments per thread of k_prep_keys when every segment is rebuilt.
-constexpr int PREP_SEGS = 4;
+// Key-operand segments per thread of k_prep_keys when every segment is rebuilt
+// (1: the most parallel; measured fastest for full rebuilds).
+constexpr int PREP_SEGS = 1;
 
 // ---------------------------------------------------------------------------
 // K-slot layout of the fp32 path for point dimension d.
@@ -357,6 +358,8 @@ __global__ __launch_bounds__(256) void k_prep_keys(const void* __restrict__ P, i
   const int cb = split_corr_begin(d);
   const int sb1 = (cb + 7 * d) / 8, sb2 = (cb + 7 * d + 1) / 8;  // segments of the remainder slots
   const bool fresh = *tag == __float_as_uint(lam);
+  // the grid is sized for a full rebuild; a bias-only pass needs one thread per key
+  if (fresh && (long long)blockIdx.x * blockDim.x >= keys_pad) return;
   const long long gtid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long stride = (long long)gridDim.x * blockDim.x;
   if (!fresh && gtid == 0 && b == 0) *tag = 0u;
