@@ -94,6 +94,7 @@ constexpr int SMALL_TC = 4;
 // Key-operand segments per thread of k_prep_keys when every segment is rebuilt
 // (1: the most parallel; measured fastest for full rebuilds).
 constexpr int PREP_SEGS = 1;
+constexpr int NXCD = 8;  // accelerator complex dies, each with its own L2
 
 // ---------------------------------------------------------------------------
 // K-slot layout of the fp32 path for point dimension d.
@@ -538,7 +539,7 @@ __host__ __device__ constexpr int cfg_MW(int mode, int nch) {
   return mode == MODE_BF16 ? (nch <= 8 ? 32 : 16) : ((nch <= 2 || (nch >= 9 && nch <= 11)) ? 32 : 16);
 }
 __host__ __device__ constexpr int cfg_R(int mode, int nch) {
-  return cfg_MW(mode, nch) == 32 ? (nch == 1 ? 4 : (nch <= 4 ? 2 : 1))
+  return cfg_MW(mode, nch) == 32 ? (nch == 1 ? (mode == MODE_SPLIT ? 3 : 4) : (nch <= 4 ? 2 : 1))
                                  : (nch <= 4 ? 4 : (nch <= 8 ? 2 : (cfg_wide_k(mode, nch) ? 2 : 1)));
 }
 __host__ __device__ constexpr int cfg_TC(int mode, int nch) {
@@ -562,6 +563,23 @@ template <int P>
 struct Par {
   static constexpr int value = P;
 };
+
+// Workgroups go to the accelerator's XCDs round-robin in dispatch order (x
+// fastest), and each XCD has its own L2.  For batched problems this remaps
+// dispatch slots so that every XCD runs one contiguous range of logical blocks:
+// the row blocks of one problem then share an L2 (measured +3% on 64 problems of
+// 2048 points; single problems lose 1-2%, so they keep the plain order).
+struct Blk {
+  int x, y, z;
+};
+__device__ __forceinline__ Blk xcd_block() {
+  const int gx = gridDim.x, gy = gridDim.y, n = gx * gy * gridDim.z;
+  if (gridDim.z == 1) return {(int)blockIdx.x, (int)blockIdx.y, 0};
+  const int p = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int q = n / NXCD, r = n % NXCD, xcd = p % NXCD, k = p / NXCD;
+  const int l = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + k;
+  return {l % gx, (l / gx) % gy, l / (gx * gy)};
+}
 
 // TCX overrides the key tiles per chunk (0: cfg_TC), for small problems.
 template <int MODE, int NCH, int TCX = 0>
@@ -592,8 +610,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane / MW, col = lane % MW;
-  const int b = blockIdx.z;
-  const int qbase = blockIdx.x * (4 * QPW) + wave * QPW;
+  const Blk blk = xcd_block();
+  const int b = blk.z;
+  const int qbase = blk.x * (4 * QPW) + wave * QPW;
   // The key operand's preparation (the previous launch on the stream) is
   // complete: record the lambda its coordinate parts now hold.
   if (tag != nullptr && tid == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) *tag = tag_val;
@@ -610,7 +629,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
       bq[c][i] = *reinterpret_cast<const u4*>(Qb + (size_t)(qbase + MW * c + col) * KP + i * T::KI + grp * 8);
 
   const int total_chunks = (keys + CK - 1) / CK;
-  const int c0 = blockIdx.y * chunks_per_split;
+  const int c0 = blk.y * chunks_per_split;
   const int c1 = min(total_chunks, c0 + chunks_per_split);
 
   float m[R], s[R];
@@ -815,7 +834,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
     if (grp == 0 && q < rows) {
       const size_t r = (size_t)b * rows + q;
       if (part != nullptr) {
-        part[(size_t)blockIdx.y * batch * rows + r] = make_float2(m[c], st);
+        part[(size_t)blk.y * batch * rows + r] = make_float2(m[c], st);
       } else {
         out[r] = (float)(qnorm[r] - ((double)m[c] + log2((double)st)) * inv_lam);
       }
