@@ -550,13 +550,6 @@ __host__ __device__ constexpr int cfg_waves(int mode, int nch) {
   return (mode == MODE_SPLIT && nch == 1) ? 3 : ((mode == MODE_BF16 && nch > 20) ? 1 : 2);
 }
 
-// Chunks of key rows in flight ahead of the one being scored: 1 loads chunk
-// c+1 while scoring c; 2 also keeps chunk c+2 in flight (two register sets),
-// which hides a global-load latency longer than one chunk's scoring.  Measured:
-// 2 loses 5-10% on the MFMA-heavy shapes and 2% on the d <= 3 path once its
-// tile loop is unrolled, so every shape uses 1.
-__host__ __device__ constexpr int cfg_PF(int mode, int nch) { return 1; }
-
 // Compile-time parity of a chunk within a workgroup's range: selects the LDS
 // buffer and the register set of the prefetch.
 template <int P>
@@ -600,7 +593,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
   constexpr int NVEC = CK * VPR;
   constexpr int NLD = (NVEC + 255) / 256;
   constexpr int QPW = R * MW;      // queries per wave
-  constexpr int PF = TCX ? 1 : cfg_PF(MODE, NCH);
   static_assert(CK % 4 == 0 && CK / 4 <= 256, "one 4-key bias vector per thread");
   // chunks must tile the padded key range: keys past it (slack rows) are not prepared
   static_assert(ROW_PAD % CK == 0 && CK <= SLACK, "a key chunk must divide the row padding");
@@ -719,18 +711,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
   };
 
   // One chunk: score the keys in LDS buffer P (chunk ci, P = parity of ci - c0),
-  // keep the next chunks in flight and move chunk ci+1 from registers into
+  // load chunk ci+1 and move it from registers into
   // buffer P^1.  Register set Q holds the chunk that buffer Q takes next.
   auto step = [&](int ci, auto par) {
     constexpr int P = decltype(par)::value;
     const int buf = P;
-    // Unconditional (clamped) loads keep the wait before each LDS store exact:
-    // it then waits for the older register set only.
-    if (PF == 2) {
-      gload(min(ci + 2, c1 - 1), Par<P>{});
-    } else {
-      gload(min(ci + 1, c1 - 1), Par<P ^ 1>{});
-    }
+    // Chunk ci+1 goes to register set P^1 (an unconditional, clamped load keeps
+    // the wait before its LDS store exact).  Keeping two chunks in flight was
+    // measured 5-10% slower on the MFMA-heavy shapes and 2% on d <= 3.
+    gload(min(ci + 1, c1 - 1), Par<P ^ 1>{});
 
     float ssave[R];
 #pragma unroll
@@ -819,7 +808,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
   if (c0 < c1) {
     gload(c0, Par<0>{});
     lstore(Par<0>{});
-    if (PF == 2) gload(min(c0 + 1, c1 - 1), Par<1>{});
     __syncthreads();
     for (int ci = c0; ci < c1; ci += 2) {
       step(ci, Par<0>{});
