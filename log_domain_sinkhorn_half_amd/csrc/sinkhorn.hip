@@ -95,6 +95,7 @@ constexpr int SMALL_TC = 4;
 // (1: the most parallel; measured fastest for full rebuilds).
 constexpr int PREP_SEGS = 1;
 constexpr int NXCD = 8;  // accelerator complex dies, each with its own L2
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
 // ---------------------------------------------------------------------------
 // K-slot layout of the fp32 path for point dimension d.
@@ -550,6 +551,14 @@ __host__ __device__ constexpr int cfg_waves(int mode, int nch) {
   return (mode == MODE_SPLIT && nch == 1) ? 3 : ((mode == MODE_BF16 && nch > 20) ? 1 : 2);
 }
 
+// Waves per workgroup.  Every wave scores its own query tiles against the key
+// chunk the workgroup stages in LDS, so more waves per workgroup divide the key
+// operand's global and LDS-store traffic per query.  Measured with 8 waves:
+// +10% at d = 64 (fp32), +2% at d = 128 (bf16), -8% for 64 problems at d = 32.
+__host__ __device__ constexpr int cfg_NW(int mode, int nch) {
+  return ((mode == MODE_SPLIT && nch >= 12 && nch <= 19) || (mode == MODE_BF16 && nch >= 3 && nch <= 8)) ? 8 : 4;
+}
+
 // Compile-time parity of a chunk within a workgroup's range: selects the LDS
 // buffer and the register set of the prefetch.
 template <int P>
@@ -576,7 +585,7 @@ __device__ __forceinline__ Blk xcd_block() {
 
 // TCX overrides the key tiles per chunk (0: cfg_TC), for small problems.
 template <int MODE, int NCH, int TCX = 0>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(MODE, NCH)))) void k_lse(
+__global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves_per_eu(cfg_waves(MODE, NCH)))) void k_lse(
     const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb,
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, float* __restrict__ out,
     float2* __restrict__ part, int rows, int rows_pad, int keys, int keys_pad, int chunks_per_split, int batch,
@@ -591,9 +600,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
   constexpr int CK = TC * MW;      // keys per chunk
   constexpr int VPR = KP / 8;      // 16-byte vectors per key row
   constexpr int NVEC = CK * VPR;
-  constexpr int NLD = (NVEC + 255) / 256;
+  constexpr int NW = cfg_NW(MODE, NCH), NT = 64 * NW;  // waves, threads per workgroup
+  constexpr int NLD = (NVEC + NT - 1) / NT;
   constexpr int QPW = R * MW;      // queries per wave
-  static_assert(CK % 4 == 0 && CK / 4 <= 256, "one 4-key bias vector per thread");
+  // the last workgroup's query rows may run past the padded rows into the slack rows
+  static_assert(NW * QPW - gcd_c(NW * QPW, ROW_PAD) <= SLACK, "query over-read beyond the slack rows");
+  static_assert(CK % 4 == 0 && CK / 4 <= NT, "one 4-key bias vector per thread");
   // chunks must tile the padded key range: keys past it (slack rows) are not prepared
   static_assert(ROW_PAD % CK == 0 && CK <= SLACK, "a key chunk must divide the row padding");
   // One spare row per buffer takes the stores of threads past the end of a chunk.
@@ -604,7 +616,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
   const int grp = lane / MW, col = lane % MW;
   const Blk blk = xcd_block();
   const int b = blk.z;
-  const int qbase = blk.x * (4 * QPW) + wave * QPW;
+  const int qbase = blk.x * (NW * QPW) + wave * QPW;
   // The key operand's preparation (the previous launch on the stream) is
   // complete: record the lambda its coordinate parts now hold.
   if (tag != nullptr && tid == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) *tag = tag_val;
@@ -639,14 +651,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(cfg_waves(M
     constexpr int P = decltype(par)::value;
     const u16* src = Kb + (size_t)chunk * CK * KP;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) pre[P][i] = *reinterpret_cast<const u4*>(src + (size_t)(tid + 256 * i) * 8);
+    for (int i = 0; i < NLD; ++i) pre[P][i] = *reinterpret_cast<const u4*>(src + (size_t)(tid + NT * i) * 8);
     if (MODE == MODE_BF16) preb[P] = *reinterpret_cast<const f4*>(hbb + (size_t)chunk * CK + (tid % (CK / 4)) * 4);
   };
   auto lstore = [&](auto par) {
     constexpr int P = decltype(par)::value;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int v = min(tid + 256 * i, NVEC);  // NVEC maps to the spare row
+      const int v = min(tid + NT * i, NVEC);  // NVEC maps to the spare row
       *reinterpret_cast<u4*>(&lds[P][(v / VPR) * LROW + (v % VPR) * 8]) = pre[P][i];
     }
     if (MODE == MODE_BF16 && tid < CK / 4) *reinterpret_cast<f4*>(&ldsb[P][tid * 4]) = preb[P];
@@ -1785,7 +1797,7 @@ sk_status check_ws(const sk_problem* p, void* ws, size_t ws_bytes, Layout* L, in
 }
 
 // Workgroups of `fn` that the current device holds at once (CUs x WGs per CU).
-sk_status resident_capacity(const void* fn, int* out) {
+sk_status resident_capacity(const void* fn, int* out, int block = 256) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, int> cache;
   int dev = 0;
@@ -1802,7 +1814,7 @@ sk_status resident_capacity(const void* fn, int* out) {
   }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) !=
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0) !=
           hipSuccess) {
     set_err("occupancy query failed");
     return SK_EHIP;
@@ -1910,17 +1922,18 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
     set_err("no kernel for %d K chunks", nch);
     return SK_EUNSUPPORTED;
   }
-  const int wg_x = (rows + 4 * cfR * cfMW - 1) / (4 * cfR * cfMW);
+  const int NW = cfg_NW(L.mode, nch);
+  const int wg_x = (rows + NW * cfR * cfMW - 1) / (NW * cfR * cfMW);
   const int CK = tc * cfMW;
   const int total_chunks = (keys + CK - 1) / CK;
   int capacity = 0;
-  st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity);
+  st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity, 64 * NW);
   if (st != SK_OK) return st;
   int cps = 0;
   const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps);
   float2* part = ks > 1 ? reinterpret_cast<float2*>(w + L.part) : nullptr;
   const double inv_lam = 1.0 / (double)lam;
-  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, qgrid, qnorm, pot_out, part, rows,
+  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NW), 0, stream, Qop, Kop, hb, qgrid, qnorm, pot_out, part, rows,
                      rows_pad, keys, keys_pad, cps, B, 2.f * lam, inv_lam, tag, __builtin_bit_cast(unsigned, lam));
   st = hip_check("half-step kernel launch");
   if (st != SK_OK || ks == 1) return st;
@@ -2262,6 +2275,10 @@ sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const flo
   };
   side(X, a, (int)p->n, L.n_pad, maxabs, L.xn, L.la, L.rx, L.qx);
   side(Y, b, (int)p->m, L.m_pad, maxabs + B, L.yn, L.lb, L.ry, L.qy);
+  // the slack rows after the last problem's operand rows: a workgroup whose
+  // query rows run past the padding reads zeros there
+  zero(L.qx + 2 * (size_t)B * L.n_pad * L.KP, 2 * (size_t)SLACK * L.KP);
+  zero(L.qy + 2 * (size_t)B * L.m_pad * L.KP, 2 * (size_t)SLACK * L.KP);
   // new clouds: the key operands hold no coordinate parts yet
   if (L.mode == MODE_SPLIT) zero(L.ktag, 16);
   return hip_check("init kernel launch");
