@@ -1,9 +1,11 @@
 """rocprofv3 harness for the streaming half-step kernel (k_lse) on one workload.
 
     python -m log_domain_sinkhorn_half_amd.rocprof_harness --config 3 --out gpurun_out/rp [--write-profiles]
+        [--kernel k_bary]
 
 Runs `bench.py` under rocprofv3 in separate passes and summarises, per launch of
-k_lse:
+k_lse (or of the kernel named by --kernel, e.g. the transport pass k_bary, whose
+counter passes then keep the benchmark's transport leg):
   * duration (kernel trace, the default benchmark command without its CPU leg);
   * MFMA utilisation (busy cycles of the matrix cores over all SIMDs) and the
     executed bf16 MFMA rate against the 2516.6 TFLOP/s dense peak;
@@ -115,6 +117,7 @@ def main() -> None:
     ap.add_argument("--steps", type=int, default=5, help="timed steps of the counter passes")
     ap.add_argument("--write-profiles", action="store_true")
     ap.add_argument("--summarize-only", action="store_true", help="reuse the outputs already under --out")
+    ap.add_argument("--kernel", default="k_lse", help="kernel name (prefix) to summarise")
     args = ap.parse_args()
     C = args.config
     out = os.path.abspath(args.out)
@@ -122,8 +125,10 @@ def main() -> None:
     os.environ.setdefault("TMPDIR", "/tmp")
     py = sys.executable
     bench = [py, "bench.py", "--config", str(C)]
-    short_bench = bench + ["--steps", str(args.steps), "--warmup", "2", "--no-cpu-baseline", "--no-transport",
-                           "--no-hvp"]
+    kname = args.kernel
+    short_bench = bench + ["--steps", str(args.steps), "--warmup", "2", "--no-cpu-baseline", "--no-hvp"]
+    if kname == "k_lse":
+        short_bench.append("--no-transport")
     cmds = {}
 
     # 1. kernel trace of the benchmark (steps, transport and HVP legs; no CPU leg)
@@ -154,9 +159,9 @@ def main() -> None:
 
     # --- kernel trace ---
     stats = list(csv.DictReader(open(glob.glob(f"{out}/trace/**/t_kernel_stats.csv", recursive=True)[0])))
-    lse = [r for r in stats if "k_lse" in r["Name"]]
+    lse = sorted((r for r in stats if short(r["Name"]).startswith(kname)), key=lambda r: -float(r["TotalDurationNs"]))
     if not lse:
-        raise SystemExit("[harness] no k_lse dispatch in the trace")
+        raise SystemExit(f"[harness] no {kname} dispatch in the trace")
     lname = short(lse[0]["Name"])
     dur_s = float(lse[0]["AverageNs"]) * 1e-9
     bench_line = None
@@ -166,14 +171,15 @@ def main() -> None:
     src_hash = kernel_source_hash()
 
     # --- counters ---
-    sq = counters(f"{out}/sq/**/s_counter_collection.csv", "k_lse")
+    kmatch = "::" + lname + "("  # the instantiation the trace ranks first
+    sq = counters(f"{out}/sq/**/s_counter_collection.csv", kmatch)
     grbm = sq.get("GRBM_GUI_ACTIVE", 0.0) / N_XCC  # summed over the XCDs
     mfma_util = 100.0 * sq.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (grbm * N_SIMD) if grbm else float("nan")
     mfma_flops = 512.0 * sq.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
     trans = 64.0 * sq.get("SQ_INSTS_VALU_TRANS_F32", 0.0)
     valu_per_cycle = sq.get("SQ_INSTS_VALU", 0.0) / (grbm * N_SIMD) if grbm else float("nan")
     valu_busy = 100.0 * sq.get("SQ_ACTIVE_INST_VALU", 0.0) / (N_CU * grbm) if grbm else float("nan")
-    ld = counters(f"{out}/lds/**/l_counter_collection.csv", "k_lse")
+    ld = counters(f"{out}/lds/**/l_counter_collection.csv", kmatch)
     grbm_l = ld.get("GRBM_GUI_ACTIVE", 0.0) / N_XCC
     lds_util = 100.0 * ld.get("SQ_LDS_IDX_ACTIVE", 0.0) / (N_CU * grbm_l) if grbm_l else float("nan")
     lds_conf = 100.0 * ld.get("SQ_LDS_BANK_CONFLICT", 0.0) / (N_CU * grbm_l) if grbm_l else float("nan")
@@ -185,7 +191,7 @@ def main() -> None:
         # the runtime's copy kernel reads and writes 256 MiB: the counter's KiB per KiB moved
         copy_kib = counters(f"{out}/copy_{ctr}/**/c_counter_collection.csv", "copyBuffer").get(ctr, 0.0)
         scale = (256 * 1024) / copy_kib if copy_kib else float("nan")
-        kib = counters(f"{out}/{ctr}/**/b_counter_collection.csv", "k_lse").get(ctr, 0.0)
+        kib = counters(f"{out}/{ctr}/**/b_counter_collection.csv", kmatch).get(ctr, 0.0)
         return kib, copy_kib, scale, kib * scale * 1024.0
 
     f_kib, f_copy, f_scale, f_bytes = scaled("FETCH_SIZE")
@@ -197,6 +203,8 @@ def main() -> None:
         return " ".join(c[c.index("rocprofv3"):]).replace(sys.executable, "python").replace(out, args.out)
 
     harness_cmd = f"python -m log_domain_sinkhorn_half_amd.rocprof_harness --config {C} --out {args.out}"
+    if kname != "k_lse":
+        harness_cmd += f" --kernel {kname}"
     desc = DESC.get(C, f"workload {C}")
 
     # kernel-trace summary
@@ -253,20 +261,22 @@ def main() -> None:
               f"| copy calibration: WRITE_SIZE of a 256 MiB copy | {w_copy:.1f} KiB (scale x{w_scale:.3f}) |",
               f"| {lname} FETCH_SIZE | {f_kib:.1f} KiB -> {f_bytes / 1e6:.2f} MB |",
               f"| {lname} WRITE_SIZE | {w_kib:.1f} KiB -> {w_bytes / 1e6:.2f} MB |",
-              f"| HBM rate over the launch | {hbm_bytes / dur_s / 1e9:.1f} GB/s of {PEAK_HBM / 1e9:.0f} |",
-              f"| algorithmic bytes (operands read once, potential written once) | "
-              f"{algorithmic_bytes(C) / 1e6:.2f} MB |",
-              f"| measured / algorithmic | {hbm_bytes / algorithmic_bytes(C):.2f} |", "",
-              "Traffic above the algorithmic bytes is the key operand re-read by the row blocks of a key split",
-              "(served mostly by the L2 and the MALL); at these rates HBM is far from its roof.", "",
+              f"| HBM rate over the launch | {hbm_bytes / dur_s / 1e9:.1f} GB/s of {PEAK_HBM / 1e9:.0f} |"]
+    if kname == "k_lse":
+        tr_md += [f"| algorithmic bytes (operands read once, potential written once) | "
+                  f"{algorithmic_bytes(C) / 1e6:.2f} MB |",
+                  f"| measured / algorithmic | {hbm_bytes / algorithmic_bytes(C):.2f} |", "",
+                  "Traffic above the algorithmic bytes is the key operand re-read by the row blocks of a key split",
+                  "(served mostly by the L2 and the MALL); at these rates HBM is far from its roof."]
+    tr_md += ["",
               f"- hbm_bytes_per_launch: {int(round(hbm_bytes))}", f"- kernel_source_sha256_16: {src_hash}", ""]
 
     files = {"kernel_trace": trace_md, "counters": cnt_md, "traffic": tr_md}
     for kind, lines in files.items():
         text = "\n".join(lines)
-        open(f"{out}/k_lse_C{C}_{kind}.md", "w").write(text)
+        open(f"{out}/{kname}_C{C}_{kind}.md", "w").write(text)
         if args.write_profiles:
-            open(os.path.join(ROOT, "profiles", f"k_lse_C{C}_{kind}.md"), "w").write(text)
+            open(os.path.join(ROOT, "profiles", f"{kname}_C{C}_{kind}.md"), "w").write(text)
     print("\n".join(cnt_md + tr_md[-8:]), flush=True)
 
 
