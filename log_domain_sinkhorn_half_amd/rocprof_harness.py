@@ -211,8 +211,11 @@ def main() -> None:
     trace_md = [f"# Kernel trace on workload C{C} ({desc})", "",
                 f"Made by `{harness_cmd}` (repository root); its trace pass is", "",
                 f"    {cmdline('trace')}", "",
-                "the benchmark's timed Sinkhorn steps, transport leg and HVP leg.  One half-step = k_prep_keys (fp32) or",
-                f"k_prep_bias (bf16) + {lname} + k_merge (when the keys are split).", "",
+                "the benchmark's timed Sinkhorn steps, transport leg and HVP leg.  " + (
+                    "One half-step = k_prep_keys (fp32) or" if kname == "k_lse" else
+                    f"The counters cover {lname}, the P.V pass of the"),
+                (f"k_prep_bias (bf16) + {lname} + k_merge (when the keys are split)." if kname == "k_lse" else
+                 "transport calls (each runs after a half-step of its own)."), "",
                 "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
     for r in stats:
         if short(r["Name"]).startswith("k_"):
