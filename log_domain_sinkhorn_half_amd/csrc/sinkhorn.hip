@@ -979,12 +979,13 @@ __device__ __forceinline__ uint2 split_pair(float a, float b) {
 // Writes the partial weighted sums pv_out[split][b][row][NCT*16] (columns
 // part*d + t, and the weight sums in the last column if SUMCOL) or, without
 // SUMCOL, the partial weight sums to s_out[split][b][row].
-template <int MODE, int NCH, int NCT, bool SUMCOL>
+template <int MODE, int NCH, int NCT, bool SUMCOL, bool LAZY = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(NCH)))) void k_bary(
     const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb, const u16* __restrict__ V,
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, const float* __restrict__ lse,
     float* __restrict__ pv_out, float* __restrict__ s_out, int rows, int rows_pad, int keys, int keys_pad,
-    int chunks_per_split, int batch, float lam, float lam2) {
+    int chunks_per_split, int batch, float lam, float lam2, float* __restrict__ m_out, unsigned* __restrict__ tag,
+    unsigned tag_val) {
   constexpr int MW = 16, R = bary_R(NCH, NCT);
   using T = Tile<16>;
   constexpr int KP = NCH * 32;
@@ -1029,8 +1030,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
   // normalisation cancels, so it is subtracted on the VALU only when it could
   // be large enough to overflow the sums.
   float sub[R];
+  // Lazy offsets (transport pass without a preceding half-step): mo is each
+  // query's running offset (base 2), -inf before its first key.  On the fp32
+  // path it also sits in the query operand; on the bf16 path it is sub.
+  float mo[R];
+  if (tag != nullptr && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) *tag = tag_val;
 #pragma unroll
   for (int c = 0; c < R; ++c) {
+    mo[c] = -INFINITY;
+    if (LAZY) {
+      sub[c] = 0.f;
+      if (MODE == MODE_SPLIT) set_offset(bq[c][0], 0.f, grp == 0);
+      continue;
+    }
     const int q = qbase + MW * c + col;
     double M = 0.0;
     if (q < rows) {
@@ -1103,7 +1115,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
   float sub_max = 0.f;
 #pragma unroll
   for (int c = 0; c < R; ++c) sub_max = fmaxf(sub_max, sub[c]);
-  const bool fine = (MODE == MODE_BF16) || __any(!(sub_max <= 32.f));
+  const bool fine = (MODE == MODE_BF16) || (!LAZY && __any(!(sub_max <= 32.f)));
 
   auto pass = [&](auto fine_c) {
     constexpr bool FINE = decltype(fine_c)::value;
@@ -1124,6 +1136,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
       f4 a0[R], a1[R];
       score(buf, 2 * vb, a0);
       score(buf, 2 * vb + 1, a1);
+      if (LAZY) {
+        // A lane whose scores exceed its query's offset by more than 2^32 (or
+        // meet its first keys) asks for a raise; the wave then takes each
+        // query's block maximum, sets its offset HEADROOM above it, rescales the
+        // sums and, on the fp32 path, scores the block again.
+        float mx[R];
+        bool want = false;
+#pragma unroll
+        for (int c = 0; c < R; ++c) {
+          float v = -INFINITY;
+#pragma unroll
+          for (int o = 0; o < 4; ++o) v = fmaxf(v, fmaxf(a0[c][o], a1[c][o]));
+          mx[c] = v;
+          // base 2, relative to mo (the fp32 path's scores already are)
+          const float rel = (MODE == MODE_BF16) ? fmaf(v, lam2, -mo[c]) : v;
+          want |= mo[c] == -INFINITY || !(rel <= 32.f);
+        }
+        if (__any(want)) {
+#pragma unroll
+          for (int c = 0; c < R; ++c) {
+            float v = fmaxf(mx[c], __shfl_xor(mx[c], 16));
+            v = fmaxf(v, __shfl_xor(v, 32));
+            const float top = (MODE == MODE_BF16) ? v * lam2 : (mo[c] == -INFINITY ? v : mo[c] + v);
+            float mn = mo[c];
+            if (mo[c] == -INFINITY || !(top - mo[c] <= 32.f)) mn = fmaxf(mo[c], offset_from_max(top + HEADROOM, qg));
+            if (!SUMCOL) s[c] = rescale(s[c], mo[c], mn);
+            // P.V rows are queries 4grp+r; their offsets live in lanes col = 4grp+r
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float o_old = __shfl(mo[c], 4 * grp + r), o_new = __shfl(mn, 4 * grp + r);
+#pragma unroll
+              for (int ct = 0; ct < NCT; ++ct) pv[c][ct][r] = rescale(pv[c][ct][r], o_old, o_new);
+            }
+            mo[c] = mn;
+            if (MODE == MODE_BF16) sub[c] = mn;
+            if (MODE == MODE_SPLIT) set_offset(bq[c][0], -mn, grp == 0);
+          }
+          if (MODE == MODE_SPLIT) {
+            score(buf, 2 * vb, a0);
+            score(buf, 2 * vb + 1, a1);
+          }
+        }
+      }
       // A operand of the P.V step: lane (query col, group grp) holds the
       // weights of keys 4grp..4grp+3 of tile 0 and of tile 1, in that order.
       u4 ehi[R], elo[R];
@@ -1174,6 +1229,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
     for (int w = MW; w < 64; w *= 2) st += __shfl_xor(st, w);
     const int q = qbase + MW * c + col;
     if (!SUMCOL && grp == 0 && q < rows) s_out[split_base + q] = st;
+    if (LAZY && grp == 0 && q < rows) m_out[split_base + q] = mo[c];
     // P.V output: lane (column col, group grp), element r = query 4grp + r
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1190,27 +1246,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
 // Barycentric projection and gradient from the split partials, one thread per
 // (problem, row, coordinate): bary = sum_parts sum_splits pv / sum_splits s,
 // grad = 2 r (p - bary) with the row mass r = w exp((pot - lse)/eps).
+// With lazy offsets (mpart != nullptr) each split's partials are relative to its
+// own offset mpart (base 2): they are brought to the largest one, and the row's
+// log-sum-exp follows from it and the weight sum, as in the half-step:
+// lse = ||p||^2 - (M + log2 S) / lambda, written to lse for later passes.
 __global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv, const float* __restrict__ sp, int ks,
                                                     int batch, int rows, int d, int ncols, int parts, int sumcol,
                                                     const void* __restrict__ P, int in_bf16,
-                                                    const float* __restrict__ pot, const float* __restrict__ lse,
+                                                    const float* __restrict__ pot, float* __restrict__ lse,
                                                     const double* __restrict__ logw, double eps,
-                                                    float* __restrict__ bary, float* __restrict__ grad) {
+                                                    const float* __restrict__ mpart, const double* __restrict__ qnorm,
+                                                    double inv_lam, float* __restrict__ bary,
+                                                    float* __restrict__ grad) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)batch * rows * d) return;
   const int t = (int)(idx % d);
   const long long rr = idx / d;  // b * rows + row
+  double M = 0.0;
+  if (mpart != nullptr) {
+    M = -INFINITY;
+    for (int k = 0; k < ks; ++k) M = fmax(M, (double)mpart[(size_t)k * batch * rows + (size_t)rr]);
+  }
   double S = 0.0, num = 0.0;
   for (int k = 0; k < ks; ++k) {
     const size_t base = (size_t)k * batch * rows + (size_t)rr;
-    S += sumcol ? (double)pv[base * ncols + ncols - 1] : (double)sp[base];
-    for (int part = 0; part < parts; ++part) num += (double)pv[base * ncols + part * d + t];
+    const double sc = mpart != nullptr ? exp2((double)mpart[base] - M) : 1.0;  // 0 for an empty split
+    S += sc * (sumcol ? (double)pv[base * ncols + ncols - 1] : (double)sp[base]);
+    for (int part = 0; part < parts; ++part) num += sc * (double)pv[base * ncols + part * d + t];
   }
   const double bc = num / S;
   bary[idx] = (float)bc;
+  double row_lse;
+  if (mpart != nullptr) {
+    row_lse = qnorm[rr] - (M + log2(S)) * inv_lam;
+    if (t == 0) lse[rr] = (float)row_lse;
+  } else {
+    row_lse = (double)lse[rr];
+  }
   if (grad != nullptr) {
     const double x = coord(P, (size_t)idx, in_bf16);
-    const double mass = exp(logw[rr] + ((double)pot[rr] - (double)lse[rr]) / eps);
+    const double mass = exp(logw[rr] + ((double)pot[rr] - row_lse) / eps);
     grad[idx] = (float)(2.0 * mass * (x - bc));
   }
 }
@@ -1628,7 +1703,7 @@ struct Layout {
   // transport application and plan products (after `total`; only their entry points need them)
   int ncols;             // widest value operand (columns) of any transport pass
   size_t bpv_bytes;      // bytes of the split-partials region
-  size_t vt, bpv, bs, ttotal;
+  size_t vt, bpv, bs, bm, ttotal;
   // Hessian-vector products (after `ttotal`)
   size_t h_lse_r, h_lse_k, h_mr, h_mk, h_py, h_mat, h_w, h_g, h_quad, h_tmp, h_zr, h_cr, h_rhs, h_dg, h_res,
       h_pd, h_pdf, h_t, h_q, h_st, h_part, htotal;
@@ -1720,6 +1795,7 @@ Layout layout_of(const sk_problem* p) {
   L.vt = take(2 * B * (size_t)L.max_pad * L.ncols);
   L.bpv = take(L.bpv_bytes);
   L.bs = take(4 * 16 * B * mx);
+  L.bm = take(4 * 16 * B * mx);  // per-split row offsets of the lazy transport pass
   L.ttotal = off;
   // Hessian-vector products: per-row vectors and small matrices, O((n+m) d)
   const size_t bm = B * mx;
@@ -1944,12 +2020,12 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
 }
 
 using BaryFn = void (*)(const u16*, const u16*, const float*, const u16*, const float*, const double*, const float*,
-                        float*, float*, int, int, int, int, int, int, float, float);
+                        float*, float*, int, int, int, int, int, int, float, float, float*, unsigned*, unsigned);
 
 template <int MODE, int D>
 BaryFn bary_fn_d() {
   constexpr int NCH = MODE == MODE_SPLIT ? split_nch(D) : (D + 31) / 32;
-  return &k_bary<MODE, NCH, val_tiles(MODE, D), val_sumcol(MODE, D)>;
+  return &k_bary<MODE, NCH, val_tiles(MODE, D), val_sumcol(MODE, D), true>;
 }
 
 template <int MODE, int... N>
@@ -1983,9 +2059,13 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   const float* pot_row = side == 0 ? f : g;
   float* lse = reinterpret_cast<float*>(w + L.scratch);
 
-  // 1. The row log-sum-exp (the half-step's output); this also prepares the
-  //    key operand of this side for the current potential and eps.
-  sk_status st = half_step(p, X, Y, ws, L, side == 0 ? g : f, eps, lse, side, stream);
+  // 1. The key operand of this side for the other potential and eps.  The P.V
+  //    pass keeps lazy row offsets, so no half-step runs first: its merge
+  //    recovers each row's log-sum-exp (into scratch) from the offsets and sums.
+  const u16* Kop = nullptr;
+  const float* hb = nullptr;
+  unsigned* tag = nullptr;
+  sk_status st = prep_keys(p, X, Y, w, L, side == 0 ? g : f, eps, side, stream, &Kop, &hb, &tag);
   if (st != SK_OK) return st;
 
   // 2. Value operand from the other cloud's coordinates.
@@ -2016,22 +2096,20 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   int cps = 0;
   const int ks_cap = (int)std::min<size_t>(16, std::max<size_t>(1, L.bpv_bytes / (4 * (size_t)B * rows * nc)));
   const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps, ks_cap);
-  const u16* Kop = (L.mode == MODE_SPLIT) ? reinterpret_cast<const u16*>(w + L.kb(side))
-                                          : reinterpret_cast<const u16*>(w + (side == 0 ? L.qy : L.qx));
-  const float* hb = (L.mode == MODE_BF16) ? reinterpret_cast<const float*>(w + L.hb) : nullptr;
   float* bpv = reinterpret_cast<float*>(w + L.bpv);
   float* bs = reinterpret_cast<float*>(w + L.bs);
+  float* bm = reinterpret_cast<float*>(w + L.bm);
   const float lam = (float)(LOG2E / (double)eps);
-  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, lse, bpv, bs, rows,
-                     rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam);
+  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, nullptr, bpv, bs, rows,
+                     rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, bm, tag, __builtin_bit_cast(unsigned, lam));
   st = hip_check("transport kernel launch");
   if (st != SK_OK) return st;
 
   // 4. Merge the splits, divide, form the gradient.
   const long long total = (long long)B * rows * d;
   hipLaunchKernelGGL(k_bary_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, bs, ks, B, rows,
-                     d, nc, val_parts(L.mode), sumcol, Praw, L.in_bf16, pot_row, lse, qlogw, (double)eps, bary,
-                     L.cosine ? nullptr : grad);
+                     d, nc, val_parts(L.mode), sumcol, Praw, L.in_bf16, pot_row, lse, qlogw, (double)eps, bm, qnorm,
+                     1.0 / (double)lam, bary, L.cosine ? nullptr : grad);
   st = hip_check("transport merge launch");
   if (st != SK_OK || !L.cosine || grad == nullptr) return st;
   const double* qrn = reinterpret_cast<const double*>(w + (side == 0 ? L.rx : L.ry));
@@ -2082,7 +2160,8 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
   const u16* Qop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qx : L.qy));
   const u16* Kop = nullptr;
   const float* hb = nullptr;
-  sk_status st = prep_keys(p, X, Y, w, L, pot_key, eps, side, stream, &Kop, &hb);
+  unsigned* ptag = nullptr;
+  sk_status st = prep_keys(p, X, Y, w, L, pot_key, eps, side, stream, &Kop, &hb, &ptag);
   if (st != SK_OK) return st;
   u16* vt = reinterpret_cast<u16*>(w + L.vt);
   float* bpv = reinterpret_cast<float*>(w + L.bpv);
@@ -2113,7 +2192,8 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
     int cps = 0;
     const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps, ks_cap);
     hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, lse, bpv, bs,
-                       rows, rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam);
+                       rows, rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, nullptr, ptag,
+                       __builtin_bit_cast(unsigned, lam));
     st = hip_check("plan-application kernel launch");
     if (st != SK_OK) return st;
     const long long total = (long long)B * rows * cb;

@@ -170,3 +170,30 @@ def test_transport_full_size_sampled(cfg):
     compare(p, k, "x", eps, bx, gx, f_x, g, rows=rx)
     _, _, by, gy = run_gpu(p, f, g_y, eps)
     compare(p, k, "y", eps, by, gy, f, g_y, rows=ry)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_transport_large_dynamic_range(dtype):
+    """Scores spanning thousands of base-2 units: the transport pass's lazy row
+    offsets must rise many times (and differ between key splits) without loss.
+    Each side's own potential is the oracle's exact update, so row masses are the
+    weights (a random one would put exp((f - lse)/eps) out of range)."""
+    p = make_case(333, 2000, 2, seed=11, weights="softmax", dist="cube", scale=8.0, dtype=dtype)
+    eps = 0.01
+    X, Y, a, b = (np.asarray(v[0], np.float64) for v in (p.X, p.Y, p.a, p.b))
+    g0 = random_potential((1, p.m), 62, 5.0).astype(np.float64)
+    f = oracle.half_step_f(X, Y, b, g0[0], eps).astype(np.float32).astype(np.float64)[None, :]
+    g1 = oracle.half_step_g(X, Y, a, f[0], eps).astype(np.float32).astype(np.float64)[None, :]
+    bx, gx, _, _ = run_gpu(p, f, g0, eps)
+    compare(p, 0, "x", eps, bx, gx, f, g0)
+    _, _, by, gy = run_gpu(p, f, g1, eps)
+    compare(p, 0, "y", eps, by, gy, f, g1)
+    # keys sorted far to near from the first query: its offset rises block after block
+    order = np.argsort(-((p.Y[0] - p.X[0][0]) ** 2).sum(1))
+    q = make_case(333, 2000, 2, seed=11, weights="softmax", dist="cube", scale=8.0, dtype=dtype)
+    q.Y[0] = p.Y[0][order]
+    q.b[0] = p.b[0][order]
+    if dtype == "bf16":
+        q.Y_bits[0] = p.Y_bits[0][order]
+    bx, gx, _, _ = run_gpu(q, f, g0[:, order], eps)
+    compare(q, 0, "x", eps, bx, gx, f, g0[:, order])
