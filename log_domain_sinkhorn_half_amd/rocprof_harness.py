@@ -133,7 +133,8 @@ def main() -> None:
 
     # 1. kernel trace of the benchmark (steps, transport and HVP legs; no CPU leg)
     cmds["trace"] = ["timeout", "-k", "10", "600", "rocprofv3", "--kernel-trace", "--stats", "-f", "csv", "-d",
-                     f"{out}/trace", "-o", "t", "--"] + bench + ["--no-cpu-baseline"]
+                     f"{out}/trace", "-o", "t", "--"] + bench + ["--no-cpu-baseline"] + (
+                         [] if args.kernel == "k_lse" else ["--no-hvp"])  # the counter passes' instantiation leads
     if not args.summarize_only:
         run(cmds["trace"], f"{out}/trace.log", "kernel trace")
     # 2. SQ / GRBM counters
@@ -211,7 +212,8 @@ def main() -> None:
     trace_md = [f"# Kernel trace on workload C{C} ({desc})", "",
                 f"Made by `{harness_cmd}` (repository root); its trace pass is", "",
                 f"    {cmdline('trace')}", "",
-                "the benchmark's timed Sinkhorn steps, transport leg and HVP leg.  " + (
+                ("the benchmark's timed Sinkhorn steps, transport leg and HVP leg.  " if kname == "k_lse" else
+                 "the benchmark's timed Sinkhorn steps and transport leg.  ") + (
                     "One half-step = k_prep_keys (fp32) or" if kname == "k_lse" else
                     f"The counters cover {lname}, the P.V pass of the"),
                 (f"k_prep_bias (bf16) + {lname} + k_merge (when the keys are split)." if kname == "k_lse" else
