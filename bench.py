@@ -251,8 +251,9 @@ def transport_leg(sk, X, Y, a, b, f, g, eps, p, contraction, reps=10):
 def hvp_leg(sk, X, Y, a, b, f, g, eps, p, cg_iters, reps=3):
     """Time one Hessian-vector product in X (fixed CG iteration count, no early stop).
     Every plan pass evaluates each of the B*n*m scores once: 2 half-steps, the plan
-    applied to Y, P^T [z, v, cr/r], 2 passes per CG iteration, P [dg, dg y] and
-    ceil(d(d+1)/2 / 64) passes for the quadratic term."""
+    applied to Y, P^T [z, v, cr/r], 2 passes per CG iteration, P [dg, dg y] (each
+    plan product takes ceil(columns / 64) passes) and one row-weighted pass for the
+    quadratic term sum_j P_ij (y_j . v_i) y_j."""
     import math
 
     import numpy as np
@@ -273,7 +274,8 @@ def hvp_leg(sk, X, Y, a, b, f, g, eps, p, cg_iters, reps=3):
     torch.cuda.synchronize()
     ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
     assert torch.isfinite(out).all(), "non-finite HVP"
-    passes = 2 + 1 + 1 + 2 * cg_iters + 1 + math.ceil(p.d * (p.d + 1) / 2 / 64)
+    d = p.d
+    passes = 2 + math.ceil(d / 64) + math.ceil((d + 2) / 64) + 2 * cg_iters + math.ceil((d + 1) / 64) + 1
     exps = passes * p.batch * p.n * p.m
     achieved = exps / (ms / 1e3)
     return {"what": f"one Hessian-vector product in X, {cg_iters} CG iterations ({passes} plan passes)",

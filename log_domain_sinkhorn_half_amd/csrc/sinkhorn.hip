@@ -979,13 +979,17 @@ __device__ __forceinline__ uint2 split_pair(float a, float b) {
 // Writes the partial weighted sums pv_out[split][b][row][NCT*16] (columns
 // part*d + t, and the weight sums in the last column if SUMCOL) or, without
 // SUMCOL, the partial weight sums to s_out[split][b][row].
-template <int MODE, int NCH, int NCT, bool SUMCOL, bool LAZY = false>
+// NU > 0: row-weighted values.  U holds NU query-layout planes of a per-row
+// vector v_i (fp32 path: one split operand; bf16 path: hi and lo bf16 parts);
+// the weights become P_ij * u_ij with u_ij = ugain * (key operand . U_i), i.e.
+// u_ij = q_j . v_i, while s_out still sums the plain weights.
+template <int MODE, int NCH, int NCT, bool SUMCOL, bool LAZY = false, int NU = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(NCH)))) void k_bary(
     const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb, const u16* __restrict__ V,
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, const float* __restrict__ lse,
     float* __restrict__ pv_out, float* __restrict__ s_out, int rows, int rows_pad, int keys, int keys_pad,
     int chunks_per_split, int batch, float lam, float lam2, float* __restrict__ m_out, unsigned* __restrict__ tag,
-    unsigned tag_val) {
+    unsigned tag_val, const u16* __restrict__ U, float ugain) {
   constexpr int MW = 16, R = bary_R(NCH, NCT);
   using T = Tile<16>;
   constexpr int KP = NCH * 32;
@@ -1022,6 +1026,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       bq[c][i] = *reinterpret_cast<const u4*>(Qb + (size_t)(qbase + MW * c + col) * KP + i * T::KI + grp * 8);
+  constexpr int NUP = NU > 0 ? NU : 1;
+  u4 bu[NUP][R][NI];
+  if (NU > 0) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int c = 0; c < R; ++c)
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+          bu[u][c][i] = *reinterpret_cast<const u4*>(U + ((size_t)u * (batch * (size_t)rows_pad + SLACK) +
+                                                          (size_t)b * rows_pad + qbase + MW * c + col) * KP +
+                                                     i * T::KI + grp * 8);
+  }
 
   // Fixed row offsets.  M = lam (||p||^2 - lse) is log2 of the row's sum of
   // 2^score, so every weight 2^(score - M) is at most about 1.  The fp32 path
@@ -1100,17 +1117,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
     if (MODE == MODE_BF16 && tid < CK / 4) *reinterpret_cast<f4*>(&ldsb[buf][tid * 4]) = preb;
   };
   // Scores of the 16-key tile t of the chunk against the R query tiles.
-  auto score = [&](int buf, int t, f4 (&acc)[R]) {
+  // Scores of the 16-key tile t against the R query tiles; with NU > 0 also
+  // the contraction of the same key rows with the U planes (into accu).
+  auto score2 = [&](int buf, int t, f4 (&acc)[R], f4 (&accu)[R]) {
     f4 cinit = {0.f, 0.f, 0.f, 0.f};
     if (MODE == MODE_BF16) cinit = *reinterpret_cast<const f4*>(&ldsb[buf][t * MW + 4 * grp]);
 #pragma unroll
-    for (int c = 0; c < R; ++c) acc[c] = cinit;
+    for (int c = 0; c < R; ++c) {
+      acc[c] = cinit;
+      accu[c] = f4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const u4 ka = *reinterpret_cast<const u4*>(&lds[buf][(t * MW + col) * LROW + i * T::KI + grp * 8]);
 #pragma unroll
-      for (int c = 0; c < R; ++c) acc[c] = T::mma(ka, bq[c][i], acc[c]);
+      for (int c = 0; c < R; ++c) {
+        acc[c] = T::mma(ka, bq[c][i], acc[c]);
+        if (NU > 0) {
+#pragma unroll
+          for (int u = 0; u < NU; ++u) accu[c] = T::mma(ka, bu[u][c][i], accu[c]);
+        }
+      }
     }
+  };
+  auto score = [&](int buf, int t, f4 (&acc)[R]) {
+    f4 unused[R];
+    score2(buf, t, acc, unused);
   };
   float sub_max = 0.f;
 #pragma unroll
@@ -1133,9 +1165,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
       if (ci + 1 < c1) gload(ci + 1);
 #pragma unroll 1
       for (int vb = 0; vb < TCB; ++vb) {
-      f4 a0[R], a1[R];
-      score(buf, 2 * vb, a0);
-      score(buf, 2 * vb + 1, a1);
+      f4 a0[R], a1[R], u0[R], u1[R];
+      score2(buf, 2 * vb, a0, u0);
+      score2(buf, 2 * vb + 1, a1, u1);
       if (LAZY) {
         // A lane whose scores exceed its query's offset by more than 2^32 (or
         // meet its first keys) asks for a raise; the wave then takes each
@@ -1191,6 +1223,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
           e[4 + o] = weight(a1[c][o], c);
         }
         if (!SUMCOL) s[c] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        if (NU > 0) {
+#pragma unroll
+          for (int o = 0; o < 4; ++o) {
+            e[o] *= u0[c][o] * ugain;
+            e[4 + o] *= u1[c][o] * ugain;
+          }
+        }
         const uint2 p0 = split_pair(e[0], e[1]), p1 = split_pair(e[2], e[3]);
         const uint2 p2 = split_pair(e[4], e[5]), p3 = split_pair(e[6], e[7]);
         ehi[c] = u4{p0.x, p1.x, p2.x, p3.x};
@@ -1610,49 +1649,77 @@ __global__ __launch_bounds__(256) void k_hvp_gmat(const void* __restrict__ Q, in
   for (int t = 0; t < d; ++t) row[1 + t] = (float)(dg[j] * (double)coord(Q, (size_t)j * d + t, in_bf16));
 }
 
-// Pairs (t, u), t <= u, of coordinates in the order (0,0) (0,1) .. (0,d-1) (1,1) ..;
-// pair k's coordinates.
-__device__ __forceinline__ void pair_of(int k, int d, int& t, int& u) {
-  t = 0;
-  while (k >= d - t) {
-    k -= d - t;
-    ++t;
+// Query-layout planes of a per-row fp32 vector v (the direction of a
+// Hessian-vector product) for the row-weighted plan pass.  fp32 path: the
+// points' split layout of v (grid part on a per-row quantum, two bf16
+// remainders, in the same slots) with zeros in the offset and bias slots, so
+// the key operand's product with it is 2 lambda (q_j . v).  bf16 path: v's hi
+// and lo bf16 parts in two planes, zero-padded to KP.  One thread per row.
+__global__ __launch_bounds__(256) void k_prep_u(const float* __restrict__ V, int rows, int rows_pad, int d, int KP,
+                                                int mode, int batch, u16* __restrict__ U) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows_pad) return;
+  const size_t plane = ((size_t)batch * rows_pad + SLACK) * KP;
+  u16* dst = U + ((size_t)b * rows_pad + i) * KP;
+  const bool real = i < rows;
+  const float* v = V + ((size_t)b * rows + (real ? i : 0)) * d;
+  if (mode == MODE_BF16) {
+    for (int k = 0; k < KP; k += 2) {
+      u16 h[2] = {0, 0}, l[2] = {0, 0};
+      for (int e = 0; e < 2; ++e)
+        if (real && k + e < d) {
+          h[e] = bf16_rne(v[k + e]);
+          l[e] = bf16_rne(v[k + e] - bf16_f(h[e]));
+        }
+      *reinterpret_cast<uint32_t*>(dst + k) = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+      *reinterpret_cast<uint32_t*>(dst + plane + k) = (uint32_t)l[0] | ((uint32_t)l[1] << 16);
+    }
+    return;
   }
-  u = t + k;
+  double vmax = 0.0;
+  if (real)
+    for (int t = 0; t < d; ++t) vmax = fmax(vmax, fabs((double)v[t]));
+  const int qe = grid_exponent(vmax);
+  const double q = ldexp(1.0, qe), iq = ldexp(1.0, -qe);
+  const int cb = split_corr_begin(d);
+  for (int k0 = 0; k0 < KP; k0 += 8) {
+    u16 w8[8];
+    for (int e = 0; e < 8; ++e) {
+      const int k = k0 + e;
+      u16 val = 0;
+      if (real && k >= 5 && k < 5 + d) {
+        val = grid_split((double)v[k - 5], q, iq).g;
+      } else if (real && k >= cb && k < cb + 7 * d) {
+        const Parts pp = grid_split((double)v[(k - cb) / 7], q, iq);
+        const int sl = (k - cb) % 7;
+        val = (sl <= 1) ? pp.g : ((sl == 3 || sl == 6) ? pp.r2 : pp.r1);
+      }
+      w8[e] = val;
+    }
+    *reinterpret_cast<u4*>(dst + k0) = pack8(w8);
+  }
 }
 
-// Matrix [q_t q_u for pairs k0 .. k0+nb-1] per row of the fixed cloud.
-__global__ __launch_bounds__(256) void k_hvp_qqmat(const void* __restrict__ Q, int in_bf16, long long total, int d,
-                                                   int k0, int nb, float* __restrict__ M) {
-  const long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= total) return;
-  int t, u;
-  pair_of(k0, d, t, u);
-  float* row = M + j * nb;
-  for (int e = 0; e < nb; ++e) {
-    row[e] = (float)((double)coord(Q, (size_t)j * d + t, in_bf16) * (double)coord(Q, (size_t)j * d + u, in_bf16));
-    if (++u == d) u = ++t;
-  }
-}
-
-// quad_i += M_i v_i with M_i = sum_j P_ij q_j q_j^T symmetric: a pair (t, u) with
-// A = (P [q_t q_u])_i adds v_i[t] A to component u and, off the diagonal,
-// v_i[u] A to component t.
-__global__ __launch_bounds__(256) void k_hvp_quad(const float* __restrict__ V, const float* __restrict__ A,
-                                                  long long total, int d, int k0, int nb,
+// Merge of the row-weighted pass: quad_i = r_i (sum_splits sum_parts pv) /
+// (sum_splits s), r_i the row mass, in fp64.  One thread per (problem, row, coordinate).
+__global__ __launch_bounds__(256) void k_uw_merge(const float* __restrict__ pv, const float* __restrict__ sp, int ks,
+                                                  int batch, int rows, int d, int ncols, int parts,
+                                                  const double* __restrict__ logw, const float* __restrict__ pot,
+                                                  const float* __restrict__ lse, double eps,
                                                   double* __restrict__ quad) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  int t, u;
-  pair_of(k0, d, t, u);
-  const float* v = V + i * d;
-  double* q = quad + i * d;
-  for (int e = 0; e < nb; ++e) {
-    const double a = A[i * nb + e];
-    q[u] += (double)v[t] * a;
-    if (t != u) q[t] += (double)v[u] * a;
-    if (++u == d) u = ++t;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)batch * rows * d) return;
+  const int t = (int)(idx % d);
+  const long long rr = idx / d;
+  double S = 0.0, num = 0.0;
+  for (int k = 0; k < ks; ++k) {
+    const size_t base = (size_t)k * batch * rows + (size_t)rr;
+    S += (double)sp[base];
+    for (int part = 0; part < parts; ++part) num += (double)pv[base * ncols + part * d + t];
   }
+  const double mass = exp(logw[rr] + ((double)pot[rr] - (double)lse[rr]) / eps);
+  quad[idx] = mass > 0.0 ? mass * num / S : 0.0;
 }
 
 // Coordinates of a cloud as an fp32 matrix.
@@ -1705,8 +1772,8 @@ struct Layout {
   size_t bpv_bytes;      // bytes of the split-partials region
   size_t vt, bpv, bs, bm, ttotal;
   // Hessian-vector products (after `ttotal`)
-  size_t h_lse_r, h_lse_k, h_mr, h_mk, h_py, h_mat, h_w, h_g, h_quad, h_tmp, h_zr, h_cr, h_rhs, h_dg, h_res,
-      h_pd, h_pdf, h_t, h_q, h_st, h_part, htotal;
+  size_t h_lse_r, h_lse_k, h_mr, h_mk, h_py, h_mat, h_w, h_g, h_quad, h_zr, h_cr, h_rhs, h_dg, h_res,
+      h_pd, h_pdf, h_t, h_q, h_st, h_part, h_u, htotal;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -1808,7 +1875,7 @@ Layout layout_of(const sk_problem* p) {
   L.h_w = take(4 * bm * (d + 2));
   L.h_g = take(4 * bm * (d + 1));
   L.h_quad = take(8 * bm * d);
-  L.h_tmp = take(4 * bm * std::max<size_t>((size_t)APPLY_COLS, d));
+  L.h_u = take(2 * 2 * (B * (size_t)L.max_pad + SLACK) * L.KP);  // two query-layout planes of the direction
   L.h_zr = take(8 * bm);
   L.h_cr = take(8 * bm);
   L.h_rhs = take(8 * bm);
@@ -2020,7 +2087,8 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
 }
 
 using BaryFn = void (*)(const u16*, const u16*, const float*, const u16*, const float*, const double*, const float*,
-                        float*, float*, int, int, int, int, int, int, float, float, float*, unsigned*, unsigned);
+                        float*, float*, int, int, int, int, int, int, float, float, float*, unsigned*, unsigned,
+                        const u16*, float);
 
 template <int MODE, int D>
 BaryFn bary_fn_d() {
@@ -2101,7 +2169,8 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   float* bm = reinterpret_cast<float*>(w + L.bm);
   const float lam = (float)(LOG2E / (double)eps);
   hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, nullptr, bpv, bs, rows,
-                     rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, bm, tag, __builtin_bit_cast(unsigned, lam));
+                     rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, bm, tag, __builtin_bit_cast(unsigned, lam), nullptr,
+                     1.f);
   st = hip_check("transport kernel launch");
   if (st != SK_OK) return st;
 
@@ -2193,7 +2262,7 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
     const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps, ks_cap);
     hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, lse, bpv, bs,
                        rows, rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, nullptr, ptag,
-                       __builtin_bit_cast(unsigned, lam));
+                       __builtin_bit_cast(unsigned, lam), nullptr, 1.f);
     st = hip_check("plan-application kernel launch");
     if (st != SK_OK) return st;
     const long long total = (long long)B * rows * cb;
@@ -2203,6 +2272,89 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
     if (st != SK_OK) return st;
   }
   return SK_OK;
+}
+
+// Row-weighted plan pass kernels: weights P_ij (q_j . v_i) applied to the
+// fixed cloud's coordinates (no ones column; the weight sums come from the VALU).
+template <int MODE, int D>
+BaryFn uw_fn_d() {
+  constexpr int NCH = MODE == MODE_SPLIT ? split_nch(D) : (D + 31) / 32;
+  return &k_bary<MODE, NCH, val_tiles(MODE, D), false, false, MODE == MODE_SPLIT ? 1 : 2>;
+}
+template <int MODE, int... N>
+BaryFn uw_lookup_impl(int d, std::integer_sequence<int, N...>) {
+  BaryFn fn = nullptr;
+  ((d == N + 1 ? (fn = uw_fn_d<MODE, N + 1>(), 0) : 0), ...);
+  return fn;
+}
+BaryFn uw_lookup(int mode, int d) {
+  if (mode == MODE_SPLIT) return uw_lookup_impl<MODE_SPLIT>(d, std::make_integer_sequence<int, SK_MAX_D_FP32>{});
+  return uw_lookup_impl<MODE_BF16>(d, std::make_integer_sequence<int, SK_MAX_D_TRANSPORT>{});
+}
+
+// quad_i = sum_j P_ij (q_j . v_i) q_j = M_i v_i with M_i = sum_j P_ij q_j q_j^T, for
+// the rows of `side` (q the other cloud), in one streaming pass: the direction v
+// enters as a second query operand whose contraction with the key rows gives
+// q_j . v_i beside each score.  quad is [B][rows][d] fp64.
+sk_status apply_uw(const sk_problem* p, const void* X, const void* Y, char* w, const Layout& L, const float* pot_row,
+                   const float* pot_key, const float* lse, float eps, int side, const float* Vdir, double* quad,
+                   hipStream_t stream) {
+  const int B = (int)p->batch, d = (int)p->d;
+  const int rows = (int)(side == 0 ? p->n : p->m);
+  const int keys = (int)(side == 0 ? p->m : p->n);
+  const int rows_pad = side == 0 ? L.n_pad : L.m_pad;
+  const int keys_pad = side == 0 ? L.m_pad : L.n_pad;
+  const double* qnorm = reinterpret_cast<const double*>(w + (side == 0 ? L.xn : L.yn));
+  const double* qlogw = reinterpret_cast<const double*>(w + (side == 0 ? L.la : L.lb));
+  const float* qgrid = reinterpret_cast<const float*>(w + L.qgrid);
+  const u16* Qop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qx : L.qy));
+  const void* Kraw = side == 0 ? Y : X;
+  const u16* Kop = nullptr;
+  const float* hb = nullptr;
+  unsigned* ptag = nullptr;
+  sk_status st = prep_keys(p, X, Y, w, L, pot_key, eps, side, stream, &Kop, &hb, &ptag);
+  if (st != SK_OK) return st;
+  u16* U = reinterpret_cast<u16*>(w + L.h_u);
+  hipLaunchKernelGGL(k_prep_u, dim3((rows_pad + 255) / 256, B), dim3(256), 0, stream, Vdir, rows, rows_pad, d, L.KP,
+                     L.mode, B, U);
+  u16* vt = reinterpret_cast<u16*>(w + L.vt);
+  const int nct = val_tiles(L.mode, d), nc = nct * 16;
+  const long long nvec = (long long)(keys_pad / VK) * nc * (VK / 8);
+  const double* krn = reinterpret_cast<const double*>(w + (side == 0 ? L.ry : L.rx));
+  hipLaunchKernelGGL(k_prep_vals, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, Kraw, L.mode,
+                     L.in_bf16, krn, keys, keys_pad, d, nc, 0, vt);
+  st = hip_check("direction and value preparation launch");
+  if (st != SK_OK) return st;
+  BaryFn fn = uw_lookup(L.mode, d);
+  if (fn == nullptr) {
+    set_err("no row-weighted plan kernel for d = %d", d);
+    return SK_EUNSUPPORTED;
+  }
+  const int nch = L.KP / 32;
+  const int R = bary_R(nch, nct);
+  const int CKb = bary_TCB(nch, nct) * VK;
+  const int total_chunks = (keys + CKb - 1) / CKb;
+  const int wg_x = (rows + 4 * R * 16 - 1) / (4 * R * 16);
+  int capacity = 0;
+  st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity);
+  if (st != SK_OK) return st;
+  const int ks_cap = (int)std::min<size_t>(16, std::max<size_t>(1, L.bpv_bytes / (4 * (size_t)B * rows * nc)));
+  int cps = 0;
+  const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps, ks_cap);
+  float* bpv = reinterpret_cast<float*>(w + L.bpv);
+  float* bs = reinterpret_cast<float*>(w + L.bs);
+  const float lam = (float)(LOG2E / (double)eps);
+  // the fp32 key operand holds 2 lambda q
+  const float ugain = L.mode == MODE_SPLIT ? 1.f / (2.f * lam) : 1.f;
+  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, lse, bpv, bs, rows,
+                     rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, nullptr, ptag, __builtin_bit_cast(unsigned, lam),
+                     U, ugain);
+  st = hip_check("row-weighted plan kernel launch");
+  if (st != SK_OK) return st;
+  const long long total = (long long)B * rows * d;
+  hipLaunchKernelGGL(k_uw_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, bs, ks, B, rows, d,
+                     nc, val_parts(L.mode), qlogw, pot_row, lse, (double)eps, quad);
+  return hip_check("row-weighted merge launch");
 }
 
 unsigned blocks_for(long long n) { return (unsigned)((n + 255) / 256); }
@@ -2233,7 +2385,6 @@ sk_status hvp(const sk_problem* p, const void* X, const void* Y, char* w, const 
   float* wk = reinterpret_cast<float*>(w + L.h_w);
   float* gm = reinterpret_cast<float*>(w + L.h_g);
   double* quad = reinterpret_cast<double*>(w + L.h_quad);
-  float* tmp = reinterpret_cast<float*>(w + L.h_tmp);
   double* zr = reinterpret_cast<double*>(w + L.h_zr);
   double* cr = reinterpret_cast<double*>(w + L.h_cr);
   double* rhs = reinterpret_cast<double*>(w + L.h_rhs);
@@ -2300,19 +2451,9 @@ sk_status hvp(const sk_problem* p, const void* X, const void* Y, char* w, const 
   st = hip_check("HVP matrix launch");
   if (st == SK_OK) st = apply_plan(p, X, Y, w, L, pot_r, pot_k, lse_r, eps, side, mat, d + 1, gm, s);
   if (st != SK_OK) return st;
-  // 6. sum_j P_ij (q_j . v_i) q_j = M_i v_i, M_i = sum_j P_ij q_j q_j^T from the plan
-  //    applied to the d(d+1)/2 products q_t q_u, APPLY_COLS pairs per pass
-  hipLaunchKernelGGL(k_fill_f32, dim3(blocks_for(2 * nr * d)), dim3(256), 0, s, reinterpret_cast<float*>(quad),
-                     (int)(2 * nr * d), 0.f);
-  const int npairs = d * (d + 1) / 2;
-  for (int k0 = 0; k0 < npairs; k0 += APPLY_COLS) {
-    const int nb = std::min(APPLY_COLS, npairs - k0);
-    hipLaunchKernelGGL(k_hvp_qqmat, dim3(blocks_for(nk)), dim3(256), 0, s, Qraw, in16, nk, d, k0, nb, mat);
-    st = hip_check("HVP matrix launch");
-    if (st == SK_OK) st = apply_plan(p, X, Y, w, L, pot_r, pot_k, lse_r, eps, side, mat, nb, tmp, s);
-    if (st != SK_OK) return st;
-    hipLaunchKernelGGL(k_hvp_quad, dim3(blocks_for(nr)), dim3(256), 0, s, V, tmp, nr, d, k0, nb, quad);
-  }
+  // 6. sum_j P_ij (q_j . v_i) q_j = M_i v_i in one row-weighted plan pass
+  st = apply_uw(p, X, Y, w, L, pot_r, pot_k, lse_r, eps, side, V, quad, s);
+  if (st != SK_OK) return st;
   // 7. assemble
   hipLaunchKernelGGL(k_hvp_final, dim3(blocks_for(nr)), dim3(256), 0, s, Praw, in16, V, py, mr, zr, cr, gm, quad, nr,
                      d, (double)eps, out);
