@@ -153,8 +153,9 @@ sk_status sinkhorn_marginal_error(const sk_problem* p, const void* X, const void
  * bary and grad are fp32 DEVICE arrays owned by the caller; grad may be NULL.
  * These calls need a workspace of sinkhorn_transport_workspace_bytes(p) (a
  * superset of the solver's; every other call accepts it too) on which
- * sinkhorn_init_norms has run.  They run one half-step internally (into
- * workspace scratch) to fix each row's offset, then one pass over the keys.
+ * sinkhorn_init_norms has run.  Each call makes one pass over the keys with
+ * lazily raised row offsets and recovers each row's log-sum-exp (for r_i) from
+ * the offsets and weight sums.
  * --------------------------------------------------------------------------- */
 
 /* Workspace bytes for the transport calls (0 if p is invalid). */
@@ -197,7 +198,8 @@ sk_status sinkhorn_apply_plan_y(const sk_problem* p, const void* X, const void* 
  * (diag(c) - P^T diag(1/r) P) dg = rhs by conjugate gradients (Jacobi
  * preconditioned, at most cg_iters iterations, stopped per problem when the
  * preconditioned residual falls below cg_tol relative to its start), each
- * iteration two one-column plan applications.  Squared-Euclidean cost only
+ * iteration two one-column plan applications; the term sum_j P_ij (q_j . v_i) q_j
+ * (q the other cloud) is one pass whose weights carry q_j . v_i.  Squared-Euclidean cost only
  * (SK_EUNSUPPORTED for the cosine cost).  Workspace: sinkhorn_hvp_workspace_bytes
  * (a superset of the transport workspace), after sinkhorn_init_norms.
  * --------------------------------------------------------------------------- */

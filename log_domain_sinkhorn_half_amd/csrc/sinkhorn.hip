@@ -35,18 +35,20 @@
 //    rescale.  Such a chunk is recomputed with its exact maximum; offsets are
 //    integers, so rescaling is an exact power of two.
 //  * Key chunks are staged through LDS (double buffered) and shared by the
-//    four waves of a workgroup; each wave keeps its own query tiles in VGPRs.
+//    four (or eight) waves of a workgroup; each wave keeps its own query tiles
+//    in VGPRs.
 //  * Key ranges are split across workgroups when rows alone cannot fill the
 //    256 CUs; the partial (max, sum) pairs are merged by a small kernel.
 //  * Norms, log-weights, the bias and the final potential are formed in fp64.
 //
 // Beyond the half-step (same page, section "Differentiation and second-order
 // optimisation"; and the closing remarks on costs):
-//  * transport application: barycentric projection and gradient, and the plan
-//    applied to any matrix, as a P.V pass that reuses the score tiles with the
-//    row offsets fixed by a half-step (k_bary);
+//  * transport application: barycentric projection and gradient in one P.V
+//    pass over the score tiles with lazy row offsets, and the plan applied to
+//    any matrix with offsets fixed by the potentials (k_bary);
 //  * Hessian-vector products of the OT value, from plan products only
-//    (conjugate gradients on a Schur system, then an assembly);
+//    (conjugate gradients on a Schur system, then an assembly; the quadratic
+//    term in one pass whose weights carry the direction's dot products);
 //  * the cosine cost, as the squared-Euclidean cost between normalised points.
 
 #include <hip/hip_runtime.h>
