@@ -19,7 +19,6 @@ oracle on a bounded row slice of the same workload on this host's cores.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -57,8 +56,8 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    src = os.path.join(ROOT, "log_domain_sinkhorn_half_amd", "csrc", "sinkhorn.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    from log_domain_sinkhorn_half_amd.rocprof_harness import kernel_source_hash as code_hash
+    return code_hash()
 
 
 def read_traffic(kernel: str, workload: str):

@@ -32,6 +32,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import subprocess
 import sys
 
@@ -79,9 +80,17 @@ def algorithmic_bytes(C: int) -> float:
     return B * (n + m) * kp * 2 + B * (n + m) / 2 * 4
 
 
+def code_hash(src: str) -> str:
+    """Hash of C/C++ source with comments and whitespace left out."""
+    code = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    code = re.sub(r"//[^\n]*", " ", code)
+    return hashlib.sha256(" ".join(code.split()).encode()).hexdigest()[:16]
+
+
 def kernel_source_hash() -> str:
-    src = os.path.join(ROOT, "log_domain_sinkhorn_half_amd", "csrc", "sinkhorn.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel source's code, so a summary stays tied to the code it
+    measured and survives comment edits."""
+    return code_hash(open(os.path.join(ROOT, "log_domain_sinkhorn_half_amd", "csrc", "sinkhorn.hip")).read())
 
 
 def short(name: str) -> str:

@@ -25,3 +25,11 @@ def test_operand_slots_match_kernel_instances():
 def test_algorithmic_bytes_of_the_headline_workload():
     # 70000 queries and 70000 keys of 32 bf16 slots, plus 70000 fp32 potentials per launch
     assert h.algorithmic_bytes(3) == 2 * 70000 * 32 * 2 + 70000 * 4
+
+
+def test_code_hash_ignores_comments_and_spacing():
+    a = "int f(int x) {\n  return x + 1;  // add one\n}\n"
+    b = "/* doc */ int f(int x) { return x + 1; }"
+    assert h.code_hash(a) == h.code_hash(b)
+    assert h.code_hash(a) != h.code_hash(a.replace("+ 1", "+ 2"))
+    assert len(h.kernel_source_hash()) == 16
