@@ -114,7 +114,9 @@ def run_hvp(p, eps, f, g, V, side, iters=400, tol=1e-7):
 
 
 @pytest.mark.parametrize("n,m,d,eps,dtype", [(64, 48, 2, 0.5, "fp32"), (200, 150, 3, 0.1, "fp32"),
-                                             (120, 140, 16, 0.2, "fp32"), (100, 90, 32, 0.5, "bf16")])
+                                             (120, 140, 16, 0.2, "fp32"), (100, 90, 32, 0.5, "bf16"),
+                                             (90, 110, 64, 0.3, "fp32"), (70, 80, 128, 0.5, "bf16"),
+                                             (60, 75, 88, 0.4, "fp32")])
 def test_hvp_against_oracle(n, m, d, eps, dtype):
     p = make_case(n, m, d, seed=23 * n + d, weights="softmax", dtype=dtype, scale=1.0 / np.sqrt(d))
     f, g = potentials(p, eps, 2000)
