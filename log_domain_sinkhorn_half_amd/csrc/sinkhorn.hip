@@ -971,12 +971,18 @@ __global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, i
 
 // Two packed bf16 parts of a weight pair: hi = e truncated to bf16 (its upper
 // half), lo = rne(e - hi), where e - hi is exact; together 16 significant bits.
-// Returns (hi pair, lo pair).
+// Returns (hi pair, lo pair).  The hi pair is one byte permute; e - hi is one
+// bf16 dot product each, hi . (-1, -0) + a and hi . (0, -1) + b (products and
+// sums exact).  The first pair is written (-1, -0) so that it is encoded as a
+// 32-bit literal: hipcc encodes (-1, 0) as the inline constant -1.0, which
+// this instruction reads as the fp32 bit pattern, i.e. as the pair (0, -1).
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 split_pair(float a, float b) {
-  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
-  const uint32_t hi = (ua >> 16) | (ub & 0xFFFF0000u);
-  const bf16x2 l = {(__bf16)(a - __uint_as_float(ua & 0xFFFF0000u)), (__bf16)(b - __uint_as_float(ub & 0xFFFF0000u))};
+  const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+  const bf16x2 h = __builtin_bit_cast(bf16x2, hi);
+  const float la = __builtin_amdgcn_fdot2_f32_bf16(h, bf16x2{(__bf16)-1.f, (__bf16)-0.f}, a, false);
+  const float lb = __builtin_amdgcn_fdot2_f32_bf16(h, bf16x2{(__bf16)0.f, (__bf16)-1.f}, b, false);
+  const bf16x2 l = {(__bf16)la, (__bf16)lb};
   return make_uint2(hi, __builtin_bit_cast(uint32_t, l));
 }
 
@@ -1173,24 +1179,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
       f4 a0[R], a1[R], u0[R], u1[R];
       score2(buf, 2 * vb, a0, u0);
       score2(buf, 2 * vb + 1, a1, u1);
+      float e[R][8];
+      auto weights = [&]() {
+#pragma unroll
+        for (int c = 0; c < R; ++c)
+#pragma unroll
+          for (int o = 0; o < 4; ++o) {
+            e[c][o] = weight(a0[c][o], c);
+            e[c][4 + o] = weight(a1[c][o], c);
+          }
+      };
+      weights();
       if (LAZY) {
-        // A lane whose scores exceed its query's offset by more than 2^32 (or
-        // meet its first keys) asks for a raise; the wave then takes each
-        // query's block maximum, sets its offset HEADROOM above it, rescales the
-        // sums and, on the fp32 path, scores the block again.
-        float mx[R];
-        bool want = false;
+        // A weight above 2^32 (a score more than 32 above its query's offset),
+        // or a query meeting its first keys, asks for a raise; the wave then
+        // takes each query's block maximum, sets its offset HEADROOM above it,
+        // rescales the sums and, on the fp32 path, scores the block again.
+        // (Weights are non-negative: their bit patterns order like their
+        // values, with NaN above all, so the maximum is an integer one.)
+        uint32_t wm = 0u;
+        bool first = false;
 #pragma unroll
         for (int c = 0; c < R; ++c) {
-          float v = -INFINITY;
+          first |= mo[c] == -INFINITY;
 #pragma unroll
-          for (int o = 0; o < 4; ++o) v = fmaxf(v, fmaxf(a0[c][o], a1[c][o]));
-          mx[c] = v;
-          // base 2, relative to mo (the fp32 path's scores already are)
-          const float rel = (MODE == MODE_BF16) ? fmaf(v, lam2, -mo[c]) : v;
-          want |= mo[c] == -INFINITY || !(rel <= 32.f);
+          for (int o = 0; o < 8; ++o) wm = max(wm, __float_as_uint(e[c][o]));
         }
-        if (__any(want)) {
+        if (__any(first || wm > __float_as_uint(0x1p32f))) {
+          float mx[R];
+#pragma unroll
+          for (int c = 0; c < R; ++c) {
+            float v = -INFINITY;
+#pragma unroll
+            for (int o = 0; o < 4; ++o) v = fmaxf(v, fmaxf(a0[c][o], a1[c][o]));
+            mx[c] = v;
+          }
 #pragma unroll
           for (int c = 0; c < R; ++c) {
             float v = fmaxf(mx[c], __shfl_xor(mx[c], 16));
@@ -1214,6 +1237,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
             score(buf, 2 * vb, a0);
             score(buf, 2 * vb + 1, a1);
           }
+          weights();
         }
       }
       // A operand of the P.V step: lane (query col, group grp) holds the
@@ -1221,22 +1245,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
       u4 ehi[R], elo[R];
 #pragma unroll
       for (int c = 0; c < R; ++c) {
-        float e[8];
-#pragma unroll
-        for (int o = 0; o < 4; ++o) {
-          e[o] = weight(a0[c][o], c);
-          e[4 + o] = weight(a1[c][o], c);
-        }
-        if (!SUMCOL) s[c] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        if (!SUMCOL) s[c] += ((e[c][0] + e[c][1]) + (e[c][2] + e[c][3])) + ((e[c][4] + e[c][5]) + (e[c][6] + e[c][7]));
         if (NU > 0) {
 #pragma unroll
           for (int o = 0; o < 4; ++o) {
-            e[o] *= u0[c][o] * ugain;
-            e[4 + o] *= u1[c][o] * ugain;
+            e[c][o] *= u0[c][o] * ugain;
+            e[c][4 + o] *= u1[c][o] * ugain;
           }
         }
-        const uint2 p0 = split_pair(e[0], e[1]), p1 = split_pair(e[2], e[3]);
-        const uint2 p2 = split_pair(e[4], e[5]), p3 = split_pair(e[6], e[7]);
+        const uint2 p0 = split_pair(e[c][0], e[c][1]), p1 = split_pair(e[c][2], e[c][3]);
+        const uint2 p2 = split_pair(e[c][4], e[c][5]), p3 = split_pair(e[c][6], e[c][7]);
         ehi[c] = u4{p0.x, p1.x, p2.x, p3.x};
         elo[c] = u4{p0.y, p1.y, p2.y, p3.y};
       }
