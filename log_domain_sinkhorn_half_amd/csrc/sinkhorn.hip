@@ -854,15 +854,15 @@ __global__ __launch_bounds__(256) void k_merge(const float2* __restrict__ part, 
                                                double inv_lam) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
+  // Two passes over the partials (the second from cache): the loads of a pass
+  // are independent, so they overlap instead of waiting on a running offset.
   float M = -FLT_MAX, S = 0.f;
+#pragma unroll 8
+  for (int k = 0; k < ks; ++k) M = fmaxf(M, part[(size_t)k * total + i].x);
+#pragma unroll 8
   for (int k = 0; k < ks; ++k) {
     const float2 v = part[(size_t)k * total + i];
-    if (v.x > M) {
-      S = rescale(S, M, v.x) + v.y;
-      M = v.x;
-    } else {
-      S += rescale(v.y, v.x, M);
-    }
+    S += rescale(v.y, v.x, M);
   }
   out[i] = (float)(qnorm[i] - ((double)M + log2((double)S)) * inv_lam);
 }
