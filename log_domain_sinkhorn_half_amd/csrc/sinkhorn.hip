@@ -1327,9 +1327,11 @@ __global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv
   double M = 0.0;
   if (mpart != nullptr) {
     M = -INFINITY;
+#pragma unroll 4
     for (int k = 0; k < ks; ++k) M = fmax(M, (double)mpart[(size_t)k * batch * rows + (size_t)rr]);
   }
   double S = 0.0, num = 0.0;
+#pragma unroll 4
   for (int k = 0; k < ks; ++k) {
     const size_t base = (size_t)k * batch * rows + (size_t)rr;
     const double sc = mpart != nullptr ? exp2((double)mpart[base] - M) : 1.0;  // 0 for an empty split
@@ -1432,6 +1434,7 @@ __global__ __launch_bounds__(256) void k_apply_merge(const float* __restrict__ p
   const int k = (int)(idx % cb);
   const long long rr = idx / cb;
   double S = 0.0, num = 0.0;
+#pragma unroll 4
   for (int sp = 0; sp < ks; ++sp) {
     const size_t base = ((size_t)sp * batch * rows + (size_t)rr) * ncols;
     S += (double)pv[base + ncols - 1];
@@ -1736,6 +1739,7 @@ __global__ __launch_bounds__(256) void k_uw_merge(const float* __restrict__ pv, 
   const int t = (int)(idx % d);
   const long long rr = idx / d;
   double S = 0.0, num = 0.0;
+#pragma unroll 4
   for (int k = 0; k < ks; ++k) {
     const size_t base = (size_t)k * batch * rows + (size_t)rr;
     S += (double)sp[base];
