@@ -179,3 +179,9 @@ def test_plan_and_hvp_entry_points_validate(lib):
         cos = binding.SkProblem(1, 300, 200, 3, 0, 1)
         hc = lib.sinkhorn_hvp_workspace_bytes(ctypes.byref(cos))
         assert fn(ctypes.byref(cos), ptr, ptr, ptr, hc, ptr, ptr, 0.1, ptr, 10, 1e-6, ptr, None) == 5
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No CPU fallback: a library path that does not exist raises, naming the build step."""
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        binding.load_library(str(tmp_path / "libsinkhorn.so"))
