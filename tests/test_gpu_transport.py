@@ -3,9 +3,11 @@ through the C ABI against the fp64 oracle (page "FlashSinkhorn: IO-aware
 entropic OT on GPU", section "Differentiation and second-order optimisation").
 
 Acceptance bounds, derived from the arithmetic of the two passes:
-  bary: fp32 inputs |d bary| <= 2e-5 * max|V|, bf16 inputs <= 5e-4 * max|V|,
-        V = the other cloud.  The weights carry the score rounding of the
-        half-step kernel (about 1e-6 relative for fp32 operands, 2.5e-5 for bf16
+  bary: fp32 inputs |d bary| <= 2e-5 * max|V|, bf16 inputs <= 5e-4 * max|V| for d <= 128,
+        V = the other cloud; past d = 128 the bf16 bound grows with the score's number
+        of fp32 roundings, d/8 + 2 (measured at eps = 0.01: 4.7e-4 at d = 200 and
+        5.8e-4 at d = 256 against bounds of 7.5e-4 and 9.4e-4).  The weights carry the
+        score rounding of the half-step kernel (about 1e-6 relative for fp32 operands, 2.5e-5 for bf16
         operands at lambda = log2(e)/0.01) and a 2^-17 two-part bf16 split; a
         convex combination moves by at most that relative error times the spread
         of V.
@@ -46,6 +48,11 @@ def dev(p):
 
 def bounds(p, eps, V, P, bary_ref, mass_ref, T_ref):
     rel = 5e-4 if p.dtype == "bf16" else 2e-5
+    d = V.shape[1]
+    if p.dtype == "bf16" and d > 128:
+        # the score's rounding error grows with its d/8 + 2 fp32 roundings (groups of
+        # 8 exact bf16 products, the bias, the base-2 scaling); 5e-4 holds up to d = 128
+        rel *= (d / 8 + 2) / (128 / 8 + 2)
     tb = rel * float(np.max(np.abs(V)))
     tT = 2e-2 * eps if p.dtype == "bf16" else 1e-3 * eps + 1e-5 * float(np.max(np.abs(T_ref)))
     dm = np.expm1(tT / eps)  # largest relative error of the row mass
@@ -110,7 +117,8 @@ def test_transport_fp32_ragged(n, m, d):
         compare(p, 0, "y", eps, by, gy, f, g)
 
 
-@pytest.mark.parametrize("n,m,d", [(300, 200, 3), (129, 257, 64), (100, 90, 128), (63, 65, 8)])
+@pytest.mark.parametrize("n,m,d", [(300, 200, 3), (129, 257, 64), (100, 90, 128), (63, 65, 8), (70, 90, 200),
+                                   (60, 75, 256)])
 def test_transport_bf16_ragged(n, m, d):
     p = make_case(n, m, d, seed=5 * n + m, weights="softmax", dtype="bf16", scale=1.0 / np.sqrt(d))
     for eps in (1.0, 0.1, 0.01):
