@@ -920,7 +920,11 @@ __host__ __device__ constexpr bool val_sumcol(int mode, int d) { return val_part
 __host__ __device__ constexpr int bary_R(int nch, int nct) {
   return nct >= 9 ? 1 : (nch == 1 ? (nct >= 4 ? 2 : 4) : (nch <= 8 ? 2 : 1));
 }
-__host__ __device__ constexpr int bary_waves(int nch) { return nch >= 12 ? 1 : 2; }
+// Waves per workgroup: operands of 12 or more K chunks take 80-120 KB of LDS per
+// workgroup (one per CU); with at most 4 value tiles the registers allow two
+// waves per SIMD, so 8 waves share the staged keys.
+__host__ __device__ constexpr int bary_NW(int nch, int nct) { return (nch >= 12 && nct <= 4) ? 8 : 4; }
+__host__ __device__ constexpr int bary_waves(int nch, int nct) { return nch >= 12 ? (nct <= 4 ? 2 : 1) : 2; }
 // 32-key value blocks per LDS chunk of the transport kernel (fewer barriers for small operands)
 __host__ __device__ constexpr int bary_TCB(int nch, int nct) { return (nch <= 2 && nct <= 4) ? 4 : 1; }
 
@@ -995,7 +999,7 @@ __device__ __forceinline__ uint2 split_pair(float a, float b) {
 // the weights become P_ij * u_ij with u_ij = ugain * (key operand . U_i), i.e.
 // u_ij = q_j . v_i, while s_out still sums the plain weights.
 template <int MODE, int NCH, int NCT, bool SUMCOL, bool LAZY = false, int NU = 0>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(NCH)))) void k_bary(
+__global__ __launch_bounds__(64 * bary_NW(NCH, NCT)) __attribute__((amdgpu_waves_per_eu(bary_waves(NCH, NCT)))) void k_bary(
     const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb, const u16* __restrict__ V,
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, const float* __restrict__ lse,
     float* __restrict__ pv_out, float* __restrict__ s_out, int rows, int rows_pad, int keys, int keys_pad,
@@ -1011,11 +1015,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
   static_assert(ROW_PAD % CK == 0 && CK <= SLACK, "a key chunk must divide the row padding");
   constexpr int VPR = KP / 8;
   constexpr int NVEC = CK * VPR;
-  constexpr int NLD = (NVEC + 255) / 256;
+  constexpr int NW = bary_NW(NCH, NCT), NT = 64 * NW;  // waves, threads per workgroup
+  constexpr int NLD = (NVEC + NT - 1) / NT;
   constexpr int NC = NCT * 16;        // value columns
   constexpr int VROW = VK + 8;        // LDS row stride of the value tile (elements)
   constexpr int NVV = TCB * NC * (VK / 8);  // 16-byte vectors per chunk of value blocks
-  constexpr int NLV = (NVV + 255) / 256;
+  constexpr int NLV = (NVV + NT - 1) / NT;
   constexpr int QPW = R * MW;
   __shared__ __attribute__((aligned(16))) u16 lds[2][(CK + 1) * LROW];
   __shared__ __attribute__((aligned(16))) u16 ldv[2][(TCB * NC + 1) * VROW];
@@ -1024,7 +1029,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane / MW, col = lane % MW;
   const int b = blockIdx.z;
-  const int qbase = blockIdx.x * (4 * QPW) + wave * QPW;
+  const int qbase = blockIdx.x * (NW * QPW) + wave * QPW;
   const u16* Qb = Q + (size_t)b * rows_pad * KP;
   const u16* Kb = K + (size_t)b * keys_pad * KP;
   const u16* Vb = V + (size_t)b * keys_pad * NC;
@@ -1108,21 +1113,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bary_waves(
   auto gload = [&](int chunk) {
     const u16* src = Kb + (size_t)chunk * CK * KP;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) pre[i] = *reinterpret_cast<const u4*>(src + (size_t)(tid + 256 * i) * 8);
+    for (int i = 0; i < NLD; ++i) pre[i] = *reinterpret_cast<const u4*>(src + (size_t)(tid + NT * i) * 8);
     const u16* vsrc = Vb + (size_t)chunk * TCB * NC * VK;
 #pragma unroll
-    for (int i = 0; i < NLV; ++i) prev[i] = *reinterpret_cast<const u4*>(vsrc + (size_t)min(tid + 256 * i, NVV - 1) * 8);
+    for (int i = 0; i < NLV; ++i) prev[i] = *reinterpret_cast<const u4*>(vsrc + (size_t)min(tid + NT * i, NVV - 1) * 8);
     if (MODE == MODE_BF16) preb = *reinterpret_cast<const f4*>(hbb + (size_t)chunk * CK + (tid % (CK / 4)) * 4);
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int v = min(tid + 256 * i, NVEC);
+      const int v = min(tid + NT * i, NVEC);
       *reinterpret_cast<u4*>(&lds[buf][(v / VPR) * LROW + (v % VPR) * 8]) = pre[i];
     }
 #pragma unroll
     for (int i = 0; i < NLV; ++i) {
-      const int v = min(tid + 256 * i, NVV);
+      const int v = min(tid + NT * i, NVV);
       *reinterpret_cast<u4*>(&ldv[buf][(v / (VK / 8)) * VROW + (v % (VK / 8)) * 8]) = prev[i];
     }
     if (MODE == MODE_BF16 && tid < CK / 4) *reinterpret_cast<f4*>(&ldsb[buf][tid * 4]) = preb;
@@ -2181,12 +2186,12 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
     return SK_EUNSUPPORTED;
   }
   const int nch = L.KP / 32;
-  const int R = bary_R(nch, val_tiles(L.mode, d));
-  const int wg_x = (rows + 4 * R * 16 - 1) / (4 * R * 16);
+  const int R = bary_R(nch, val_tiles(L.mode, d)), NWb = bary_NW(nch, val_tiles(L.mode, d));
+  const int wg_x = (rows + NWb * R * 16 - 1) / (NWb * R * 16);
   const int CKb = bary_TCB(nch, val_tiles(L.mode, d)) * VK;
   const int total_chunks = (keys + CKb - 1) / CKb;
   int capacity = 0;
-  st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity);
+  st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity, 64 * NWb);
   if (st != SK_OK) return st;
   int cps = 0;
   const int ks_cap = (int)std::min<size_t>(16, std::max<size_t>(1, L.bpv_bytes / (4 * (size_t)B * rows * nc)));
@@ -2195,7 +2200,7 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   float* bs = reinterpret_cast<float*>(w + L.bs);
   float* bm = reinterpret_cast<float*>(w + L.bm);
   const float lam = (float)(LOG2E / (double)eps);
-  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, nullptr, bpv, bs, rows,
+  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NWb), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, nullptr, bpv, bs, rows,
                      rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, bm, tag, __builtin_bit_cast(unsigned, lam), nullptr,
                      1.f);
   st = hip_check("transport kernel launch");
@@ -2270,7 +2275,8 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
     const int R = bary_R(nch, nct);
     const int CKb = bary_TCB(nch, nct) * VK;
     const int total_chunks = (keys + CKb - 1) / CKb;
-    const int wg_x = (rows + 4 * R * 16 - 1) / (4 * R * 16);
+    const int NWb = bary_NW(nch, nct);
+    const int wg_x = (rows + NWb * R * 16 - 1) / (NWb * R * 16);
     const long long nvec = (long long)(keys_pad / VK) * nc * (VK / 8);
     hipLaunchKernelGGL(k_prep_mat, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, M, keys, keys_pad,
                        c, col0, cb, nc, vt);
@@ -2282,12 +2288,12 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
       return SK_EUNSUPPORTED;
     }
     int capacity = 0;
-    st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity);
+    st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity, 64 * NWb);
     if (st != SK_OK) return st;
     const int ks_cap = (int)std::min<size_t>(16, std::max<size_t>(1, L.bpv_bytes / (4 * (size_t)B * rows * nc)));
     int cps = 0;
     const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps, ks_cap);
-    hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, lse, bpv, bs,
+    hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NWb), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, lse, bpv, bs,
                        rows, rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, nullptr, ptag,
                        __builtin_bit_cast(unsigned, lam), nullptr, 1.f);
     st = hip_check("plan-application kernel launch");
@@ -2358,12 +2364,12 @@ sk_status apply_uw(const sk_problem* p, const void* X, const void* Y, char* w, c
     return SK_EUNSUPPORTED;
   }
   const int nch = L.KP / 32;
-  const int R = bary_R(nch, nct);
+  const int R = bary_R(nch, nct), NWb = bary_NW(nch, nct);
   const int CKb = bary_TCB(nch, nct) * VK;
   const int total_chunks = (keys + CKb - 1) / CKb;
-  const int wg_x = (rows + 4 * R * 16 - 1) / (4 * R * 16);
+  const int wg_x = (rows + NWb * R * 16 - 1) / (NWb * R * 16);
   int capacity = 0;
-  st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity);
+  st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity, 64 * NWb);
   if (st != SK_OK) return st;
   const int ks_cap = (int)std::min<size_t>(16, std::max<size_t>(1, L.bpv_bytes / (4 * (size_t)B * rows * nc)));
   int cps = 0;
@@ -2373,7 +2379,7 @@ sk_status apply_uw(const sk_problem* p, const void* X, const void* Y, char* w, c
   const float lam = (float)(LOG2E / (double)eps);
   // the fp32 key operand holds 2 lambda q
   const float ugain = L.mode == MODE_SPLIT ? 1.f / (2.f * lam) : 1.f;
-  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(256), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, lse, bpv, bs, rows,
+  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NWb), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, lse, bpv, bs, rows,
                      rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, nullptr, ptag, __builtin_bit_cast(unsigned, lam),
                      U, ugain);
   st = hip_check("row-weighted plan kernel launch");
