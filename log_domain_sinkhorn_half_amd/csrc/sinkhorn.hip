@@ -1887,10 +1887,13 @@ Layout layout_of(const sk_problem* p) {
   L.scratch = take(4 * B * mx);
   L.total = off;
   // Transport: the value operand and the split partials of the P.V pass: room
-  // for 16 splits of a one-tile pass or one split of the widest pass.
+  // for 16 splits of a one-tile pass, and for the widest pass the partials of
+  // 131072 rows (split_rows below, at least one split and at most 16): a few
+  // thousand rows of a wide pass need several key splits to fill the GPU.
   const size_t d = (size_t)p->d;
   L.ncols = std::max(p->d <= SK_MAX_D_TRANSPORT ? val_tiles(L.mode, (int)p->d) : 0, apply_tiles(APPLY_COLS)) * 16;
-  L.bpv_bytes = std::max<size_t>(4 * 16 * 16 * B * mx, 4 * B * mx * (size_t)L.ncols);
+  const size_t split_rows = std::max(B * mx, std::min(16 * B * mx, (size_t)131072));
+  L.bpv_bytes = std::max<size_t>(4 * 16 * 16 * B * mx, 4 * split_rows * (size_t)L.ncols);
   L.vt = take(2 * B * (size_t)L.max_pad * L.ncols);
   L.bpv = take(L.bpv_bytes);
   L.bs = take(4 * 16 * B * mx);
