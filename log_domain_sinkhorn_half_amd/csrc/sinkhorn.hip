@@ -933,8 +933,15 @@ __device__ __forceinline__ u4 pack8(const u16 (&v)[8]) {
             (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
 }
 
+// Key order inside a 32-key value block: lane group g of the P.V MFMA takes the
+// weights of keys 4g..4g+3 and 16+4g..16+4g+3 as its A operand, so those eight
+// keys sit together at positions 8g..8g+7 and the lane reads its B operand as
+// one 16-byte vector (two 8-byte reads of the plain order conflict on the LDS
+// banks).  Element e of the 8-key vector at position k0 holds key vkey(k0, e).
+__host__ __device__ constexpr int vkey(int k0, int e) { return (k0 / 8) * 4 + (e < 4 ? e : 12 + e); }
+
 // Value operand of one cloud: per problem and 32-key block a [ncols][32] bf16
-// tile, col = part*d + t (the LDS image of the block), and ones in the last
+// tile, col = part*d + t (the LDS image of the block, keys in vkey order), and ones in the last
 // column when it is spare (sumcol).  Padding keys and other columns are zero.
 // One thread per 8 keys of one column.
 __global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, int mode, int in_bf16,
@@ -951,7 +958,7 @@ __global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, i
   u16 v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int j = blk * VK + k0 + e;
+    const int j = blk * VK + vkey(k0, e);
     u16 val = 0;
     if (j < keys && sumcol && c == ncols - 1) {
       val = BF16_ONE;
@@ -1266,10 +1273,7 @@ __global__ __launch_bounds__(64 * bary_NW(NCH, NCT)) __attribute__((amdgpu_waves
       // B operand: lane (column col, group grp) reads the same keys of V.
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const u16* vr = &ldv[buf][(vb * NC + ct * 16 + col) * VROW];
-        const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * grp);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * grp);
-        const u4 vv = u4{v0.x, v0.y, v1.x, v1.y};
+        const u4 vv = *reinterpret_cast<const u4*>(&ldv[buf][(vb * NC + ct * 16 + col) * VROW + 8 * grp]);
 #pragma unroll
         for (int c = 0; c < R; ++c) {
           pv[c][ct] = T::mma(ehi[c], vv, pv[c][ct]);
@@ -1398,7 +1402,8 @@ __host__ __device__ constexpr int apply_tiles(int cb) { return cb <= 5 ? 1 : (cb
 
 // Value operand from columns col0 .. col0+cb-1 of an fp32 matrix M [B][keys][c]:
 // three exact bf16 parts per column (col = part*cb + k) and ones in the last
-// column.  One thread per 8 keys of one column.
+// column, keys in vkey order within each 32-key block.  One thread per 8 keys
+// of one column.
 __global__ __launch_bounds__(256) void k_prep_mat(const float* __restrict__ M, int keys, int keys_pad, int c, int col0,
                                                   int cb, int ncols, u16* __restrict__ vt) {
   const int b = blockIdx.y;
@@ -1411,7 +1416,7 @@ __global__ __launch_bounds__(256) void k_prep_mat(const float* __restrict__ M, i
   u16 v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int j = blk * VK + k0 + e;
+    const int j = blk * VK + vkey(k0, e);
     u16 val = 0;
     if (j < keys && cc == ncols - 1) {
       val = BF16_ONE;
