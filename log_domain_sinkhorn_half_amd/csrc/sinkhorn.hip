@@ -920,16 +920,21 @@ __host__ __device__ constexpr bool val_sumcol(int mode, int d) { return val_part
 __host__ __device__ constexpr int bary_R(int nch, int nct) {
   return nct >= 9 ? 1 : (nch == 1 ? (nct >= 4 ? 2 : 4) : (nch <= 8 ? 2 : 1));
 }
-// Waves per workgroup: operands of 12 or more K chunks take 80-120 KB of LDS per
-// workgroup (one per CU); with at most 4 value tiles, or the 13 of a 64-column
-// plan product, the registers allow two waves per SIMD, so 8 waves share the
-// staged keys (other wide passes spill at two waves per SIMD).
-__host__ __device__ constexpr bool bary_wide8(int nch, int nct, int nu) {
-  return nch >= 12 && (nct <= 4 || (nct == 13 && nu == 0));
+// 8 waves per workgroup share the staged key chunk, halving the key loads and
+// LDS stores per query row.  Measured: plan products -21% at d = 32 (fp32),
+// -8% at d = 128 (bf16); transport -3% at d = 128 (bf16) but +16% at d <= 3,
+// which keeps 4.  Operands of 12 or more K chunks take 80-120 KB of LDS per
+// workgroup (one per CU): there the registers allow two waves per SIMD only with
+// at most 4 value tiles or the 13 of a 64-column plan product (other wide
+// passes spill and keep 4 waves, one per SIMD).
+__host__ __device__ constexpr bool bary_wide8(int mode, int nch, int nct, int nu) {
+  return nu == 0 && (nch >= 12 ? (nct <= 4 || nct == 13) : (nch >= 9 || (mode == MODE_BF16 && nch >= 3)));
 }
-__host__ __device__ constexpr int bary_NW(int nch, int nct, int nu) { return bary_wide8(nch, nct, nu) ? 8 : 4; }
-__host__ __device__ constexpr int bary_waves(int nch, int nct, int nu) {
-  return nch >= 12 ? (bary_wide8(nch, nct, nu) ? 2 : 1) : 2;
+__host__ __device__ constexpr int bary_NW(int mode, int nch, int nct, int nu) {
+  return bary_wide8(mode, nch, nct, nu) ? 8 : 4;
+}
+__host__ __device__ constexpr int bary_waves(int mode, int nch, int nct, int nu) {
+  return nch >= 12 ? (bary_wide8(mode, nch, nct, nu) ? 2 : 1) : 2;
 }
 // 32-key value blocks per LDS chunk of the transport kernel (fewer barriers for small operands)
 __host__ __device__ constexpr int bary_TCB(int nch, int nct) { return (nch <= 2 && nct <= 4) ? 4 : 1; }
@@ -1012,7 +1017,8 @@ __device__ __forceinline__ uint2 split_pair(float a, float b) {
 // the weights become P_ij * u_ij with u_ij = ugain * (key operand . U_i), i.e.
 // u_ij = q_j . v_i, while s_out still sums the plain weights.
 template <int MODE, int NCH, int NCT, bool SUMCOL, bool LAZY = false, int NU = 0>
-__global__ __launch_bounds__(64 * bary_NW(NCH, NCT, NU)) __attribute__((amdgpu_waves_per_eu(bary_waves(NCH, NCT, NU)))) void k_bary(
+__global__ __launch_bounds__(64 * bary_NW(MODE, NCH, NCT, NU))
+    __attribute__((amdgpu_waves_per_eu(bary_waves(MODE, NCH, NCT, NU)))) void k_bary(
     const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb, const u16* __restrict__ V,
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, const float* __restrict__ lse,
     float* __restrict__ pv_out, float* __restrict__ s_out, int rows, int rows_pad, int keys, int keys_pad,
@@ -1028,7 +1034,7 @@ __global__ __launch_bounds__(64 * bary_NW(NCH, NCT, NU)) __attribute__((amdgpu_w
   static_assert(ROW_PAD % CK == 0 && CK <= SLACK, "a key chunk must divide the row padding");
   constexpr int VPR = KP / 8;
   constexpr int NVEC = CK * VPR;
-  constexpr int NW = bary_NW(NCH, NCT, NU), NT = 64 * NW;  // waves, threads per workgroup
+  constexpr int NW = bary_NW(MODE, NCH, NCT, NU), NT = 64 * NW;  // waves, threads per workgroup
   constexpr int NLD = (NVEC + NT - 1) / NT;
   constexpr int NC = NCT * 16;        // value columns
   constexpr int VROW = VK + 8;        // LDS row stride of the value tile (elements)
@@ -2200,7 +2206,7 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
     return SK_EUNSUPPORTED;
   }
   const int nch = L.KP / 32;
-  const int R = bary_R(nch, val_tiles(L.mode, d)), NWb = bary_NW(nch, val_tiles(L.mode, d), 0);
+  const int R = bary_R(nch, val_tiles(L.mode, d)), NWb = bary_NW(L.mode, nch, val_tiles(L.mode, d), 0);
   const int wg_x = (rows + NWb * R * 16 - 1) / (NWb * R * 16);
   const int CKb = bary_TCB(nch, val_tiles(L.mode, d)) * VK;
   const int total_chunks = (keys + CKb - 1) / CKb;
@@ -2289,7 +2295,7 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
     const int R = bary_R(nch, nct);
     const int CKb = bary_TCB(nch, nct) * VK;
     const int total_chunks = (keys + CKb - 1) / CKb;
-    const int NWb = bary_NW(nch, nct, 0);
+    const int NWb = bary_NW(L.mode, nch, nct, 0);
     const int wg_x = (rows + NWb * R * 16 - 1) / (NWb * R * 16);
     const long long nvec = (long long)(keys_pad / VK) * nc * (VK / 8);
     hipLaunchKernelGGL(k_prep_mat, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, M, keys, keys_pad,
@@ -2378,7 +2384,7 @@ sk_status apply_uw(const sk_problem* p, const void* X, const void* Y, char* w, c
     return SK_EUNSUPPORTED;
   }
   const int nch = L.KP / 32;
-  const int R = bary_R(nch, nct), NWb = bary_NW(nch, nct, L.mode == MODE_SPLIT ? 1 : 2);
+  const int R = bary_R(nch, nct), NWb = bary_NW(L.mode, nch, nct, L.mode == MODE_SPLIT ? 1 : 2);
   const int CKb = bary_TCB(nch, nct) * VK;
   const int total_chunks = (keys + CKb - 1) / CKb;
   const int wg_x = (rows + NWb * R * 16 - 1) / (NWb * R * 16);
