@@ -1,6 +1,6 @@
 """rocprofv3 harness for the streaming half-step kernel (k_lse) on one workload.
 
-    python -m log_domain_sinkhorn_half_amd.rocprof_harness --config 3 --out gpurun_out/rp [--write-profiles]
+    python -m log_domain_sinkhorn_half_amd.rocprof_harness --config 3 --out rocprof_out/rp [--write-profiles]
         [--kernel k_bary]
 
 Runs `bench.py` under rocprofv3 in separate passes and summarises, per launch of
@@ -122,7 +122,7 @@ def counters(path_glob: str, kernel: str) -> dict:
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", type=int, default=3)
-    ap.add_argument("--out", default="gpurun_out/rocprof")
+    ap.add_argument("--out", default="rocprof_out")
     ap.add_argument("--steps", type=int, default=5, help="timed steps of the counter passes")
     ap.add_argument("--write-profiles", action="store_true")
     ap.add_argument("--summarize-only", action="store_true", help="reuse the outputs already under --out")
