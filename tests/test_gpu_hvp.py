@@ -71,7 +71,8 @@ def check_apply(p, eps, f, g, side, M, got):
 @pytest.mark.parametrize("n,m,d,dtype,c", [(300, 200, 3, "fp32", 1), (129, 257, 16, "fp32", 5),
                                            (200, 333, 64, "fp32", 21), (150, 140, 4, "fp32", 70),
                                            (100, 90, 128, "bf16", 7), (63, 65, 8, "bf16", 64),
-                                           (40, 50, 88, "fp32", 65), (50, 45, 256, "bf16", 3)])
+                                           (40, 50, 88, "fp32", 65), (50, 45, 256, "bf16", 3),
+                                           (140, 300, 32, "fp32", 1), (90, 120, 40, "fp32", 30)])
 def test_apply_plan(n, m, d, dtype, c):
     p = make_case(n, m, d, seed=17 * n + c, weights="softmax", dtype=dtype, scale=1.0 / np.sqrt(d))
     eps = 0.1
@@ -117,7 +118,8 @@ def run_hvp(p, eps, f, g, V, side, iters=400, tol=1e-7):
 @pytest.mark.parametrize("n,m,d,eps,dtype", [(64, 48, 2, 0.5, "fp32"), (200, 150, 3, 0.1, "fp32"),
                                              (120, 140, 16, 0.2, "fp32"), (100, 90, 32, 0.5, "bf16"),
                                              (90, 110, 64, 0.3, "fp32"), (70, 80, 128, 0.5, "bf16"),
-                                             (60, 75, 88, 0.4, "fp32"), (50, 60, 256, 0.5, "bf16")])
+                                             (60, 75, 88, 0.4, "fp32"), (50, 60, 256, 0.5, "bf16"),
+                                             (80, 100, 32, 0.3, "fp32")])
 def test_hvp_against_oracle(n, m, d, eps, dtype):
     p = make_case(n, m, d, seed=23 * n + d, weights="softmax", dtype=dtype, scale=1.0 / np.sqrt(d))
     f, g = potentials(p, eps, 2000)
