@@ -1,8 +1,9 @@
 /*
  * sinkhorn.h -- C ABI of the MI355X (gfx950) log-domain Sinkhorn half-step library.
  *
- * The method (page "FlashSinkhorn: IO-aware entropic OT on GPU", section
- * "Methodology", part 1, Proposition 1): for squared-Euclidean cost
+ * The method (page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU",
+ * section "Metodologia", part "1. Riformulazione in Forma di Attenzione", Proposizione 1): for
+ * squared-Euclidean cost
  * C_ij = ||x_i - y_j||^2 the stabilised log-domain update
  *
  *     f_i <- -eps * LSE_j [ (g_j - C_ij)/eps + log b_j ]
@@ -10,8 +11,8 @@
  * equals ||x_i||^2 - eps * LSE_j [ (2 x_i.y_j + g_j - ||y_j||^2 + eps log b_j) / eps ],
  * i.e. the row log-sum-exp of a dot-product score matrix plus a per-column bias.
  * The g update is the same operation with the two clouds exchanged.  Each half-step
- * runs as one streaming pass (part 2 of the same section: no n x m matrix in HBM,
- * online max / sum-exp, row-stationary traversal).
+ * runs as one streaming pass (part "2. Kernel di Streaming e Tassellazione" of the
+ * same section: no n x m matrix in HBM, online max / sum-exp, row-stationary traversal).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -38,6 +39,23 @@
  *    sinkhorn_last_error() describes it.  A failed launch returns SK_EHIP.
  *    NaN or inf inside the data is not checked and propagates.
  *  - eps: positive and finite.  Log base is natural everywhere in the outputs.
+ *  - Centring: the squared-Euclidean cost depends only on x_i - y_j, so
+ *    sinkhorn_init_norms moves both clouds of each problem by one common vector c
+ *    (the centre of their joint bounding box, computed in fp64 on the device)
+ *    before any norm or operand is formed.  f and g are unchanged by this (they
+ *    are the potentials of the given points); barycentric projections are
+ *    returned in the given coordinates.  bf16 inputs are centred only when every
+ *    x - c is itself a bf16 value (clouds far from the origin compared with
+ *    their spread); otherwise c = 0.  The cosine cost is never centred.
+ *  - Supported score range: with lambda = log2(e)/eps and R the largest
+ *    |coordinate - c| of the two clouds (1 under the cosine cost), the base-2
+ *    scores lambda*(2 x.y + g_j - |y_j|^2 + eps log b_j) of the centred points
+ *    must stay below 2^22 in magnitude, roughly lambda * 6 d R^2 < 4e6 (for
+ *    eps = 0.01 and d = 3: R up to a few tens).  Beyond it the lazy row offsets
+ *    lose the headroom that keeps the exponentials finite: the kernels then set
+ *    SK_FLAG_SCORE_RANGE in the workspace's status word, and outputs may be
+ *    inaccurate or non-finite.  Any non-finite potential written sets
+ *    SK_FLAG_NONFINITE.  sinkhorn_range_flags reads the word; init clears it.
  */
 #ifndef SINKHORN_MI355X_H
 #define SINKHORN_MI355X_H
@@ -61,6 +79,11 @@ typedef enum {
 
 typedef enum { SK_FP32 = 0, SK_BF16 = 1 } sk_dtype; /* element type of X and Y */
 
+/* Bits of the workspace's status word (an OR over every call since the last
+ * sinkhorn_init_norms on that workspace). */
+#define SK_FLAG_SCORE_RANGE 1u /* a score beyond the supported range (see above) */
+#define SK_FLAG_NONFINITE 2u   /* a potential written as NaN or +-inf */
+
 /* Largest supported point dimension: bf16 inputs up to SK_MAX_D, fp32 inputs up
  * to SK_MAX_D_FP32 (their operands carry seven remainder products per coordinate
  * that must stay in registers).  The transport, plan-product and HVP calls keep
@@ -72,8 +95,9 @@ typedef enum { SK_FP32 = 0, SK_BF16 = 1 } sk_dtype; /* element type of X and Y *
 #define SK_MAX_D_TRANSPORT 256
 
 /* Ground cost.  SK_COST_SQEUCLID: C_ij = ||x_i - y_j||^2 (the pages' cost).
- * SK_COST_COSINE: the cosine distance after normalisation (page "FlashSinkhorn:
- * IO-aware entropic OT on GPU", closing remarks), taken as the squared distance
+ * SK_COST_COSINE: the cosine distance after normalisation (page "FlashSinkhorn: Trasporto Ottimo
+ * Entropico Consapevole delle I/O su GPU", section "Significato e Affermazioni"), taken as the
+ * squared distance
  * between the normalised points, C_ij = ||x_i/|x_i| - y_j/|y_j|||^2
  * = 2 - 2 cos(x_i, y_j); a zero point stays zero (cost 1 to any other point).
  * The cosine cost runs on the split fp32 layout, so d <= SK_MAX_D_FP32 for
@@ -94,7 +118,7 @@ typedef struct {
 size_t sinkhorn_workspace_bytes(const sk_problem* p);
 
 /* Precompute ||x_i||^2, ||y_j||^2, log a_i, log b_j and the kernels' operand
- * layouts of X and Y into ws (the precomputed biases of Proposition 1).
+ * layouts of X and Y into ws (the precomputed log-weight biases of Proposizione 1).
  * X, Y: [batch][n|m][d] of dtype p->dtype; a, b: fp32 weights. */
 sk_status sinkhorn_init_norms(const sk_problem* p, const void* X, const void* Y,
                               const float* a, const float* b, void* ws, size_t ws_bytes,
@@ -112,7 +136,10 @@ sk_status sinkhorn_half_step_f(const sk_problem* p, const void* X, const void* Y
 sk_status sinkhorn_half_step_g(const sk_problem* p, const void* X, const void* Y, void* ws,
                                size_t ws_bytes, const float* f, float eps, float* g, void* stream);
 
-/* Full solve: init_norms, then `iters` iterations of (f half-step, g half-step).
+/* Full solve: init_norms, then `iters` iterations of (f half-step, g half-step): the
+ * repeated Sinkhorn iterations of the problem statement (same page, section
+ * "Enunciato del Problema": entropic OT solved by Sinkhorn iterations, at scale and
+ * repeatedly) with the updates of part "1. Riformulazione in Forma di Attenzione".
  * eps: HOST array of n_eps floats; n_eps == 1 means a constant eps, n_eps == iters
  * means iteration k uses eps[k] for both half-steps (an annealing schedule).
  * f and g are in/out: the f half-step runs first, so only the incoming g matters
@@ -122,7 +149,14 @@ sk_status sinkhorn_solve(const sk_problem* p, const void* X, const void* Y, cons
                          const float* b, const float* eps, int64_t n_eps, int64_t iters,
                          float* f, float* g, void* ws, size_t ws_bytes, void* stream);
 
-/* L1 marginal errors of the plan P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps):
+/* Copy the status word of ws (an OR of SK_FLAG_* over every call since the last
+ * sinkhorn_init_norms on ws) into the DEVICE word *flags, stream-ordered (no
+ * synchronisation).  A diagnostic of this library, not an operation of the pages. */
+sk_status sinkhorn_range_flags(const sk_problem* p, const void* ws, size_t ws_bytes, uint32_t* flags,
+                               void* stream);
+
+/* L1 marginal errors of the plan P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps).  Not an
+ * operation of the pages: a requested convergence diagnostic of this library's API.
  * err[2*k]   = sum_i | sum_j P_ij - a_i |   (rows of problem k)
  * err[2*k+1] = sum_j | sum_i P_ij - b_j |   (columns of problem k)
  * computed without forming P (row sums are a_i exp((f_i - T_f(g)_i)/eps)).
@@ -132,8 +166,8 @@ sk_status sinkhorn_marginal_error(const sk_problem* p, const void* X, const void
                                   float* err, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Transport application (page "FlashSinkhorn: IO-aware entropic OT on GPU",
- * section "Differentiation and second-order optimisation": the barycentric
+ * Transport application (page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU",
+ * section "Metodologia", part "3. Differenziazione e Ottimizzazione del Secondo Ordine": the barycentric
  * projection and the gradient are weighted averages over the transport plan,
  * computed by the same streaming pass without forming the plan).
  *
@@ -170,9 +204,9 @@ sk_status sinkhorn_barycentric_y(const sk_problem* p, const void* X, const void*
                                  float* bary, float* grad, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Plan application: vector- and matrix-transport products (page "FlashSinkhorn:
- * IO-aware entropic OT on GPU", section "Differentiation and second-order
- * optimisation"), streamed like the transport calls, the plan never formed:
+ * Plan application: vector- and matrix-transport products (page "FlashSinkhorn: Trasporto Ottimo
+ * Entropico Consapevole delle I/O su GPU", section "Metodologia", part "3. Differenziazione e
+ * Ottimizzazione del Secondo Ordine"), streamed like the transport calls, the plan never formed:
  *   sinkhorn_apply_plan_x:  out[b][i][k] = sum_j P_ij V[b][j][k]   V [batch][m][c] -> out [batch][n][c]
  *   sinkhorn_apply_plan_y:  out[b][j][k] = sum_i P_ij U[b][i][k]   U [batch][n][c] -> out [batch][m][c]
  * fp32 DEVICE arrays; c >= 1 columns (processed in passes of 64).  Each value is

@@ -29,7 +29,9 @@ EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_init_norms", "sinkhorn_half_ste
            "sinkhorn_half_step_g", "sinkhorn_solve", "sinkhorn_marginal_error",
            "sinkhorn_transport_workspace_bytes", "sinkhorn_barycentric_x", "sinkhorn_barycentric_y",
            "sinkhorn_apply_plan_x", "sinkhorn_apply_plan_y", "sinkhorn_hvp_workspace_bytes",
-           "sinkhorn_hvp_x", "sinkhorn_hvp_y", "sinkhorn_last_error")
+           "sinkhorn_hvp_x", "sinkhorn_hvp_y", "sinkhorn_last_error",
+           "sinkhorn_range_flags")
+SK_FLAG_SCORE_RANGE, SK_FLAG_NONFINITE = 1, 2  # bits of the workspace's status word
 
 
 class SkProblem(ctypes.Structure):
@@ -88,6 +90,8 @@ def load_library(path: Optional[str] = None):
         fn.argtypes = [P, vp, vp, vp, sz, f32p, f32p, ctypes.c_float, f32p, ctypes.c_int64, ctypes.c_float,
                        f32p, vp]
         fn.restype = ctypes.c_int
+    lib.sinkhorn_range_flags.argtypes = [P, vp, sz, vp, vp]
+    lib.sinkhorn_range_flags.restype = ctypes.c_int
     lib.sinkhorn_last_error.argtypes = []
     lib.sinkhorn_last_error.restype = ctypes.c_char_p
     if path is None:
@@ -99,6 +103,12 @@ def _check(status: int):
     if status != 0:
         msg = load_library().sinkhorn_last_error().decode(errors="replace")
         raise SinkhornError(status, msg)
+
+
+def _call(name: str, *args) -> None:
+    """Call one entry point of the library; the arguments (and so every check
+    made while marshalling them) are evaluated before the library is loaded."""
+    _check(getattr(load_library(), name)(*args))
 
 
 def _as3(t: torch.Tensor) -> torch.Tensor:
@@ -129,8 +139,27 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
     return t.data_ptr()
 
 
-def _stream() -> int:
-    return torch.cuda.current_stream().cuda_stream
+def _shape(t: Optional[torch.Tensor], name: str, shape) -> None:
+    """Raise ValueError unless t has `shape` ([B, ...]; a single problem may also
+    drop the leading 1).  The kernels index every array by (batch, n, m, d, c),
+    so a wrongly sized tensor would be read or written out of bounds."""
+    if t is None:
+        return
+    got = tuple(t.shape)
+    want = tuple(int(v) for v in shape)
+    if got != want and not (want[0] == 1 and got == want[1:]):
+        raise ValueError(f"{name} has shape {got}, expected {want}")
+
+
+def _same_device(X: torch.Tensor, *named) -> None:
+    for name, t in named:
+        if t is not None and t.device != X.device:
+            raise ValueError(f"{name} is on {t.device}, but X is on {X.device}")
+
+
+def _stream(X: torch.Tensor) -> int:
+    """The current HIP stream of X's device (the library launches there)."""
+    return torch.cuda.current_stream(X.device).cuda_stream
 
 
 def workspace_bytes(batch: int, n: int, m: int, d: int, dtype: int = SK_FP32, cost: int = SK_SQEUCLID) -> int:
@@ -157,28 +186,37 @@ def alloc_workspace(X: torch.Tensor, Y: torch.Tensor, transport: bool = False, c
 
 def init_norms(X, Y, a, b, ws, cost: int = SK_SQEUCLID):
     p = problem_of(X, Y, cost)
-    _check(load_library().sinkhorn_init_norms(
+    _shape(a, "a", (p.batch, p.n))
+    _shape(b, "b", (p.batch, p.m))
+    _same_device(X, ("Y", Y), ("a", a), ("b", b), ("ws", ws))
+    _call("sinkhorn_init_norms",
         ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(a, "a", torch.float32),
-        _dev(b, "b", torch.float32), _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream()))
+        _dev(b, "b", torch.float32), _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream(X))
 
 
 def half_step_f(X, Y, ws, g, eps: float, f: Optional[torch.Tensor] = None, cost: int = SK_SQEUCLID) -> torch.Tensor:
     p = problem_of(X, Y, cost)
+    _shape(g, "g", (p.batch, p.m))
+    _shape(f, "f", (p.batch, p.n))
+    _same_device(X, ("Y", Y), ("ws", ws), ("g", g), ("f", f))
     if f is None:
         f = torch.empty((p.batch, p.n), dtype=torch.float32, device=X.device)
-    _check(load_library().sinkhorn_half_step_f(
+    _call("sinkhorn_half_step_f",
         ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(ws, "ws"), ws.numel() * ws.element_size(),
-        _dev(g, "g", torch.float32), float(eps), _dev(f, "f", torch.float32), _stream()))
+        _dev(g, "g", torch.float32), float(eps), _dev(f, "f", torch.float32), _stream(X))
     return f
 
 
 def half_step_g(X, Y, ws, f, eps: float, g: Optional[torch.Tensor] = None, cost: int = SK_SQEUCLID) -> torch.Tensor:
     p = problem_of(X, Y, cost)
+    _shape(f, "f", (p.batch, p.n))
+    _shape(g, "g", (p.batch, p.m))
+    _same_device(X, ("Y", Y), ("ws", ws), ("f", f), ("g", g))
     if g is None:
         g = torch.empty((p.batch, p.m), dtype=torch.float32, device=X.device)
-    _check(load_library().sinkhorn_half_step_g(
+    _call("sinkhorn_half_step_g",
         ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(ws, "ws"), ws.numel() * ws.element_size(),
-        _dev(f, "f", torch.float32), float(eps), _dev(g, "g", torch.float32), _stream()))
+        _dev(f, "f", torch.float32), float(eps), _dev(g, "g", torch.float32), _stream(X))
     return g
 
 
@@ -186,6 +224,10 @@ def solve(X, Y, a, b, eps: Union[float, Sequence[float]], iters: int, f=None, g=
           cost: int = SK_SQEUCLID):
     """Run sinkhorn_solve; f and g are in/out (zeros if not given).  Returns (f, g)."""
     p = problem_of(X, Y, cost)
+    for name, t, shp in (("a", a, (p.batch, p.n)), ("b", b, (p.batch, p.m)), ("f", f, (p.batch, p.n)),
+                         ("g", g, (p.batch, p.m))):
+        _shape(t, name, shp)
+    _same_device(X, ("Y", Y), ("a", a), ("b", b), ("f", f), ("g", g), ("ws", ws))
     if f is None:
         f = torch.zeros((p.batch, p.n), dtype=torch.float32, device=X.device)
     if g is None:
@@ -194,36 +236,56 @@ def solve(X, Y, a, b, eps: Union[float, Sequence[float]], iters: int, f=None, g=
         ws = alloc_workspace(X, Y, cost=cost)
     e = [float(eps)] if isinstance(eps, (int, float)) else [float(v) for v in eps]
     earr = (ctypes.c_float * len(e))(*e)
-    _check(load_library().sinkhorn_solve(
+    _call("sinkhorn_solve",
         ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(a, "a", torch.float32), _dev(b, "b", torch.float32),
         earr, len(e), int(iters), _dev(f, "f", torch.float32), _dev(g, "g", torch.float32), _dev(ws, "ws"),
-        ws.numel() * ws.element_size(), _stream()))
+        ws.numel() * ws.element_size(), _stream(X))
     return f, g
+
+
+def range_flags(X, Y, ws, cost: int = SK_SQEUCLID) -> int:
+    """Status word of ws (SK_FLAG_* bits set since the last init_norms); synchronises
+    the current stream to read it."""
+    p = problem_of(X, Y, cost)
+    _same_device(X, ("ws", ws))
+    out = torch.zeros(1, dtype=torch.int32, device=X.device)
+    _call("sinkhorn_range_flags", ctypes.byref(p), _dev(ws, "ws"), ws.numel() * ws.element_size(),
+          _dev(out, "flags", torch.int32), _stream(X))
+    return int(out.item())
 
 
 def marginal_error(X, Y, ws, f, g, eps: float, err: Optional[torch.Tensor] = None,
                    cost: int = SK_SQEUCLID) -> torch.Tensor:
     p = problem_of(X, Y, cost)
+    _shape(f, "f", (p.batch, p.n))
+    _shape(g, "g", (p.batch, p.m))
+    _shape(err, "err", (p.batch, 2))
+    _same_device(X, ("Y", Y), ("ws", ws), ("f", f), ("g", g), ("err", err))
     if err is None:
         err = torch.empty((p.batch, 2), dtype=torch.float32, device=X.device)
-    _check(load_library().sinkhorn_marginal_error(
+    _call("sinkhorn_marginal_error",
         ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(ws, "ws"), ws.numel() * ws.element_size(),
         _dev(f, "f", torch.float32), _dev(g, "g", torch.float32), float(eps), _dev(err, "err", torch.float32),
-        _stream()))
+        _stream(X))
     return err
 
 
 def _barycentric(name, X, Y, ws, f, g, eps, rows, bary, grad, with_grad, cost):
     p = problem_of(X, Y, cost)
     shape = (p.batch, rows(p), p.d)
+    _shape(f, "f", (p.batch, p.n))
+    _shape(g, "g", (p.batch, p.m))
+    _shape(bary, "bary", shape)
+    _shape(grad, "grad", shape)
+    _same_device(X, ("Y", Y), ("ws", ws), ("f", f), ("g", g), ("bary", bary), ("grad", grad))
     if bary is None:
         bary = torch.empty(shape, dtype=torch.float32, device=X.device)
     if grad is None and with_grad:
         grad = torch.empty(shape, dtype=torch.float32, device=X.device)
-    _check(getattr(load_library(), name)(
+    _call(name,
         ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(ws, "ws"), ws.numel() * ws.element_size(),
         _dev(f, "f", torch.float32), _dev(g, "g", torch.float32), float(eps), _dev(bary, "bary", torch.float32),
-        None if grad is None else _dev(grad, "grad", torch.float32), _stream()))
+        None if grad is None else _dev(grad, "grad", torch.float32), _stream(X))
     return bary, grad
 
 
@@ -241,47 +303,59 @@ def barycentric_y(X, Y, ws, f, g, eps: float, bary=None, grad=None, with_grad: b
     return _barycentric("sinkhorn_barycentric_y", X, Y, ws, f, g, eps, lambda p: p.m, bary, grad, with_grad, cost)
 
 
-def _apply(name, X, Y, ws, f, g, eps, M, rows, out, cost):
+def _apply(name, X, Y, ws, f, g, eps, M, keys, rows, out, cost):
     p = problem_of(X, Y, cost)
     squeeze = M.dim() == 2
     M3 = M.unsqueeze(-1) if squeeze else M
     c = M3.shape[-1]
+    _shape(f, "f", (p.batch, p.n))
+    _shape(g, "g", (p.batch, p.m))
+    _shape(M3, "matrix", (p.batch, keys(p), c))
+    _shape(out, "out", (p.batch, rows(p), c) if not squeeze else (p.batch, rows(p)))
+    _same_device(X, ("Y", Y), ("ws", ws), ("f", f), ("g", g), ("matrix", M), ("out", out))
+    if out is not None and squeeze:
+        out = out.reshape(p.batch, rows(p), 1)
     if out is None:
         out = torch.empty((p.batch, rows(p), c), dtype=torch.float32, device=X.device)
-    _check(getattr(load_library(), name)(
+    _call(name,
         ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(ws, "ws"), ws.numel() * ws.element_size(),
         _dev(f, "f", torch.float32), _dev(g, "g", torch.float32), float(eps), _dev(M3, "matrix", torch.float32),
-        int(c), _dev(out, "out", torch.float32), _stream()))
+        int(c), _dev(out, "out", torch.float32), _stream(X))
     return out.squeeze(-1) if squeeze else out
 
 
 def apply_plan_x(X, Y, ws, f, g, eps: float, V, out=None, cost: int = SK_SQEUCLID):
     """(P V)_i = sum_j P_ij V_j for V [B, m, c] (or [B, m]); ws from alloc_workspace(..., transport=True)."""
-    return _apply("sinkhorn_apply_plan_x", X, Y, ws, f, g, eps, V, lambda p: p.n, out, cost)
+    return _apply("sinkhorn_apply_plan_x", X, Y, ws, f, g, eps, V, lambda p: p.m, lambda p: p.n, out, cost)
 
 
 def apply_plan_y(X, Y, ws, f, g, eps: float, U, out=None, cost: int = SK_SQEUCLID):
     """(P^T U)_j = sum_i P_ij U_i for U [B, n, c] (or [B, n])."""
-    return _apply("sinkhorn_apply_plan_y", X, Y, ws, f, g, eps, U, lambda p: p.m, out, cost)
+    return _apply("sinkhorn_apply_plan_y", X, Y, ws, f, g, eps, U, lambda p: p.n, lambda p: p.m, out, cost)
 
 
-def _hvp(name, X, Y, ws, f, g, eps, V, cg_iters, cg_tol, out):
+def _hvp(name, X, Y, ws, f, g, eps, V, cg_iters, cg_tol, out, rows):
     p = problem_of(X, Y)
+    _shape(f, "f", (p.batch, p.n))
+    _shape(g, "g", (p.batch, p.m))
+    _shape(V, "V", (p.batch, rows(p), p.d))
+    _shape(out, "out", (p.batch, rows(p), p.d))
+    _same_device(X, ("Y", Y), ("ws", ws), ("f", f), ("g", g), ("V", V), ("out", out))
     if out is None:
         out = torch.empty_like(V, dtype=torch.float32)
-    _check(getattr(load_library(), name)(
+    _call(name,
         ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(ws, "ws"), ws.numel() * ws.element_size(),
         _dev(f, "f", torch.float32), _dev(g, "g", torch.float32), float(eps), _dev(V, "V", torch.float32),
-        int(cg_iters), float(cg_tol), _dev(out, "out", torch.float32), _stream()))
+        int(cg_iters), float(cg_tol), _dev(out, "out", torch.float32), _stream(X))
     return out
 
 
 def hvp_x(X, Y, ws, f, g, eps: float, V, cg_iters: int = 200, cg_tol: float = 1e-6, out=None):
     """Hessian of the entropic OT value in X applied to V [B, n, d], at optimal (f, g).
     ws from alloc_workspace(..., hvp=True)."""
-    return _hvp("sinkhorn_hvp_x", X, Y, ws, f, g, eps, V, cg_iters, cg_tol, out)
+    return _hvp("sinkhorn_hvp_x", X, Y, ws, f, g, eps, V, cg_iters, cg_tol, out, lambda p: p.n)
 
 
 def hvp_y(X, Y, ws, f, g, eps: float, V, cg_iters: int = 200, cg_tol: float = 1e-6, out=None):
     """Hessian of the entropic OT value in Y applied to V [B, m, d], at optimal (f, g)."""
-    return _hvp("sinkhorn_hvp_y", X, Y, ws, f, g, eps, V, cg_iters, cg_tol, out)
+    return _hvp("sinkhorn_hvp_y", X, Y, ws, f, g, eps, V, cg_iters, cg_tol, out, lambda p: p.m)

@@ -1,13 +1,14 @@
 // Log-domain Sinkhorn half-steps for squared-Euclidean cost on MI355X (gfx950).
 //
-// Method: page "FlashSinkhorn: IO-aware entropic OT on GPU", section
-// "Methodology".  Part 1 (Proposition 1) rewrites the stabilised update
+// Method: page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU", section
+// "Metodologia".  Part "1. Riformulazione in Forma di Attenzione" (Proposizione 1) rewrites the
+// stabilised update
 //   f_i <- -eps LSE_j[(g_j - C_ij)/eps + log b_j],  C_ij = ||x_i - y_j||^2
 // as f_i = ||x_i||^2 - eps * LSE_j[(2 x_i.y_j + beta_j)/eps] with the per-column
 // bias beta_j = g_j - ||y_j||^2 + eps log b_j: a dot-product score matrix with a
-// bias, reduced by a row log-sum-exp.  Part 2 streams it: query tiles stay on
-// chip (row-stationary), key tiles stream past them, the LSE is accumulated
-// online and the n x m scores never reach HBM.  The g update is the same
+// bias, reduced by a row log-sum-exp.  Part "2. Kernel di Streaming e Tassellazione"
+// streams it: query tiles stay on chip (row-stationary), key tiles stream past
+// them, the LSE is accumulated online and the n x m scores never reach HBM.  The g update is the same
 // kernel with the clouds exchanged.
 //
 // MI355X design (not the pages' Triton/A100 design):
@@ -41,8 +42,8 @@
 //    256 CUs; the partial (max, sum) pairs are merged by a small kernel.
 //  * Norms, log-weights, the bias and the final potential are formed in fp64.
 //
-// Beyond the half-step (same page, section "Differentiation and second-order
-// optimisation"; and the closing remarks on costs):
+// Beyond the half-step (same page, section "Metodologia", part "3. Differenziazione e
+// Ottimizzazione del Secondo Ordine"; and the section "Significato e Affermazioni" on costs):
 //  * transport application: barycentric projection and gradient in one P.V
 //    pass over the score tiles with lazy row offsets, and the plan applied to
 //    any matrix with offsets fixed by the potentials (k_bary);
@@ -189,40 +190,136 @@ __device__ __forceinline__ float coord(const void* P, size_t k, int in_bf16) {
 // ---------------------------------------------------------------------------
 // Set-up kernels
 // ---------------------------------------------------------------------------
-// Largest |coordinate| of each problem's X (side 0) and Y (side 1): a strided
-// block reduction, then atomicMax on the float bits (values are >= 0, so the
-// unsigned order is the float order).  maxabs must be zero beforehand.
-__global__ __launch_bounds__(256) void k_maxabs(const void* __restrict__ X, const void* __restrict__ Y, int in_bf16,
-                                                long long nx, long long ny, unsigned* __restrict__ maxabs,
-                                                int batch) {
-  __shared__ float red[256];
-  const int b = blockIdx.y, side = blockIdx.z;
-  const long long cnt = side == 0 ? nx : ny;
+// Centring.  The squared-Euclidean cost only depends on differences x_i - y_j,
+// so both clouds of a problem are moved by one common vector c (the centre of
+// their joint bounding box) before anything else is formed: the potentials do
+// not change, while the norms and the dot-product scores shrink from the size
+// of |x| to the size of the clouds' spread.  The cosine cost is not
+// translation-invariant and keeps c = 0.
+//
+// Order-preserving unsigned code of a float, so that atomicMin / atomicMax on
+// codes give the minimum / maximum of the values in any order (deterministic).
+__device__ __forceinline__ unsigned ordered_code(float v) {
+  const unsigned u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ordered_value(unsigned c) {
+  return __uint_as_float((c & 0x80000000u) ? (c & 0x7FFFFFFFu) : ~c);
+}
+
+// Per (problem, side, coordinate) bounding box of the clouds: box[(b*2+side)*2d + t]
+// is the code of the minimum of coordinate t, box[... + d + t] of the maximum.
+// The slots start at 0xFFFFFFFF (minima) and 0 (maxima).  grid: (point chunks,
+// blocks of 64 coordinates, 2*batch); the 4 waves of a block take every fourth point.
+__global__ __launch_bounds__(256) void k_bbox(const void* __restrict__ X, const void* __restrict__ Y, int in_bf16,
+                                              int n, int m, int d, unsigned* __restrict__ box) {
+  __shared__ float rlo[256], rhi[256];
+  const int side = blockIdx.z & 1, b = blockIdx.z >> 1;
+  const int rows = side == 0 ? n : m;
   const void* P = side == 0 ? X : Y;
-  float mx = 0.f;
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < cnt; i += (long long)gridDim.x * 256) {
-    const long long k = (long long)b * cnt + i;
-    mx = fmaxf(mx, fabsf(coord(P, (size_t)k, in_bf16)));
+  const int t = blockIdx.y * 64 + (threadIdx.x & 63);
+  float lo = INFINITY, hi = -INFINITY;
+  if (t < d)
+    for (long long i = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); i < rows; i += (long long)gridDim.x * 4) {
+      const float v = coord(P, ((size_t)b * rows + i) * d + t, in_bf16);
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+    }
+  rlo[threadIdx.x] = lo;
+  rhi[threadIdx.x] = hi;
+  __syncthreads();
+  if (threadIdx.x < 64 && t < d) {
+    for (int k = 1; k < 4; ++k) {
+      lo = fminf(lo, rlo[threadIdx.x + 64 * k]);
+      hi = fmaxf(hi, rhi[threadIdx.x + 64 * k]);
+    }
+    unsigned* bx = box + (size_t)(b * 2 + side) * 2 * d;
+    atomicMin(&bx[t], ordered_code(lo));
+    atomicMax(&bx[d + t], ordered_code(hi));
   }
-  red[threadIdx.x] = mx;
+}
+
+// Centre c of each problem (fp64 [batch][d]) from the two boxes, and the largest
+// |coordinate - c| of each side (maxabs[side*batch + b], rounded up to a float;
+// it sizes the grid quantum of the split operand layout).  bf16 inputs take a
+// bf16 centre, so that x - c can be exact in bf16.  One workgroup per problem.
+__global__ __launch_bounds__(256) void k_centre(const unsigned* __restrict__ box, int d, int batch, int in_bf16,
+                                                int centre, double* __restrict__ cen, float* __restrict__ maxabs) {
+  __shared__ double red[2][256];
+  const int b = blockIdx.x;
+  const unsigned* bx = box + (size_t)b * 4 * d;  // side 0: [0, 2d), side 1: [2d, 4d)
+  double mx0 = 0.0, mx1 = 0.0;
+  for (int t = threadIdx.x; t < d; t += 256) {
+    const double lo0 = ordered_value(bx[t]), hi0 = ordered_value(bx[d + t]);
+    const double lo1 = ordered_value(bx[2 * d + t]), hi1 = ordered_value(bx[3 * d + t]);
+    double c = 0.0;
+    if (centre) {
+      c = 0.5 * (fmin(lo0, lo1) + fmax(hi0, hi1));  // exact: a sum of two floats, halved
+      if (!isfinite(c)) c = 0.0;
+      if (in_bf16) c = (double)bf16_f(bf16_rne((float)c));
+    }
+    cen[(size_t)b * d + t] = c;
+    mx0 = fmax(mx0, fmax(fabs(hi0 - c), fabs(lo0 - c)));
+    mx1 = fmax(mx1, fmax(fabs(hi1 - c), fabs(lo1 - c)));
+  }
+  red[0][threadIdx.x] = mx0;
+  red[1][threadIdx.x] = mx1;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    if ((int)threadIdx.x < w) {
+      red[0][threadIdx.x] = fmax(red[0][threadIdx.x], red[0][threadIdx.x + w]);
+      red[1][threadIdx.x] = fmax(red[1][threadIdx.x], red[1][threadIdx.x + w]);
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) atomicMax(&maxabs[side * batch + b], __float_as_uint(red[0]));
+  if (threadIdx.x == 0) {
+    maxabs[b] = __double2float_ru(red[0][0]);
+    maxabs[batch + b] = __double2float_ru(red[1][0]);
+  }
+}
+
+// bf16 inputs keep their values in the operands, so a problem is centred only if
+// every x - c of both clouds is a bf16 value itself (true for clouds far from the
+// origin compared with their spread, where centring matters).  Sets inexact[b]
+// otherwise.  grid: (element chunks, batch, 2 sides).
+__global__ __launch_bounds__(256) void k_bf16_exact(const u16* __restrict__ X, const u16* __restrict__ Y,
+                                                    long long nx, long long ny, int d,
+                                                    const double* __restrict__ cen, unsigned* __restrict__ inexact) {
+  const int b = blockIdx.y, side = blockIdx.z;
+  const long long cnt = side == 0 ? nx : ny;
+  const u16* P = (side == 0 ? X : Y) + (size_t)b * cnt;
+  bool bad = false;
+  for (long long k = (long long)blockIdx.x * 256 + threadIdx.x; k < cnt; k += (long long)gridDim.x * 256) {
+    const double v = (double)bf16_f(P[k]) - cen[(size_t)b * d + k % d];
+    bad |= (double)bf16_f(bf16_rne((float)v)) != v;
+  }
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(&inexact[b], 1u);
+}
+
+// Problems whose differences are not all bf16 values keep c = 0.
+__global__ __launch_bounds__(256) void k_cen_fix(const unsigned* __restrict__ inexact, int d, double* __restrict__ cen) {
+  const int b = blockIdx.x;
+  if (inexact[b] == 0u) return;
+  for (int t = threadIdx.x; t < d; t += 256) cen[(size_t)b * d + t] = 0.0;
+}
+
+// Coordinate t of point r (row index over all problems) of a cloud, minus the centre.
+__device__ __forceinline__ double ccoord(const void* P, size_t r, int t, int d, int in_bf16,
+                                         const double* __restrict__ cen, int b) {
+  return (double)coord(P, r * d + t, in_bf16) - cen[(size_t)b * d + t];
 }
 
 // Norms (fp64), log-weights (fp64), inverse norms and operand rows of one
-// cloud: the split query layout (fp32 inputs, or any input under the cosine
-// cost, whose points are first divided by their norm) or a zero-padded bf16
-// copy (bf16 inputs, squared-Euclidean cost).
+// cloud, from the centred points x - c: the split query layout (fp32 inputs, or
+// any input under the cosine cost, whose points are first divided by their norm
+// and not centred) or a zero-padded bf16 copy (bf16 inputs, squared-Euclidean
+// cost; x - c is a bf16 value there).
 template <int MODE>
 __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, const float* __restrict__ w,
                                                    int rows, int rows_pad, int d, int KP, int in_bf16, int cosine,
-                                                   const float* __restrict__ maxabs, double* __restrict__ norm,
-                                                   double* __restrict__ logw, double* __restrict__ rnorm,
-                                                   u16* __restrict__ opnd) {
+                                                   const float* __restrict__ maxabs, const double* __restrict__ cen,
+                                                   double* __restrict__ norm, double* __restrict__ logw,
+                                                   double* __restrict__ rnorm, u16* __restrict__ opnd) {
   const int b = blockIdx.y;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= rows_pad) return;
@@ -232,18 +329,20 @@ __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, c
     return;
   }
   const size_t r = (size_t)b * rows + i;
+  const double* cb_ = cen + (size_t)b * d;
   if (MODE == MODE_BF16) {
     const u16* src = static_cast<const u16*>(P) + r * d;
+    auto cv = [&](int t) -> u16 { return bf16_rne((float)((double)bf16_f(src[t]) - cb_[t])); };
     double nrm = 0.0;
     for (int t = 0; t < d; ++t) {
-      const double v = bf16_f(src[t]);
+      const double v = bf16_f(cv(t));
       nrm += v * v;
     }
     norm[r] = nrm;
     rnorm[r] = 1.0;
     logw[r] = log((double)w[r]);
     for (int k = 0; k < KP; k += 2) {
-      const uint32_t lo = (k < d) ? src[k] : 0, hi = (k + 1 < d) ? src[k + 1] : 0;
+      const uint32_t lo = (k < d) ? cv(k) : 0, hi = (k + 1 < d) ? cv(k + 1) : 0;
       *reinterpret_cast<uint32_t*>(dst + k) = lo | (hi << 16);
     }
     return;
@@ -259,7 +358,7 @@ __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, c
     }
     rn = raw > 0.0 ? 1.0 / sqrt(raw) : 0.0;  // a zero point stays zero
   }
-  auto val = [&](int t) { return (double)coord(P, r * d + t, in_bf16) * rn; };
+  auto val = [&](int t) { return (double)coord(P, r * d + t, in_bf16) * rn - cb_[t]; };
   double nrm = 0.0;
   for (int t = 0; t < d; ++t) nrm += val(t) * val(t);
   norm[r] = nrm;
@@ -289,20 +388,14 @@ __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, c
   }
 }
 
-// Grid and remainder parts of v = l2*y*rn (l2 = 2*lambda) for the key operand,
-// in fp32: v is carried as vh + vl, exactly when rn == 1 (the product of two
-// fp32 numbers and its fma error term), so the remainder takes one fp32
-// rounding, as in the fp64 split.  q = 2^k and iq = 1/q must be normal floats.
-__device__ __forceinline__ Parts key_split(float y, double rn, float l2, float q, float iq) {
-  float vh, vl;
-  if (rn == 1.0) {
-    vh = l2 * y;
-    vl = fmaf(l2, y, -vh);
-  } else {
-    const double v = (double)l2 * (double)y * rn;
-    vh = (float)v;
-    vl = (float)(v - (double)vh);
-  }
+// Grid and remainder parts of v = l2*yc (l2 = 2*lambda, yc the centred or
+// normalised coordinate, exact in fp64) for the key operand: v is formed in fp64
+// and carried as vh + vl (two floats), so the remainder takes one fp32 rounding,
+// as in the fp64 split.  q = 2^k and iq = 1/q must be normal floats.
+__device__ __forceinline__ Parts key_split(double yc, float l2, float q, float iq) {
+  const double v = (double)l2 * yc;
+  const float vh = (float)v;
+  const float vl = (float)(v - (double)vh);
   const float g = rintf(vh * iq) * q;
   const float r = (vh - g) + vl;  // vh - g is exact: both are multiples of ulp(vh)
   Parts p;
@@ -351,7 +444,8 @@ __device__ __forceinline__ void bias_parts(bool real, size_t r, const float* __r
 // a clear written during this launch cannot change any thread's decision, since
 // neither the old tag nor 0 equals lam.
 __global__ __launch_bounds__(256) void k_prep_keys(const void* __restrict__ P, int in_bf16,
-                                                   const double* __restrict__ rnorm, const float* __restrict__ pot,
+                                                   const double* __restrict__ rnorm, const double* __restrict__ cen,
+                                                   const float* __restrict__ pot,
                                                    const double* __restrict__ norm, const double* __restrict__ logw,
                                                    int keys, int keys_pad, int d, int KP, float lam, float eps,
                                                    const float* __restrict__ qmax, const float* __restrict__ kmax,
@@ -397,8 +491,8 @@ __global__ __launch_bounds__(256) void k_prep_keys(const void* __restrict__ P, i
     const size_t r = (size_t)b * keys + j;
     const double rn = real ? rnorm[r] : 1.0;
     auto split = [&](int t) {
-      const float y = coord(P, r * d + t, in_bf16);
-      return f32 ? key_split(y, rn, l2f, qkf, iqkf) : grid_split(lam2 * (double)y * rn, qk, iqk);
+      const double yc = (double)coord(P, r * d + t, in_bf16) * rn - cen[(size_t)b * d + t];
+      return f32 ? key_split(yc, l2f, qkf, iqkf) : grid_split(lam2 * yc, qk, iqk);
     };
     u16 bp[5] = {0, 0, 0, 0, 0};
     if (seg == 0 || seg == sb1 || seg == sb2) bias_parts(real, r, pot, norm, logw, lam, eps, Q, iQ, bp);
@@ -460,6 +554,26 @@ __global__ __launch_bounds__(256) void k_zero(u4* __restrict__ p, size_t n) {
     p[i] = u4{0, 0, 0, 0};
 }
 
+// Copy of the status word to a caller's device word.
+__global__ void k_copy_u32(const unsigned* __restrict__ src, unsigned* __restrict__ dst) {
+  if (threadIdx.x == 0) *dst = *src;
+}
+
+// Start values of the set-up words: bounding-box slots (minima 0xFFFFFFFF, maxima
+// 0, see k_bbox), the bf16 centring flags, the status word and the four lambda tags.
+__global__ __launch_bounds__(256) void k_init_words(unsigned* __restrict__ box, int d, int batch,
+                                                    unsigned* __restrict__ inexact, unsigned* __restrict__ status,
+                                                    unsigned* __restrict__ tags) {
+  const long long n = 4LL * batch * d;
+  const long long i0 = (long long)blockIdx.x * blockDim.x + threadIdx.x, st = (long long)gridDim.x * blockDim.x;
+  for (long long i = i0; i < n; i += st) box[i] = ((i / d) % 2 == 0) ? 0xFFFFFFFFu : 0u;
+  for (long long i = i0; i < batch; i += st) inexact[i] = 0u;
+  if (i0 == 0) {
+    status[0] = 0u;
+    for (int k = 0; k < 4; ++k) tags[k] = 0u;
+  }
+}
+
 // Half bias (pot - norm + eps*logw)/2 per key (bf16 inputs); padding -> -1e30.
 __global__ __launch_bounds__(256) void k_prep_bias(const float* __restrict__ pot, const double* __restrict__ norm,
                                                    const double* __restrict__ logw, int keys, int keys_pad,
@@ -519,13 +633,24 @@ __device__ __forceinline__ void set_offset(u4& q, float off, bool owner) {
 }
 
 // New offset from a chunk maximum: an integer that two bf16 parts hold exactly
-// and, on the fp32 path, a multiple of the grid quantum Q.
-__device__ __forceinline__ float offset_from_max(float mx, float Q) {
+// and, on the fp32 path, a multiple of the grid quantum Q.  Two bf16 parts hold
+// 16 significant bits, so past 2^21 the quantum grows; once it exceeds the
+// headroom the exponents are no longer safe from overflow and flush, and
+// `coarse` is set (scores beyond the supported range of 2^22 base-2 units).
+__device__ __forceinline__ float offset_from_max(float mx, float Q, bool& coarse) {
   float mq = floorf(mx);
   if (!(fabsf(mq) < 1e30f)) return mq;
   float quantum = fmaxf(Q, 1.f);
   if (fabsf(mq) >= 65536.f) quantum = fmaxf(quantum, ldexpf(1.f, ilogbf(mq) - 15));
+  coarse |= quantum > HEADROOM;
   return floorf(mq / quantum) * quantum;
+}
+
+// Bits of the status word in the workspace (an OR over every launch since the
+// last init): the header's SK_FLAG_SCORE_RANGE and SK_FLAG_NONFINITE.
+constexpr unsigned FLAG_SCORE_RANGE = 1u, FLAG_NONFINITE = 2u;
+__device__ __forceinline__ void flag_if(unsigned* status, bool cond, unsigned bit) {
+  if (cond && status != nullptr) atomicOr(status, bit);
 }
 
 // Launch shape per (path, K chunks of 32 slots): tile width MW, query tiles per
@@ -594,7 +719,7 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
     const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb,
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, float* __restrict__ out,
     float2* __restrict__ part, int rows, int rows_pad, int keys, int keys_pad, int chunks_per_split, int batch,
-    float lam2, double inv_lam, unsigned* __restrict__ tag, unsigned tag_val) {
+    float lam2, double inv_lam, unsigned* __restrict__ tag, unsigned tag_val, unsigned* __restrict__ status) {
   constexpr int MW = cfg_MW(MODE, NCH), R = cfg_R(MODE, NCH), TC = TCX ? TCX : cfg_TC(MODE, NCH);
   using T = Tile<MW>;
   using Acc = typename T::Acc;
@@ -752,14 +877,16 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
       }
       Acc acc[R];
       tile(buf, 0, acc);
+      bool coarse = false;
 #pragma unroll
       for (int c = 0; c < R; ++c) {
         float mx = -INFINITY;
 #pragma unroll
         for (int o = 0; o < NO; ++o) mx = fmaxf(mx, raw(acc[c][o]));
-        m[c] = offset_from_max(lanes_max(mx) + HEADROOM, qg);
+        m[c] = offset_from_max(lanes_max(mx) + HEADROOM, qg, coarse);
         if (MODE == MODE_SPLIT) set_offset(bq[c][0], -m[c], grp == 0);
       }
+      flag_if(status, coarse && lane == 0, FLAG_SCORE_RANGE);
     }
     if constexpr (NCH == 1) {
       // short K: the unrolled tiles let the scheduler overlap one tile's MFMAs
@@ -803,14 +930,16 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
 #pragma unroll
           for (int o = 0; o < NO; ++o) mx[c] = fmaxf(mx[c], raw(acc[c][o]));
       }
+      bool coarse = false;
 #pragma unroll
       for (int c = 0; c < R; ++c) {
         mx[c] = lanes_max(mx[c]);
-        const float mn = fmaxf(m[c], offset_from_max(mx[c] + HEADROOM, qg));
+        const float mn = fmaxf(m[c], offset_from_max(mx[c] + HEADROOM, qg, coarse));
         s[c] = rescale(s[c], m[c], mn);
         m[c] = mn;
         if (MODE == MODE_SPLIT) set_offset(bq[c][0], -m[c], grp == 0);
       }
+      flag_if(status, coarse && lane == 0, FLAG_SCORE_RANGE);
 #pragma unroll 1
       for (int t = 0; t < TC; ++t) {
         Acc acc[R];
@@ -841,7 +970,9 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
       if (part != nullptr) {
         part[(size_t)blk.y * batch * rows + r] = make_float2(m[c], st);
       } else {
-        out[r] = (float)(qnorm[r] - ((double)m[c] + log2((double)st)) * inv_lam);
+        const float v = (float)(qnorm[r] - ((double)m[c] + log2((double)st)) * inv_lam);
+        out[r] = v;
+        flag_if(status, !isfinite(v), FLAG_NONFINITE);
       }
     }
   }
@@ -851,7 +982,7 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
 // rescaling) and write the potential.
 __global__ __launch_bounds__(256) void k_merge(const float2* __restrict__ part, int ks, int total,
                                                const double* __restrict__ qnorm, float* __restrict__ out,
-                                               double inv_lam) {
+                                               double inv_lam, unsigned* __restrict__ status) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
   // Two passes over the partials (the second from cache): the loads of a pass
@@ -864,7 +995,9 @@ __global__ __launch_bounds__(256) void k_merge(const float2* __restrict__ part, 
     const float2 v = part[(size_t)k * total + i];
     S += rescale(v.y, v.x, M);
   }
-  out[i] = (float)(qnorm[i] - ((double)M + log2((double)S)) * inv_lam);
+  const float v = (float)(qnorm[i] - ((double)M + log2((double)S)) * inv_lam);
+  out[i] = v;
+  flag_if(status, !isfinite(v), FLAG_NONFINITE);
 }
 
 // sum_i exp(logw_i) * |expm1((pot_i - tilde_i)/eps)|, one workgroup per problem, fixed order.
@@ -888,8 +1021,8 @@ __global__ __launch_bounds__(256) void k_marginal(const float* __restrict__ pot,
 }
 
 // ---------------------------------------------------------------------------
-// Transport application (page "FlashSinkhorn: IO-aware entropic OT on GPU",
-// section "Differentiation and second-order optimisation"): the barycentric
+// Transport application (page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU",
+// section "Metodologia", part "3. Differenziazione e Ottimizzazione del Secondo Ordine"): the barycentric
 // projection bary_i = sum_j P_ij y_j / sum_j P_ij and the gradient
 // sum_j P_ij 2 (x_i - y_j) = 2 r_i (x_i - bary_i), r_i = sum_j P_ij, are
 // softmax-weighted averages of the other cloud: an attention-style P.V product
@@ -956,8 +1089,9 @@ __host__ __device__ constexpr int vkey(int k0, int e) { return (k0 / 8) * 4 + (e
 // column when it is spare (sumcol).  Padding keys and other columns are zero.
 // One thread per 8 keys of one column.
 __global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, int mode, int in_bf16,
-                                                   const double* __restrict__ rnorm, int keys, int keys_pad, int d,
-                                                   int ncols, int sumcol, u16* __restrict__ vt) {
+                                                   const double* __restrict__ rnorm, const double* __restrict__ cen,
+                                                   int keys, int keys_pad, int d, int ncols, int sumcol,
+                                                   u16* __restrict__ vt) {
   const int b = blockIdx.y;
   const long long per_blk = (long long)ncols * (VK / 8);
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -975,11 +1109,12 @@ __global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, i
       val = BF16_ONE;
     } else if (j < keys && part < val_parts(mode)) {
       const size_t r = ((size_t)b * keys + j) * d + t;
+      const double c = cen[(size_t)b * d + t];
       if (mode == MODE_BF16) {
-        val = static_cast<const u16*>(P)[r];
+        val = bf16_rne((float)((double)bf16_f(static_cast<const u16*>(P)[r]) - c));  // exact (see k_bf16_exact)
       } else {
         // x = h0 + h1 + h2 exactly: each remainder is exact in fp32
-        const float x = (float)((double)coord(P, r, in_bf16) * rnorm[(size_t)b * keys + j]);
+        const float x = (float)((double)coord(P, r, in_bf16) * rnorm[(size_t)b * keys + j] - c);
         const u16 h0 = bf16_rne(x);
         const float r1 = x - bf16_f(h0);
         const u16 h1 = bf16_rne(r1);
@@ -1023,7 +1158,7 @@ __global__ __launch_bounds__(64 * bary_NW(MODE, NCH, NCT, NU))
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, const float* __restrict__ lse,
     float* __restrict__ pv_out, float* __restrict__ s_out, int rows, int rows_pad, int keys, int keys_pad,
     int chunks_per_split, int batch, float lam, float lam2, float* __restrict__ m_out, unsigned* __restrict__ tag,
-    unsigned tag_val, const u16* __restrict__ U, float ugain) {
+    unsigned tag_val, const u16* __restrict__ U, float ugain, unsigned* __restrict__ status) {
   constexpr int MW = 16, R = bary_R(NCH, NCT);
   using T = Tile<16>;
   constexpr int KP = NCH * 32;
@@ -1103,7 +1238,9 @@ __global__ __launch_bounds__(64 * bary_NW(MODE, NCH, NCT, NU))
     }
     if (!(fabs(M) < 1e30)) M = 0.0;
     if (MODE == MODE_SPLIT) {
-      const float mo = offset_from_max((float)M, qg);
+      bool coarse = false;
+      const float mo = offset_from_max((float)M, qg, coarse);
+      flag_if(status, coarse, FLAG_SCORE_RANGE);
       set_offset(bq[c][0], -mo, grp == 0);
       sub[c] = (float)(M - (double)mo);
     } else {
@@ -1244,7 +1381,9 @@ __global__ __launch_bounds__(64 * bary_NW(MODE, NCH, NCT, NU))
             v = fmaxf(v, __shfl_xor(v, 32));
             const float top = (MODE == MODE_BF16) ? v * lam2 : (mo[c] == -INFINITY ? v : mo[c] + v);
             float mn = mo[c];
-            if (mo[c] == -INFINITY || !(top - mo[c] <= 32.f)) mn = fmaxf(mo[c], offset_from_max(top + HEADROOM, qg));
+            bool coarse = false;
+            if (mo[c] == -INFINITY || !(top - mo[c] <= 32.f)) mn = fmaxf(mo[c], offset_from_max(top + HEADROOM, qg, coarse));
+            flag_if(status, coarse, FLAG_SCORE_RANGE);
             if (!SUMCOL) s[c] = rescale(s[c], mo[c], mn);
             // P.V rows are queries 4grp+r; their offsets live in lanes col = 4grp+r
 #pragma unroll
@@ -1327,7 +1466,7 @@ __global__ __launch_bounds__(64 * bary_NW(MODE, NCH, NCT, NU))
 }
 
 // Barycentric projection and gradient from the split partials, one thread per
-// (problem, row, coordinate): bary = sum_parts sum_splits pv / sum_splits s,
+// (problem, row, coordinate): bary = sum_parts sum_splits pv / sum_splits s + c,
 // grad = 2 r (p - bary) with the row mass r = w exp((pot - lse)/eps).
 // With lazy offsets (mpart != nullptr) each split's partials are relative to its
 // own offset mpart (base 2): they are brought to the largest one, and the row's
@@ -1339,8 +1478,8 @@ __global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv
                                                     const float* __restrict__ pot, float* __restrict__ lse,
                                                     const double* __restrict__ logw, double eps,
                                                     const float* __restrict__ mpart, const double* __restrict__ qnorm,
-                                                    double inv_lam, float* __restrict__ bary,
-                                                    float* __restrict__ grad) {
+                                                    double inv_lam, const double* __restrict__ cen,
+                                                    float* __restrict__ bary, float* __restrict__ grad) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)batch * rows * d) return;
   const int t = (int)(idx % d);
@@ -1359,7 +1498,8 @@ __global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv
     S += sc * (sumcol ? (double)pv[base * ncols + ncols - 1] : (double)sp[base]);
     for (int part = 0; part < parts; ++part) num += sc * (double)pv[base * ncols + part * d + t];
   }
-  const double bc = num / S;
+  // the values were centred: the projection moves back by the centre
+  const double bc = num / S + cen[(size_t)(rr / rows) * d + t];
   bary[idx] = (float)bc;
   double row_lse;
   if (mpart != nullptr) {
@@ -1401,9 +1541,9 @@ __global__ __launch_bounds__(256) void k_cosine_grad(const float* __restrict__ b
 }
 
 // ---------------------------------------------------------------------------
-// Plan application and Hessian-vector products (page "FlashSinkhorn: IO-aware
-// entropic OT on GPU", section "Differentiation and second-order
-// optimisation": the Hessian-vector product decomposes into vector- and
+// Plan application and Hessian-vector products (page "FlashSinkhorn: Trasporto Ottimo Entropico
+// Consapevole delle I/O su GPU", section "Metodologia", part "3. Differenziazione e Ottimizzazione
+// del Secondo Ordine": the Hessian-vector product decomposes into vector- and
 // matrix-transport products, so neither the Hessian nor the plan is formed).
 // A plan application out_i = sum_j P_ij V_j is the transport pass above with V
 // an arbitrary fp32 matrix, scaled by the row mass.
@@ -1479,14 +1619,15 @@ __global__ __launch_bounds__(256) void k_mass(const double* __restrict__ logw, c
 // that the other side's plan application turns into the right-hand side.
 __global__ __launch_bounds__(256) void k_hvp_rows(const void* __restrict__ P, int in_bf16, const float* __restrict__ V,
                                                   const float* __restrict__ PY, const double* __restrict__ mass,
-                                                  long long total, int d, double* __restrict__ zr,
-                                                  double* __restrict__ cr, float* __restrict__ M) {
+                                                  long long total, int d, int rows, const double* __restrict__ cen,
+                                                  double* __restrict__ zr, double* __restrict__ cr,
+                                                  float* __restrict__ M) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
   double z = 0.0, vpy = 0.0;
   for (int t = 0; t < d; ++t) {
     const double v = V[i * d + t];
-    z += (double)coord(P, (size_t)i * d + t, in_bf16) * v;
+    z += ccoord(P, (size_t)i, t, d, in_bf16, cen, (int)(i / rows)) * v;
     vpy += v * (double)PY[i * d + t];
   }
   const double r = mass[i];
@@ -1502,12 +1643,13 @@ __global__ __launch_bounds__(256) void k_hvp_rows(const void* __restrict__ P, in
 // Right-hand side of the Schur system per row of the fixed cloud (points q):
 //   rhs = 2 (W0 - q.W1) - W2  with W = P^T [z, v, cr/r].
 __global__ __launch_bounds__(256) void k_hvp_rhs(const void* __restrict__ Q, int in_bf16, const float* __restrict__ W,
-                                                 long long total, int d, double* __restrict__ rhs) {
+                                                 long long total, int d, int keys, const double* __restrict__ cen,
+                                                 double* __restrict__ rhs) {
   const long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= total) return;
   const float* w = W + j * (d + 2);
   double qw = 0.0;
-  for (int t = 0; t < d; ++t) qw += (double)coord(Q, (size_t)j * d + t, in_bf16) * (double)w[1 + t];
+  for (int t = 0; t < d; ++t) qw += ccoord(Q, (size_t)j, t, d, in_bf16, cen, (int)(j / keys)) * (double)w[1 + t];
   rhs[j] = 2.0 * ((double)w[0] - qw) - (double)w[d + 1];
 }
 
@@ -1688,13 +1830,13 @@ __global__ __launch_bounds__(256) void k_cg_d(const double* __restrict__ cmass, 
 
 // Matrix [dg, dg * q] per row of the fixed cloud (points q).
 __global__ __launch_bounds__(256) void k_hvp_gmat(const void* __restrict__ Q, int in_bf16,
-                                                  const double* __restrict__ dg, long long total, int d,
-                                                  float* __restrict__ M) {
+                                                  const double* __restrict__ dg, long long total, int d, int keys,
+                                                  const double* __restrict__ cen, float* __restrict__ M) {
   const long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= total) return;
   float* row = M + j * (d + 1);
   row[0] = (float)dg[j];
-  for (int t = 0; t < d; ++t) row[1 + t] = (float)(dg[j] * (double)coord(Q, (size_t)j * d + t, in_bf16));
+  for (int t = 0; t < d; ++t) row[1 + t] = (float)(dg[j] * ccoord(Q, (size_t)j, t, d, in_bf16, cen, (int)(j / keys)));
 }
 
 // Query-layout planes of a per-row fp32 vector v (the direction of a
@@ -1771,11 +1913,11 @@ __global__ __launch_bounds__(256) void k_uw_merge(const float* __restrict__ pv, 
   quad[idx] = mass > 0.0 ? mass * num / S : 0.0;
 }
 
-// Coordinates of a cloud as an fp32 matrix.
-__global__ __launch_bounds__(256) void k_coords(const void* __restrict__ P, int in_bf16, long long total,
-                                                float* __restrict__ M) {
+// Centred coordinates of a cloud as an fp32 matrix (rows points per problem).
+__global__ __launch_bounds__(256) void k_coords(const void* __restrict__ P, int in_bf16, long long total, int d,
+                                                int rows, const double* __restrict__ cen, float* __restrict__ M) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < total) M[i] = coord(P, (size_t)i, in_bf16);
+  if (i < total) M[i] = (float)ccoord(P, (size_t)(i / d), (int)(i % d), d, in_bf16, cen, (int)(i / ((long long)rows * d)));
 }
 
 // HV_i = 2 r v + (2/eps) [ df (r p - PY) + p (P dg) - P(dg q) - 2 (z (r p - PY) - (v.PY) p + quad) ]
@@ -1785,7 +1927,8 @@ __global__ __launch_bounds__(256) void k_hvp_final(const void* __restrict__ P, i
                                                    const double* __restrict__ mass, const double* __restrict__ zr,
                                                    const double* __restrict__ cr, const float* __restrict__ G,
                                                    const double* __restrict__ quad, long long total, int d,
-                                                   double eps, float* __restrict__ out) {
+                                                   int rows, const double* __restrict__ cen, double eps,
+                                                   float* __restrict__ out) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
   const double r = mass[i];
@@ -1799,7 +1942,7 @@ __global__ __launch_bounds__(256) void k_hvp_final(const void* __restrict__ P, i
   for (int t = 0; t < d; ++t) vpy += (double)V[i * d + t] * (double)PY[i * d + t];
   const double z = zr[i];
   for (int t = 0; t < d; ++t) {
-    const double pt = coord(P, (size_t)i * d + t, in_bf16);
+    const double pt = ccoord(P, (size_t)i, t, d, in_bf16, cen, (int)(i / rows));
     const double grad_half = r * pt - (double)PY[i * d + t];
     const double K = 2.0 * (z * grad_half - vpy * pt + quad[i * d + t]);
     const double inner = df * grad_half + pt * (double)g[0] - (double)g[1 + t] - K;
@@ -1813,7 +1956,8 @@ __global__ __launch_bounds__(256) void k_hvp_final(const void* __restrict__ P, i
 struct Layout {
   int mode, KP, n_pad, m_pad, max_pad;
   int in_bf16, cosine;
-  size_t xn, yn, la, lb, rx, ry, maxabs, qgrid, ktag, qx, qy, kbx, kby, hb, part, scratch, total;
+  size_t xn, yn, la, lb, rx, ry, maxabs, cen, box, inexact, status, qgrid, ktag, qx, qy, kbx, kby, hb, part, scratch,
+      total;
   // key operand of the fp32 path for side 0 (Y as keys) or side 1 (X as keys)
   size_t kb(int side) const { return side == 0 ? kby : kbx; }
   // transport application and plan products (after `total`; only their entry points need them)
@@ -1891,6 +2035,10 @@ Layout layout_of(const sk_problem* p) {
   L.rx = take(8 * B * n);
   L.ry = take(8 * B * m);
   L.maxabs = take(align_up(4 * 2 * B, 16));
+  L.cen = take(8 * B * (size_t)p->d);               // centre of each problem (fp64)
+  L.box = take(4 * 4 * B * (size_t)p->d);           // bounding boxes of both clouds (ordered codes)
+  L.inexact = take(4 * B);                          // bf16 problems left uncentred
+  L.status = take(16);                              // range flags (SK_FLAG_*)
   L.qgrid = take(4 * B);
   L.ktag = take(16);  // lambda tags of the two key operands
   // SLACK extra rows after each operand buffer absorb the kernels' unguarded
@@ -1944,7 +2092,7 @@ Layout layout_of(const sk_problem* p) {
 }
 
 using LseFn = void (*)(const u16*, const u16*, const float*, const float*, const double*, float*, float2*, int, int,
-                       int, int, int, int, float, double, unsigned*, unsigned);
+                       int, int, int, int, float, double, unsigned*, unsigned, unsigned*);
 
 template <int MODE, int NCH>
 LseFn lse_fn() {
@@ -1992,29 +2140,38 @@ sk_status check_ws(const sk_problem* p, void* ws, size_t ws_bytes, Layout* L, in
 }
 
 // Workgroups of `fn` that the current device holds at once (CUs x WGs per CU).
+// Cached per (device, kernel) in a fixed table (no heap use, so the
+// allocation-free entry point stays allocation-free); a full table just
+// queries again.
 sk_status resident_capacity(const void* fn, int* out, int block = 256) {
+  struct Entry {
+    int dev;
+    const void* fn;
+    int value;
+  };
+  constexpr int CACHE = 512;
   static std::mutex mu;
-  static std::map<std::pair<int, const void*>, int> cache;
+  static Entry cache[CACHE];
+  static int used = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     set_err("hipGetDevice failed");
     return SK_EHIP;
   }
-  const auto key = std::make_pair(dev, fn);
   std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find(key);
-  if (it != cache.end()) {
-    *out = it->second;
-    return SK_OK;
-  }
+  for (int k = 0; k < used; ++k)
+    if (cache[k].dev == dev && cache[k].fn == fn) {
+      *out = cache[k].value;
+      return SK_OK;
+    }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0) !=
-          hipSuccess) {
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0) != hipSuccess) {
     set_err("occupancy query failed");
     return SK_EHIP;
   }
-  *out = cache[key] = std::max(1, cus * std::max(1, per_cu));
+  *out = std::max(1, cus * std::max(1, per_cu));
+  if (used < CACHE) cache[used++] = Entry{dev, fn, *out};
   return SK_OK;
 }
 
@@ -2069,7 +2226,8 @@ sk_status prep_keys(const sk_problem* p, const void* X, const void* Y, char* w, 
     // about PREP_SEGS segments per thread when every segment is rebuilt
     const dim3 kgrid((unsigned)(((long long)keys_pad * (L.KP / 8) + 256 * PREP_SEGS - 1) / (256 * PREP_SEGS)), B);
     const double* krn = reinterpret_cast<const double*>(w + (side == 0 ? L.ry : L.rx));
-    hipLaunchKernelGGL(k_prep_keys, kgrid, dim3(256), 0, stream, Kraw, L.in_bf16, krn, pot_in, knorm,
+    hipLaunchKernelGGL(k_prep_keys, kgrid, dim3(256), 0, stream, Kraw, L.in_bf16, krn,
+                       reinterpret_cast<const double*>(w + L.cen), pot_in, knorm,
                        klogw, keys, keys_pad, (int)p->d, L.KP, lam, eps, maxabs + (side == 0 ? 0 : B),
                        maxabs + (side == 0 ? B : 0), qgrid, tag, kb);
     *Kop = kb;
@@ -2128,19 +2286,21 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps);
   float2* part = ks > 1 ? reinterpret_cast<float2*>(w + L.part) : nullptr;
   const double inv_lam = 1.0 / (double)lam;
+  unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
   hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NW), 0, stream, Qop, Kop, hb, qgrid, qnorm, pot_out, part, rows,
-                     rows_pad, keys, keys_pad, cps, B, 2.f * lam, inv_lam, tag, __builtin_bit_cast(unsigned, lam));
+                     rows_pad, keys, keys_pad, cps, B, 2.f * lam, inv_lam, tag, __builtin_bit_cast(unsigned, lam),
+                     status);
   st = hip_check("half-step kernel launch");
   if (st != SK_OK || ks == 1) return st;
   const int total = B * rows;
   hipLaunchKernelGGL(k_merge, dim3((total + 255) / 256), dim3(256), 0, stream, part, ks, total, qnorm, pot_out,
-                     inv_lam);
+                     inv_lam, status);
   return hip_check("split merge launch");
 }
 
 using BaryFn = void (*)(const u16*, const u16*, const float*, const u16*, const float*, const double*, const float*,
                         float*, float*, int, int, int, int, int, int, float, float, float*, unsigned*, unsigned,
-                        const u16*, float);
+                        const u16*, float, unsigned*);
 
 template <int MODE, int D>
 BaryFn bary_fn_d() {
@@ -2194,8 +2354,10 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   const long long nvec = (long long)(keys_pad / VK) * nc * (VK / 8);
   const int sumcol = val_sumcol(L.mode, d) ? 1 : 0;
   const double* krn = reinterpret_cast<const double*>(w + (side == 0 ? L.ry : L.rx));
+  const double* cen = reinterpret_cast<const double*>(w + L.cen);
+  unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
   hipLaunchKernelGGL(k_prep_vals, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, Kraw, L.mode,
-                     L.in_bf16, krn, keys, keys_pad, d, nc, sumcol, vt);
+                     L.in_bf16, krn, cen, keys, keys_pad, d, nc, sumcol, vt);
   st = hip_check("value preparation launch");
   if (st != SK_OK) return st;
 
@@ -2222,7 +2384,7 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   const float lam = (float)(LOG2E / (double)eps);
   hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NWb), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, nullptr, bpv, bs, rows,
                      rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, bm, tag, __builtin_bit_cast(unsigned, lam), nullptr,
-                     1.f);
+                     1.f, status);
   st = hip_check("transport kernel launch");
   if (st != SK_OK) return st;
 
@@ -2230,7 +2392,7 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   const long long total = (long long)B * rows * d;
   hipLaunchKernelGGL(k_bary_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, bs, ks, B, rows,
                      d, nc, val_parts(L.mode), sumcol, Praw, L.in_bf16, pot_row, lse, qlogw, (double)eps, bm, qnorm,
-                     1.0 / (double)lam, bary, L.cosine ? nullptr : grad);
+                     1.0 / (double)lam, cen, bary, L.cosine ? nullptr : grad);
   st = hip_check("transport merge launch");
   if (st != SK_OK || !L.cosine || grad == nullptr) return st;
   const double* qrn = reinterpret_cast<const double*>(w + (side == 0 ? L.rx : L.ry));
@@ -2315,7 +2477,7 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
     const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps, ks_cap);
     hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NWb), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, lse, bpv, bs,
                        rows, rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, nullptr, ptag,
-                       __builtin_bit_cast(unsigned, lam), nullptr, 1.f);
+                       __builtin_bit_cast(unsigned, lam), nullptr, 1.f, reinterpret_cast<unsigned*>(w + L.status));
     st = hip_check("plan-application kernel launch");
     if (st != SK_OK) return st;
     const long long total = (long long)B * rows * cb;
@@ -2375,7 +2537,7 @@ sk_status apply_uw(const sk_problem* p, const void* X, const void* Y, char* w, c
   const long long nvec = (long long)(keys_pad / VK) * nc * (VK / 8);
   const double* krn = reinterpret_cast<const double*>(w + (side == 0 ? L.ry : L.rx));
   hipLaunchKernelGGL(k_prep_vals, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, Kraw, L.mode,
-                     L.in_bf16, krn, keys, keys_pad, d, nc, 0, vt);
+                     L.in_bf16, krn, reinterpret_cast<const double*>(w + L.cen), keys, keys_pad, d, nc, 0, vt);
   st = hip_check("direction and value preparation launch");
   if (st != SK_OK) return st;
   BaryFn fn = uw_lookup(L.mode, d);
@@ -2401,7 +2563,7 @@ sk_status apply_uw(const sk_problem* p, const void* X, const void* Y, char* w, c
   const float ugain = L.mode == MODE_SPLIT ? 1.f / (2.f * lam) : 1.f;
   hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NWb), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, lse, bpv, bs, rows,
                      rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, nullptr, ptag, __builtin_bit_cast(unsigned, lam),
-                     U, ugain);
+                     U, ugain, reinterpret_cast<unsigned*>(w + L.status));
   st = hip_check("row-weighted plan kernel launch");
   if (st != SK_OK) return st;
   const long long total = (long long)B * rows * d;
@@ -2459,16 +2621,18 @@ sk_status hvp(const sk_problem* p, const void* X, const void* Y, char* w, const 
   hipLaunchKernelGGL(k_mass, dim3(blocks_for(nr)), dim3(256), 0, s, logw_r, pot_r, lse_r, (double)eps, nr, mr);
   hipLaunchKernelGGL(k_mass, dim3(blocks_for(nk)), dim3(256), 0, s, logw_k, pot_k, lse_k, (double)eps, nk, mk);
   // 2. P Q (the plan applied to the fixed cloud's coordinates)
-  hipLaunchKernelGGL(k_coords, dim3(blocks_for(nk * d)), dim3(256), 0, s, Qraw, in16, nk * d, mat);
+  const double* cen = reinterpret_cast<const double*>(w + L.cen);
+  hipLaunchKernelGGL(k_coords, dim3(blocks_for(nk * d)), dim3(256), 0, s, Qraw, in16, nk * d, d, keys, cen, mat);
   st = hip_check("HVP set-up launch");
   if (st == SK_OK) st = apply_plan(p, X, Y, w, L, pot_r, pot_k, lse_r, eps, side, mat, d, py, s);
   if (st != SK_OK) return st;
   // 3. right-hand side: cr per moving row, then P^T [z, v, cr/r] per fixed row
-  hipLaunchKernelGGL(k_hvp_rows, dim3(blocks_for(nr)), dim3(256), 0, s, Praw, in16, V, py, mr, nr, d, zr, cr, mat);
+  hipLaunchKernelGGL(k_hvp_rows, dim3(blocks_for(nr)), dim3(256), 0, s, Praw, in16, V, py, mr, nr, d, rows, cen, zr, cr,
+                     mat);
   st = hip_check("HVP rows launch");
   if (st == SK_OK) st = apply_plan(p, X, Y, w, L, pot_k, pot_r, lse_k, eps, 1 - side, mat, d + 2, wk, s);
   if (st != SK_OK) return st;
-  hipLaunchKernelGGL(k_hvp_rhs, dim3(blocks_for(nk)), dim3(256), 0, s, Qraw, in16, wk, nk, d, rhs);
+  hipLaunchKernelGGL(k_hvp_rhs, dim3(blocks_for(nk)), dim3(256), 0, s, Qraw, in16, wk, nk, d, keys, cen, rhs);
   // 4. conjugate gradients on the Schur system in dg
   const int nblk = (keys + CG_BLK - 1) / CG_BLK;
   double* pa = reinterpret_cast<double*>(w + L.h_part);
@@ -2500,7 +2664,7 @@ sk_status hvp(const sk_problem* p, const void* X, const void* Y, char* w, const 
     if (st != SK_OK) return st;
   }
   // 5. P [dg, dg q]
-  hipLaunchKernelGGL(k_hvp_gmat, dim3(blocks_for(nk)), dim3(256), 0, s, Qraw, in16, dg, nk, d, mat);
+  hipLaunchKernelGGL(k_hvp_gmat, dim3(blocks_for(nk)), dim3(256), 0, s, Qraw, in16, dg, nk, d, keys, cen, mat);
   st = hip_check("HVP matrix launch");
   if (st == SK_OK) st = apply_plan(p, X, Y, w, L, pot_r, pot_k, lse_r, eps, side, mat, d + 1, gm, s);
   if (st != SK_OK) return st;
@@ -2509,41 +2673,57 @@ sk_status hvp(const sk_problem* p, const void* X, const void* Y, char* w, const 
   if (st != SK_OK) return st;
   // 7. assemble
   hipLaunchKernelGGL(k_hvp_final, dim3(blocks_for(nr)), dim3(256), 0, s, Praw, in16, V, py, mr, zr, cr, gm, quad, nr,
-                     d, (double)eps, out);
+                     d, rows, cen, (double)eps, out);
   return hip_check("HVP assembly launch");
 }
 
 sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const float* a, const float* b, void* ws,
                     const Layout& L, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
-  const int B = (int)p->batch;
+  const int B = (int)p->batch, d = (int)p->d;
   float* maxabs = reinterpret_cast<float*>(w + L.maxabs);
+  double* cen = reinterpret_cast<double*>(w + L.cen);
+  unsigned* box = reinterpret_cast<unsigned*>(w + L.box);
+  unsigned* inexact = reinterpret_cast<unsigned*>(w + L.inexact);
   auto zero = [&](size_t off, size_t bytes) {
     const size_t n16 = bytes / 16;
     if (n16) hipLaunchKernelGGL(k_zero, dim3((unsigned)std::min<size_t>((n16 + 255) / 256, 4096)), dim3(256), 0,
                                 stream, reinterpret_cast<u4*>(w + off), n16);
   };
+  // box slots, bf16 centring flags, the status word and the key operands' lambda
+  // tags (new clouds: the key operands hold no coordinate parts yet)
+  hipLaunchKernelGGL(k_init_words, dim3((unsigned)std::min<long long>((4LL * B * d + 255) / 256, 1024)), dim3(256), 0,
+                     stream, box, d, B, inexact, reinterpret_cast<unsigned*>(w + L.status),
+                     reinterpret_cast<unsigned*>(w + L.ktag));
   if (L.cosine) {
-    // normalised points: every coordinate is at most 1 in magnitude
+    // normalised points: not centred, every coordinate at most 1 in magnitude
+    zero(L.cen, align_up(8 * (size_t)B * d, 16));
     hipLaunchKernelGGL(k_fill_f32, dim3((2 * B + 255) / 256), dim3(256), 0, stream, maxabs, 2 * B, 1.f);
   } else {
-    zero(L.maxabs, align_up(8 * (size_t)B, 16));
-    const long long most = std::max(p->n, p->m) * p->d;
-    const unsigned mblocks = (unsigned)std::min<long long>((most + 255) / 256, 64);
-    hipLaunchKernelGGL(k_maxabs, dim3(mblocks, B, 2), dim3(256), 0, stream, X, Y, L.in_bf16,
-                       (long long)(p->n * p->d), (long long)(p->m * p->d), reinterpret_cast<unsigned*>(maxabs), B);
+    const int most = (int)std::max(p->n, p->m);
+    const unsigned chunks = (unsigned)std::min(64, std::max(1, (most + 255) / 256));
+    hipLaunchKernelGGL(k_bbox, dim3(chunks, (d + 63) / 64, 2 * B), dim3(256), 0, stream, X, Y, L.in_bf16, (int)p->n,
+                       (int)p->m, d, box);
+    hipLaunchKernelGGL(k_centre, dim3(B), dim3(256), 0, stream, box, d, B, L.in_bf16, 1, cen, maxabs);
+    if (L.in_bf16) {
+      const long long elems = (long long)most * d;
+      const unsigned ch = (unsigned)std::min<long long>(64, std::max<long long>(1, (elems + 255) / 256));
+      hipLaunchKernelGGL(k_bf16_exact, dim3(ch, B, 2), dim3(256), 0, stream, static_cast<const u16*>(X),
+                         static_cast<const u16*>(Y), (long long)(p->n * p->d), (long long)(p->m * p->d), d, cen, inexact);
+      hipLaunchKernelGGL(k_cen_fix, dim3(B), dim3(256), 0, stream, inexact, d, cen);
+    }
   }
   auto side = [&](const void* P, const float* wt, int rows, int rows_pad, const float* mabs, size_t norm,
                   size_t logw, size_t rnorm, size_t op) {
     const dim3 grid((rows_pad + 255) / 256, B);
     if (L.mode == MODE_SPLIT)
-      hipLaunchKernelGGL(k_init_side<MODE_SPLIT>, grid, dim3(256), 0, stream, P, wt, rows, rows_pad, (int)p->d,
-                         L.KP, L.in_bf16, L.cosine, mabs, reinterpret_cast<double*>(w + norm),
+      hipLaunchKernelGGL(k_init_side<MODE_SPLIT>, grid, dim3(256), 0, stream, P, wt, rows, rows_pad, d, L.KP,
+                         L.in_bf16, L.cosine, mabs, cen, reinterpret_cast<double*>(w + norm),
                          reinterpret_cast<double*>(w + logw), reinterpret_cast<double*>(w + rnorm),
                          reinterpret_cast<u16*>(w + op));
     else
-      hipLaunchKernelGGL(k_init_side<MODE_BF16>, grid, dim3(256), 0, stream, P, wt, rows, rows_pad, (int)p->d,
-                         L.KP, L.in_bf16, L.cosine, mabs, reinterpret_cast<double*>(w + norm),
+      hipLaunchKernelGGL(k_init_side<MODE_BF16>, grid, dim3(256), 0, stream, P, wt, rows, rows_pad, d, L.KP,
+                         L.in_bf16, L.cosine, mabs, cen, reinterpret_cast<double*>(w + norm),
                          reinterpret_cast<double*>(w + logw), reinterpret_cast<double*>(w + rnorm),
                          reinterpret_cast<u16*>(w + op));
   };
@@ -2553,9 +2733,44 @@ sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const flo
   // query rows run past the padding reads zeros there
   zero(L.qx + 2 * (size_t)B * L.n_pad * L.KP, 2 * (size_t)SLACK * L.KP);
   zero(L.qy + 2 * (size_t)B * L.m_pad * L.KP, 2 * (size_t)SLACK * L.KP);
-  // new clouds: the key operands hold no coordinate parts yet
-  if (L.mode == MODE_SPLIT) zero(L.ktag, 16);
   return hip_check("init kernel launch");
+}
+
+// Argument checks of the solve entry points (after the problem and workspace checks).
+sk_status check_solve_args(const void* X, const void* Y, const float* a, const float* b, const float* eps,
+                           int64_t n_eps, int64_t iters, const float* f, const float* g) {
+  if (!X || !Y || !a || !b || !f || !g) {
+    set_err("X, Y, a, b, f and g must be non-NULL device pointers");
+    return SK_EINVAL;
+  }
+  if (iters < 0) {
+    set_err("iters must be >= 0 (got %lld)", (long long)iters);
+    return SK_EINVAL;
+  }
+  if (eps == nullptr || !(n_eps == 1 || (n_eps == iters && iters > 0))) {
+    set_err("eps must be a host array of 1 or iters values (n_eps = %lld, iters = %lld)", (long long)n_eps,
+            (long long)iters);
+    return SK_EINVAL;
+  }
+  for (int64_t k = 0; k < n_eps; ++k)
+    if (!eps_ok(eps[k])) {
+      set_err("eps[%lld] must be positive and finite (got %g)", (long long)k, (double)eps[k]);
+      return SK_EINVAL;
+    }
+  return SK_OK;
+}
+
+// init, then iters x (f half-step, g half-step), all enqueued on one stream.
+sk_status solve_impl(const sk_problem* p, const void* X, const void* Y, const float* a, const float* b,
+                     const float* eps, int64_t n_eps, int64_t iters, float* f, float* g, void* ws, const Layout& L,
+                     hipStream_t s) {
+  sk_status st = init_impl(p, X, Y, a, b, ws, L, s);
+  for (int64_t k = 0; k < iters && st == SK_OK; ++k) {
+    const float e = eps[n_eps == 1 ? 0 : k];
+    st = half_step(p, X, Y, ws, L, g, e, f, 0, s);
+    if (st == SK_OK) st = half_step(p, X, Y, ws, L, f, e, g, 1, s);
+  }
+  return st;
 }
 
 }  // namespace
@@ -2623,32 +2838,23 @@ sk_status sinkhorn_solve(const sk_problem* p, const void* X, const void* Y, cons
   Layout L;
   sk_status st = check_ws(p, ws, ws_bytes, &L);
   if (st != SK_OK) return st;
-  if (!X || !Y || !a || !b || !f || !g) {
-    set_err("X, Y, a, b, f and g must be non-NULL device pointers");
+  st = check_solve_args(X, Y, a, b, eps, n_eps, iters, f, g);
+  if (st != SK_OK) return st;
+  return solve_impl(p, X, Y, a, b, eps, n_eps, iters, f, g, ws, L, static_cast<hipStream_t>(stream));
+}
+
+sk_status sinkhorn_range_flags(const sk_problem* p, const void* ws, size_t ws_bytes, uint32_t* flags, void* stream) {
+  g_err[0] = 0;
+  Layout L;
+  sk_status st = check_ws(p, const_cast<void*>(ws), ws_bytes, &L);
+  if (st != SK_OK) return st;
+  if (flags == nullptr) {
+    set_err("flags must be a non-NULL device pointer");
     return SK_EINVAL;
   }
-  if (iters < 0) {
-    set_err("iters must be >= 0 (got %lld)", (long long)iters);
-    return SK_EINVAL;
-  }
-  if (eps == nullptr || !(n_eps == 1 || (n_eps == iters && iters > 0))) {
-    set_err("eps must be a host array of 1 or iters values (n_eps = %lld, iters = %lld)", (long long)n_eps,
-            (long long)iters);
-    return SK_EINVAL;
-  }
-  for (int64_t k = 0; k < n_eps; ++k)
-    if (!eps_ok(eps[k])) {
-      set_err("eps[%lld] must be positive and finite (got %g)", (long long)k, (double)eps[k]);
-      return SK_EINVAL;
-    }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  st = init_impl(p, X, Y, a, b, ws, L, s);
-  for (int64_t k = 0; k < iters && st == SK_OK; ++k) {
-    const float e = eps[n_eps == 1 ? 0 : k];
-    st = half_step(p, X, Y, ws, L, g, e, f, 0, s);
-    if (st == SK_OK) st = half_step(p, X, Y, ws, L, f, e, g, 1, s);
-  }
-  return st;
+  hipLaunchKernelGGL(k_copy_u32, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     reinterpret_cast<const unsigned*>(static_cast<const char*>(ws) + L.status), flags);
+  return hip_check("status copy launch");
 }
 
 sk_status sinkhorn_marginal_error(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,

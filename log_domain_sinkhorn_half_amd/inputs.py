@@ -11,8 +11,8 @@ float32 array returned alongside holds exactly the bfloat16 values, so the
 oracle sees the same numbers the kernels read.
 
 The five named workloads (``make_config``) follow the benchmark settings of the
-FlashSinkhorn summary (page "FlashSinkhorn: IO-aware entropic OT on GPU",
-section "Experimental results": synthetic point clouds, n up to ~70k), with
+FlashSinkhorn summary (page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU",
+section "Risultati Sperimentali": synthetic point clouds, n up to ~70k), with
 the shapes, distributions, epsilon and iteration counts fixed per workload.
 """
 
@@ -31,6 +31,7 @@ __all__ = [
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
     "random_potential",
+    "translate",
 ]
 
 
@@ -202,8 +203,10 @@ def make_case(n: int, m: int, d: int, *, batch: int = 1, eps=0.1, iters: int = 5
               dist: str = "gauss", shift: float = 0.5, scale: float = 1.0) -> Problem:
     """A small seeded instance for tests (same draw conventions as make_config).
 
-    dist: "gauss"  X ~ N(0, s^2 I), Y ~ N(shift, s^2 I)
-          "cube"   X, Y ~ U[0, s]^d
+    dist: "gauss"    X ~ N(0, s^2 I), Y ~ N(shift, s^2 I)
+          "cube"     X, Y ~ U[0, s]^d
+          "mixture"  X ~ U[0, s]^d, Y a mixture of 8 Gaussians of std 0.05 s with
+                     means in U[0, s]^d (the shapes of the 70000-point workload)
     weights: "uniform" or "softmax" (softmax of i.i.d. N(0,1))
     """
     rng = np.random.default_rng(seed)
@@ -213,6 +216,11 @@ def make_case(n: int, m: int, d: int, *, batch: int = 1, eps=0.1, iters: int = 5
     elif dist == "cube":
         X = scale * rng.random((batch, n, d))
         Y = scale * rng.random((batch, m, d))
+    elif dist == "mixture":
+        X = scale * rng.random((batch, n, d))
+        means = scale * rng.random((batch, 8, d))
+        labels = rng.integers(0, 8, size=(batch, m))
+        Y = np.take_along_axis(means, labels[..., None], axis=1) + 0.05 * scale * rng.standard_normal((batch, m, d))
     else:
         raise ValueError(dist)
     if weights == "uniform":
@@ -223,6 +231,19 @@ def make_case(n: int, m: int, d: int, *, batch: int = 1, eps=0.1, iters: int = 5
         raise ValueError(weights)
     return _finish(f"case{n}x{m}x{d}", X, Y, a, b, eps, iters, dtype,
                    {"seed": seed, "dist": dist})
+
+
+def translate(p: Problem, t) -> Problem:
+    """The same problem with both clouds moved by the vector t (a scalar moves every
+    coordinate): x + t and y + t are formed in fp64 from the problem's values and
+    rounded to its dtype again (round to nearest even), so the result is a new,
+    exactly representable instance."""
+    t = np.broadcast_to(np.asarray(t, dtype=np.float64), (p.d,))
+    X = p.X.astype(np.float64) + t
+    Y = p.Y.astype(np.float64) + t
+    meta = dict(p.meta)
+    meta["translate"] = t.tolist()
+    return _finish(p.name + "+t", X, Y, p.a, p.b, p.eps.astype(np.float64), p.iters, p.dtype, meta)
 
 
 def random_potential(shape, seed: int, scale: float = 1.0) -> np.ndarray:

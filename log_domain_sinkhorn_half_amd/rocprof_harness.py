@@ -73,8 +73,18 @@ def operand_slots(d: int, bf16: bool) -> int:
 
 
 def algorithmic_bytes(C: int) -> float:
-    """Bytes one half-step launch must move at least, averaged over the f and g
-    launches: both operands read once, the potential written once (fp32)."""
+    """Algorithmic HBM bytes of one half-step launch, averaged over the f and g
+    launches: half of an iteration's 2 (n+m) d s + 20 (n+m) bytes per problem
+    (both clouds read once at s bytes per coordinate; potentials, weights and
+    norms: 20 bytes per point), the figure the roofline tables use."""
+    B, n, m, d, bf16 = SHAPE[C]
+    s = 2 if bf16 else 4
+    return B * ((n + m) * d * s + 10 * (n + m))
+
+
+def operand_bytes(C: int) -> float:
+    """Bytes of the kernel's own operand rows read once per half-step launch (K
+    slots of 2 bytes per point of both sides, averaged), plus the potential."""
     B, n, m, d, bf16 = SHAPE[C]
     kp = operand_slots(d, bf16)
     return B * (n + m) * kp * 2 + B * (n + m) / 2 * 4
@@ -277,9 +287,12 @@ def main() -> None:
               f"| {lname} WRITE_SIZE | {w_kib:.1f} KiB -> {w_bytes / 1e6:.2f} MB |",
               f"| HBM rate over the launch | {hbm_bytes / dur_s / 1e9:.1f} GB/s of {PEAK_HBM / 1e9:.0f} |"]
     if kname == "k_lse":
-        tr_md += [f"| algorithmic bytes (operands read once, potential written once) | "
+        tr_md += [f"| algorithmic bytes (clouds read once at their input precision, 20 B per point) | "
                   f"{algorithmic_bytes(C) / 1e6:.2f} MB |",
-                  f"| measured / algorithmic | {hbm_bytes / algorithmic_bytes(C):.2f} |", "",
+                  f"| measured / algorithmic | {hbm_bytes / algorithmic_bytes(C):.2f} |",
+                  f"| operand-layout bytes (the kernel's K-slot rows read once, potential written once) | "
+                  f"{operand_bytes(C) / 1e6:.2f} MB |",
+                  f"| measured / operand-layout bytes | {hbm_bytes / operand_bytes(C):.2f} |", "",
                   "Traffic above the algorithmic bytes is the key operand re-read by the row blocks of a key split",
                   "(served mostly by the L2 and the MALL); at these rates HBM is far from its roof."]
     tr_md += ["",

@@ -9,8 +9,9 @@ rows); this module compiles it with gcc and wraps it with ctypes.  Inputs are
 converted to float64 copies of whatever values the caller passes (for bf16
 problems: the exact bf16 values).
 
-Method (page "FlashSinkhorn: IO-aware entropic OT on GPU", section
-"Methodology", part 1): f_i <- -eps LSE_j[(g_j - C_ij)/eps + log b_j] with
+Method (page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU", section
+"Metodologia", part "1. Riformulazione in Forma di Attenzione"): f_i <- -eps LSE_j[(g_j - C_ij)/eps
++ log b_j] with
 C_ij = ||x_i - y_j||^2, then the mirrored update for g with the new f.
 
 Parity status of each function:
@@ -224,8 +225,9 @@ def transport_y(X, Y, a, b, f, g, eps: float, rows=None, threads=None):
 
 
 # ---------------------------------------------------------------------------
-# Cosine cost (page "FlashSinkhorn: IO-aware entropic OT on GPU", closing
-# remarks: the method covers squared-Euclidean cost and the cosine distance
+# Cosine cost (page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU",
+# section "Significato e Affermazioni": the method covers squared-Euclidean cost and the cosine
+# distance
 # after normalisation).  C_ij = ||x_i/|x_i| - y_j/|y_j|||^2 = 2 - 2 cos(x_i, y_j);
 # a zero point stays zero.  Every routine above applies unchanged to the
 # normalised clouds; only the gradient in the raw points needs the chain rule.
@@ -284,8 +286,9 @@ def apply_plan_y(X, Y, a, b, f, g, eps: float, U, rows=None, threads=None):
 
 def hvp_x(X, Y, a, b, f, g, eps: float, V) -> np.ndarray:
     """Hessian of the entropic OT value in the points X, applied to the direction V
-    (page "FlashSinkhorn: IO-aware entropic OT on GPU", section "Differentiation and
-    second-order optimisation": Hessian-vector products without the Hessian).
+    (page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU", section
+    "Metodologia", part "3. Differenziazione e Ottimizzazione del Secondo Ordine": Hessian-vector
+    products without the Hessian).
 
     Plain dense definition for small problems, at potentials (f, g) taken as optimal:
     the gradient is G_i = sum_j P_ij 2 (x_i - y_j).  Moving X along V moves the cost by

@@ -6,8 +6,8 @@
  * and the benchmark's CPU-baseline leg may build or call it; the product path
  * never does.  It shares no code, header or table with the HIP library.
  *
- * What it computes (page "FlashSinkhorn: IO-aware entropic OT on GPU",
- * section "Methodology", part 1 "attention-form reformulation"): the
+ * What it computes (page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU",
+ * section "Metodologia", part "1. Riformulazione in Forma di Attenzione"): the
  * stabilised log-domain update
  *
  *     f_i <- -eps * LSE_j [ (g_j - C_ij)/eps + log b_j ],
@@ -106,7 +106,8 @@ void oracle_half_step(int64_t np_, int64_t nq, int64_t d, const double* P, const
 
 /*
  * Sinkhorn iterations, alternating: f from g, then g from the new f
- * (page "FlashSinkhorn: IO-aware entropic OT on GPU", Methodology part 1;
+ * (page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU", section
+ * "Metodologia", part "1. Riformulazione in Forma di Attenzione";
  * the solver repeats the two updates a fixed number of times).
  * X [n, d], Y [m, d], a [n], b [m]; f [n], g [m] are in/out: only the
  * incoming g matters because every iteration starts with the f update.
@@ -157,9 +158,9 @@ void oracle_plan_marginals(int64_t n, int64_t m, int64_t d, const double* X, con
 }
 
 /*
- * Transport application for the rows of P (page "FlashSinkhorn: IO-aware
- * entropic OT on GPU", section "Differentiation and second-order
- * optimisation": the barycentric projection and the gradient are weighted
+ * Transport application for the rows of P (page "FlashSinkhorn: Trasporto Ottimo Entropico
+ * Consapevole delle I/O su GPU", section "Metodologia", part "3. Differenziazione e Ottimizzazione
+ * del Secondo Ordine": the barycentric projection and the gradient are weighted
  * averages over the transport plan, evaluated without forming the plan).
  *
  * With the plan entries pi_rj = wp_r wq_j exp((hp_r + hq_j - C_rj)/eps):
@@ -216,8 +217,8 @@ void oracle_transport(int64_t np_, int64_t nq, int64_t d, const double* P, const
 }
 
 /*
- * Plan applied to a matrix (page "FlashSinkhorn: IO-aware entropic OT on GPU",
- * section "Differentiation and second-order optimisation": vector- and
+ * Plan applied to a matrix (page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU",
+ * section "Metodologia", part "3. Differenziazione e Ottimizzazione del Secondo Ordine": vector- and
  * matrix-transport products):
  *   out[r*c + k] = sum_j pi_rj V[j*c + k],  pi_rj = wp_r wq_j exp((hp_r + hq_j - C_rj)/eps)
  * for the selected rows r of P (rows NULL = all).  V is [nq, c].

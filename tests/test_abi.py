@@ -185,3 +185,17 @@ def test_missing_library_fails_loudly(tmp_path):
     """No CPU fallback: a library path that does not exist raises, naming the build step."""
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         binding.load_library(str(tmp_path / "libsinkhorn.so"))
+
+
+def test_range_flags_query_validates(lib):
+    p = _prob(1, 300, 200, 3)
+    bp = ctypes.byref(p)
+    need = lib.sinkhorn_workspace_bytes(bp)
+    ptr = ctypes.c_void_p(0x1000)
+    assert lib.sinkhorn_range_flags(bp, ptr, need - 1, ptr, None) == 6
+    assert lib.sinkhorn_range_flags(bp, None, need, ptr, None) == 6
+    assert lib.sinkhorn_range_flags(bp, ptr, need, None, None) == 1
+    assert lib.sinkhorn_range_flags(None, ptr, need, ptr, None) == 1
+    text = open(HEADER).read()
+    assert "#define SK_FLAG_SCORE_RANGE 1u" in text and "#define SK_FLAG_NONFINITE 2u" in text
+    assert binding.SK_FLAG_SCORE_RANGE == 1 and binding.SK_FLAG_NONFINITE == 2

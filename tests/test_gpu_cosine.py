@@ -1,5 +1,6 @@
-"""GPU parity of the cosine cost (page "FlashSinkhorn: IO-aware entropic OT on
-GPU", closing remarks: cosine distance after normalisation) through the C ABI.
+"""GPU parity of the cosine cost (page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle
+I/O su GPU", section "Significato e Affermazioni": cosine distance after normalisation) through the
+C ABI.
 
 The oracle normalises the clouds in fp64 and runs its squared-Euclidean
 routines on them; the raw-point gradient applies the chain rule through the

@@ -1,6 +1,6 @@
 """GPU parity of the plan application (vector- and matrix-transport products) and
-the Hessian-vector product (page "FlashSinkhorn: IO-aware entropic OT on GPU",
-section "Differentiation and second-order optimisation") against the oracle.
+the Hessian-vector product (page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU",
+section "Metodologia", part "3. Differenziazione e Ottimizzazione del Secondo Ordine") against the oracle.
 
 Bounds:
   apply_plan: |d(PV)_ik| <= r_i (rel * max|V_k| (1 + dm) + |avg_ik| dm) with rel = 2e-5

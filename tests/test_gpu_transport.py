@@ -1,6 +1,7 @@
 """GPU parity of the transport application (barycentric projection and gradient)
-through the C ABI against the fp64 oracle (page "FlashSinkhorn: IO-aware
-entropic OT on GPU", section "Differentiation and second-order optimisation").
+through the C ABI against the fp64 oracle (page "FlashSinkhorn: Trasporto Ottimo Entropico
+Consapevole delle I/O su GPU", section "Metodologia", part "3. Differenziazione e Ottimizzazione del
+Secondo Ordine").
 
 Acceptance bounds, derived from the arithmetic of the two passes:
   bary: fp32 inputs |d bary| <= 2e-5 * max|V|, bf16 inputs <= 5e-4 * max|V| for d <= 128,

@@ -23,8 +23,11 @@ def test_operand_slots_match_kernel_instances():
 
 
 def test_algorithmic_bytes_of_the_headline_workload():
-    # 70000 queries and 70000 keys of 32 bf16 slots, plus 70000 fp32 potentials per launch
-    assert h.algorithmic_bytes(3) == 2 * 70000 * 32 * 2 + 70000 * 4
+    # half of an iteration's 2 (n+m) d s + 20 (n+m) bytes: fp32 coordinates, d = 3
+    assert h.algorithmic_bytes(3) == (2 * 140000 * 3 * 4 + 20 * 140000) / 2
+    # bf16 inputs at d = 128: 2-byte coordinates
+    assert h.algorithmic_bytes(4) == (2 * 98304 * 128 * 2 + 20 * 98304) / 2
+    assert h.operand_bytes(3) == 2 * 70000 * 32 * 2 + 70000 * 4
 
 
 def test_code_hash_ignores_comments_and_spacing():

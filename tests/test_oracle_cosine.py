@@ -1,5 +1,5 @@
-"""Pins for the oracle's cosine cost (page "FlashSinkhorn: IO-aware entropic OT
-on GPU", closing remarks: cosine distance after normalisation).
+"""Pins for the oracle's cosine cost (page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole
+delle I/O su GPU", section "Significato e Affermazioni": cosine distance after normalisation).
 
 The oracle runs the squared-Euclidean routines on normalised clouds, so the pins
 check the normalisation and the chain rule against independent facts:

@@ -1,6 +1,7 @@
 """Pins for the oracle's plan application and Hessian-vector product (page
-"FlashSinkhorn: IO-aware entropic OT on GPU", section "Differentiation and
-second-order optimisation": vector- and matrix-transport products, streaming HVP).
+"FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU", section "Metodologia",
+part "3. Differenziazione e Ottimizzazione del Secondo Ordine": vector- and matrix-transport
+products, streaming HVP).
 
 * apply_plan: a dense numpy plan; applied to the other cloud it equals
   mass * barycentric projection from the transport routine;

@@ -1,8 +1,9 @@
 """Pins for the fp64 CPU oracle, each against something other than the oracle.
 
 The pages print no worked example, so every pin here comes from mathematics the
-method fixes (page "FlashSinkhorn: IO-aware entropic OT on GPU", Methodology
-part 1: the stabilised log-domain update with squared-Euclidean cost):
+method fixes (page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU", section
+"Metodologia", part "1. Riformulazione in Forma di Attenzione": the stabilised log-domain update
+with squared-Euclidean cost):
 
 * plan marginals formed by brute force in numpy after each half-step,
 * closed forms for m = 1 and n = 1 (the latter through scipy's logsumexp),

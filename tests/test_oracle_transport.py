@@ -1,7 +1,8 @@
 """Pins for the oracle's transport application (barycentric projection, gradient, row mass).
 
-Page "FlashSinkhorn: IO-aware entropic OT on GPU", section "Differentiation and
-second-order optimisation": the barycentric projection and the gradient are
+Page "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU", section
+"Metodologia", part "3. Differenziazione e Ottimizzazione del Secondo Ordine": the barycentric
+projection and the gradient are
 weighted averages over the transport plan.  The pages print no numbers for
 them, so each pin comes from mathematics the definitions fix:
 
