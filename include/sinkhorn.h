@@ -84,6 +84,9 @@ typedef enum { SK_FP32 = 0, SK_BF16 = 1 } sk_dtype; /* element type of X and Y *
 #define SK_FLAG_SCORE_RANGE 1u /* a score beyond the supported range (see above) */
 #define SK_FLAG_NONFINITE 2u   /* a potential written as NaN or +-inf */
 
+/* Size of the built-in scratch array of sinkhorn_solve_noalloc (bytes). */
+#define SK_NOALLOC_MAX_BYTES (64u * 1024u * 1024u)
+
 /* Largest supported point dimension: bf16 inputs up to SK_MAX_D, fp32 inputs up
  * to SK_MAX_D_FP32 (their operands carry seven remainder products per coordinate
  * that must stay in registers).  The transport, plan-product and HVP calls keep
@@ -148,6 +151,23 @@ sk_status sinkhorn_half_step_g(const sk_problem* p, const void* X, const void* Y
 sk_status sinkhorn_solve(const sk_problem* p, const void* X, const void* Y, const float* a,
                          const float* b, const float* eps, int64_t n_eps, int64_t iters,
                          float* f, float* g, void* ws, size_t ws_bytes, void* stream);
+
+/* Allocation-free solve, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): sinkhorn_solve without ws and ws_bytes.  Its workspace is a
+ * scratch array built into the library, SK_NOALLOC_MAX_BYTES per GPU, held by
+ * every GPU the library runs on until the process ends.  Problems whose
+ * sinkhorn_workspace_bytes exceeds that size return SK_EWORKSPACE before
+ * anything is enqueued.  Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (other streams or threads) race, and the
+ * array keeps the last call's contents (each call starts with the set-up of
+ * sinkhorn_init_norms, which clears what must start at zero).
+ * flags: optional DEVICE word (NULL: not reported) that receives the status
+ * word (SK_FLAG_*) of this solve, stream-ordered.  Allocates nothing: no
+ * hipMalloc, no hipFree, no allocating library call. */
+sk_status sinkhorn_solve_noalloc(const sk_problem* p, const void* X, const void* Y, const float* a,
+                                 const float* b, const float* eps, int64_t n_eps, int64_t iters,
+                                 float* f, float* g, uint32_t* flags, void* stream);
 
 /* Copy the status word of ws (an OR of SK_FLAG_* over every call since the last
  * sinkhorn_init_norms on ws) into the DEVICE word *flags, stream-ordered (no

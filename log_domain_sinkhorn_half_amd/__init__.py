@@ -7,10 +7,10 @@ synthetic workloads.
 
 from .binding import (SK_BF16, SK_COSINE, SK_FP32, SK_SQEUCLID, SinkhornError, alloc_workspace, apply_plan_x,
                       apply_plan_y, barycentric_x, barycentric_y, half_step_f, half_step_g, hvp_x, hvp_y,
-                      init_norms, load_library, marginal_error, problem_of, range_flags, solve,
+                      init_norms, load_library, marginal_error, problem_of, range_flags, solve, solve_noalloc,
                       workspace_bytes)
 
 __all__ = ["SK_BF16", "SK_COSINE", "SK_FP32", "SK_SQEUCLID", "SinkhornError", "alloc_workspace", "apply_plan_x",
            "apply_plan_y", "barycentric_x", "barycentric_y", "half_step_f", "half_step_g", "hvp_x", "hvp_y",
-           "init_norms", "load_library", "marginal_error", "problem_of", "range_flags", "solve",
+           "init_norms", "load_library", "marginal_error", "problem_of", "range_flags", "solve", "solve_noalloc",
            "workspace_bytes"]

@@ -29,9 +29,10 @@ EXPORTS = ("sinkhorn_workspace_bytes", "sinkhorn_init_norms", "sinkhorn_half_ste
            "sinkhorn_half_step_g", "sinkhorn_solve", "sinkhorn_marginal_error",
            "sinkhorn_transport_workspace_bytes", "sinkhorn_barycentric_x", "sinkhorn_barycentric_y",
            "sinkhorn_apply_plan_x", "sinkhorn_apply_plan_y", "sinkhorn_hvp_workspace_bytes",
-           "sinkhorn_hvp_x", "sinkhorn_hvp_y", "sinkhorn_last_error",
+           "sinkhorn_hvp_x", "sinkhorn_hvp_y", "sinkhorn_last_error", "sinkhorn_solve_noalloc",
            "sinkhorn_range_flags")
 SK_FLAG_SCORE_RANGE, SK_FLAG_NONFINITE = 1, 2  # bits of the workspace's status word
+SK_NOALLOC_MAX_BYTES = 64 * 1024 * 1024  # built-in scratch array of sinkhorn_solve_noalloc
 
 
 class SkProblem(ctypes.Structure):
@@ -90,6 +91,9 @@ def load_library(path: Optional[str] = None):
         fn.argtypes = [P, vp, vp, vp, sz, f32p, f32p, ctypes.c_float, f32p, ctypes.c_int64, ctypes.c_float,
                        f32p, vp]
         fn.restype = ctypes.c_int
+    lib.sinkhorn_solve_noalloc.argtypes = [P, vp, vp, f32p, f32p, ctypes.POINTER(ctypes.c_float), ctypes.c_int64,
+                                           ctypes.c_int64, f32p, f32p, vp, vp]
+    lib.sinkhorn_solve_noalloc.restype = ctypes.c_int
     lib.sinkhorn_range_flags.argtypes = [P, vp, sz, vp, vp]
     lib.sinkhorn_range_flags.restype = ctypes.c_int
     lib.sinkhorn_last_error.argtypes = []
@@ -240,6 +244,30 @@ def solve(X, Y, a, b, eps: Union[float, Sequence[float]], iters: int, f=None, g=
         ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(a, "a", torch.float32), _dev(b, "b", torch.float32),
         earr, len(e), int(iters), _dev(f, "f", torch.float32), _dev(g, "g", torch.float32), _dev(ws, "ws"),
         ws.numel() * ws.element_size(), _stream(X))
+    return f, g
+
+
+def solve_noalloc(X, Y, a, b, eps: Union[float, Sequence[float]], iters: int, f=None, g=None,
+                  flags: Optional[torch.Tensor] = None, cost: int = SK_SQEUCLID):
+    """sinkhorn_solve_noalloc: the solve on the library's built-in scratch array (no
+    workspace; problems up to SK_NOALLOC_MAX_BYTES of workspace).  f and g are in/out
+    (zeros if not given); flags, if given, is a device int32 [1] that receives the
+    status word.  Returns (f, g)."""
+    p = problem_of(X, Y, cost)
+    for name, t, shp in (("a", a, (p.batch, p.n)), ("b", b, (p.batch, p.m)), ("f", f, (p.batch, p.n)),
+                         ("g", g, (p.batch, p.m)), ("flags", flags, (1,))):
+        _shape(t, name, shp)
+    _same_device(X, ("Y", Y), ("a", a), ("b", b), ("f", f), ("g", g), ("flags", flags))
+    if f is None:
+        f = torch.zeros((p.batch, p.n), dtype=torch.float32, device=X.device)
+    if g is None:
+        g = torch.zeros((p.batch, p.m), dtype=torch.float32, device=X.device)
+    e = [float(eps)] if isinstance(eps, (int, float)) else [float(v) for v in eps]
+    earr = (ctypes.c_float * len(e))(*e)
+    _call("sinkhorn_solve_noalloc",
+          ctypes.byref(p), _dev(X, "X"), _dev(Y, "Y"), _dev(a, "a", torch.float32), _dev(b, "b", torch.float32),
+          earr, len(e), int(iters), _dev(f, "f", torch.float32), _dev(g, "g", torch.float32),
+          None if flags is None else _dev(flags, "flags", torch.int32), _stream(X))
     return f, g
 
 

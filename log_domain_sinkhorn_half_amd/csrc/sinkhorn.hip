@@ -69,6 +69,12 @@
 
 #include "sinkhorn.h"
 
+// Built-in workspace of sinkhorn_solve_noalloc: SK_NOALLOC_MAX_BYTES of device
+// memory per GPU the library runs on, held until the process ends.  Host code
+// never uses this name as a device address: it takes each device's address
+// from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[SK_NOALLOC_MAX_BYTES];
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
@@ -2773,6 +2779,31 @@ sk_status solve_impl(const sk_problem* p, const void* X, const void* Y, const fl
   return st;
 }
 
+// Device address of this device's copy of the built-in scratch array (see
+// sinkhorn_solve_noalloc), looked up once per device with that device current.
+sk_status scratch_address(void** out) {
+  constexpr int MAX_DEV = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEV] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) {
+    set_err("no usable current device (hipGetDevice failed or device index >= %d)", MAX_DEV);
+    return SK_EHIP;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      set_err("hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+      return SK_EHIP;
+    }
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return SK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2841,6 +2872,31 @@ sk_status sinkhorn_solve(const sk_problem* p, const void* X, const void* Y, cons
   st = check_solve_args(X, Y, a, b, eps, n_eps, iters, f, g);
   if (st != SK_OK) return st;
   return solve_impl(p, X, Y, a, b, eps, n_eps, iters, f, g, ws, L, static_cast<hipStream_t>(stream));
+}
+
+sk_status sinkhorn_solve_noalloc(const sk_problem* p, const void* X, const void* Y, const float* a, const float* b,
+                                 const float* eps, int64_t n_eps, int64_t iters, float* f, float* g,
+                                 uint32_t* flags, void* stream) {
+  g_err[0] = 0;
+  sk_status st = check_problem(p);
+  if (st != SK_OK) return st;
+  const Layout L = layout_of(p);
+  if (L.total > (size_t)SK_NOALLOC_MAX_BYTES) {
+    set_err("problem needs %zu bytes of workspace, more than the %zu of the built-in scratch array "
+            "(use sinkhorn_solve with a workspace)", L.total, (size_t)SK_NOALLOC_MAX_BYTES);
+    return SK_EWORKSPACE;
+  }
+  st = check_solve_args(X, Y, a, b, eps, n_eps, iters, f, g);
+  if (st != SK_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != SK_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = solve_impl(p, X, Y, a, b, eps, n_eps, iters, f, g, ws, L, s);
+  if (st != SK_OK || flags == nullptr) return st;
+  hipLaunchKernelGGL(k_copy_u32, dim3(1), dim3(64), 0, s,
+                     reinterpret_cast<const unsigned*>(static_cast<char*>(ws) + L.status), flags);
+  return hip_check("status copy launch");
 }
 
 sk_status sinkhorn_range_flags(const sk_problem* p, const void* ws, size_t ws_bytes, uint32_t* flags, void* stream) {
