@@ -8,12 +8,15 @@ d = 3, fp32, eps = 0.01 (X uniform in the unit cube, Y an 8-Gaussian
 mixture), the scale the FlashSinkhorn summary calls the pain point (page
 "FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU", section "Enunciato del Problema").
 
-Prints ONE JSON line.  `roofline` covers the dominant kernel (the streaming
-half-step kernel k_lse): its launch duration is measured with HIP events on
-the stream the library launches on, around each half-step call (the window
-also holds the small key-preparation and split-merge kernels; the rocprofv3
-summary under profiles/ separates them).  `cpu_baseline` times the fp64 CPU
-oracle on a bounded row slice of the same workload on this host's cores.
+Prints ONE JSON line.  The timed region is one sinkhorn_solve call of --steps
+iterations (the product path: set-up, then fused half-steps that each write the
+next one's key bias), continuing a trajectory after --warmup lead-in
+iterations, after at least --min-warmup-s of untimed solves.  `roofline` covers
+the dominant kernel (the streaming half-step kernel k_lse): its duration is the
+timed solve's HIP-event time on the library's stream divided by its half-steps
+(that window also holds the split merges and the amortised set-up; the
+rocprofv3 summary under profiles/ separates them).  `cpu_baseline` times the
+fp64 CPU oracle on a bounded row slice of the same workload on this host's cores.
 """
 
 from __future__ import annotations
@@ -129,47 +132,65 @@ def main():
     def eps_at(k):
         return eps_sched[k % len(eps_sched)] if len(eps_sched) > 1 else eps_sched[0]
 
-    sk.init_norms(X, Y, a, b, ws)
-    # untimed warm-up: at least --warmup iterations and at least --min-warmup-s of
-    # wall time (the stream is synchronised every few iterations so that the wall
-    # time is GPU time, not host run-ahead)
+    K, W = args.steps, args.warmup
+
+    def sched(k0, count):
+        """eps of iterations k0 .. k0+count-1 (the schedule repeats past its end)."""
+        if len(eps_sched) == 1:
+            return eps_sched[0]
+        return [eps_at(k) for k in range(k0, k0 + count)]
+
+    # untimed warm-up: whole solves of max(W, 8) iterations until at least
+    # --min-warmup-s of wall time has passed (each solve synchronises, so the
+    # wall time is GPU time, not host run-ahead)
     t_warm = time.perf_counter()
     warm_iters = 0
-    while warm_iters < args.warmup or time.perf_counter() - t_warm < args.min_warmup_s:
-        sk.half_step_f(X, Y, ws, g, eps_at(warm_iters), f=f)
-        sk.half_step_g(X, Y, ws, f, eps_at(warm_iters), g=g)
-        warm_iters += 1
-        if warm_iters % 8 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
+    while warm_iters < W or time.perf_counter() - t_warm < args.min_warmup_s:
+        it = max(W, 8)
+        f.zero_()
+        g.zero_()
+        sk.solve(X, Y, a, b, sched(0, it), it, f=f, g=g, ws=ws)
+        torch.cuda.synchronize()
+        warm_iters += it
     warm_s = time.perf_counter() - t_warm
-    # restart the trajectory so the timed steps see the same potentials whatever
-    # the warm-up length was
-    sk.init_norms(X, Y, a, b, ws)
+    # the timed steps continue a trajectory from f = g = 0 after W lead-in iterations
     f.zero_()
     g.zero_()
-    for k in range(args.warmup):
-        sk.half_step_f(X, Y, ws, g, eps_at(k), f=f)
-        sk.half_step_g(X, Y, ws, f, eps_at(k), g=g)
+    if W > 0:
+        sk.solve(X, Y, a, b, sched(0, W), W, f=f, g=g, ws=ws)
     torch.cuda.synchronize()
 
-    K = args.steps
+    # timed region: ONE sinkhorn_solve of K iterations (its set-up of norms,
+    # centre and operands included), HIP events on the library's stream around it
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K + 1)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev[0].record(stream)
-    for k in range(K):
-        e = eps_at(args.warmup + k)
-        sk.half_step_f(X, Y, ws, g, e, f=f)
-        ev[2 * k + 1].record(stream)
-        sk.half_step_g(X, Y, ws, f, e, g=g)
-        ev[2 * k + 2].record(stream)
+    ev0.record(stream)
+    sk.solve(X, Y, a, b, sched(W, K), K, f=f, g=g, ws=ws)
+    ev1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    half_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(2 * K)])
-    f_ms, g_ms = half_ms[0::2], half_ms[1::2]
+    solve_ms = ev0.elapsed_time(ev1)
     assert torch.isfinite(f).all() and torch.isfinite(g).all(), "non-finite potentials"
+    flags = sk.range_flags(X, Y, ws)
+
+    # side measurement (not the headline): the same iterations as standalone
+    # half-step calls, each preparing its key operand, with events per half-step
+    M = min(K, 10)
+    f2, g2 = f.clone(), g.clone()
+    evh = [torch.cuda.Event(enable_timing=True) for _ in range(2 * M + 1)]
+    torch.cuda.synchronize()
+    evh[0].record(stream)
+    for k in range(M):
+        e = eps_at(W + k)
+        sk.half_step_f(X, Y, ws, g2, e, f=f2)
+        evh[2 * k + 1].record(stream)
+        sk.half_step_g(X, Y, ws, f2, e, g=g2)
+        evh[2 * k + 2].record(stream)
+    torch.cuda.synchronize()
+    half_ms = np.array([evh[i].elapsed_time(evh[i + 1]) for i in range(2 * M)])
+    f_ms, g_ms = half_ms[0::2], half_ms[1::2]
 
     iters_per_s = K / elapsed
     ms_per_step = 1e3 * elapsed / K
@@ -183,8 +204,11 @@ def main():
     t_roof = max(t_exp, t_mfma)
     frac_iter = t_roof / (elapsed / K)
 
-    # dominant kernel: one half-step launch processes B*n*m (f) or B*m*n (g) score elements
-    launch_s = float(np.mean(half_ms)) / 1e3
+    # dominant kernel: one half-step launch processes B*n*m (f) or B*m*n (g) score
+    # elements; its duration is taken as the timed solve's event time over its 2K
+    # half-steps (which also holds the split merges and the amortised set-up, so
+    # the fraction errs low; the rocprofv3 summary gives the kernel alone)
+    launch_s = solve_ms / (2 * K) / 1e3
     elems_launch = B * n * m
     workload = f"C{args.config}"
     traffic = read_traffic("k_lse", workload)
@@ -198,7 +222,7 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_MFMA[contraction], 4)}
     roof["traffic"] = traffic
     roof["launch_ms"] = round(launch_s * 1e3, 4)
-    roof["launch_ms_median"] = round(float(np.median(half_ms)), 4)
+    roof["window"] = f"one sinkhorn_solve of {K} iterations, HIP events on its stream, per half-step"
 
     out = {
         "metric": METRIC,
@@ -218,7 +242,12 @@ def main():
                    "batch": B, "n": n, "m": m, "d": d, "parallelism": "single GPU"},
         "effective_tflops": round(eff_tflops, 3),
         "roofline_frac_per_iteration": round(frac_iter, 4),
-        "half_step_ms": {"f": round(float(np.mean(f_ms)), 4), "g": round(float(np.mean(g_ms)), 4)},
+        "solve_event_ms": round(solve_ms, 4),
+        "range_flags": flags,
+        "standalone_half_steps": {
+            "what": f"{M} iterations as half_step_f / half_step_g calls, each preparing its key operand",
+            "half_step_ms": {"f": round(float(np.mean(f_ms)), 4), "g": round(float(np.mean(g_ms)), 4)},
+            "iters_per_s": round(1e3 / float(np.sum(half_ms) / M), 2)},
         "roofline": roof,
         "warmup_done": {"iterations": warm_iters, "seconds": round(warm_s, 3),
                         "rule": f"max(--warmup, {args.min_warmup_s} s of iterations), then the trajectory restarts "

@@ -411,15 +411,14 @@ __device__ __forceinline__ Parts key_split(double yc, float l2, float q, float i
   return p;
 }
 
-// Bias lambda*(pot - norm + eps*logw) of key r in parts: bp[0..2] its multiple
+// Bias lambda*(pot - norm + eps*logw) of one key in parts: bp[0..2] its multiple
 // of the grid quantum Q (exact in three bf16 parts), bp[3..4] the remainder.
 // Keys of zero weight and padding keys (real == false) take NEG_BIG alone.
-__device__ __forceinline__ void bias_parts(bool real, size_t r, const float* __restrict__ pot,
-                                           const double* __restrict__ norm, const double* __restrict__ logw,
-                                           float lam, float eps, double Q, double iQ, u16 (&bp)[5]) {
+__device__ __forceinline__ void bias_parts(bool real, float pot, double norm, double logw, float lam, float eps,
+                                           double Q, double iQ, u16 (&bp)[5]) {
   double bias = (double)NEG_BIG;
   if (real) {
-    bias = (double)lam * ((double)pot[r] - norm[r] + (double)eps * logw[r]);
+    bias = (double)lam * ((double)pot - norm + (double)eps * logw);
     if (!(bias >= (double)NEG_BIG)) bias = (double)NEG_BIG;  // zero weight (-inf) or underflow
   }
   for (int e = 0; e < 5; ++e) bp[e] = 0;
@@ -479,7 +478,8 @@ __global__ __launch_bounds__(256) void k_prep_keys(const void* __restrict__ P, i
   if (fresh) {
     for (long long j = gtid; j < keys_pad; j += stride) {
       u16 bp[5];
-      bias_parts(j < keys, (size_t)b * keys + j, pot, norm, logw, lam, eps, Q, iQ, bp);
+      const size_t r = (size_t)b * keys + (j < keys ? j : 0);
+      bias_parts(j < keys, pot[r], norm[r], logw[r], lam, eps, Q, iQ, bp);
       u16* row = kb + ((size_t)b * keys_pad + j) * KP;
       row[2] = bp[0];
       row[3] = bp[1];
@@ -501,7 +501,10 @@ __global__ __launch_bounds__(256) void k_prep_keys(const void* __restrict__ P, i
       return f32 ? key_split(yc, l2f, qkf, iqkf) : grid_split(lam2 * yc, qk, iqk);
     };
     u16 bp[5] = {0, 0, 0, 0, 0};
-    if (seg == 0 || seg == sb1 || seg == sb2) bias_parts(real, r, pot, norm, logw, lam, eps, Q, iQ, bp);
+    if (seg == 0 || seg == sb1 || seg == sb2) {
+      const size_t rr = real ? r : (size_t)b * keys;
+      bias_parts(real, pot[rr], norm[rr], logw[rr], lam, eps, Q, iQ, bp);
+    }
     u16 v[8];
     if (k0 < cb) {
       // grid section: offset slots (ones), bias grid parts, coordinate grid parts;
@@ -719,13 +722,54 @@ __device__ __forceinline__ Blk xcd_block() {
   return {l % gx, (l / gx) % gy, l / (gx * gy)};
 }
 
+// The next half-step's key bias, written where a potential is finalised (the
+// fused update of the page's part "2. Kernel di Streaming e Tassellazione": score,
+// bias, reduction and potential in one pass).  The rows of this half-step are
+// the keys of the next one, so once p_i is known its bias there follows:
+// lambda'(p_i - |x_i|^2 + eps' log w_i) in grid parts into the five bias slots of
+// row i of the split key operand (fp32 path; only valid while that operand's
+// coordinate parts are built for lambda'), or (p_i - |x_i|^2 + eps' log w_i)/2
+// into the half-bias vector (bf16 path).  The values are the ones the
+// preparation kernels would write, so skipping them changes no result.
+struct NextBias {
+  u16* kb;              // split key operand of the next half-step (fp32 path), or nullptr
+  float* hb;            // half bias of the next half-step (bf16 path), or nullptr
+  const double* logw;   // log-weights of this half-step's rows
+  const float* qmax;    // largest |coordinate| of the next half-step's query cloud, per problem
+  const float* kmax;    // the same for this half-step's rows (the next keys)
+  float lam, eps;       // the next half-step's lambda and eps
+  int rows_pad, KP, cb, d;
+};
+
+__device__ __forceinline__ void write_next_bias(const NextBias& nb, int b, int q, float pot, double norm,
+                                                double logw) {
+  if (nb.kb != nullptr) {
+    const int qqe = grid_exponent(nb.qmax[b]);
+    const int qke = grid_exponent(2.0 * (double)nb.lam * (double)nb.kmax[b]);
+    const double Q = ldexp(1.0, qqe + qke), iQ = ldexp(1.0, -(qqe + qke));
+    u16 bp[5];
+    bias_parts(true, pot, norm, logw, nb.lam, nb.eps, Q, iQ, bp);
+    u16* row = nb.kb + ((size_t)b * nb.rows_pad + q) * nb.KP;
+    row[2] = bp[0];
+    row[3] = bp[1];
+    row[4] = bp[2];
+    row[nb.cb + 7 * nb.d] = bp[3];
+    row[nb.cb + 7 * nb.d + 1] = bp[4];
+  } else if (nb.hb != nullptr) {
+    float v = (float)(0.5 * ((double)pot - norm + (double)nb.eps * logw));
+    if (!(v >= NEG_BIG)) v = NEG_BIG;
+    nb.hb[(size_t)b * nb.rows_pad + q] = v;
+  }
+}
+
 // TCX overrides the key tiles per chunk (0: cfg_TC), for small problems.
 template <int MODE, int NCH, int TCX = 0>
 __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves_per_eu(cfg_waves(MODE, NCH)))) void k_lse(
     const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb,
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, float* __restrict__ out,
     float2* __restrict__ part, int rows, int rows_pad, int keys, int keys_pad, int chunks_per_split, int batch,
-    float lam2, double inv_lam, unsigned* __restrict__ tag, unsigned tag_val, unsigned* __restrict__ status) {
+    float lam2, double inv_lam, unsigned* __restrict__ tag, unsigned tag_val, unsigned* __restrict__ status,
+    NextBias nb) {
   constexpr int MW = cfg_MW(MODE, NCH), R = cfg_R(MODE, NCH), TC = TCX ? TCX : cfg_TC(MODE, NCH);
   using T = Tile<MW>;
   using Acc = typename T::Acc;
@@ -979,6 +1023,7 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
         const float v = (float)(qnorm[r] - ((double)m[c] + log2((double)st)) * inv_lam);
         out[r] = v;
         flag_if(status, !isfinite(v), FLAG_NONFINITE);
+        if (nb.logw != nullptr) write_next_bias(nb, b, q, v, qnorm[r], nb.logw[r]);
       }
     }
   }
@@ -986,9 +1031,9 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
 
 // Merge the (max, sum) pairs of the key splits (one pass, exact power-of-two
 // rescaling) and write the potential.
-__global__ __launch_bounds__(256) void k_merge(const float2* __restrict__ part, int ks, int total,
+__global__ __launch_bounds__(256) void k_merge(const float2* __restrict__ part, int ks, int total, int rows,
                                                const double* __restrict__ qnorm, float* __restrict__ out,
-                                               double inv_lam, unsigned* __restrict__ status) {
+                                               double inv_lam, unsigned* __restrict__ status, NextBias nb) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
   // Two passes over the partials (the second from cache): the loads of a pass
@@ -1004,6 +1049,7 @@ __global__ __launch_bounds__(256) void k_merge(const float2* __restrict__ part, 
   const float v = (float)(qnorm[i] - ((double)M + log2((double)S)) * inv_lam);
   out[i] = v;
   flag_if(status, !isfinite(v), FLAG_NONFINITE);
+  if (nb.logw != nullptr) write_next_bias(nb, i / rows, i % rows, v, qnorm[i], nb.logw[i]);
 }
 
 // sum_i exp(logw_i) * |expm1((pot_i - tilde_i)/eps)|, one workgroup per problem, fixed order.
@@ -1962,8 +2008,9 @@ __global__ __launch_bounds__(256) void k_hvp_final(const void* __restrict__ P, i
 struct Layout {
   int mode, KP, n_pad, m_pad, max_pad;
   int in_bf16, cosine;
-  size_t xn, yn, la, lb, rx, ry, maxabs, cen, box, inexact, status, qgrid, ktag, qx, qy, kbx, kby, hb, part, scratch,
-      total;
+  size_t xn, yn, la, lb, rx, ry, maxabs, cen, box, inexact, status, qgrid, ktag, qx, qy, kbx, kby, hb, hb1, part,
+      scratch, total;
+  size_t hbs(int side) const { return side == 0 ? hb : hb1; }
   // key operand of the fp32 path for side 0 (Y as keys) or side 1 (X as keys)
   size_t kb(int side) const { return side == 0 ? kby : kbx; }
   // transport application and plan products (after `total`; only their entry points need them)
@@ -2045,7 +2092,7 @@ Layout layout_of(const sk_problem* p) {
   L.box = take(4 * 4 * B * (size_t)p->d);           // bounding boxes of both clouds (ordered codes)
   L.inexact = take(4 * B);                          // bf16 problems left uncentred
   L.status = take(16);                              // range flags (SK_FLAG_*)
-  L.qgrid = take(4 * B);
+  L.qgrid = take(4 * 2 * B);  // grid quantum of each side's key operand, [side][B]
   L.ktag = take(16);  // lambda tags of the two key operands
   // SLACK extra rows after each operand buffer absorb the kernels' unguarded
   // over-reads at the end of the last chunk.
@@ -2053,7 +2100,9 @@ Layout layout_of(const sk_problem* p) {
   L.qy = take(2 * (B * L.m_pad + SLACK) * L.KP);
   L.kbx = (L.mode == MODE_SPLIT) ? take(2 * (B * L.n_pad + SLACK) * L.KP) : 0;
   L.kby = (L.mode == MODE_SPLIT) ? take(2 * (B * L.m_pad + SLACK) * L.KP) : 0;
-  L.hb = (L.mode == MODE_BF16) ? take(4 * (B * L.max_pad + SLACK)) : 0;
+  // half bias of each side's keys (bf16 path): side 0 (keys Y) then side 1 (keys X)
+  L.hb = (L.mode == MODE_BF16) ? take(4 * (B * L.m_pad + SLACK)) : 0;
+  L.hb1 = (L.mode == MODE_BF16) ? take(4 * (B * L.n_pad + SLACK)) : 0;
   L.part = take(8 * (size_t)KS_MAX * B * mx);
   L.scratch = take(4 * B * mx);
   L.total = off;
@@ -2098,7 +2147,7 @@ Layout layout_of(const sk_problem* p) {
 }
 
 using LseFn = void (*)(const u16*, const u16*, const float*, const float*, const double*, float*, float2*, int, int,
-                       int, int, int, int, float, double, unsigned*, unsigned, unsigned*);
+                       int, int, int, int, float, double, unsigned*, unsigned, unsigned*, NextBias);
 
 template <int MODE, int NCH>
 LseFn lse_fn() {
@@ -2213,22 +2262,37 @@ bool eps_ok(float eps) { return eps > 0.f && isfinite(eps) && isfinite((float)(L
 
 // Key operand of one side for the potential pot_in and eps: the split key rows
 // (fp32 path) or the half bias (bf16 path).  Returns the key operand and bias.
+// Key operand of one side (side 0: keys Y for the f half-step; side 1: keys X)
+// for the potential pot_in and eps: the split key rows (fp32 path) or the half
+// bias (bf16 path), and the grid quantum of that side (fp32 path).  With
+// launch == false nothing is enqueued: the operand's bias was already written
+// for this potential and eps by the kernel that produced pot_in.
+struct KeyOperand {
+  const u16* K = nullptr;
+  const float* hb = nullptr;
+  const float* qgrid = nullptr;
+  unsigned* tag = nullptr;
+};
+
 sk_status prep_keys(const sk_problem* p, const void* X, const void* Y, char* w, const Layout& L, const float* pot_in,
-                    float eps, int side, hipStream_t stream, const u16** Kop, const float** hb,
-                    unsigned** tag_out = nullptr) {
+                    float eps, int side, hipStream_t stream, KeyOperand* out, bool launch = true) {
   const int B = (int)p->batch;
   const int keys = (int)(side == 0 ? p->m : p->n);
   const int keys_pad = side == 0 ? L.m_pad : L.n_pad;
   const double* knorm = reinterpret_cast<const double*>(w + (side == 0 ? L.yn : L.xn));
   const double* klogw = reinterpret_cast<const double*>(w + (side == 0 ? L.lb : L.la));
   const float* maxabs = reinterpret_cast<const float*>(w + L.maxabs);
-  float* qgrid = reinterpret_cast<float*>(w + L.qgrid);
+  float* qgrid = reinterpret_cast<float*>(w + L.qgrid) + side * B;
   const void* Kraw = side == 0 ? Y : X;
   const float lam = (float)(LOG2E / (double)eps);
-  *hb = nullptr;
+  *out = KeyOperand{};
+  out->qgrid = qgrid;
   if (L.mode == MODE_SPLIT) {
     u16* kb = reinterpret_cast<u16*>(w + L.kb(side));
     unsigned* tag = reinterpret_cast<unsigned*>(w + L.ktag) + side;
+    out->K = kb;
+    out->tag = tag;
+    if (!launch) return SK_OK;
     // about PREP_SEGS segments per thread when every segment is rebuilt
     const dim3 kgrid((unsigned)(((long long)keys_pad * (L.KP / 8) + 256 * PREP_SEGS - 1) / (256 * PREP_SEGS)), B);
     const double* krn = reinterpret_cast<const double*>(w + (side == 0 ? L.ry : L.rx));
@@ -2236,21 +2300,47 @@ sk_status prep_keys(const sk_problem* p, const void* X, const void* Y, char* w, 
                        reinterpret_cast<const double*>(w + L.cen), pot_in, knorm,
                        klogw, keys, keys_pad, (int)p->d, L.KP, lam, eps, maxabs + (side == 0 ? 0 : B),
                        maxabs + (side == 0 ? B : 0), qgrid, tag, kb);
-    *Kop = kb;
-    if (tag_out != nullptr) *tag_out = tag;
   } else {
-    float* hbw = reinterpret_cast<float*>(w + L.hb);
+    float* hbw = reinterpret_cast<float*>(w + L.hbs(side));
+    out->hb = hbw;
+    out->K = reinterpret_cast<const u16*>(w + (side == 0 ? L.qy : L.qx));
+    if (!launch) return SK_OK;
     const dim3 pgrid((keys_pad + 255) / 256, B);
     hipLaunchKernelGGL(k_prep_bias, pgrid, dim3(256), 0, stream, pot_in, knorm, klogw, keys, keys_pad, eps, hbw);
-    *hb = hbw;
-    *Kop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qy : L.qx));
   }
   return hip_check("key preparation launch");
 }
 
+// The NextBias of a half-step on `side` whose successor runs on 1 - side at
+// eps_next (writes the successor's key bias), or an empty one.
+NextBias next_bias(const sk_problem* p, char* w, const Layout& L, int side, float eps_next, bool enable) {
+  NextBias nb{};
+  if (!enable) return nb;
+  const int B = (int)p->batch, ns = 1 - side;
+  const float* maxabs = reinterpret_cast<const float*>(w + L.maxabs);
+  nb.logw = reinterpret_cast<const double*>(w + (side == 0 ? L.la : L.lb));
+  nb.qmax = maxabs + (ns == 0 ? 0 : B);
+  nb.kmax = maxabs + (ns == 0 ? B : 0);
+  nb.lam = (float)(LOG2E / (double)eps_next);
+  nb.eps = eps_next;
+  nb.rows_pad = side == 0 ? L.n_pad : L.m_pad;
+  nb.KP = L.KP;
+  nb.cb = split_corr_begin((int)p->d);
+  nb.d = (int)p->d;
+  if (L.mode == MODE_SPLIT)
+    nb.kb = reinterpret_cast<u16*>(w + L.kb(ns));
+  else
+    nb.hb = reinterpret_cast<float*>(w + L.hbs(ns));
+  return nb;
+}
+
 // One half-step.  side 0: f from g (queries X, keys Y); side 1: g from f.
+// bias_ready: the key bias for pot_in and eps is already in place (written by
+// the producer of pot_in), so no preparation kernel runs.  nb: write the next
+// half-step's key bias where the potential is finalised (see NextBias).
 sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws, const Layout& L,
-                    const float* pot_in, float eps, float* pot_out, int side, hipStream_t stream) {
+                    const float* pot_in, float eps, float* pot_out, int side, hipStream_t stream,
+                    bool bias_ready = false, NextBias nb = NextBias{}) {
   char* w = static_cast<char*>(ws);
   const int B = (int)p->batch;
   const int rows = (int)(side == 0 ? p->n : p->m);
@@ -2258,16 +2348,13 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   const int rows_pad = side == 0 ? L.n_pad : L.m_pad;
   const int keys_pad = side == 0 ? L.m_pad : L.n_pad;
   const double* qnorm = reinterpret_cast<const double*>(w + (side == 0 ? L.xn : L.yn));
-  const float* qgrid = reinterpret_cast<const float*>(w + L.qgrid);
   const u16* Qop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qx : L.qy));
   const int nch = L.KP / 32;
   const int cfMW = cfg_MW(L.mode, nch), cfR = cfg_R(L.mode, nch), cfTC = cfg_TC(L.mode, nch);
   const float lam = (float)(LOG2E / (double)eps);
 
-  const u16* Kop = nullptr;
-  const float* hb = nullptr;
-  unsigned* tag = nullptr;
-  sk_status st = prep_keys(p, X, Y, w, L, pot_in, eps, side, stream, &Kop, &hb, &tag);
+  KeyOperand ko;
+  sk_status st = prep_keys(p, X, Y, w, L, pot_in, eps, side, stream, &ko, !bias_ready);
   if (st != SK_OK) return st;
 
   LseFn fn = (L.mode == MODE_SPLIT) ? lse_lookup<MODE_SPLIT>(nch) : lse_lookup<MODE_BF16>(nch);
@@ -2293,14 +2380,14 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   float2* part = ks > 1 ? reinterpret_cast<float2*>(w + L.part) : nullptr;
   const double inv_lam = 1.0 / (double)lam;
   unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
-  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NW), 0, stream, Qop, Kop, hb, qgrid, qnorm, pot_out, part, rows,
-                     rows_pad, keys, keys_pad, cps, B, 2.f * lam, inv_lam, tag, __builtin_bit_cast(unsigned, lam),
-                     status);
+  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NW), 0, stream, Qop, ko.K, ko.hb, ko.qgrid, qnorm, pot_out,
+                     part, rows, rows_pad, keys, keys_pad, cps, B, 2.f * lam, inv_lam, ko.tag,
+                     __builtin_bit_cast(unsigned, lam), status, ks == 1 ? nb : NextBias{});
   st = hip_check("half-step kernel launch");
   if (st != SK_OK || ks == 1) return st;
   const int total = B * rows;
-  hipLaunchKernelGGL(k_merge, dim3((total + 255) / 256), dim3(256), 0, stream, part, ks, total, qnorm, pot_out,
-                     inv_lam, status);
+  hipLaunchKernelGGL(k_merge, dim3((total + 255) / 256), dim3(256), 0, stream, part, ks, total, rows, qnorm, pot_out,
+                     inv_lam, status, nb);
   return hip_check("split merge launch");
 }
 
@@ -2338,7 +2425,6 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   const int keys_pad = side == 0 ? L.m_pad : L.n_pad;
   const double* qnorm = reinterpret_cast<const double*>(w + (side == 0 ? L.xn : L.yn));
   const double* qlogw = reinterpret_cast<const double*>(w + (side == 0 ? L.la : L.lb));
-  const float* qgrid = reinterpret_cast<const float*>(w + L.qgrid);
   const u16* Qop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qx : L.qy));
   const void* Praw = side == 0 ? X : Y;
   const void* Kraw = side == 0 ? Y : X;
@@ -2348,10 +2434,8 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   // 1. The key operand of this side for the other potential and eps.  The P.V
   //    pass keeps lazy row offsets, so no half-step runs first: its merge
   //    recovers each row's log-sum-exp (into scratch) from the offsets and sums.
-  const u16* Kop = nullptr;
-  const float* hb = nullptr;
-  unsigned* tag = nullptr;
-  sk_status st = prep_keys(p, X, Y, w, L, side == 0 ? g : f, eps, side, stream, &Kop, &hb, &tag);
+  KeyOperand ko;
+  sk_status st = prep_keys(p, X, Y, w, L, side == 0 ? g : f, eps, side, stream, &ko);
   if (st != SK_OK) return st;
 
   // 2. Value operand from the other cloud's coordinates.
@@ -2388,9 +2472,9 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   float* bs = reinterpret_cast<float*>(w + L.bs);
   float* bm = reinterpret_cast<float*>(w + L.bm);
   const float lam = (float)(LOG2E / (double)eps);
-  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NWb), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, nullptr, bpv, bs, rows,
-                     rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, bm, tag, __builtin_bit_cast(unsigned, lam), nullptr,
-                     1.f, status);
+  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NWb), 0, stream, Qop, ko.K, ko.hb, vt, ko.qgrid, qnorm, nullptr,
+                     bpv, bs, rows, rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, bm, ko.tag,
+                     __builtin_bit_cast(unsigned, lam), nullptr, 1.f, status);
   st = hip_check("transport kernel launch");
   if (st != SK_OK) return st;
 
@@ -2445,12 +2529,9 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
   const int keys_pad = side == 0 ? L.m_pad : L.n_pad;
   const double* qnorm = reinterpret_cast<const double*>(w + (side == 0 ? L.xn : L.yn));
   const double* qlogw = reinterpret_cast<const double*>(w + (side == 0 ? L.la : L.lb));
-  const float* qgrid = reinterpret_cast<const float*>(w + L.qgrid);
   const u16* Qop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qx : L.qy));
-  const u16* Kop = nullptr;
-  const float* hb = nullptr;
-  unsigned* ptag = nullptr;
-  sk_status st = prep_keys(p, X, Y, w, L, pot_key, eps, side, stream, &Kop, &hb, &ptag);
+  KeyOperand ko;
+  sk_status st = prep_keys(p, X, Y, w, L, pot_key, eps, side, stream, &ko);
   if (st != SK_OK) return st;
   u16* vt = reinterpret_cast<u16*>(w + L.vt);
   float* bpv = reinterpret_cast<float*>(w + L.bpv);
@@ -2481,8 +2562,8 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
     const int ks_cap = (int)std::min<size_t>(16, std::max<size_t>(1, L.bpv_bytes / (4 * (size_t)B * rows * nc)));
     int cps = 0;
     const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps, ks_cap);
-    hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NWb), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, lse, bpv, bs,
-                       rows, rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, nullptr, ptag,
+    hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NWb), 0, stream, Qop, ko.K, ko.hb, vt, ko.qgrid, qnorm, lse,
+                       bpv, bs, rows, rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, nullptr, ko.tag,
                        __builtin_bit_cast(unsigned, lam), nullptr, 1.f, reinterpret_cast<unsigned*>(w + L.status));
     st = hip_check("plan-application kernel launch");
     if (st != SK_OK) return st;
@@ -2527,13 +2608,10 @@ sk_status apply_uw(const sk_problem* p, const void* X, const void* Y, char* w, c
   const int keys_pad = side == 0 ? L.m_pad : L.n_pad;
   const double* qnorm = reinterpret_cast<const double*>(w + (side == 0 ? L.xn : L.yn));
   const double* qlogw = reinterpret_cast<const double*>(w + (side == 0 ? L.la : L.lb));
-  const float* qgrid = reinterpret_cast<const float*>(w + L.qgrid);
   const u16* Qop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qx : L.qy));
   const void* Kraw = side == 0 ? Y : X;
-  const u16* Kop = nullptr;
-  const float* hb = nullptr;
-  unsigned* ptag = nullptr;
-  sk_status st = prep_keys(p, X, Y, w, L, pot_key, eps, side, stream, &Kop, &hb, &ptag);
+  KeyOperand ko;
+  sk_status st = prep_keys(p, X, Y, w, L, pot_key, eps, side, stream, &ko);
   if (st != SK_OK) return st;
   u16* U = reinterpret_cast<u16*>(w + L.h_u);
   hipLaunchKernelGGL(k_prep_u, dim3((rows_pad + 255) / 256, B), dim3(256), 0, stream, Vdir, rows, rows_pad, d, L.KP,
@@ -2567,9 +2645,9 @@ sk_status apply_uw(const sk_problem* p, const void* X, const void* Y, char* w, c
   const float lam = (float)(LOG2E / (double)eps);
   // the fp32 key operand holds 2 lambda q
   const float ugain = L.mode == MODE_SPLIT ? 1.f / (2.f * lam) : 1.f;
-  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NWb), 0, stream, Qop, Kop, hb, vt, qgrid, qnorm, lse, bpv, bs, rows,
-                     rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, nullptr, ptag, __builtin_bit_cast(unsigned, lam),
-                     U, ugain, reinterpret_cast<unsigned*>(w + L.status));
+  hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NWb), 0, stream, Qop, ko.K, ko.hb, vt, ko.qgrid, qnorm, lse, bpv,
+                     bs, rows, rows_pad, keys, keys_pad, cps, B, lam, 2.f * lam, nullptr, ko.tag,
+                     __builtin_bit_cast(unsigned, lam), U, ugain, reinterpret_cast<unsigned*>(w + L.status));
   st = hip_check("row-weighted plan kernel launch");
   if (st != SK_OK) return st;
   const long long total = (long long)B * rows * d;
@@ -2735,6 +2813,15 @@ sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const flo
   };
   side(X, a, (int)p->n, L.n_pad, maxabs, L.xn, L.la, L.rx, L.qx);
   side(Y, b, (int)p->m, L.m_pad, maxabs + B, L.yn, L.lb, L.ry, L.qy);
+  if (L.mode == MODE_BF16) {
+    // half-bias vectors: padding keys (never written by a potential's epilogue)
+    // remove themselves with the most negative bias
+    const int nh0 = B * L.m_pad + SLACK, nh1 = B * L.n_pad + SLACK;
+    hipLaunchKernelGGL(k_fill_f32, dim3((nh0 + 255) / 256), dim3(256), 0, stream,
+                       reinterpret_cast<float*>(w + L.hb), nh0, NEG_BIG);
+    hipLaunchKernelGGL(k_fill_f32, dim3((nh1 + 255) / 256), dim3(256), 0, stream,
+                       reinterpret_cast<float*>(w + L.hb1), nh1, NEG_BIG);
+  }
   // the slack rows after the last problem's operand rows: a workgroup whose
   // query rows run past the padding reads zeros there
   zero(L.qx + 2 * (size_t)B * L.n_pad * L.KP, 2 * (size_t)SLACK * L.KP);
@@ -2767,14 +2854,41 @@ sk_status check_solve_args(const void* X, const void* Y, const float* a, const f
 }
 
 // init, then iters x (f half-step, g half-step), all enqueued on one stream.
+// Each half-step writes the key bias its successor needs where it finalises
+// its potential, so the successor launches no preparation kernel.  bf16 path:
+// always (the bias is all that changes with the potential and eps).  fp32
+// path: while eps stays the same, once the successor's key operand holds its
+// coordinate parts for that eps (built by a preparation earlier in this solve);
+// an eps change rebuilds them with a preparation kernel.
 sk_status solve_impl(const sk_problem* p, const void* X, const void* Y, const float* a, const float* b,
                      const float* eps, int64_t n_eps, int64_t iters, float* f, float* g, void* ws, const Layout& L,
                      hipStream_t s) {
   sk_status st = init_impl(p, X, Y, a, b, ws, L, s);
+  char* w = static_cast<char*>(ws);
+  bool built[2] = {false, false};  // key operand of each side prepared in this solve ...
+  float built_eps[2] = {0.f, 0.f};  // ... for this eps
+  bool ready[2] = {false, false};   // its bias for the coming half-step already written
+  auto writable = [&](int side, float e) {
+    return L.mode == MODE_BF16 || (built[side] && built_eps[side] == e);
+  };
+  auto step = [&](int side, float e, bool has_next, float e_next) {
+    const bool fuse = has_next && writable(1 - side, e_next);
+    const NextBias nb = next_bias(p, w, L, side, e_next, fuse);
+    const sk_status r = half_step(p, X, Y, ws, L, side == 0 ? g : f, e, side == 0 ? f : g, side, s, ready[side], nb);
+    if (!ready[side]) {
+      built[side] = true;
+      built_eps[side] = e;
+    }
+    ready[side] = false;
+    ready[1 - side] = fuse;
+    return r;
+  };
   for (int64_t k = 0; k < iters && st == SK_OK; ++k) {
     const float e = eps[n_eps == 1 ? 0 : k];
-    st = half_step(p, X, Y, ws, L, g, e, f, 0, s);
-    if (st == SK_OK) st = half_step(p, X, Y, ws, L, f, e, g, 1, s);
+    const bool more = k + 1 < iters;
+    const float e1 = more ? eps[n_eps == 1 ? 0 : k + 1] : e;
+    st = step(0, e, true, e);
+    if (st == SK_OK) st = step(1, e, more, e1);
   }
   return st;
 }
