@@ -186,3 +186,88 @@ def test_transport_and_hvp_are_deterministic():
     b1, g1 = sk.barycentric_x(X, Y, ws, ft, gt, eps)
     b2, g2 = sk.barycentric_x(X, Y, ws, ft, gt, eps)
     assert torch.equal(b1, b2) and torch.equal(g1, g2)
+
+
+# ---------------------------------------------------------------------------
+# HVPs whose conjugate-gradient system spans several 2048-element blocks, against
+# the dense oracle (fixture tests/golden/hvp_multiblock.json, written by
+# tests/golden/make_hvp_golden.py from the oracle alone)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("side", ["x", "y"])
+def test_hvp_multiblock_against_dense_oracle(side):
+    import hashlib
+    import json
+    import os
+
+    path = os.path.join(os.path.dirname(__file__), "golden", "hvp_multiblock.json")
+    if not os.path.exists(path):
+        pytest.skip("fixture not generated (python tests/golden/make_hvp_golden.py)")
+    gold = json.load(open(path))
+    case = gold["cases"][side]
+    eps = gold["eps"]
+    p = make_case(case["n"], case["m"], 3, seed=case["seed"], weights="softmax", eps=eps)
+    f, g = oracle.solve(p.X[0], p.Y[0], p.a[0], p.b[0], eps, gold["iters"])
+    f, g = f.astype(np.float32), g.astype(np.float32)
+    assert hashlib.sha256(f.tobytes() + g.tobytes()).hexdigest()[:16] == case["potentials_sha256_16"]
+    rows = p.n if side == "x" else p.m
+    V = np.random.default_rng(case["seed"] + 7).standard_normal((rows, 3)).astype(np.float32)
+    ref = np.array(case["hv"])
+    got = run_hvp(p, eps, f[None], g[None], V[None], side, iters=600, tol=1e-8)[0]
+    err = np.max(np.abs(got - ref))
+    assert err <= 5e-4 * np.max(np.abs(ref)), err / np.max(np.abs(ref))
+
+
+# ---------------------------------------------------------------------------
+# plan products at the full sizes of the 8192^2 d = 64 (fp32) and the
+# 65536 x 32768 d = 128 (bf16) workloads, on sampled rows computed by the oracle
+# one at a time; c = 1, 64 (one pass) and 65 (two passes) columns
+# ---------------------------------------------------------------------------
+def _sample(n, k, seed):
+    rng = np.random.default_rng(seed)
+    return np.sort(np.concatenate([rng.choice(n, size=k, replace=False), [0, n - 1]]))
+
+
+@pytest.mark.parametrize("cfg,c", [(2, 1), (2, 65), (4, 1), (4, 64), (4, 65)])
+def test_apply_plan_full_size_sampled_rows(cfg, c):
+    from log_domain_sinkhorn_half_amd.inputs import make_config, random_potential
+
+    p = make_config(cfg)
+    eps = float(p.eps[-1])
+    X, Y, a, b = dev(p)
+    ws = sk.alloc_workspace(X, Y, transport=True)
+    sk.init_norms(X, Y, a, b, ws)
+    Xo, Yo, ao, bo = (np.asarray(v[0], np.float64) for v in (p.X, p.Y, p.a, p.b))
+    rng = np.random.default_rng(100 * cfg + c)
+    for side in ("x", "y"):
+        rows_n, keys_n = (p.n, p.m) if side == "x" else (p.m, p.n)
+        R = _sample(rows_n, 48, 7 * cfg + c)
+        key_pot = random_potential(keys_n, 50 + cfg, 0.1)
+        # the rows' potential: the oracle half-step at the sampled rows (zero elsewhere;
+        # those rows' outputs are not checked)
+        if side == "x":
+            T = oracle.half_step_f(Xo, Yo, bo, key_pot, eps, rows=R)
+        else:
+            T = oracle.half_step_g(Xo, Yo, ao, key_pot, eps, rows=R)
+        row_pot = np.zeros(rows_n, np.float32)
+        row_pot[R] = T.astype(np.float32)
+        M = rng.standard_normal((keys_n, c)).astype(np.float32)
+        f = row_pot if side == "x" else key_pot
+        g = key_pot if side == "x" else row_pot
+        ft, gt = torch.from_numpy(f[None]).cuda(), torch.from_numpy(g[None]).cuda()
+        call = sk.apply_plan_x if side == "x" else sk.apply_plan_y
+        got = call(X, Y, ws, ft, gt, eps, torch.from_numpy(M[None]).cuda()).cpu().numpy()[0][R]
+        fo, go = f.astype(np.float64), g.astype(np.float64)
+        if side == "x":
+            ref = oracle.apply_plan_x(Xo, Yo, ao, bo, fo, go, eps, M.astype(np.float64), rows=R)
+            mass = oracle.apply_plan_x(Xo, Yo, ao, bo, fo, go, eps, np.ones(keys_n), rows=R)
+        else:
+            ref = oracle.apply_plan_y(Xo, Yo, ao, bo, fo, go, eps, M.astype(np.float64), rows=R)
+            mass = oracle.apply_plan_y(Xo, Yo, ao, bo, fo, go, eps, np.ones(keys_n), rows=R)
+        rel = 5e-4 if p.dtype == "bf16" else 2e-5
+        tT = 2e-2 * eps if p.dtype == "bf16" else 1e-3 * eps + 1e-5 * float(np.max(np.abs(T)))
+        dm = np.expm1(tT / eps)
+        avg = ref / mass[:, None]
+        tol = mass[:, None] * (rel * np.max(np.abs(M), axis=0)[None, :] * (1 + dm) + np.abs(avg) * dm)
+        err = np.abs(got - ref)
+        assert np.all(np.isfinite(got)), side
+        assert np.all(err <= tol), f"{side}: worst err/tol {(err / tol).max():.3f}"
