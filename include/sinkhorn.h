@@ -87,14 +87,19 @@ typedef enum { SK_FP32 = 0, SK_BF16 = 1 } sk_dtype; /* element type of X and Y *
 /* Size of the built-in scratch array of sinkhorn_solve_noalloc (bytes). */
 #define SK_NOALLOC_MAX_BYTES (64u * 1024u * 1024u)
 
-/* Largest supported point dimension: bf16 inputs up to SK_MAX_D, fp32 inputs up
- * to SK_MAX_D_FP32 (their operands carry seven remainder products per coordinate
- * that must stay in registers).  The transport, plan-product and HVP calls keep
- * the query operand of their P.V pass in registers too: d <= SK_MAX_D_TRANSPORT
- * (and <= SK_MAX_D_FP32 for fp32 inputs or the cosine cost).  Larger d returns
- * SK_EUNSUPPORTED. */
+/* Largest supported point dimension (the pages' largest, section "Risultati
+ * Sperimentali": d up to 1024).  Half-steps, solves and marginal errors: d <=
+ * SK_MAX_D for bf16 inputs and d <= SK_MAX_D_FP32 for fp32 inputs.  fp32 inputs
+ * with d <= SK_MAX_D_SPLIT take the exact grid/remainder operand layout (seven
+ * correction products per coordinate, kept in registers); wider ones a hi/lo
+ * layout (three bf16 products per coordinate, 2^-16 relative per product,
+ * accumulated in fp32) streamed through LDS with a K loop.  The transport,
+ * plan-product and HVP calls keep the query operand of their P.V pass in
+ * registers: d <= SK_MAX_D_TRANSPORT, and <= SK_MAX_D_SPLIT for fp32 inputs or
+ * the cosine cost.  Larger d returns SK_EUNSUPPORTED. */
 #define SK_MAX_D 1024
-#define SK_MAX_D_FP32 88
+#define SK_MAX_D_FP32 1024
+#define SK_MAX_D_SPLIT 88
 #define SK_MAX_D_TRANSPORT 256
 
 /* Ground cost.  SK_COST_SQEUCLID: C_ij = ||x_i - y_j||^2 (the pages' cost).
@@ -103,7 +108,7 @@ typedef enum { SK_FP32 = 0, SK_BF16 = 1 } sk_dtype; /* element type of X and Y *
  * squared distance
  * between the normalised points, C_ij = ||x_i/|x_i| - y_j/|y_j|||^2
  * = 2 - 2 cos(x_i, y_j); a zero point stays zero (cost 1 to any other point).
- * The cosine cost runs on the split fp32 layout, so d <= SK_MAX_D_FP32 for
+ * The cosine cost runs on the split fp32 layout, so d <= SK_MAX_D_SPLIT for
  * either dtype. */
 typedef enum { SK_COST_SQEUCLID = 0, SK_COST_COSINE = 1 } sk_cost;
 
@@ -111,7 +116,7 @@ typedef struct {
     int64_t batch; /* >= 1 independent problems */
     int64_t n;     /* >= 1 source points per problem */
     int64_t m;     /* >= 1 target points per problem */
-    int64_t d;     /* 1 .. SK_MAX_D (bf16) or SK_MAX_D_FP32 (fp32, or cosine cost) */
+    int64_t d;     /* 1 .. SK_MAX_D (bf16), SK_MAX_D_FP32 (fp32), SK_MAX_D_SPLIT (cosine cost) */
     int32_t dtype; /* sk_dtype of X and Y */
     int32_t cost;  /* sk_cost; 0 = squared Euclidean */
 } sk_problem;

@@ -55,10 +55,11 @@ void check_layout(const sk_problem& p) {
                          {L.rx, 8 * B * n},  {L.ry, 8 * B * m},      {L.maxabs, 8 * B},        {L.cen, 8 * B * d},
                          {L.box, 16 * B * d}, {L.inexact, 4 * B},   {L.status, 4},            {L.qgrid, 8 * B},
                          {L.ktag, 16},       {L.qx, 2 * B * n * (size_t)L.KP}, {L.qy, 2 * B * m * (size_t)L.KP}};
-  if (L.mode == MODE_SPLIT) {
+  if (L.mode != MODE_BF16) {
     regs.push_back({L.kbx, 2 * B * n * (size_t)L.KP});
     regs.push_back({L.kby, 2 * B * m * (size_t)L.KP});
-  } else {
+  }
+  if (L.mode != MODE_SPLIT) {
     regs.push_back({L.hb, 4 * B * m});
     regs.push_back({L.hb1, 4 * B * n});
   }
@@ -75,7 +76,11 @@ void check_layout(const sk_problem& p) {
   expect(ordered, "workspace regions in order without overlap", p);
   expect(L.total <= L.ttotal && L.ttotal <= L.htotal, "nested workspace sizes", p);
   expect(L.n_pad % ROW_PAD == 0 && L.m_pad % ROW_PAD == 0 && L.n_pad >= p.n && L.m_pad >= p.m, "row padding", p);
-  expect(L.KP % 32 == 0 && L.KP >= (L.mode == MODE_SPLIT ? 8 * (int)d + 7 : (int)d), "operand slots", p);
+  const int min_slots = L.mode == MODE_SPLIT ? 8 * (int)d + 7 : (L.mode == MODE_HILO ? 3 * (int)d : (int)d);
+  expect(L.KP % 32 == 0 && L.KP >= min_slots, "operand slots", p);
+  expect((L.mode == MODE_HILO) == (p.dtype == SK_FP32 && p.cost == SK_COST_SQEUCLID && p.d > SK_MAX_D_SPLIT),
+         "hi/lo layout exactly for wide fp32 inputs", p);
+  expect(L.mode != MODE_HILO || L.KP >= 2 * 32, "hi/lo operands span at least two K chunks", p);
 }
 
 void check_linear(sk_problem p) {
@@ -94,7 +99,7 @@ int main() {
 
   // rejected problems
   const sk_problem bad[] = {{0, 5, 5, 3, 0, 0},   {1, 0, 5, 3, 0, 0},    {1, 5, -1, 3, 0, 0}, {1, 5, 5, 0, 0, 0},
-                            {1, 5, 5, 89, 0, 0},  {1, 5, 5, 1025, 1, 0}, {1, 5, 5, 3, 2, 0},  {1, 5, 5, 3, 0, 2},
+                            {1, 5, 5, 1025, 0, 0}, {1, 5, 5, 1025, 1, 0}, {1, 5, 5, 3, 2, 0},  {1, 5, 5, 3, 0, 2},
                             {1, 5, 5, 100, 1, 1}, {65536, 5, 5, 3, 0, 0}, {1, 1LL << 30, 5, 3, 0, 0},
                             {4096, 1 << 20, 5, 3, 0, 0}};
   const sk_status want[] = {SK_ESHAPE, SK_ESHAPE,       SK_ESHAPE,       SK_ESHAPE, SK_EUNSUPPORTED, SK_EUNSUPPORTED,
@@ -111,7 +116,7 @@ int main() {
     sk_problem p{};
     p.dtype = (int32_t)pick(0, 1);
     p.cost = (int32_t)pick(0, 1);
-    const int dmax = (p.dtype == SK_FP32 || p.cost == SK_COST_COSINE) ? SK_MAX_D_FP32 : SK_MAX_D;
+    const int dmax = p.cost == SK_COST_COSINE ? SK_MAX_D_SPLIT : (p.dtype == SK_FP32 ? SK_MAX_D_FP32 : SK_MAX_D);
     p.d = pick(1, dmax);
     p.batch = pick(1, it % 10 == 0 ? 300 : 4);
     p.n = pick(1, it % 7 == 0 ? 200000 : 5000);

@@ -13,6 +13,7 @@ void set_err(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
 
 constexpr int MODE_SPLIT = 0;  // fp32 inputs
 constexpr int MODE_BF16 = 1;   // bf16 inputs
+constexpr int MODE_HILO = 2;   // fp32 inputs wider than SK_MAX_D_SPLIT: hi/lo operands, K loop
 constexpr int ROW_PAD = 512;   // operand buffers are padded to a multiple of this many rows
 constexpr int KS_MAX = 64;     // most key splits per half-step
 constexpr int SLACK = 256;     // slack rows after operand buffers (>= one chunk)
@@ -57,7 +58,7 @@ SK_HD constexpr int split_corr_begin(int d) {
 SK_HD constexpr int split_nch(int d) {
   return split_single(d) ? 1 : (split_corr_begin(d) + split_corr_slots(d) + 31) / 32;
 }
-constexpr int MAX_NCH_SPLIT = split_nch(SK_MAX_D_FP32);
+constexpr int MAX_NCH_SPLIT = split_nch(SK_MAX_D_SPLIT);
 constexpr int MAX_NCH_BF16 = (SK_MAX_D + 31) / 32;
 
 // ---------------------------------------------------------------------------
@@ -101,6 +102,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int kp_for(int mode, int64_t d) {
   if (mode == MODE_SPLIT) return split_nch((int)d) * 32;
+  if (mode == MODE_HILO) return (int)align_up((size_t)(3 * d), 32);  // (x_h, x_h, x_l) per coordinate
   return (int)align_up((size_t)d, 32);
 }
 
@@ -126,9 +128,12 @@ sk_status check_problem(const sk_problem* p) {
     set_err("unknown cost %d (expected SK_COST_SQEUCLID=0 or SK_COST_COSINE=1)", (int)p->cost);
     return SK_EINVAL;
   }
-  if ((p->dtype == SK_FP32 || p->cost == SK_COST_COSINE) && p->d > SK_MAX_D_FP32) {
-    set_err("d = %lld exceeds SK_MAX_D_FP32 = %d for fp32 inputs and the cosine cost", (long long)p->d,
-            SK_MAX_D_FP32);
+  if (p->dtype == SK_FP32 && p->d > SK_MAX_D_FP32) {
+    set_err("d = %lld exceeds SK_MAX_D_FP32 = %d for fp32 inputs", (long long)p->d, SK_MAX_D_FP32);
+    return SK_EUNSUPPORTED;
+  }
+  if (p->cost == SK_COST_COSINE && p->d > SK_MAX_D_SPLIT) {
+    set_err("d = %lld exceeds SK_MAX_D_SPLIT = %d for the cosine cost", (long long)p->d, SK_MAX_D_SPLIT);
     return SK_EUNSUPPORTED;
   }
   const int64_t lim = (int64_t)1 << 30;
@@ -143,8 +148,9 @@ Layout layout_of(const sk_problem* p) {
   Layout L{};
   L.in_bf16 = p->dtype == SK_BF16;
   L.cosine = p->cost == SK_COST_COSINE;
-  // bf16 operands are used as they are; fp32 inputs and normalised points take the split layout
-  L.mode = (L.in_bf16 && !L.cosine) ? MODE_BF16 : MODE_SPLIT;
+  // bf16 operands are used as they are; fp32 inputs and normalised points take
+  // the split layout, fp32 inputs wider than SK_MAX_D_SPLIT the hi/lo layout
+  L.mode = (L.in_bf16 && !L.cosine) ? MODE_BF16 : (p->d > SK_MAX_D_SPLIT ? MODE_HILO : MODE_SPLIT);
   L.KP = kp_for(L.mode, p->d);
   L.n_pad = (int)align_up((size_t)p->n, ROW_PAD);
   L.m_pad = (int)align_up((size_t)p->m, ROW_PAD);
@@ -173,11 +179,11 @@ Layout layout_of(const sk_problem* p) {
   // over-reads at the end of the last chunk.
   L.qx = take(2 * (B * L.n_pad + SLACK) * L.KP);
   L.qy = take(2 * (B * L.m_pad + SLACK) * L.KP);
-  L.kbx = (L.mode == MODE_SPLIT) ? take(2 * (B * L.n_pad + SLACK) * L.KP) : 0;
-  L.kby = (L.mode == MODE_SPLIT) ? take(2 * (B * L.m_pad + SLACK) * L.KP) : 0;
+  L.kbx = (L.mode != MODE_BF16) ? take(2 * (B * L.n_pad + SLACK) * L.KP) : 0;
+  L.kby = (L.mode != MODE_BF16) ? take(2 * (B * L.m_pad + SLACK) * L.KP) : 0;
   // half bias of each side's keys (bf16 path): side 0 (keys Y) then side 1 (keys X)
-  L.hb = (L.mode == MODE_BF16) ? take(4 * (B * L.m_pad + SLACK)) : 0;
-  L.hb1 = (L.mode == MODE_BF16) ? take(4 * (B * L.n_pad + SLACK)) : 0;
+  L.hb = (L.mode != MODE_SPLIT) ? take(4 * (B * L.m_pad + SLACK)) : 0;
+  L.hb1 = (L.mode != MODE_SPLIT) ? take(4 * (B * L.n_pad + SLACK)) : 0;
   L.part = take(8 * (size_t)KS_MAX * B * mx);
   L.scratch = take(4 * B * mx);
   L.total = off;

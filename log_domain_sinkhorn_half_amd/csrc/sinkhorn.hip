@@ -308,6 +308,35 @@ __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, c
     }
     return;
   }
+  if (MODE == MODE_HILO) {
+    // hi/lo query rows: (x_h, x_h, x_l) per coordinate, x = x_h + x_l the centred
+    // coordinate in two bf16 parts (paired with the key's v_h, v_l, v_h)
+    const void* src = P;
+    double nrm = 0.0;
+    for (int t = 0; t < d; ++t) {
+      const double v = (double)coord(src, r * d + t, in_bf16) - cb_[t];
+      nrm += v * v;
+    }
+    norm[r] = nrm;
+    rnorm[r] = 1.0;
+    logw[r] = log((double)w[r]);
+    for (int k0 = 0; k0 < KP; k0 += 8) {
+      u16 v8[8];
+      for (int e = 0; e < 8; ++e) {
+        const int k = k0 + e, t = k / 3;
+        u16 h = 0;
+        if (t < d) {
+          const double x = (double)coord(src, r * d + t, in_bf16) - cb_[t];
+          const u16 xh = bf16_of(x);
+          h = (k % 3 == 2) ? bf16_of(x - (double)bf16_f(xh)) : xh;
+        }
+        v8[e] = h;
+      }
+      *reinterpret_cast<u4*>(dst + k0) = u4{(uint32_t)v8[0] | ((uint32_t)v8[1] << 16), (uint32_t)v8[2] | ((uint32_t)v8[3] << 16),
+                                           (uint32_t)v8[4] | ((uint32_t)v8[5] << 16), (uint32_t)v8[6] | ((uint32_t)v8[7] << 16)};
+    }
+    return;
+  }
   const int qe = grid_exponent(maxabs[b]);
   const double q = ldexp(1.0, qe), iq = ldexp(1.0, -qe);
   double rn = 1.0;
@@ -538,17 +567,19 @@ __global__ __launch_bounds__(256) void k_init_words(unsigned* __restrict__ box, 
   }
 }
 
-// Half bias (pot - norm + eps*logw)/2 per key (bf16 inputs); padding -> -1e30.
+// Bias vector scale * (pot - norm + eps*logw) per key: scale 1/2 (bf16 inputs:
+// the MFMA's product is x.y, scaled by 2 lambda afterwards) or lambda (hi/lo
+// operands: the product is already 2 lambda x.y); padding -> -1e30.
 __global__ __launch_bounds__(256) void k_prep_bias(const float* __restrict__ pot, const double* __restrict__ norm,
                                                    const double* __restrict__ logw, int keys, int keys_pad,
-                                                   float eps, float* __restrict__ hb) {
+                                                   float eps, float scale, float* __restrict__ hb) {
   const int b = blockIdx.y;
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= keys_pad) return;
   float v = NEG_BIG;
   if (j < keys) {
     const size_t r = (size_t)b * keys + j;
-    v = (float)(0.5 * ((double)pot[r] - norm[r] + (double)eps * logw[r]));
+    v = (float)((double)scale * ((double)pot[r] - norm[r] + (double)eps * logw[r]));
     if (!(v >= NEG_BIG)) v = NEG_BIG;
   }
   hb[(size_t)b * keys_pad + j] = v;
@@ -688,11 +719,12 @@ __device__ __forceinline__ Blk xcd_block() {
 // preparation kernels would write, so skipping them changes no result.
 struct NextBias {
   u16* kb;              // split key operand of the next half-step (fp32 path), or nullptr
-  float* hb;            // half bias of the next half-step (bf16 path), or nullptr
+  float* hb;            // bias vector of the next half-step (bf16 and hi/lo paths), or nullptr
   const double* logw;   // log-weights of this half-step's rows
   const float* qmax;    // largest |coordinate| of the next half-step's query cloud, per problem
   const float* kmax;    // the same for this half-step's rows (the next keys)
   float lam, eps;       // the next half-step's lambda and eps
+  float hscale;         // scale of the bias vector: 1/2 (bf16 path) or lambda (hi/lo path)
   int rows_pad, KP, cb, d;
 };
 
@@ -711,7 +743,7 @@ __device__ __forceinline__ void write_next_bias(const NextBias& nb, int b, int q
     row[nb.cb + 7 * nb.d] = bp[3];
     row[nb.cb + 7 * nb.d + 1] = bp[4];
   } else if (nb.hb != nullptr) {
-    float v = (float)(0.5 * ((double)pot - norm + (double)nb.eps * logw));
+    float v = (float)((double)nb.hscale * ((double)pot - norm + (double)nb.eps * logw));
     if (!(v >= NEG_BIG)) v = NEG_BIG;
     nb.hb[(size_t)b * nb.rows_pad + q] = v;
   }
@@ -988,6 +1020,227 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
       }
     }
   }
+}
+
+
+// ---------------------------------------------------------------------------
+// Wide operands: the half-step with a K loop (fp32 inputs with d > 88 in the
+// hi/lo layout; bf16 inputs with d > 256).  The query operand no longer fits
+// in registers, so both operands pass through LDS in chunks of 32 K slots, and
+// each workgroup keeps a 256-query x 256-key block of scores in registers:
+// eight waves in a 4 x 2 arrangement, each 64 queries x 128 keys (2 x 4 tiles
+// of v_mfma_f32_32x32x16_bf16, 128 accumulators per lane).  A 16-slot step
+// reads 6 fragments for 8 MFMAs.  When a key block's scores are complete, each
+// query's exact block maximum (its two lanes combined) moves the running
+// offset only when it passes it, so no block is ever recomputed, then the
+// block's exponentials are summed.  The two key halves of a query (two waves)
+// are merged through LDS at the end; key splits go to k_merge as usual.
+//   hi/lo: acc starts at lambda*beta_j and adds 2 lambda x.y from the products
+//          x_h v_h + x_h v_l + x_l v_h (sc = 1);
+//   bf16:  acc starts at beta_j / 2 and adds x.y (sc = 2 lambda).
+// The exponent is fma(acc, sc, -m).
+// ---------------------------------------------------------------------------
+constexpr int KL_NW = 8, KL_WQ = 4, KL_QT = 2, KL_KT = 4;
+constexpr int KL_BQ = KL_WQ * KL_QT * 32;              // 256 queries per workgroup
+constexpr int KL_BK = (KL_NW / KL_WQ) * KL_KT * 32;    // 256 keys per block
+constexpr int KL_KC = 32;                               // K slots per LDS chunk
+constexpr int KL_LR = KL_KC + 8;                        // LDS row stride (elements)
+static_assert(ROW_PAD % KL_BQ == 0 && ROW_PAD % KL_BK == 0, "blocks must tile the row padding");
+
+__global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2))) void k_lsek(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb,
+    const double* __restrict__ qnorm, float* __restrict__ out, float2* __restrict__ part, int rows, int rows_pad,
+    int keys, int keys_pad, int KP, int blocks_per_split, int batch, float sc, double inv_lam,
+    unsigned* __restrict__ tag, unsigned tag_val, unsigned* __restrict__ status, NextBias nb) {
+  using T = Tile<32>;
+  using Acc = typename T::Acc;
+  constexpr int NT = 64 * KL_NW;
+  constexpr int ROWS = KL_BQ + KL_BK;                 // operand rows staged per chunk
+  constexpr int NLD = ROWS * (KL_KC / 8) / NT;        // 16-byte loads per thread per chunk
+  static_assert(ROWS * (KL_KC / 8) % NT == 0, "whole loads per thread");
+  __shared__ __attribute__((aligned(16))) u16 lds[2][ROWS * KL_LR];
+  __shared__ float ldb[KL_BK];
+  __shared__ float2 ldm[KL_BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 5, col = lane & 31;
+  const int wq = wave % KL_WQ, wk = wave / KL_WQ;
+  const int b = blockIdx.z;
+  const int q0 = blockIdx.x * KL_BQ;
+  if (tag != nullptr && tid == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) *tag = tag_val;
+  const u16* Qb = Q + ((size_t)b * rows_pad + q0) * KP;
+  const u16* Kb = K + (size_t)b * keys_pad * KP;
+  const float* hbb = hb + (size_t)b * keys_pad;
+  const int nblk = (keys + KL_BK - 1) / KL_BK;
+  const int kb0 = blockIdx.y * blocks_per_split, kb1 = min(nblk, kb0 + blocks_per_split);
+  const int nkc = KP / KL_KC;
+
+  float m[KL_QT], s[KL_QT];
+#pragma unroll
+  for (int c = 0; c < KL_QT; ++c) {
+    m[c] = -FLT_MAX;
+    s[c] = 0.f;
+  }
+
+  // staging: load i of thread tid takes 16-byte segment (tid + NT i) % 4 of row
+  // (tid + NT i) / 4 (rows 0..255 queries of this workgroup, 256..511 keys of the block)
+  u4 pre[NLD];
+  auto gload = [&](int kb, int kc) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int idx = tid + NT * i, row = idx >> 2, seg = idx & 3;
+      const u16* src = row < KL_BQ ? Qb + (size_t)row * KP : Kb + ((size_t)kb * KL_BK + (row - KL_BQ)) * KP;
+      pre[i] = *reinterpret_cast<const u4*>(src + kc * KL_KC + seg * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int idx = tid + NT * i, row = idx >> 2, seg = idx & 3;
+      *reinterpret_cast<u4*>(&lds[buf][row * KL_LR + seg * 8]) = pre[i];
+    }
+  };
+
+  if (kb0 < kb1) {
+    Acc acc[KL_QT][KL_KT];
+    int buf = 0;
+    gload(kb0, 0);
+    if (tid < KL_BK) ldb[tid] = hbb[(size_t)kb0 * KL_BK + tid];
+    lstore(0);
+    __syncthreads();
+    for (int kb = kb0; kb < kb1; ++kb) {
+      // accumulators start at the keys' bias
+#pragma unroll
+      for (int t = 0; t < KL_KT; ++t) {
+        Acc ci;
+#pragma unroll
+        for (int o = 0; o < 16; ++o) ci[o] = ldb[wk * (KL_KT * 32) + t * 32 + T::key_of(o, grp)];
+#pragma unroll
+        for (int c = 0; c < KL_QT; ++c) acc[c][t] = ci;
+      }
+      float nbias = 0.f;
+      for (int kc = 0; kc < nkc; ++kc) {
+        const bool more = kc + 1 < nkc || kb + 1 < kb1;
+        if (kc + 1 < nkc)
+          gload(kb, kc + 1);
+        else if (kb + 1 < kb1)
+          gload(kb + 1, 0);
+        if (kc + 1 == nkc && kb + 1 < kb1 && tid < KL_BK) nbias = hbb[(size_t)(kb + 1) * KL_BK + tid];
+        const u16* L = lds[buf];
+#pragma unroll
+        for (int ks = 0; ks < KL_KC / 16; ++ks) {
+          u4 bq[KL_QT];
+#pragma unroll
+          for (int c = 0; c < KL_QT; ++c)
+            bq[c] = *reinterpret_cast<const u4*>(&L[(wq * (KL_QT * 32) + c * 32 + col) * KL_LR + ks * 16 + grp * 8]);
+#pragma unroll
+          for (int t = 0; t < KL_KT; ++t) {
+            const u4 ka = *reinterpret_cast<const u4*>(
+                &L[(KL_BQ + wk * (KL_KT * 32) + t * 32 + col) * KL_LR + ks * 16 + grp * 8]);
+#pragma unroll
+            for (int c = 0; c < KL_QT; ++c) acc[c][t] = T::mma(ka, bq[c], acc[c][t]);
+          }
+        }
+        if (more) lstore(buf ^ 1);
+        // the bias of the next block: every wave has read this block's at its start
+        if (kc + 1 == nkc && kb + 1 < kb1 && tid < KL_BK) ldb[tid] = nbias;
+        __syncthreads();
+        buf ^= 1;
+      }
+      // block epilogue: exact block maximum, offset moves only past it, then the sums
+      bool coarse = false;
+#pragma unroll
+      for (int c = 0; c < KL_QT; ++c) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < KL_KT; ++t)
+#pragma unroll
+          for (int o = 0; o < 16; ++o) mx = fmaxf(mx, acc[c][t][o] * sc);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (!(mx <= m[c])) {
+          const float mn = fmaxf(m[c], offset_from_max(mx + HEADROOM, 1.f, coarse));
+          s[c] = rescale(s[c], m[c], mn);
+          m[c] = mn;
+        }
+        float e[16];
+#pragma unroll
+        for (int o = 0; o < 16; ++o) e[o] = 0.f;
+#pragma unroll
+        for (int t = 0; t < KL_KT; ++t)
+#pragma unroll
+          for (int o = 0; o < 16; ++o) e[o] += __builtin_amdgcn_exp2f(fmaf(acc[c][t][o], sc, -m[c]));
+#pragma unroll
+        for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+          for (int o = 0; o + w < 16; o += 2 * w) e[o] += e[o + w];
+        s[c] += e[0];
+      }
+      flag_if(status, coarse && lane == 0, FLAG_SCORE_RANGE);
+    }
+  }
+  // the two lanes of a query share its offset; then the two key halves (waves
+  // wk = 0, 1) merge through LDS
+#pragma unroll
+  for (int c = 0; c < KL_QT; ++c) s[c] += __shfl_xor(s[c], 32);
+  if (wk == 1 && grp == 0) {
+#pragma unroll
+    for (int c = 0; c < KL_QT; ++c) ldm[wq * (KL_QT * 32) + c * 32 + col] = make_float2(m[c], s[c]);
+  }
+  __syncthreads();
+  if (wk == 0 && grp == 0) {
+#pragma unroll
+    for (int c = 0; c < KL_QT; ++c) {
+      const int ql = wq * (KL_QT * 32) + c * 32 + col;
+      const float2 o = ldm[ql];
+      const float M = fmaxf(m[c], o.x);
+      const float S = rescale(s[c], m[c], M) + rescale(o.y, o.x, M);
+      const int q = q0 + ql;
+      if (q < rows) {
+        const size_t r = (size_t)b * rows + q;
+        if (part != nullptr) {
+          part[(size_t)blockIdx.y * batch * rows + r] = make_float2(M, S);
+        } else {
+          const float v = (float)(qnorm[r] - ((double)M + log2((double)S)) * inv_lam);
+          out[r] = v;
+          flag_if(status, !isfinite(v), FLAG_NONFINITE);
+          if (nb.logw != nullptr) write_next_bias(nb, b, q, v, qnorm[r], nb.logw[r]);
+        }
+      }
+    }
+  }
+}
+
+// Key rows of the hi/lo layout for one side: (v_h, v_l, v_h) per coordinate,
+// v = 2 lambda (y - c) in two bf16 parts (fp64 arithmetic).  They depend only on
+// the cloud and lambda: *tag holds the bit pattern of the lambda they were built
+// for, a launch with the same lambda writes nothing, and a rebuild clears the
+// tag (the half-step kernel that follows sets it).  One thread per 16-byte segment.
+__global__ __launch_bounds__(256) void k_prep_keys_hilo(const void* __restrict__ P, int in_bf16,
+                                                        const double* __restrict__ cen, int keys, int keys_pad,
+                                                        int d, int KP, float lam, unsigned* __restrict__ tag,
+                                                        u16* __restrict__ kb) {
+  const int b = blockIdx.y;
+  if (*tag == __float_as_uint(lam)) return;
+  const long long gtid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gtid == 0 && b == 0) *tag = 0u;
+  const int vpr = KP / 8;
+  if (gtid >= (long long)keys_pad * vpr) return;
+  const int j = (int)(gtid / vpr), k0 = (int)(gtid % vpr) * 8;
+  const double l2 = 2.0 * (double)lam;
+  u16 v8[8];
+  for (int e = 0; e < 8; ++e) {
+    const int k = k0 + e, t = k / 3;
+    u16 h = 0;
+    if (j < keys && t < d) {
+      const double v = l2 * ((double)coord(P, ((size_t)b * keys + j) * d + t, in_bf16) - cen[(size_t)b * d + t]);
+      const u16 vh = bf16_of(v);
+      h = (k % 3 == 1) ? bf16_of(v - (double)bf16_f(vh)) : vh;
+    }
+    v8[e] = h;
+  }
+  *reinterpret_cast<u4*>(kb + ((size_t)b * keys_pad + j) * KP + k0) =
+      u4{(uint32_t)v8[0] | ((uint32_t)v8[1] << 16), (uint32_t)v8[2] | ((uint32_t)v8[3] << 16),
+         (uint32_t)v8[4] | ((uint32_t)v8[5] << 16), (uint32_t)v8[6] | ((uint32_t)v8[7] << 16)};
 }
 
 // Merge the (max, sum) pairs of the key splits (one pass, exact power-of-two
@@ -2081,13 +2334,29 @@ sk_status prep_keys(const sk_problem* p, const void* X, const void* Y, char* w, 
                        reinterpret_cast<const double*>(w + L.cen), pot_in, knorm,
                        klogw, keys, keys_pad, (int)p->d, L.KP, lam, eps, maxabs + (side == 0 ? 0 : B),
                        maxabs + (side == 0 ? B : 0), qgrid, tag, kb);
+  } else if (L.mode == MODE_HILO) {
+    // hi/lo key rows (rebuilt only when lambda changes) and the bias vector lambda*beta
+    u16* kb = reinterpret_cast<u16*>(w + L.kb(side));
+    unsigned* tag = reinterpret_cast<unsigned*>(w + L.ktag) + side;
+    float* hbw = reinterpret_cast<float*>(w + L.hbs(side));
+    out->K = kb;
+    out->tag = tag;
+    out->hb = hbw;
+    if (!launch) return SK_OK;
+    const long long segs = (long long)keys_pad * (L.KP / 8);
+    hipLaunchKernelGGL(k_prep_keys_hilo, dim3((unsigned)((segs + 255) / 256), B), dim3(256), 0, stream, Kraw,
+                       L.in_bf16, reinterpret_cast<const double*>(w + L.cen), keys, keys_pad, (int)p->d, L.KP, lam,
+                       tag, kb);
+    hipLaunchKernelGGL(k_prep_bias, dim3((keys_pad + 255) / 256, B), dim3(256), 0, stream, pot_in, knorm, klogw,
+                       keys, keys_pad, eps, lam, hbw);
   } else {
     float* hbw = reinterpret_cast<float*>(w + L.hbs(side));
     out->hb = hbw;
     out->K = reinterpret_cast<const u16*>(w + (side == 0 ? L.qy : L.qx));
     if (!launch) return SK_OK;
     const dim3 pgrid((keys_pad + 255) / 256, B);
-    hipLaunchKernelGGL(k_prep_bias, pgrid, dim3(256), 0, stream, pot_in, knorm, klogw, keys, keys_pad, eps, hbw);
+    hipLaunchKernelGGL(k_prep_bias, pgrid, dim3(256), 0, stream, pot_in, knorm, klogw, keys, keys_pad, eps, 0.5f,
+                       hbw);
   }
   return hip_check("key preparation launch");
 }
@@ -2108,10 +2377,12 @@ NextBias next_bias(const sk_problem* p, char* w, const Layout& L, int side, floa
   nb.KP = L.KP;
   nb.cb = split_corr_begin((int)p->d);
   nb.d = (int)p->d;
-  if (L.mode == MODE_SPLIT)
+  if (L.mode == MODE_SPLIT) {
     nb.kb = reinterpret_cast<u16*>(w + L.kb(ns));
-  else
+  } else {
     nb.hb = reinterpret_cast<float*>(w + L.hbs(ns));
+    nb.hscale = L.mode == MODE_HILO ? nb.lam : 0.5f;
+  }
   return nb;
 }
 
@@ -2137,6 +2408,33 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   KeyOperand ko;
   sk_status st = prep_keys(p, X, Y, w, L, pot_in, eps, side, stream, &ko, !bias_ready);
   if (st != SK_OK) return st;
+  unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
+  const double inv_lam = 1.0 / (double)lam;
+
+  if (L.mode == MODE_HILO) {
+    // K-looped kernel: 256-query x 256-key blocks, splits over key blocks
+    if (L.KP < 2 * KL_KC) {
+      set_err("internal: the K-looped half-step needs at least two K chunks (KP = %d)", L.KP);
+      return SK_EUNSUPPORTED;
+    }
+    const int wg_x = (rows + KL_BQ - 1) / KL_BQ;
+    const int nblk = (keys + KL_BK - 1) / KL_BK;
+    int capacity = 0;
+    st = resident_capacity(reinterpret_cast<const void*>(&k_lsek), &capacity, 64 * KL_NW);
+    if (st != SK_OK) return st;
+    int bps = 0;
+    const int ks = choose_key_splits(wg_x * B, nblk, capacity, &bps);
+    float2* part = ks > 1 ? reinterpret_cast<float2*>(w + L.part) : nullptr;
+    hipLaunchKernelGGL(k_lsek, dim3(wg_x, ks, B), dim3(64 * KL_NW), 0, stream, reinterpret_cast<const u16*>(Qop), ko.K,
+                       ko.hb, qnorm, pot_out, part, rows, rows_pad, keys, keys_pad, L.KP, bps, B, 1.f, inv_lam,
+                       ko.tag, __builtin_bit_cast(unsigned, lam), status, ks == 1 ? nb : NextBias{});
+    st = hip_check("half-step kernel launch");
+    if (st != SK_OK || ks == 1) return st;
+    const int total = B * rows;
+    hipLaunchKernelGGL(k_merge, dim3((total + 255) / 256), dim3(256), 0, stream, part, ks, total, rows, qnorm,
+                       pot_out, inv_lam, status, nb);
+    return hip_check("split merge launch");
+  }
 
   LseFn fn = (L.mode == MODE_SPLIT) ? lse_lookup<MODE_SPLIT>(nch) : lse_lookup<MODE_BF16>(nch);
   int tc = cfTC;
@@ -2159,8 +2457,6 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   int cps = 0;
   const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps);
   float2* part = ks > 1 ? reinterpret_cast<float2*>(w + L.part) : nullptr;
-  const double inv_lam = 1.0 / (double)lam;
-  unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
   hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NW), 0, stream, Qop, ko.K, ko.hb, ko.qgrid, qnorm, pot_out,
                      part, rows, rows_pad, keys, keys_pad, cps, B, 2.f * lam, inv_lam, ko.tag,
                      __builtin_bit_cast(unsigned, lam), status, ks == 1 ? nb : NextBias{});
@@ -2190,7 +2486,7 @@ BaryFn bary_lookup_impl(int d, std::integer_sequence<int, N...>) {
 }
 
 BaryFn bary_lookup(int mode, int d) {
-  if (mode == MODE_SPLIT) return bary_lookup_impl<MODE_SPLIT>(d, std::make_integer_sequence<int, SK_MAX_D_FP32>{});
+  if (mode == MODE_SPLIT) return bary_lookup_impl<MODE_SPLIT>(d, std::make_integer_sequence<int, SK_MAX_D_SPLIT>{});
   return bary_lookup_impl<MODE_BF16>(d, std::make_integer_sequence<int, SK_MAX_D_TRANSPORT>{});
 }
 
@@ -2293,7 +2589,7 @@ BaryFn apply_lookup_impl(int d, int nct, std::integer_sequence<int, N...>) {
 
 BaryFn apply_lookup(int mode, int d, int nct) {
   if (mode == MODE_SPLIT)
-    return apply_lookup_impl<MODE_SPLIT>(d, nct, std::make_integer_sequence<int, SK_MAX_D_FP32>{});
+    return apply_lookup_impl<MODE_SPLIT>(d, nct, std::make_integer_sequence<int, SK_MAX_D_SPLIT>{});
   return apply_lookup_impl<MODE_BF16>(d, nct, std::make_integer_sequence<int, SK_MAX_D_TRANSPORT>{});
 }
 
@@ -2371,7 +2667,7 @@ BaryFn uw_lookup_impl(int d, std::integer_sequence<int, N...>) {
   return fn;
 }
 BaryFn uw_lookup(int mode, int d) {
-  if (mode == MODE_SPLIT) return uw_lookup_impl<MODE_SPLIT>(d, std::make_integer_sequence<int, SK_MAX_D_FP32>{});
+  if (mode == MODE_SPLIT) return uw_lookup_impl<MODE_SPLIT>(d, std::make_integer_sequence<int, SK_MAX_D_SPLIT>{});
   return uw_lookup_impl<MODE_BF16>(d, std::make_integer_sequence<int, SK_MAX_D_TRANSPORT>{});
 }
 
@@ -2586,6 +2882,11 @@ sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const flo
                          L.in_bf16, L.cosine, mabs, cen, reinterpret_cast<double*>(w + norm),
                          reinterpret_cast<double*>(w + logw), reinterpret_cast<double*>(w + rnorm),
                          reinterpret_cast<u16*>(w + op));
+    else if (L.mode == MODE_HILO)
+      hipLaunchKernelGGL(k_init_side<MODE_HILO>, grid, dim3(256), 0, stream, P, wt, rows, rows_pad, d, L.KP,
+                         L.in_bf16, L.cosine, mabs, cen, reinterpret_cast<double*>(w + norm),
+                         reinterpret_cast<double*>(w + logw), reinterpret_cast<double*>(w + rnorm),
+                         reinterpret_cast<u16*>(w + op));
     else
       hipLaunchKernelGGL(k_init_side<MODE_BF16>, grid, dim3(256), 0, stream, P, wt, rows, rows_pad, d, L.KP,
                          L.in_bf16, L.cosine, mabs, cen, reinterpret_cast<double*>(w + norm),
@@ -2594,8 +2895,8 @@ sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const flo
   };
   side(X, a, (int)p->n, L.n_pad, maxabs, L.xn, L.la, L.rx, L.qx);
   side(Y, b, (int)p->m, L.m_pad, maxabs + B, L.yn, L.lb, L.ry, L.qy);
-  if (L.mode == MODE_BF16) {
-    // half-bias vectors: padding keys (never written by a potential's epilogue)
+  if (L.mode != MODE_SPLIT) {
+    // bias vectors: padding keys (never written by a potential's epilogue)
     // remove themselves with the most negative bias
     const int nh0 = B * L.m_pad + SLACK, nh1 = B * L.n_pad + SLACK;
     hipLaunchKernelGGL(k_fill_f32, dim3((nh0 + 255) / 256), dim3(256), 0, stream,
@@ -2650,6 +2951,8 @@ sk_status solve_impl(const sk_problem* p, const void* X, const void* Y, const fl
   float built_eps[2] = {0.f, 0.f};  // ... for this eps
   bool ready[2] = {false, false};   // its bias for the coming half-step already written
   auto writable = [&](int side, float e) {
+    // bf16: the bias is all that changes; split and hi/lo: the key operand's
+    // coordinate parts must already be built for this eps
     return L.mode == MODE_BF16 || (built[side] && built_eps[side] == e);
   };
   auto step = [&](int side, float e, bool has_next, float e_next) {
@@ -2849,6 +3152,11 @@ size_t sinkhorn_transport_workspace_bytes(const sk_problem* p) {
 // Transport, plan products and HVPs keep the query operand of the P.V kernel in
 // registers: d <= SK_MAX_D_TRANSPORT.
 static sk_status check_transport_d(const sk_problem* p) {
+  if (layout_of(p).mode == MODE_HILO) {
+    set_err("d = %lld exceeds SK_MAX_D_SPLIT = %d for transport, plan and HVP calls with fp32 inputs", (long long)p->d,
+            SK_MAX_D_SPLIT);
+    return SK_EUNSUPPORTED;
+  }
   if (p->d > SK_MAX_D_TRANSPORT) {
     set_err("d = %lld exceeds SK_MAX_D_TRANSPORT = %d for transport, plan and HVP calls", (long long)p->d,
             SK_MAX_D_TRANSPORT);

@@ -1,0 +1,128 @@
+"""GPU parity for wide fp32 operands (d > 88: the hi/lo layout and the K-looped
+half-step) against the fp64 oracle, up to d = 1024 (the pages' largest, page
+"FlashSinkhorn: Trasporto Ottimo Entropico Consapevole delle I/O su GPU",
+section "Risultati Sperimentali").
+
+Bound: the fp32 one, max|pot_gpu - pot_ref| <= 1e-3 eps + 1e-5 max|pot_ref|.
+Each score is accumulated in fp32 from three exact bf16 products per
+coordinate (x_h v_h + x_h v_l + x_l v_h, v = 2 lambda (y - c)); the dropped
+x_l v_l and the parts' residuals are below 2^-16 of |x_t v_t| per coordinate,
+so the base-2 score error is at most 2^-16 * 2 lambda * sum_t |x_t y_t| plus the
+fp32 accumulation (worst case, for the clouds here about 1e-3 at eps = 0.05;
+the potential moves by eps ln 2 times that, against the 5e-5 bound).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from log_domain_sinkhorn_half_amd import binding as sk
+from log_domain_sinkhorn_half_amd.inputs import make_case, random_potential, translate
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sk.load_library()
+
+
+def dev(p):
+    return (torch.from_numpy(p.X).cuda(), torch.from_numpy(p.Y).cuda(), torch.from_numpy(p.a).cuda(),
+            torch.from_numpy(p.b).cuda())
+
+
+def bound(eps, ref):
+    return 1e-3 * eps + 1e-5 * float(np.max(np.abs(ref)))
+
+
+def check(got, ref, b, what):
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= b, f"{what}: max err {err:.3e} > bound {b:.3e}"
+
+
+@pytest.mark.parametrize("n,m,d", [(300, 513, 89), (700, 520, 128), (257, 1029, 300), (600, 300, 512),
+                                   (150, 170, 1024), (1, 7, 200), (513, 1, 96)])
+def test_half_steps_fp32_wide(n, m, d):
+    p = make_case(n, m, d, seed=5 * n + d, weights="softmax", scale=1.0 / np.sqrt(d))
+    X, Y, a, b = dev(p)
+    ws = sk.alloc_workspace(X, Y)
+    sk.init_norms(X, Y, a, b, ws)
+    for eps in (0.5, 0.05):
+        g = random_potential((1, m), d, 0.3)
+        f_in = random_potential((1, n), d + 1, 0.3)
+        f = sk.half_step_f(X, Y, ws, torch.from_numpy(g).cuda(), eps)
+        gg = sk.half_step_g(X, Y, ws, torch.from_numpy(f_in).cuda(), eps)
+        torch.cuda.synchronize()
+        rf = oracle.half_step_f(p.X[0], p.Y[0], p.b[0], g[0], eps)
+        rg = oracle.half_step_g(p.X[0], p.Y[0], p.a[0], f_in[0], eps)
+        check(f[0].cpu().numpy(), rf, bound(eps, rf), f"f d={d} eps={eps}")
+        check(gg[0].cpu().numpy(), rg, bound(eps, rg), f"g d={d} eps={eps}")
+    assert sk.range_flags(X, Y, ws) == 0
+
+
+@pytest.mark.parametrize("d,eps,iters", [(128, 0.05, 25), (512, 0.05, 15), (1024, 0.1, 10)])
+def test_trajectory_fp32_wide(d, eps, iters):
+    p = make_case(900, 800, d, seed=d, weights="softmax", scale=1.0 / np.sqrt(d), eps=eps, iters=iters)
+    X, Y, a, b = dev(p)
+    f, g = sk.solve(X, Y, a, b, eps, iters)
+    torch.cuda.synchronize()
+    rf, rg = oracle.solve(p.X[0], p.Y[0], p.a[0], p.b[0], eps, iters)
+    check(f[0].cpu().numpy(), rf, bound(eps, rf), f"f d={d}")
+    check(g[0].cpu().numpy(), rg, bound(eps, rg), f"g d={d}")
+
+
+def test_fp32_wide_annealed_batched_translated():
+    """Three problems at d = 256, moved far from the origin, eps annealed 0.5 -> 0.05:
+    every iteration rebuilds the key operand, and the centring keeps the bound."""
+    p = translate(make_case(400, 350, 256, batch=3, seed=9, weights="softmax", scale=1.0 / 16), 30.0)
+    sched = (0.5 * (0.1) ** (np.arange(12) / 11)).astype(np.float32)
+    X, Y, a, b = dev(p)
+    f, g = sk.solve(X, Y, a, b, sched.tolist(), 12)
+    torch.cuda.synchronize()
+    for k in range(3):
+        rf, rg = oracle.solve(p.X[k], p.Y[k], p.a[k], p.b[k], sched.astype(np.float64), 12)
+        check(f[k].cpu().numpy(), rf, bound(float(sched[-1]), rf), f"f problem {k}")
+        check(g[k].cpu().numpy(), rg, bound(float(sched[-1]), rg), f"g problem {k}")
+
+
+def test_fp32_wide_deterministic_role_swap_and_marginals():
+    p = make_case(1100, 900, 160, seed=13, weights="softmax", scale=1.0 / np.sqrt(160))
+    X, Y, a, b = dev(p)
+    ws = sk.alloc_workspace(X, Y)
+    sk.init_norms(X, Y, a, b, ws)
+    g = torch.from_numpy(random_potential((1, 900), 4, 0.2)).cuda()
+    f1 = sk.half_step_f(X, Y, ws, g, 0.07).clone()
+    f2 = sk.half_step_f(X, Y, ws, g, 0.07).clone()
+    ws2 = sk.alloc_workspace(Y, X)
+    sk.init_norms(Y, X, b, a, ws2)
+    f3 = sk.half_step_g(Y, X, ws2, g, 0.07)
+    torch.cuda.synchronize()
+    assert torch.equal(f1, f2) and torch.equal(f1, f3)
+    f, gg = sk.solve(X, Y, a, b, 0.1, 5, ws=ws)
+    err = sk.marginal_error(X, Y, ws, f, gg, 0.1)
+    torch.cuda.synchronize()
+    fn = f[0].cpu().numpy().astype(np.float64)
+    ra, _ = oracle.marginal_error(p.X[0], p.Y[0], p.a[0], p.b[0], fn, gg[0].cpu().numpy().astype(np.float64), 0.1)
+    e = err.cpu().numpy()[0]
+    # the row sums come from the GPU half-step T_f(g): within the potential bound
+    # tol_T, each sum moves by at most expm1(tol_T / eps) of its weight
+    slack = np.expm1((1e-3 * 0.1 + 1e-5 * float(np.max(np.abs(fn)))) / 0.1)
+    assert abs(e[0] - ra) <= slack * (1.0 + ra), (e, ra, slack)
+    assert e[1] <= 2e-5, e
+
+
+def test_fp32_wide_transport_is_refused():
+    p = make_case(50, 40, 100, seed=2)
+    X, Y, a, b = dev(p)
+    ws = sk.alloc_workspace(X, Y, transport=True)
+    sk.init_norms(X, Y, a, b, ws)
+    f = torch.zeros((1, 50), device="cuda")
+    g = torch.zeros((1, 40), device="cuda")
+    with pytest.raises(sk.SinkhornError, match="SK_EUNSUPPORTED"):
+        sk.barycentric_x(X, Y, ws, f, g, 0.1)
