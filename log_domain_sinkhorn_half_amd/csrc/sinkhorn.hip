@@ -1056,8 +1056,9 @@ __global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2)))
   using Acc = typename T::Acc;
   constexpr int NT = 64 * KL_NW;
   constexpr int ROWS = KL_BQ + KL_BK;                 // operand rows staged per chunk
-  constexpr int NLD = ROWS * (KL_KC / 8) / NT;        // 16-byte loads per thread per chunk
-  static_assert(ROWS * (KL_KC / 8) % NT == 0, "whole loads per thread");
+  constexpr int SEGS = KL_KC / 8;                     // 16-byte segments per row and chunk
+  constexpr int NLD = ROWS * SEGS / NT;               // 16-byte loads per thread per chunk
+  static_assert(KL_KC % 16 == 0 && ROWS * SEGS % NT == 0, "whole K steps and whole loads per thread");
   __shared__ __attribute__((aligned(16))) u16 lds[2][ROWS * KL_LR];
   __shared__ float ldb[KL_BK];
   __shared__ float2 ldm[KL_BQ];
@@ -1082,13 +1083,13 @@ __global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2)))
     s[c] = 0.f;
   }
 
-  // staging: load i of thread tid takes 16-byte segment (tid + NT i) % 4 of row
-  // (tid + NT i) / 4 (rows 0..255 queries of this workgroup, 256..511 keys of the block)
+  // staging: load i of thread tid takes 16-byte segment (tid + NT i) % SEGS of row
+  // (tid + NT i) / SEGS (rows 0..BQ-1 queries of this workgroup, then the block's keys)
   u4 pre[NLD];
   auto gload = [&](int kb, int kc) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int idx = tid + NT * i, row = idx >> 2, seg = idx & 3;
+      const int idx = tid + NT * i, row = idx / SEGS, seg = idx % SEGS;
       const u16* src = row < KL_BQ ? Qb + (size_t)row * KP : Kb + ((size_t)kb * KL_BK + (row - KL_BQ)) * KP;
       pre[i] = *reinterpret_cast<const u4*>(src + kc * KL_KC + seg * 8);
     }
@@ -1096,7 +1097,7 @@ __global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2)))
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int idx = tid + NT * i, row = idx >> 2, seg = idx & 3;
+      const int idx = tid + NT * i, row = idx / SEGS, seg = idx % SEGS;
       *reinterpret_cast<u4*>(&lds[buf][row * KL_LR + seg * 8]) = pre[i];
     }
   };
@@ -2214,7 +2215,8 @@ using LseFn = void (*)(const u16*, const u16*, const float*, const float*, const
 
 template <int MODE, int NCH>
 LseFn lse_fn() {
-  if constexpr ((MODE == MODE_SPLIT && NCH <= MAX_NCH_SPLIT) || (MODE == MODE_BF16 && NCH <= MAX_NCH_BF16))
+  // bf16 operands past 256 slots take the K-looped kernel (k_lsek)
+  if constexpr ((MODE == MODE_SPLIT && NCH <= MAX_NCH_SPLIT) || (MODE == MODE_BF16 && NCH <= 8))
     return &k_lse<MODE, NCH>;
   else
     return nullptr;
@@ -2411,8 +2413,10 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
   const double inv_lam = 1.0 / (double)lam;
 
-  if (L.mode == MODE_HILO) {
-    // K-looped kernel: 256-query x 256-key blocks, splits over key blocks
+  if (L.mode == MODE_HILO || (L.mode == MODE_BF16 && p->d > 256)) {
+    // K-looped kernel: 256-query x 256-key blocks, splits over key blocks (fp32
+    // hi/lo operands; bf16 operands past 256 slots, measured +58% at d = 1024
+    // and +1% at d = 512 against 16x16 tiles with the query operand in registers)
     if (L.KP < 2 * KL_KC) {
       set_err("internal: the K-looped half-step needs at least two K chunks (KP = %d)", L.KP);
       return SK_EUNSUPPORTED;
@@ -2426,7 +2430,8 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
     const int ks = choose_key_splits(wg_x * B, nblk, capacity, &bps);
     float2* part = ks > 1 ? reinterpret_cast<float2*>(w + L.part) : nullptr;
     hipLaunchKernelGGL(k_lsek, dim3(wg_x, ks, B), dim3(64 * KL_NW), 0, stream, reinterpret_cast<const u16*>(Qop), ko.K,
-                       ko.hb, qnorm, pot_out, part, rows, rows_pad, keys, keys_pad, L.KP, bps, B, 1.f, inv_lam,
+                       ko.hb, qnorm, pot_out, part, rows, rows_pad, keys, keys_pad, L.KP, bps, B,
+                       L.mode == MODE_HILO ? 1.f : 2.f * lam, inv_lam,
                        ko.tag, __builtin_bit_cast(unsigned, lam), status, ks == 1 ? nb : NextBias{});
     st = hip_check("half-step kernel launch");
     if (st != SK_OK || ks == 1) return st;
