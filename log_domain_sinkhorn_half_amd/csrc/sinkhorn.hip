@@ -109,6 +109,12 @@ __device__ __forceinline__ u16 bf16_of(double v) { return bf16_rne((float)v); }
 
 constexpr u16 BF16_ONE = 0x3F80;
 
+// Eight bf16 values as one 16-byte vector (element 0 in the low half of x).
+__device__ __forceinline__ u4 pack8(const u16 (&v)[8]) {
+  return u4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
+            (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
+}
+
 // Exponent k of the smallest power of two q = 2^k with |v| / q <= 255 (k = 0
 // when v == 0).  Callers form q and 1/q exactly with ldexp.
 __device__ __forceinline__ int grid_exponent(double vmax) {
@@ -171,44 +177,73 @@ __device__ __forceinline__ float ordered_value(unsigned c) {
 // Per (problem, side, coordinate) bounding box of the clouds: box[(b*2+side)*2d + t]
 // is the code of the minimum of coordinate t, box[... + d + t] of the maximum.
 // The slots start at 0xFFFFFFFF (minima) and 0 (maxima).  grid: (point chunks,
-// blocks of 64 coordinates, 2*batch); the 4 waves of a block take every fourth point.
+// 2 sides, batch).  For d <= 256 the 256 threads of a block hold 256/d points side
+// by side (thread = point * d + coordinate, so a load instruction reads whole
+// rows); wider points take one coordinate per thread and loop over the rest.
+// Minima and maxima meet in LDS, then once per block and coordinate in memory.
 __global__ __launch_bounds__(256) void k_bbox(const void* __restrict__ X, const void* __restrict__ Y, int in_bf16,
                                               int n, int m, int d, unsigned* __restrict__ box) {
-  __shared__ float rlo[256], rhi[256];
-  const int side = blockIdx.z & 1, b = blockIdx.z >> 1;
+  __shared__ unsigned lmin[SK_MAX_D], lmax[SK_MAX_D];
+  const int side = blockIdx.y, b = blockIdx.z;
   const int rows = side == 0 ? n : m;
   const void* P = side == 0 ? X : Y;
-  const int t = blockIdx.y * 64 + (threadIdx.x & 63);
-  float lo = INFINITY, hi = -INFINITY;
-  if (t < d)
-    for (long long i = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); i < rows; i += (long long)gridDim.x * 4) {
-      const float v = coord(P, ((size_t)b * rows + i) * d + t, in_bf16);
-      lo = fminf(lo, v);
-      hi = fmaxf(hi, v);
-    }
-  rlo[threadIdx.x] = lo;
-  rhi[threadIdx.x] = hi;
+  const int tid = threadIdx.x;
+  for (int k = tid; k < d; k += 256) {
+    lmin[k] = 0xFFFFFFFFu;
+    lmax[k] = 0u;
+  }
   __syncthreads();
-  if (threadIdx.x < 64 && t < d) {
-    for (int k = 1; k < 4; ++k) {
-      lo = fminf(lo, rlo[threadIdx.x + 64 * k]);
-      hi = fmaxf(hi, rhi[threadIdx.x + 64 * k]);
+  const int per = d <= 256 ? 256 / d : 1;  // points per pass of the block
+  const int lanes = d <= 256 ? per * d : 256;
+  if (tid < lanes) {
+    const int pp = d <= 256 ? tid / d : 0;
+    for (int t = d <= 256 ? tid % d : tid; t < d; t += 256) {
+      float lo = INFINITY, hi = -INFINITY;
+      for (long long i = (long long)blockIdx.x * per + pp; i < rows; i += (long long)gridDim.x * per) {
+        const float v = coord(P, ((size_t)b * rows + i) * d + t, in_bf16);
+        lo = fminf(lo, v);
+        hi = fmaxf(hi, v);
+      }
+      atomicMin(&lmin[t], ordered_code(lo));
+      atomicMax(&lmax[t], ordered_code(hi));
+      if (d <= 256) break;
     }
-    unsigned* bx = box + (size_t)(b * 2 + side) * 2 * d;
-    atomicMin(&bx[t], ordered_code(lo));
-    atomicMax(&bx[d + t], ordered_code(hi));
+  }
+  __syncthreads();
+  unsigned* bx = box + (size_t)(b * 2 + side) * 2 * d;
+  for (int k = tid; k < d; k += 256) {
+    atomicMin(&bx[k], lmin[k]);
+    atomicMax(&bx[d + k], lmax[k]);
   }
 }
 
 // Centre c of each problem (fp64 [batch][d]) from the two boxes, and the largest
 // |coordinate - c| of each side (maxabs[side*batch + b], rounded up to a float;
 // it sizes the grid quantum of the split operand layout).  bf16 inputs take a
-// bf16 centre, so that x - c can be exact in bf16.  One workgroup per problem.
+// bf16 centre, so that x - c can be exact in bf16, and only when the joint box
+// leaves out the origin in some coordinate (otherwise the norms shrink little);
+// an uncentred bf16 problem gets inexact[b] = 2, so no exactness check runs.
+// One workgroup per problem.
 __global__ __launch_bounds__(256) void k_centre(const unsigned* __restrict__ box, int d, int batch, int in_bf16,
-                                                int centre, double* __restrict__ cen, float* __restrict__ maxabs) {
+                                                int centre, double* __restrict__ cen, float* __restrict__ maxabs,
+                                                unsigned* __restrict__ inexact) {
   __shared__ double red[2][256];
+  __shared__ int off_origin;
   const int b = blockIdx.x;
   const unsigned* bx = box + (size_t)b * 4 * d;  // side 0: [0, 2d), side 1: [2d, 4d)
+  if (threadIdx.x == 0) off_origin = 0;
+  __syncthreads();
+  if (in_bf16)
+    for (int t = threadIdx.x; t < d; t += 256) {
+      const double lo = fmin((double)ordered_value(bx[t]), (double)ordered_value(bx[2 * d + t]));
+      const double hi = fmax((double)ordered_value(bx[d + t]), (double)ordered_value(bx[3 * d + t]));
+      if (lo > 0.0 || hi < 0.0) off_origin = 1;
+    }
+  __syncthreads();
+  if (in_bf16 && centre && !off_origin) {
+    centre = 0;
+    if (threadIdx.x == 0) inexact[b] = 2u;
+  }
   double mx0 = 0.0, mx1 = 0.0;
   for (int t = threadIdx.x; t < d; t += 256) {
     const double lo0 = ordered_value(bx[t]), hi0 = ordered_value(bx[d + t]);
@@ -242,19 +277,28 @@ __global__ __launch_bounds__(256) void k_centre(const unsigned* __restrict__ box
 // bf16 inputs keep their values in the operands, so a problem is centred only if
 // every x - c of both clouds is a bf16 value itself (true for clouds far from the
 // origin compared with their spread, where centring matters).  Sets inexact[b]
-// otherwise.  grid: (element chunks, batch, 2 sides).
+// otherwise (one atomic per block).  Problems already left uncentred are
+// skipped.  grid: (element chunks, batch, 2 sides).
 __global__ __launch_bounds__(256) void k_bf16_exact(const u16* __restrict__ X, const u16* __restrict__ Y,
                                                     long long nx, long long ny, int d,
                                                     const double* __restrict__ cen, unsigned* __restrict__ inexact) {
+  __shared__ int any_bad;
   const int b = blockIdx.y, side = blockIdx.z;
+  if (inexact[b] != 0u) return;  // uniform across the block
+  if (threadIdx.x == 0) any_bad = 0;
+  __syncthreads();
   const long long cnt = side == 0 ? nx : ny;
   const u16* P = (side == 0 ? X : Y) + (size_t)b * cnt;
   bool bad = false;
+  const double* cb_ = cen + (size_t)b * d;
   for (long long k = (long long)blockIdx.x * 256 + threadIdx.x; k < cnt; k += (long long)gridDim.x * 256) {
-    const double v = (double)bf16_f(P[k]) - cen[(size_t)b * d + k % d];
+    const int t = cnt < (1LL << 31) ? (int)((unsigned)k % (unsigned)d) : (int)(k % d);
+    const double v = (double)bf16_f(P[k]) - cb_[t];
     bad |= (double)bf16_f(bf16_rne((float)v)) != v;
   }
-  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(&inexact[b], 1u);
+  if (bad) any_bad = 1;
+  __syncthreads();
+  if (threadIdx.x == 0 && any_bad) atomicOr(&inexact[b], 1u);
 }
 
 // Problems whose differences are not all bf16 values keep c = 0.
@@ -270,77 +314,22 @@ __device__ __forceinline__ double ccoord(const void* P, size_t r, int t, int d, 
   return (double)coord(P, r * d + t, in_bf16) - cen[(size_t)b * d + t];
 }
 
-// Norms (fp64), log-weights (fp64), inverse norms and operand rows of one
-// cloud, from the centred points x - c: the split query layout (fp32 inputs, or
-// any input under the cosine cost, whose points are first divided by their norm
-// and not centred) or a zero-padded bf16 copy (bf16 inputs, squared-Euclidean
-// cost; x - c is a bf16 value there).
+// Norms (fp64), log-weights (fp64) and inverse norms of one cloud, from the
+// centred points x - c (under the cosine cost: the normalised points, not
+// centred).  One thread per point.  bf16 inputs: the norm of the centred bf16
+// values (x - c is a bf16 value there).
 template <int MODE>
-__global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, const float* __restrict__ w,
-                                                   int rows, int rows_pad, int d, int KP, int in_bf16, int cosine,
-                                                   const float* __restrict__ maxabs, const double* __restrict__ cen,
+__global__ __launch_bounds__(256) void k_init_rows(const void* __restrict__ P, const float* __restrict__ w, int rows,
+                                                   int d, int in_bf16, int cosine, const double* __restrict__ cen,
                                                    double* __restrict__ norm, double* __restrict__ logw,
-                                                   double* __restrict__ rnorm, u16* __restrict__ opnd) {
+                                                   double* __restrict__ rnorm) {
   const int b = blockIdx.y;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= rows_pad) return;
-  u16* dst = opnd + ((size_t)b * rows_pad + i) * KP;
-  if (i >= rows) {
-    for (int k = 0; k < KP; k += 8) *reinterpret_cast<u4*>(dst + k) = u4{0, 0, 0, 0};
-    return;
-  }
+  if (i >= rows) return;
   const size_t r = (size_t)b * rows + i;
   const double* cb_ = cen + (size_t)b * d;
-  if (MODE == MODE_BF16) {
-    const u16* src = static_cast<const u16*>(P) + r * d;
-    auto cv = [&](int t) -> u16 { return bf16_rne((float)((double)bf16_f(src[t]) - cb_[t])); };
-    double nrm = 0.0;
-    for (int t = 0; t < d; ++t) {
-      const double v = bf16_f(cv(t));
-      nrm += v * v;
-    }
-    norm[r] = nrm;
-    rnorm[r] = 1.0;
-    logw[r] = log((double)w[r]);
-    for (int k = 0; k < KP; k += 2) {
-      const uint32_t lo = (k < d) ? cv(k) : 0, hi = (k + 1 < d) ? cv(k + 1) : 0;
-      *reinterpret_cast<uint32_t*>(dst + k) = lo | (hi << 16);
-    }
-    return;
-  }
-  if (MODE == MODE_HILO) {
-    // hi/lo query rows: (x_h, x_h, x_l) per coordinate, x = x_h + x_l the centred
-    // coordinate in two bf16 parts (paired with the key's v_h, v_l, v_h)
-    const void* src = P;
-    double nrm = 0.0;
-    for (int t = 0; t < d; ++t) {
-      const double v = (double)coord(src, r * d + t, in_bf16) - cb_[t];
-      nrm += v * v;
-    }
-    norm[r] = nrm;
-    rnorm[r] = 1.0;
-    logw[r] = log((double)w[r]);
-    for (int k0 = 0; k0 < KP; k0 += 8) {
-      u16 v8[8];
-      for (int e = 0; e < 8; ++e) {
-        const int k = k0 + e, t = k / 3;
-        u16 h = 0;
-        if (t < d) {
-          const double x = (double)coord(src, r * d + t, in_bf16) - cb_[t];
-          const u16 xh = bf16_of(x);
-          h = (k % 3 == 2) ? bf16_of(x - (double)bf16_f(xh)) : xh;
-        }
-        v8[e] = h;
-      }
-      *reinterpret_cast<u4*>(dst + k0) = u4{(uint32_t)v8[0] | ((uint32_t)v8[1] << 16), (uint32_t)v8[2] | ((uint32_t)v8[3] << 16),
-                                           (uint32_t)v8[4] | ((uint32_t)v8[5] << 16), (uint32_t)v8[6] | ((uint32_t)v8[7] << 16)};
-    }
-    return;
-  }
-  const int qe = grid_exponent(maxabs[b]);
-  const double q = ldexp(1.0, qe), iq = ldexp(1.0, -qe);
   double rn = 1.0;
-  if (cosine) {
+  if (MODE == MODE_SPLIT && cosine) {
     double raw = 0.0;
     for (int t = 0; t < d; ++t) {
       const double v = coord(P, r * d + t, in_bf16);
@@ -348,34 +337,95 @@ __global__ __launch_bounds__(256) void k_init_side(const void* __restrict__ P, c
     }
     rn = raw > 0.0 ? 1.0 / sqrt(raw) : 0.0;  // a zero point stays zero
   }
-  auto val = [&](int t) { return (double)coord(P, r * d + t, in_bf16) * rn - cb_[t]; };
   double nrm = 0.0;
-  for (int t = 0; t < d; ++t) nrm += val(t) * val(t);
+  for (int t = 0; t < d; ++t) {
+    double v = (double)coord(P, r * d + t, in_bf16) * rn - cb_[t];
+    if (MODE == MODE_BF16) v = (double)bf16_f(bf16_of(v));
+    nrm += v * v;
+  }
   norm[r] = nrm;
   rnorm[r] = rn;
   logw[r] = log((double)w[r]);
-  const int cb = split_corr_begin(d);
-  for (int k0 = 0; k0 < KP; k0 += 8) {
-    u16 v[8];
-    for (int e = 0; e < 8; ++e) {
-      const int k = k0 + e;
-      u16 v_ = 0;
-      if (k >= 2 && k <= 4) {
-        v_ = BF16_ONE;
-      } else if (k >= 5 && k < 5 + d) {
-        v_ = grid_split(val(k - 5), q, iq).g;
-      } else if (k >= cb && k < cb + 7 * d) {
-        const Parts pp = grid_split(val((k - cb) / 7), q, iq);
-        const int s = (k - cb) % 7;
-        v_ = (s <= 1) ? pp.g : ((s == 3 || s == 6) ? pp.r2 : pp.r1);
-      } else if (k == cb + 7 * d || k == cb + 7 * d + 1) {
-        v_ = BF16_ONE;
-      }
-      v[e] = v_;
-    }
-    *reinterpret_cast<u4*>(dst + k0) = u4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
-                                         (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
+}
+
+// Operand rows of one cloud (queries of its half-steps), one thread per 16-byte
+// segment (8 K slots) of a row; rows past the points are zero.
+//   split layout (fp32 inputs up to SK_MAX_D_SPLIT, and the cosine cost): the
+//     query side of the K-slot layout above, from x*rn - c;
+//   hi/lo layout (wider fp32 inputs): (x_h, x_h, x_l) per coordinate, x = x_h + x_l
+//     the centred coordinate in two bf16 parts (paired with the key's v_h, v_l, v_h);
+//   bf16 inputs: the centred bf16 values, zero-padded.
+// Needs rnorm from k_init_rows.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_init_ops(const void* __restrict__ P, int rows, int rows_pad, int d, int KP,
+                                                  int in_bf16, const float* __restrict__ maxabs,
+                                                  const double* __restrict__ cen, const double* __restrict__ rnorm,
+                                                  u16* __restrict__ opnd) {
+  const int b = blockIdx.y;
+  const int vpr = KP / 8;
+  const long long gtid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gtid >= (long long)rows_pad * vpr) return;
+  const int i = (int)(gtid / vpr), k0 = (int)(gtid % vpr) * 8;
+  u16* dst = opnd + ((size_t)b * rows_pad + i) * KP + k0;
+  if (i >= rows) {
+    *reinterpret_cast<u4*>(dst) = u4{0, 0, 0, 0};
+    return;
   }
+  const size_t r = (size_t)b * rows + i;
+  const double* cb_ = cen + (size_t)b * d;
+  const double rn = rnorm[r];
+  auto val = [&](int t) { return (double)coord(P, r * d + t, in_bf16) * rn - cb_[t]; };
+  u16 v[8];
+  if (MODE == MODE_BF16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (k0 + e < d) ? bf16_of(val(k0 + e)) : (u16)0;
+  } else if (MODE == MODE_HILO) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = k0 + e, t = k / 3;
+      u16 h = 0;
+      if (t < d) {
+        const double x = val(t);
+        const u16 xh = bf16_of(x);
+        h = (k % 3 == 2) ? bf16_of(x - (double)bf16_f(xh)) : xh;
+      }
+      v[e] = h;
+    }
+  } else {
+    const int qe = grid_exponent(maxabs[b]);
+    const double q = ldexp(1.0, qe), iq = ldexp(1.0, -qe);
+    const int cb = split_corr_begin(d);
+    if (k0 < cb) {
+      // grid section: offset slots (zero here, set in registers), ones, grid parts
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = k0 + e;
+        v[e] = (k >= 2 && k <= 4) ? BF16_ONE : ((k >= 5 && k < 5 + d) ? grid_split(val(k - 5), q, iq).g : (u16)0);
+      }
+    } else {
+      // corrections (x_g x_g x_1 x_2 x_1 x_1 x_2 per coordinate), then the two ones
+      // of the bias remainder; a segment touches at most two coordinates
+      const int t0 = (k0 - cb) / 7;
+      const Parts zero{0, 0, 0};
+      const Parts p0 = t0 < d ? grid_split(val(t0), q, iq) : zero;
+      const Parts p1 = t0 + 1 < d ? grid_split(val(t0 + 1), q, iq) : zero;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int rel = k0 + e - cb;
+        u16 v_ = 0;
+        if (rel < 7 * d) {
+          const bool first = rel / 7 == t0;
+          const int sl = rel % 7;
+          const u16 pg = first ? p0.g : p1.g, pr1 = first ? p0.r1 : p1.r1, pr2 = first ? p0.r2 : p1.r2;
+          v_ = (sl <= 1) ? pg : ((sl == 3 || sl == 6) ? pr2 : pr1);
+        } else if (rel == 7 * d || rel == 7 * d + 1) {
+          v_ = BF16_ONE;
+        }
+        v[e] = v_;
+      }
+    }
+  }
+  *reinterpret_cast<u4*>(dst) = pack8(v);
 }
 
 // Grid and remainder parts of v = l2*yc (l2 = 2*lambda, yc the centred or
@@ -1333,10 +1383,6 @@ __host__ __device__ constexpr int bary_waves(int mode, int nch, int nct, int nu)
 // 32-key value blocks per LDS chunk of the transport kernel (fewer barriers for small operands)
 __host__ __device__ constexpr int bary_TCB(int nch, int nct) { return (nch <= 2 && nct <= 4) ? 4 : 1; }
 
-__device__ __forceinline__ u4 pack8(const u16 (&v)[8]) {
-  return u4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
-            (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
-}
 
 // Key order inside a 32-key value block: lane group g of the P.V MFMA takes the
 // weights of keys 4g..4g+3 and 16+4g..16+4g+3 as its A operand, so those eight
@@ -2867,13 +2913,16 @@ sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const flo
     hipLaunchKernelGGL(k_fill_f32, dim3((2 * B + 255) / 256), dim3(256), 0, stream, maxabs, 2 * B, 1.f);
   } else {
     const int most = (int)std::max(p->n, p->m);
-    const unsigned chunks = (unsigned)std::min(64, std::max(1, (most + 255) / 256));
-    hipLaunchKernelGGL(k_bbox, dim3(chunks, (d + 63) / 64, 2 * B), dim3(256), 0, stream, X, Y, L.in_bf16, (int)p->n,
-                       (int)p->m, d, box);
-    hipLaunchKernelGGL(k_centre, dim3(B), dim3(256), 0, stream, box, d, B, L.in_bf16, 1, cen, maxabs);
+    // about 16 points per thread
+    const int per = d <= 256 ? 256 / d : 1;
+    // (at most 256 blocks per side and problem: each adds d minima and maxima to the same words)
+    const unsigned chunks = (unsigned)std::min(256, std::max(1, (most + 16 * per - 1) / (16 * per)));
+    hipLaunchKernelGGL(k_bbox, dim3(chunks, 2, B), dim3(256), 0, stream, X, Y, L.in_bf16, (int)p->n, (int)p->m, d,
+                       box);
+    hipLaunchKernelGGL(k_centre, dim3(B), dim3(256), 0, stream, box, d, B, L.in_bf16, 1, cen, maxabs, inexact);
     if (L.in_bf16) {
-      const long long elems = (long long)most * d;
-      const unsigned ch = (unsigned)std::min<long long>(64, std::max<long long>(1, (elems + 255) / 256));
+      const long long elems = (long long)most * d;  // about 8 elements per thread
+      const unsigned ch = (unsigned)std::min<long long>(65535, std::max<long long>(1, (elems + 2047) / 2048));
       hipLaunchKernelGGL(k_bf16_exact, dim3(ch, B, 2), dim3(256), 0, stream, static_cast<const u16*>(X),
                          static_cast<const u16*>(Y), (long long)(p->n * p->d), (long long)(p->m * p->d), d, cen, inexact);
       hipLaunchKernelGGL(k_cen_fix, dim3(B), dim3(256), 0, stream, inexact, d, cen);
@@ -2881,22 +2930,28 @@ sk_status init_impl(const sk_problem* p, const void* X, const void* Y, const flo
   }
   auto side = [&](const void* P, const float* wt, int rows, int rows_pad, const float* mabs, size_t norm,
                   size_t logw, size_t rnorm, size_t op) {
-    const dim3 grid((rows_pad + 255) / 256, B);
-    if (L.mode == MODE_SPLIT)
-      hipLaunchKernelGGL(k_init_side<MODE_SPLIT>, grid, dim3(256), 0, stream, P, wt, rows, rows_pad, d, L.KP,
-                         L.in_bf16, L.cosine, mabs, cen, reinterpret_cast<double*>(w + norm),
-                         reinterpret_cast<double*>(w + logw), reinterpret_cast<double*>(w + rnorm),
-                         reinterpret_cast<u16*>(w + op));
-    else if (L.mode == MODE_HILO)
-      hipLaunchKernelGGL(k_init_side<MODE_HILO>, grid, dim3(256), 0, stream, P, wt, rows, rows_pad, d, L.KP,
-                         L.in_bf16, L.cosine, mabs, cen, reinterpret_cast<double*>(w + norm),
-                         reinterpret_cast<double*>(w + logw), reinterpret_cast<double*>(w + rnorm),
-                         reinterpret_cast<u16*>(w + op));
-    else
-      hipLaunchKernelGGL(k_init_side<MODE_BF16>, grid, dim3(256), 0, stream, P, wt, rows, rows_pad, d, L.KP,
-                         L.in_bf16, L.cosine, mabs, cen, reinterpret_cast<double*>(w + norm),
-                         reinterpret_cast<double*>(w + logw), reinterpret_cast<double*>(w + rnorm),
-                         reinterpret_cast<u16*>(w + op));
+    double* nrm = reinterpret_cast<double*>(w + norm);
+    double* lw = reinterpret_cast<double*>(w + logw);
+    double* rn = reinterpret_cast<double*>(w + rnorm);
+    u16* dst = reinterpret_cast<u16*>(w + op);
+    const dim3 rgrid((rows + 255) / 256, B);
+    const dim3 ogrid((unsigned)(((long long)rows_pad * (L.KP / 8) + 255) / 256), B);
+    if (L.mode == MODE_SPLIT) {
+      hipLaunchKernelGGL(k_init_rows<MODE_SPLIT>, rgrid, dim3(256), 0, stream, P, wt, rows, d, L.in_bf16, L.cosine,
+                         cen, nrm, lw, rn);
+      hipLaunchKernelGGL(k_init_ops<MODE_SPLIT>, ogrid, dim3(256), 0, stream, P, rows, rows_pad, d, L.KP, L.in_bf16,
+                         mabs, cen, rn, dst);
+    } else if (L.mode == MODE_HILO) {
+      hipLaunchKernelGGL(k_init_rows<MODE_HILO>, rgrid, dim3(256), 0, stream, P, wt, rows, d, L.in_bf16, L.cosine,
+                         cen, nrm, lw, rn);
+      hipLaunchKernelGGL(k_init_ops<MODE_HILO>, ogrid, dim3(256), 0, stream, P, rows, rows_pad, d, L.KP, L.in_bf16,
+                         mabs, cen, rn, dst);
+    } else {
+      hipLaunchKernelGGL(k_init_rows<MODE_BF16>, rgrid, dim3(256), 0, stream, P, wt, rows, d, L.in_bf16, L.cosine,
+                         cen, nrm, lw, rn);
+      hipLaunchKernelGGL(k_init_ops<MODE_BF16>, ogrid, dim3(256), 0, stream, P, rows, rows_pad, d, L.KP, L.in_bf16,
+                         mabs, cen, rn, dst);
+    }
   };
   side(X, a, (int)p->n, L.n_pad, maxabs, L.xn, L.la, L.rx, L.qx);
   side(Y, b, (int)p->m, L.m_pad, maxabs + B, L.yn, L.lb, L.ry, L.qy);
