@@ -94,9 +94,14 @@ typedef enum { SK_FP32 = 0, SK_BF16 = 1 } sk_dtype; /* element type of X and Y *
  * correction products per coordinate, kept in registers); wider ones a hi/lo
  * layout (three bf16 products per coordinate, 2^-16 relative per product,
  * accumulated in fp32) streamed through LDS with a K loop.  The transport,
- * plan-product and HVP calls keep the query operand of their P.V pass in
- * registers: d <= SK_MAX_D_TRANSPORT, and <= SK_MAX_D_SPLIT for fp32 inputs or
- * the cosine cost.  Larger d returns SK_EUNSUPPORTED. */
+ * plan-product and HVP calls take the same d.  Up to SK_MAX_D_TRANSPORT (bf16
+ * inputs) or SK_MAX_D_SPLIT (fp32 inputs, cosine cost) their P.V pass keeps the
+ * query operand in registers and never stores a weight; wider problems first
+ * take the rows' half-step, then write the weights of one block of rows against
+ * all keys (bf16 hi/lo parts, at most 1 GiB of the transport workspace) and
+ * multiply them with the value rows in a second blocked MFMA pass; fp32
+ * coordinates enter that product in two bf16 parts (16 significant bits).
+ * Larger d returns SK_EUNSUPPORTED. */
 #define SK_MAX_D 1024
 #define SK_MAX_D_FP32 1024
 #define SK_MAX_D_SPLIT 88

@@ -74,6 +74,25 @@ void check_layout(const sk_problem& p) {
   }
   expect(aligned, "256-byte alignment of the workspace regions", p);
   expect(ordered, "workspace regions in order without overlap", p);
+  // transport regions, between total and ttotal
+  const size_t kcov = align_up(mx, 256);
+  std::vector<R> tregs;
+  tregs.push_back({L.vt, L.wide ? 2 * B * align_up((size_t)L.ncols, 256) * kcov : 2 * B * (size_t)L.max_pad * L.ncols});
+  if (L.wide) tregs.push_back({L.wt, 2 * B * (size_t)L.wt_rows * 2 * kcov});
+  tregs.push_back({L.bpv, std::max<size_t>(L.bpv_bytes, 4 * B * mx * (size_t)L.ncols)});
+  tregs.push_back({L.bs, 4 * 16 * B * mx});
+  tregs.push_back({L.bm, 4 * 16 * B * mx});
+  bool tordered = tregs[0].off >= L.total;
+  for (size_t k = 0; k < tregs.size(); ++k) {
+    const size_t next = k + 1 < tregs.size() ? tregs[k + 1].off : L.ttotal;
+    tordered &= tregs[k].off % 256 == 0 && tregs[k].off + tregs[k].min_bytes <= next;
+  }
+  expect(tordered, "transport regions aligned, in order, without overlap", p);
+  expect(!L.wide || (L.ncols % 16 == 0 && L.ncols >= val_parts(L.mode) * (int)d + 1 &&
+                     3 * L.wide_cols + 1 <= L.ncols && L.wide_cols >= APPLY_COLS),
+         "wide value columns hold the parts and the ones column", p);
+  expect(L.wide == (L.mode == MODE_HILO || (L.mode == MODE_BF16 && p.d > SK_MAX_D_TRANSPORT)),
+         "wide passes exactly past the register-resident widths", p);
   expect(L.total <= L.ttotal && L.ttotal <= L.htotal, "nested workspace sizes", p);
   expect(L.n_pad % ROW_PAD == 0 && L.m_pad % ROW_PAD == 0 && L.n_pad >= p.n && L.m_pad >= p.m, "row padding", p);
   const int min_slots = L.mode == MODE_SPLIT ? 8 * (int)d + 7 : (L.mode == MODE_HILO ? 3 * (int)d : (int)d);
@@ -84,11 +103,20 @@ void check_layout(const sk_problem& p) {
 }
 
 void check_linear(sk_problem p) {
-  const size_t a = layout_of(&p).htotal;
+  const Layout L0 = layout_of(&p);
+  const size_t a = L0.htotal;
   p.n *= 2;
   p.m *= 2;
-  const size_t b = layout_of(&p).htotal;
-  expect(b <= 2 * a + (1u << 24), "workspace linear in the point counts", p);
+  const Layout L1 = layout_of(&p);
+  const size_t b = L1.htotal;
+  // linear, apart from the wide passes' weights buffer (rows x keys, capped)
+  expect(b <= 2 * a + (1u << 24) + (L1.wide ? WIDE_WT_BYTES : 0), "workspace linear in the point counts", p);
+  const size_t kcov = align_up((size_t)std::max(p.n, p.m), 256);
+  const size_t row_bytes = 2 * (size_t)p.batch * 2 * kcov;
+  expect(!L1.wide || (L1.wt_rows % 256 == 0 && L1.wt_rows >= 256 &&
+                      (size_t)L1.wt_rows * row_bytes <= std::max(WIDE_WT_BYTES, 256 * row_bytes) &&
+                      (size_t)L1.wt_rows <= align_up((size_t)std::max(p.n, p.m), 256)),
+         "weights buffer: whole 256-row blocks within its byte cap", p);
 }
 
 }  // namespace

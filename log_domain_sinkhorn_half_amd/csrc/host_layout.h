@@ -66,7 +66,10 @@ constexpr int MAX_NCH_BF16 = (SK_MAX_D + 31) / 32;
 // ---------------------------------------------------------------------------
 constexpr int VK = 32;  // keys per value block: one 16x16x32 K step, two 16-key score tiles
 
-SK_HD constexpr int val_parts(int mode) { return mode == MODE_SPLIT ? 3 : 1; }
+// bf16 parts of a coordinate in the value operand: three hold an fp32 value
+// exactly (split path), two hold 16 significant bits (hi/lo path), and bf16
+// inputs are exact in one.
+SK_HD constexpr int val_parts(int mode) { return mode == MODE_SPLIT ? 3 : (mode == MODE_HILO ? 2 : 1); }
 SK_HD constexpr int val_tiles(int mode, int d) { return (val_parts(mode) * d + 15) / 16; }
 // A spare value column holds ones, so the P.V product also yields the sum of the weights.
 SK_HD constexpr bool val_sumcol(int mode, int d) { return val_parts(mode) * d < val_tiles(mode, d) * 16; }
@@ -74,6 +77,11 @@ SK_HD constexpr bool val_sumcol(int mode, int d) { return val_parts(mode) * d < 
 constexpr int APPLY_COLS = 64;  // matrix columns per pass (3 parts each + the ones column <= 13 tiles)
 
 SK_HD constexpr int apply_tiles(int cb) { return cb <= 5 ? 1 : (cb <= 21 ? 4 : 13); }
+
+// Wide plan passes (hi/lo operands, or bf16 operands past SK_MAX_D_TRANSPORT)
+// go through a weights buffer of one block of rows against all keys, at most
+// this many bytes (the block shrinks to fit, down to 256 rows).
+constexpr size_t WIDE_WT_BYTES = (size_t)1 << 30;
 
 // Conjugate-gradient vectors are reduced in blocks of this many elements.
 constexpr int CG_BLK = 2048;
@@ -91,6 +99,10 @@ struct Layout {
   size_t kb(int side) const { return side == 0 ? kby : kbx; }
   // transport application and plan products (after `total`; only their entry points need them)
   int ncols;             // widest value operand (columns) of any transport pass
+  bool wide;             // plan passes through the weights buffer
+  int wt_rows;           // rows per block of the weights buffer (wide)
+  int wide_cols;         // matrix columns per wide plan-application pass (3 parts each)
+  size_t wt;             // weights buffer (wide)
   size_t bpv_bytes;      // bytes of the split-partials region
   size_t vt, bpv, bs, bm, ttotal;
   // Hessian-vector products (after `ttotal`)
@@ -192,10 +204,26 @@ Layout layout_of(const sk_problem* p) {
   // 131072 rows (split_rows below, at least one split and at most 16): a few
   // thousand rows of a wide pass need several key splits to fill the GPU.
   const size_t d = (size_t)p->d;
-  L.ncols = std::max(p->d <= SK_MAX_D_TRANSPORT ? val_tiles(L.mode, (int)p->d) : 0, apply_tiles(APPLY_COLS)) * 16;
+  L.wide = L.mode == MODE_HILO || (L.mode == MODE_BF16 && p->d > SK_MAX_D_TRANSPORT);
+  // keys of a wide pass, rounded up to whole 256-key blocks
+  const size_t kcov = align_up(mx, 256);
+  if (L.wide) {
+    // value columns (parts of each coordinate, then the ones column) or three
+    // parts of wide_cols matrix columns and the ones column
+    L.ncols = (int)align_up(std::max<size_t>(val_parts(L.mode) * d + 1, 3 * APPLY_COLS + 1), 16);
+    L.wide_cols = (L.ncols - 1) / 3;
+    const size_t per_row = 2 * B * 2 * kcov;  // bytes of one weights row (hi and lo) over the batch
+    L.wt_rows = (int)std::min(align_up(mx, 256), std::max<size_t>(256, WIDE_WT_BYTES / per_row / 256 * 256));
+  } else {
+    L.ncols = std::max(p->d <= SK_MAX_D_TRANSPORT ? val_tiles(L.mode, (int)p->d) : 0, apply_tiles(APPLY_COLS)) * 16;
+    L.wide_cols = 0;
+    L.wt_rows = 0;
+  }
   const size_t split_rows = std::max(B * mx, std::min(16 * B * mx, (size_t)131072));
   L.bpv_bytes = std::max<size_t>(4 * 16 * 16 * B * mx, 4 * split_rows * (size_t)L.ncols);
-  L.vt = take(2 * B * (size_t)L.max_pad * L.ncols);
+  // value operand: [B][max_pad / 32][ncols][32] (narrow) or [B][ncols rounded to 256][kcov] (wide)
+  L.vt = L.wide ? take(2 * B * align_up((size_t)L.ncols, 256) * kcov) : take(2 * B * (size_t)L.max_pad * L.ncols);
+  L.wt = L.wide ? take(2 * B * (size_t)L.wt_rows * 2 * kcov) : 0;
   L.bpv = take(L.bpv_bytes);
   L.bs = take(4 * 16 * B * mx);
   L.bm = take(4 * 16 * B * mx);  // per-split row offsets of the lazy transport pass

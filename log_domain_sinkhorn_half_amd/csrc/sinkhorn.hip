@@ -1073,6 +1073,23 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
 }
 
 
+// Two packed bf16 parts of a weight pair: hi = e truncated to bf16 (its upper
+// half), lo = rne(e - hi), where e - hi is exact; together 16 significant bits.
+// Returns (hi pair, lo pair).  The hi pair is one byte permute; e - hi is one
+// bf16 dot product each, hi . (-1, -0) + a and hi . (0, -1) + b (products and
+// sums exact).  The first pair is written (-1, -0) so that it is encoded as a
+// 32-bit literal: hipcc encodes (-1, 0) as the inline constant -1.0, which
+// this instruction reads as the fp32 bit pattern, i.e. as the pair (0, -1).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 split_pair(float a, float b) {
+  const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+  const bf16x2 h = __builtin_bit_cast(bf16x2, hi);
+  const float la = __builtin_amdgcn_fdot2_f32_bf16(h, bf16x2{(__bf16)-1.f, (__bf16)-0.f}, a, false);
+  const float lb = __builtin_amdgcn_fdot2_f32_bf16(h, bf16x2{(__bf16)0.f, (__bf16)-1.f}, b, false);
+  const bf16x2 l = {(__bf16)la, (__bf16)lb};
+  return make_uint2(hi, __builtin_bit_cast(uint32_t, l));
+}
+
 // ---------------------------------------------------------------------------
 // Wide operands: the half-step with a K loop (fp32 inputs with d > 88 in the
 // hi/lo layout; bf16 inputs with d > 256).  The query operand no longer fits
@@ -1089,6 +1106,22 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
 //          x_h v_h + x_h v_l + x_l v_h (sc = 1);
 //   bf16:  acc starts at beta_j / 2 and adds x.y (sc = 2 lambda).
 // The exponent is fma(acc, sc, -m).
+//
+// The same blocked product serves the wide plan passes (transport, plan
+// application, the HVP's row-weighted pass), which go through a weights buffer
+// holding one block of rows against all keys (the value product at these widths
+// is compute bound many times over the buffer's traffic):
+//   EPI_W:    the row block's weights 2^(score - M_i), M_i = lambda (|x_i|^2 - T_i)
+//             from the row's half-step value T_i (so a row's weights sum to 1),
+//             written as bf16 hi/lo parts;
+//   EPI_U:    with the direction planes as rows and no bias, u_ij = ugain * acc
+//             = (y_j - c) . v_i; the buffered weights are multiplied by u_ij and
+//             their plain sums per key split written out;
+//   EPI_GEMM: rows = weight rows (K = hi keys then lo keys), columns = value
+//             columns (K wraps over the keys once), partial products per K split.
+// In the weights buffer the 32 keys of a tile sit in the order in which a lane
+// holds them (position 16 grp + o is key key_of(o, grp)); the value rows use the
+// same order, so a lane moves its 16 weights as two 16-byte vectors.
 // ---------------------------------------------------------------------------
 constexpr int KL_NW = 8, KL_WQ = 4, KL_QT = 2, KL_KT = 4;
 constexpr int KL_BQ = KL_WQ * KL_QT * 32;              // 256 queries per workgroup
@@ -1096,12 +1129,47 @@ constexpr int KL_BK = (KL_NW / KL_WQ) * KL_KT * 32;    // 256 keys per block
 constexpr int KL_KC = 32;                               // K slots per LDS chunk
 constexpr int KL_LR = KL_KC + 8;                        // LDS row stride (elements)
 static_assert(ROW_PAD % KL_BQ == 0 && ROW_PAD % KL_BK == 0, "blocks must tile the row padding");
+constexpr int EPI_LSE = 0, EPI_W = 1, EPI_U = 2, EPI_GEMM = 3;
 
-__global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2))) void k_lsek(
-    const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb,
-    const double* __restrict__ qnorm, float* __restrict__ out, float2* __restrict__ part, int rows, int rows_pad,
-    int keys, int keys_pad, int KP, int blocks_per_split, int batch, float sc, double inv_lam,
-    unsigned* __restrict__ tag, unsigned tag_val, unsigned* __restrict__ status, NextBias nb) {
+// Key of position p (0..31) of a 32-key tile in the lane order of the weights.
+__host__ __device__ constexpr int lane_key(int p) { return 8 * ((p % 16) / 4) + 4 * (p / 16) + (p % 4); }
+
+// Arguments of the K-looped kernel.  A (row operand): rows of a_ld elements,
+// a_rows rows per problem, the launch's first row a_row0; K chunk kc reads
+// chunk kc % a_nkc of plane kc / a_nkc (planes a_plane elements apart).
+// B (column operand): rows of b_ld elements, b_rows per problem; K chunk kc
+// reads chunk kc % b_nkc.  Rows of the launch are rows row0.. of the problem.
+struct KlArgs {
+  const u16* A;
+  const u16* B;
+  const float* hb;       // bias of the B rows (accumulator start), or nullptr for 0
+  const double* qnorm;   // |x_i|^2 of the rows (LSE, W)
+  const float* lse;      // half-step values of the rows (W)
+  float* out;            // potential (LSE without splits)
+  float2* part;          // (max, sum) per split (LSE with splits)
+  u16* wt;               // weights buffer (W, U)
+  float* pv;             // partial products [split][batch][rows][nc] (GEMM)
+  float* sp;             // plain weight sums [split][batch][rows] (U)
+  unsigned* tag;
+  unsigned tag_val;
+  unsigned* status;
+  long long a_plane;
+  int a_ld, a_rows, a_row0, a_nkc;
+  int b_ld, b_rows, b_nkc;
+  int rows, row0, keys;
+  int nkc;               // K chunks per key block (LSE, W, U)
+  int per_split;         // key blocks (LSE, W, U) or K chunks (GEMM) per split
+  int total_kc;          // K chunks in all (GEMM)
+  int ncolt, nc;         // column blocks and stored columns (GEMM)
+  int wt_ld, kcov, wt_rows;  // weights buffer: row stride, offset of the lo parts, rows per problem
+  int batch;
+  float sc, lam, ugain;
+  double inv_lam;
+  NextBias nb;
+};
+
+template <int EPI>
+__global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2))) void k_lsek(const KlArgs a) {
   using T = Tile<32>;
   using Acc = typename T::Acc;
   constexpr int NT = 64 * KL_NW;
@@ -1117,31 +1185,53 @@ __global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2)))
   const int grp = lane >> 5, col = lane & 31;
   const int wq = wave % KL_WQ, wk = wave / KL_WQ;
   const int b = blockIdx.z;
-  const int q0 = blockIdx.x * KL_BQ;
-  if (tag != nullptr && tid == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) *tag = tag_val;
-  const u16* Qb = Q + ((size_t)b * rows_pad + q0) * KP;
-  const u16* Kb = K + (size_t)b * keys_pad * KP;
-  const float* hbb = hb + (size_t)b * keys_pad;
-  const int nblk = (keys + KL_BK - 1) / KL_BK;
-  const int kb0 = blockIdx.y * blocks_per_split, kb1 = min(nblk, kb0 + blocks_per_split);
-  const int nkc = KP / KL_KC;
+  const int q0 = blockIdx.x * KL_BQ;  // first row of the workgroup within the launch
+  if (a.tag != nullptr && tid == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) *a.tag = a.tag_val;
+  const u16* Ab = a.A + ((size_t)b * a.a_rows + a.a_row0 + q0) * a.a_ld;
+  const u16* Bb = a.B + (size_t)b * a.b_rows * a.b_ld;
+  const float* hbb = a.hb != nullptr ? a.hb + (size_t)b * a.b_rows : nullptr;
+  int kb0, kb1, kc0, kc1;
+  if (EPI == EPI_GEMM) {
+    kb0 = blockIdx.y % a.ncolt;
+    kb1 = kb0 + 1;
+    kc0 = (blockIdx.y / a.ncolt) * a.per_split;
+    kc1 = min(a.total_kc, kc0 + a.per_split);
+  } else {
+    const int nblk = (a.keys + KL_BK - 1) / KL_BK;
+    kb0 = blockIdx.y * a.per_split;
+    kb1 = min(nblk, kb0 + a.per_split);
+    kc0 = 0;
+    kc1 = a.nkc;
+  }
 
-  float m[KL_QT], s[KL_QT];
+  float m[KL_QT], s[KL_QT], Mrow[KL_QT];
 #pragma unroll
   for (int c = 0; c < KL_QT; ++c) {
     m[c] = -FLT_MAX;
     s[c] = 0.f;
+    Mrow[c] = 0.f;
+    if (EPI == EPI_W) {
+      const int q = a.row0 + q0 + wq * (KL_QT * 32) + c * 32 + col;
+      if (q < a.rows) {
+        const size_t r = (size_t)b * a.rows + q;
+        const double M = (double)a.lam * (a.qnorm[r] - (double)a.lse[r]);
+        Mrow[c] = fabs(M) < 1e30 ? (float)M : 0.f;
+      }
+    }
   }
 
   // staging: load i of thread tid takes 16-byte segment (tid + NT i) % SEGS of row
-  // (tid + NT i) / SEGS (rows 0..BQ-1 queries of this workgroup, then the block's keys)
+  // (tid + NT i) / SEGS (rows 0..BQ-1 the workgroup's A rows, then the block's B rows)
   u4 pre[NLD];
   auto gload = [&](int kb, int kc) {
+    const long long aoff = (long long)(kc / a.a_nkc) * a.a_plane + (long long)(kc % a.a_nkc) * KL_KC;
+    const int boff = (kc % a.b_nkc) * KL_KC;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int idx = tid + NT * i, row = idx / SEGS, seg = idx % SEGS;
-      const u16* src = row < KL_BQ ? Qb + (size_t)row * KP : Kb + ((size_t)kb * KL_BK + (row - KL_BQ)) * KP;
-      pre[i] = *reinterpret_cast<const u4*>(src + kc * KL_KC + seg * 8);
+      const u16* src = row < KL_BQ ? Ab + (size_t)row * a.a_ld + aoff
+                                   : Bb + ((size_t)kb * KL_BK + (row - KL_BQ)) * a.b_ld + boff;
+      pre[i] = *reinterpret_cast<const u4*>(src + seg * 8);
     }
   };
   auto lstore = [&](int buf) {
@@ -1151,12 +1241,17 @@ __global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2)))
       *reinterpret_cast<u4*>(&lds[buf][row * KL_LR + seg * 8]) = pre[i];
     }
   };
+  // the weights-buffer row of query tile c and the start of key tile t of block kb
+  auto wrow = [&](int c, int kb, int t) {
+    return a.wt + ((size_t)b * a.wt_rows + q0 + wq * (KL_QT * 32) + c * 32 + col) * a.wt_ld + (size_t)kb * KL_BK +
+           wk * (KL_KT * 32) + t * 32 + grp * 16;
+  };
 
   if (kb0 < kb1) {
     Acc acc[KL_QT][KL_KT];
     int buf = 0;
-    gload(kb0, 0);
-    if (tid < KL_BK) ldb[tid] = hbb[(size_t)kb0 * KL_BK + tid];
+    if (kc0 < kc1) gload(kb0, kc0);
+    if (hbb != nullptr && tid < KL_BK) ldb[tid] = hbb[(size_t)kb0 * KL_BK + tid];
     lstore(0);
     __syncthreads();
     for (int kb = kb0; kb < kb1; ++kb) {
@@ -1165,18 +1260,19 @@ __global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2)))
       for (int t = 0; t < KL_KT; ++t) {
         Acc ci;
 #pragma unroll
-        for (int o = 0; o < 16; ++o) ci[o] = ldb[wk * (KL_KT * 32) + t * 32 + T::key_of(o, grp)];
+        for (int o = 0; o < 16; ++o) ci[o] = hbb != nullptr ? ldb[wk * (KL_KT * 32) + t * 32 + T::key_of(o, grp)] : 0.f;
 #pragma unroll
         for (int c = 0; c < KL_QT; ++c) acc[c][t] = ci;
       }
       float nbias = 0.f;
-      for (int kc = 0; kc < nkc; ++kc) {
-        const bool more = kc + 1 < nkc || kb + 1 < kb1;
-        if (kc + 1 < nkc)
+      for (int kc = kc0; kc < kc1; ++kc) {
+        const bool more = kc + 1 < kc1 || kb + 1 < kb1;
+        if (kc + 1 < kc1)
           gload(kb, kc + 1);
         else if (kb + 1 < kb1)
-          gload(kb + 1, 0);
-        if (kc + 1 == nkc && kb + 1 < kb1 && tid < KL_BK) nbias = hbb[(size_t)(kb + 1) * KL_BK + tid];
+          gload(kb + 1, kc0);
+        const bool nb_load = hbb != nullptr && kc + 1 == kc1 && kb + 1 < kb1 && tid < KL_BK;
+        if (nb_load) nbias = hbb[(size_t)(kb + 1) * KL_BK + tid];
         const u16* L = lds[buf];
 #pragma unroll
         for (int ks = 0; ks < KL_KC / 16; ++ks) {
@@ -1194,68 +1290,142 @@ __global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2)))
         }
         if (more) lstore(buf ^ 1);
         // the bias of the next block: every wave has read this block's at its start
-        if (kc + 1 == nkc && kb + 1 < kb1 && tid < KL_BK) ldb[tid] = nbias;
+        if (nb_load) ldb[tid] = nbias;
         __syncthreads();
         buf ^= 1;
       }
-      // block epilogue: exact block maximum, offset moves only past it, then the sums
-      bool coarse = false;
+      if (EPI == EPI_LSE) {
+        // block epilogue: exact block maximum, offset moves only past it, then the sums
+        bool coarse = false;
 #pragma unroll
-      for (int c = 0; c < KL_QT; ++c) {
-        float mx = -INFINITY;
+        for (int c = 0; c < KL_QT; ++c) {
+          float mx = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < KL_KT; ++t)
+          for (int t = 0; t < KL_KT; ++t)
 #pragma unroll
-          for (int o = 0; o < 16; ++o) mx = fmaxf(mx, acc[c][t][o] * sc);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (!(mx <= m[c])) {
-          const float mn = fmaxf(m[c], offset_from_max(mx + HEADROOM, 1.f, coarse));
-          s[c] = rescale(s[c], m[c], mn);
-          m[c] = mn;
+            for (int o = 0; o < 16; ++o) mx = fmaxf(mx, acc[c][t][o] * a.sc);
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          if (!(mx <= m[c])) {
+            const float mn = fmaxf(m[c], offset_from_max(mx + HEADROOM, 1.f, coarse));
+            s[c] = rescale(s[c], m[c], mn);
+            m[c] = mn;
+          }
+          float e[16];
+#pragma unroll
+          for (int o = 0; o < 16; ++o) e[o] = 0.f;
+#pragma unroll
+          for (int t = 0; t < KL_KT; ++t)
+#pragma unroll
+            for (int o = 0; o < 16; ++o) e[o] += __builtin_amdgcn_exp2f(fmaf(acc[c][t][o], a.sc, -m[c]));
+#pragma unroll
+          for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+            for (int o = 0; o + w < 16; o += 2 * w) e[o] += e[o + w];
+          s[c] += e[0];
         }
-        float e[16];
+        flag_if(a.status, coarse && lane == 0, FLAG_SCORE_RANGE);
+      } else if (EPI == EPI_W || EPI == EPI_U) {
 #pragma unroll
-        for (int o = 0; o < 16; ++o) e[o] = 0.f;
+        for (int c = 0; c < KL_QT; ++c)
 #pragma unroll
-        for (int t = 0; t < KL_KT; ++t)
+          for (int t = 0; t < KL_KT; ++t) {
+            u16* wp = wrow(c, kb, t);
+            float e[16];
+            if (EPI == EPI_W) {
 #pragma unroll
-          for (int o = 0; o < 16; ++o) e[o] += __builtin_amdgcn_exp2f(fmaf(acc[c][t][o], sc, -m[c]));
+              for (int o = 0; o < 16; ++o) e[o] = __builtin_amdgcn_exp2f(fmaf(acc[c][t][o], a.sc, -Mrow[c]));
+            } else {
+              const u4 h0 = *reinterpret_cast<const u4*>(wp), h1 = *reinterpret_cast<const u4*>(wp + 8);
+              const u4 l0 = *reinterpret_cast<const u4*>(wp + a.kcov), l1 = *reinterpret_cast<const u4*>(wp + a.kcov + 8);
+              const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+              const uint32_t lw[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
-        for (int w = 1; w < 16; w *= 2)
+              for (int h = 0; h < 8; ++h) {
+                e[2 * h] = __uint_as_float(hw[h] << 16) + __uint_as_float(lw[h] << 16);
+                e[2 * h + 1] = __uint_as_float(hw[h] & 0xffff0000u) + __uint_as_float(lw[h] & 0xffff0000u);
+              }
+              float sum = 0.f;
 #pragma unroll
-          for (int o = 0; o + w < 16; o += 2 * w) e[o] += e[o + w];
-        s[c] += e[0];
+              for (int o = 0; o < 16; ++o) sum += e[o];
+              s[c] += sum;
+#pragma unroll
+              for (int o = 0; o < 16; ++o) e[o] *= acc[c][t][o] * a.ugain;
+            }
+            uint2 pr[8];
+#pragma unroll
+            for (int h = 0; h < 8; ++h) pr[h] = split_pair(e[2 * h], e[2 * h + 1]);
+            *reinterpret_cast<u4*>(wp) = u4{pr[0].x, pr[1].x, pr[2].x, pr[3].x};
+            *reinterpret_cast<u4*>(wp + 8) = u4{pr[4].x, pr[5].x, pr[6].x, pr[7].x};
+            *reinterpret_cast<u4*>(wp + a.kcov) = u4{pr[0].y, pr[1].y, pr[2].y, pr[3].y};
+            *reinterpret_cast<u4*>(wp + a.kcov + 8) = u4{pr[4].y, pr[5].y, pr[6].y, pr[7].y};
+          }
+      } else {
+        // partial products: lane (row col, group grp) holds columns key_of(o, grp) of each tile
+        const int split = blockIdx.y / a.ncolt;
+#pragma unroll
+        for (int c = 0; c < KL_QT; ++c) {
+          const int q = a.row0 + q0 + wq * (KL_QT * 32) + c * 32 + col;
+          if (q >= a.rows) continue;
+          float* dst = a.pv + ((size_t)split * a.batch * a.rows + (size_t)b * a.rows + q) * a.nc;
+#pragma unroll
+          for (int t = 0; t < KL_KT; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int cc = kb * KL_BK + wk * (KL_KT * 32) + t * 32 + 8 * u + 4 * grp;
+              if (cc < a.nc)
+                *reinterpret_cast<f4*>(dst + cc) =
+                    f4{acc[c][t][4 * u], acc[c][t][4 * u + 1], acc[c][t][4 * u + 2], acc[c][t][4 * u + 3]};
+            }
+        }
       }
-      flag_if(status, coarse && lane == 0, FLAG_SCORE_RANGE);
     }
   }
-  // the two lanes of a query share its offset; then the two key halves (waves
-  // wk = 0, 1) merge through LDS
+  if (EPI == EPI_LSE) {
+    // the two lanes of a query share its offset; then the two key halves (waves
+    // wk = 0, 1) merge through LDS
 #pragma unroll
-  for (int c = 0; c < KL_QT; ++c) s[c] += __shfl_xor(s[c], 32);
-  if (wk == 1 && grp == 0) {
+    for (int c = 0; c < KL_QT; ++c) s[c] += __shfl_xor(s[c], 32);
+    if (wk == 1 && grp == 0) {
 #pragma unroll
-    for (int c = 0; c < KL_QT; ++c) ldm[wq * (KL_QT * 32) + c * 32 + col] = make_float2(m[c], s[c]);
-  }
-  __syncthreads();
-  if (wk == 0 && grp == 0) {
+      for (int c = 0; c < KL_QT; ++c) ldm[wq * (KL_QT * 32) + c * 32 + col] = make_float2(m[c], s[c]);
+    }
+    __syncthreads();
+    if (wk == 0 && grp == 0) {
 #pragma unroll
-    for (int c = 0; c < KL_QT; ++c) {
-      const int ql = wq * (KL_QT * 32) + c * 32 + col;
-      const float2 o = ldm[ql];
-      const float M = fmaxf(m[c], o.x);
-      const float S = rescale(s[c], m[c], M) + rescale(o.y, o.x, M);
-      const int q = q0 + ql;
-      if (q < rows) {
-        const size_t r = (size_t)b * rows + q;
-        if (part != nullptr) {
-          part[(size_t)blockIdx.y * batch * rows + r] = make_float2(M, S);
-        } else {
-          const float v = (float)(qnorm[r] - ((double)M + log2((double)S)) * inv_lam);
-          out[r] = v;
-          flag_if(status, !isfinite(v), FLAG_NONFINITE);
-          if (nb.logw != nullptr) write_next_bias(nb, b, q, v, qnorm[r], nb.logw[r]);
+      for (int c = 0; c < KL_QT; ++c) {
+        const int ql = wq * (KL_QT * 32) + c * 32 + col;
+        const float2 o = ldm[ql];
+        const float M = fmaxf(m[c], o.x);
+        const float S = rescale(s[c], m[c], M) + rescale(o.y, o.x, M);
+        const int q = q0 + ql;
+        if (q < a.rows) {
+          const size_t r = (size_t)b * a.rows + q;
+          if (a.part != nullptr) {
+            a.part[(size_t)blockIdx.y * a.batch * a.rows + r] = make_float2(M, S);
+          } else {
+            const float v = (float)(a.qnorm[r] - ((double)M + log2((double)S)) * a.inv_lam);
+            a.out[r] = v;
+            flag_if(a.status, !isfinite(v), FLAG_NONFINITE);
+            if (a.nb.logw != nullptr) write_next_bias(a.nb, b, q, v, a.qnorm[r], a.nb.logw[r]);
+          }
         }
+      }
+    }
+  } else if (EPI == EPI_U) {
+    // plain weight sums of the split: both lanes of a row, then both key halves
+#pragma unroll
+    for (int c = 0; c < KL_QT; ++c) s[c] += __shfl_xor(s[c], 32);
+    if (wk == 1 && grp == 0) {
+#pragma unroll
+      for (int c = 0; c < KL_QT; ++c) ldm[wq * (KL_QT * 32) + c * 32 + col] = make_float2(0.f, s[c]);
+    }
+    __syncthreads();
+    if (wk == 0 && grp == 0) {
+#pragma unroll
+      for (int c = 0; c < KL_QT; ++c) {
+        const int ql = wq * (KL_QT * 32) + c * 32 + col;
+        const int q = a.row0 + q0 + ql;
+        if (q < a.rows) a.sp[(size_t)blockIdx.y * a.batch * a.rows + (size_t)b * a.rows + q] = s[c] + ldm[ql].y;
       }
     }
   }
@@ -1292,6 +1462,47 @@ __global__ __launch_bounds__(256) void k_prep_keys_hilo(const void* __restrict__
   *reinterpret_cast<u4*>(kb + ((size_t)b * keys_pad + j) * KP + k0) =
       u4{(uint32_t)v8[0] | ((uint32_t)v8[1] << 16), (uint32_t)v8[2] | ((uint32_t)v8[3] << 16),
          (uint32_t)v8[4] | ((uint32_t)v8[5] << 16), (uint32_t)v8[6] | ((uint32_t)v8[7] << 16)};
+}
+
+// Value rows of a wide plan pass, [batch][ncp][kcov] bf16 with the keys of each
+// 32-key tile in lane order (lane_key).  Row cc: without M, the centred
+// coordinates of the key cloud in `parts` bf16 parts (cc = part d + t; one part
+// holds a bf16 input exactly, two parts hold 16 significant bits of an fp32 one,
+// from fp64); with M, three parts of the fp32 matrix columns col0.. (cc = part cb
+// + k, exact).  Row ones_col (if >= 0) holds ones; other rows and padding keys
+// are zero.  One thread per 8 positions.
+__global__ __launch_bounds__(256) void k_prep_vt(const void* __restrict__ P, int in_bf16,
+                                                 const double* __restrict__ cen, const float* __restrict__ M, int c,
+                                                 int col0, int cb, int parts, int keys, int kcov, int d, int ncp,
+                                                 int ones_col, u16* __restrict__ vt) {
+  const int b = blockIdx.y;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per_row = kcov / 8;
+  if (idx >= (long long)ncp * per_row) return;
+  const int cc = (int)(idx / per_row), p0 = (int)(idx % per_row) * 8;
+  u16 v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int p = p0 + e, j = (p / 32) * 32 + lane_key(p % 32);
+    u16 val = 0;
+    if (j < keys && cc == ones_col) {
+      val = BF16_ONE;
+    } else if (j < keys && M != nullptr && cc < 3 * cb) {
+      const float x = M[((size_t)b * keys + j) * c + col0 + cc % cb];
+      const u16 h0 = bf16_rne(x);
+      const float r1 = x - bf16_f(h0);
+      const u16 h1 = bf16_rne(r1);
+      const int part = cc / cb;
+      val = part == 0 ? h0 : (part == 1 ? h1 : bf16_rne(r1 - bf16_f(h1)));
+    } else if (j < keys && M == nullptr && cc < parts * d) {
+      const int t = cc % d;
+      const double x = (double)coord(P, ((size_t)b * keys + j) * d + t, in_bf16) - cen[(size_t)b * d + t];
+      const u16 h = bf16_of(x);
+      val = cc / d == 0 ? h : bf16_of(x - (double)bf16_f(h));
+    }
+    v[e] = val;
+  }
+  *reinterpret_cast<u4*>(vt + ((size_t)b * ncp + cc) * kcov + p0) = pack8(v);
 }
 
 // Merge the (max, sum) pairs of the key splits (one pass, exact power-of-two
@@ -1431,23 +1642,6 @@ __global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, i
     v[e] = val;
   }
   *reinterpret_cast<u4*>(vt + (((size_t)b * (keys_pad / VK) + blk) * ncols + c) * VK + k0) = pack8(v);
-}
-
-// Two packed bf16 parts of a weight pair: hi = e truncated to bf16 (its upper
-// half), lo = rne(e - hi), where e - hi is exact; together 16 significant bits.
-// Returns (hi pair, lo pair).  The hi pair is one byte permute; e - hi is one
-// bf16 dot product each, hi . (-1, -0) + a and hi . (0, -1) + b (products and
-// sums exact).  The first pair is written (-1, -0) so that it is encoded as a
-// 32-bit literal: hipcc encodes (-1, 0) as the inline constant -1.0, which
-// this instruction reads as the fp32 bit pattern, i.e. as the pair (0, -1).
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint2 split_pair(float a, float b) {
-  const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
-  const bf16x2 h = __builtin_bit_cast(bf16x2, hi);
-  const float la = __builtin_amdgcn_fdot2_f32_bf16(h, bf16x2{(__bf16)-1.f, (__bf16)-0.f}, a, false);
-  const float lb = __builtin_amdgcn_fdot2_f32_bf16(h, bf16x2{(__bf16)0.f, (__bf16)-1.f}, b, false);
-  const bf16x2 l = {(__bf16)la, (__bf16)lb};
-  return make_uint2(hi, __builtin_bit_cast(uint32_t, l));
 }
 
 // One pass of P.V over a key range for 4 waves x R query tiles of 16 rows.
@@ -2157,6 +2351,23 @@ __global__ __launch_bounds__(256) void k_prep_u(const float* __restrict__ V, int
   u16* dst = U + ((size_t)b * rows_pad + i) * KP;
   const bool real = i < rows;
   const float* v = V + ((size_t)b * rows + (real ? i : 0)) * d;
+  if (mode == MODE_HILO) {
+    // (u_h, u_h, u_l) per coordinate against the key rows' (v_h, v_l, v_h)
+    for (int k0 = 0; k0 < KP; k0 += 8) {
+      u16 w8[8];
+      for (int e = 0; e < 8; ++e) {
+        const int k = k0 + e, t = k / 3;
+        u16 val = 0;
+        if (real && t < d) {
+          const u16 h = bf16_rne(v[t]);
+          val = (k % 3 == 2) ? bf16_rne(v[t] - bf16_f(h)) : h;
+        }
+        w8[e] = val;
+      }
+      *reinterpret_cast<u4*>(dst + k0) = pack8(w8);
+    }
+    return;
+  }
   if (mode == MODE_BF16) {
     for (int k = 0; k < KP; k += 2) {
       u16 h[2] = {0, 0}, l[2] = {0, 0};
@@ -2434,6 +2645,28 @@ NextBias next_bias(const sk_problem* p, char* w, const Layout& L, int side, floa
   return nb;
 }
 
+// Arguments of the K-looped kernel for scores of the query operand Qop (rows
+// of one side) against a key operand: the fields every epilogue shares.
+KlArgs kl_scores(const Layout& L, const u16* Qop, const KeyOperand& ko, int rows_pad, int keys_pad, int rows,
+                 int keys, int B, float lam) {
+  KlArgs a{};
+  a.A = Qop;
+  a.B = ko.K;
+  a.hb = ko.hb;
+  a.tag = ko.tag;
+  a.tag_val = __builtin_bit_cast(unsigned, lam);
+  a.a_ld = a.b_ld = L.KP;
+  a.a_rows = rows_pad;
+  a.b_rows = keys_pad;
+  a.a_nkc = a.b_nkc = a.nkc = L.KP / KL_KC;
+  a.rows = rows;
+  a.keys = keys;
+  a.batch = B;
+  a.sc = L.mode == MODE_HILO ? 1.f : 2.f * lam;
+  a.lam = lam;
+  return a;
+}
+
 // One half-step.  side 0: f from g (queries X, keys Y); side 1: g from f.
 // bias_ready: the key bias for pot_in and eps is already in place (written by
 // the producer of pot_in), so no preparation kernel runs.  nb: write the next
@@ -2470,15 +2703,20 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
     const int wg_x = (rows + KL_BQ - 1) / KL_BQ;
     const int nblk = (keys + KL_BK - 1) / KL_BK;
     int capacity = 0;
-    st = resident_capacity(reinterpret_cast<const void*>(&k_lsek), &capacity, 64 * KL_NW);
+    st = resident_capacity(reinterpret_cast<const void*>(&k_lsek<EPI_LSE>), &capacity, 64 * KL_NW);
     if (st != SK_OK) return st;
     int bps = 0;
     const int ks = choose_key_splits(wg_x * B, nblk, capacity, &bps);
     float2* part = ks > 1 ? reinterpret_cast<float2*>(w + L.part) : nullptr;
-    hipLaunchKernelGGL(k_lsek, dim3(wg_x, ks, B), dim3(64 * KL_NW), 0, stream, reinterpret_cast<const u16*>(Qop), ko.K,
-                       ko.hb, qnorm, pot_out, part, rows, rows_pad, keys, keys_pad, L.KP, bps, B,
-                       L.mode == MODE_HILO ? 1.f : 2.f * lam, inv_lam,
-                       ko.tag, __builtin_bit_cast(unsigned, lam), status, ks == 1 ? nb : NextBias{});
+    KlArgs ka = kl_scores(L, Qop, ko, rows_pad, keys_pad, rows, keys, B, lam);
+    ka.qnorm = qnorm;
+    ka.out = pot_out;
+    ka.part = part;
+    ka.per_split = bps;
+    ka.inv_lam = inv_lam;
+    ka.status = status;
+    ka.nb = ks == 1 ? nb : NextBias{};
+    hipLaunchKernelGGL(k_lsek<EPI_LSE>, dim3(wg_x, ks, B), dim3(64 * KL_NW), 0, stream, ka);
     st = hip_check("half-step kernel launch");
     if (st != SK_OK || ks == 1) return st;
     const int total = B * rows;
@@ -2541,6 +2779,112 @@ BaryFn bary_lookup(int mode, int d) {
   return bary_lookup_impl<MODE_BF16>(d, std::make_integer_sequence<int, SK_MAX_D_TRANSPORT>{});
 }
 
+// Plan pass for wide operands (see EPI_W): per block of L.wt_rows rows of
+// `side`, the weights at the rows' fixed offsets (their half-step values lse),
+// times u_ij when the direction planes U are given (then the plain weight sums
+// per split go to bs), then their product with the value rows vt (ncp rows;
+// L.ncols columns stored) into the split partials bpv.  *ks_out: the number of
+// splits, the same for every row block.
+sk_status wide_pass(const sk_problem* p, const void* X, const void* Y, char* w, const Layout& L, const float* pot_key,
+                    const float* lse, float eps, int side, const u16* vt, int ncp, const u16* U, float ugain,
+                    int* ks_out, hipStream_t stream) {
+  const int B = (int)p->batch;
+  const int rows = (int)(side == 0 ? p->n : p->m);
+  const int keys = (int)(side == 0 ? p->m : p->n);
+  const int rows_pad = side == 0 ? L.n_pad : L.m_pad;
+  const int keys_pad = side == 0 ? L.m_pad : L.n_pad;
+  const double* qnorm = reinterpret_cast<const double*>(w + (side == 0 ? L.xn : L.yn));
+  const u16* Qop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qx : L.qy));
+  KeyOperand ko;
+  sk_status st = prep_keys(p, X, Y, w, L, pot_key, eps, side, stream, &ko);
+  if (st != SK_OK) return st;
+  if (L.KP < 2 * KL_KC || ncp % KL_BK != 0) {
+    set_err("internal: wide plan pass with KP = %d, %d value rows", L.KP, ncp);
+    return SK_EUNSUPPORTED;
+  }
+  const int nblk = (keys + KL_BK - 1) / KL_BK, kcov = nblk * KL_BK;
+  const int rb = L.wt_rows;
+  const int wg_full = (std::min(rb, rows) + KL_BQ - 1) / KL_BQ;
+  const float lam = (float)(LOG2E / (double)eps);
+  const int planes = L.mode == MODE_BF16 ? 2 : 1;  // direction planes (hi, lo) of the bf16 path
+  int cap_w = 0, cap_g = 0;
+  st = resident_capacity(reinterpret_cast<const void*>(&k_lsek<EPI_W>), &cap_w, 64 * KL_NW);
+  if (st == SK_OK) st = resident_capacity(reinterpret_cast<const void*>(&k_lsek<EPI_GEMM>), &cap_g, 64 * KL_NW);
+  if (st != SK_OK) return st;
+  // splits of the product over its K range (hi keys, then lo keys)
+  const int ncolt = ncp / KL_BK, total_kc = 2 * kcov / KL_KC;
+  const int ks_cap = (int)std::min<size_t>(16, std::max<size_t>(1, L.bpv_bytes / (4 * (size_t)B * rows * L.ncols)));
+  int cps = 0;
+  const int ks = choose_key_splits(wg_full * ncolt * B, total_kc, cap_g, &cps, ks_cap);
+  int bps_w = 0;
+  const int ks_w = choose_key_splits(wg_full * B, nblk, cap_w, &bps_w);
+  u16* wt = reinterpret_cast<u16*>(w + L.wt);
+  unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
+  for (int r0 = 0; r0 < rows; r0 += rb) {
+    const int wg = (std::min(rb, rows - r0) + KL_BQ - 1) / KL_BQ;
+    KlArgs aw = kl_scores(L, Qop, ko, rows_pad, keys_pad, rows, keys, B, lam);
+    aw.a_row0 = aw.row0 = r0;
+    aw.qnorm = qnorm;
+    aw.lse = lse;
+    aw.wt = wt;
+    aw.wt_ld = 2 * kcov;
+    aw.kcov = kcov;
+    aw.wt_rows = rb;
+    aw.per_split = bps_w;
+    aw.status = status;
+    hipLaunchKernelGGL(k_lsek<EPI_W>, dim3(wg, ks_w, B), dim3(64 * KL_NW), 0, stream, aw);
+    if (U != nullptr) {
+      KlArgs au = aw;
+      au.A = U;
+      au.hb = nullptr;
+      au.tag = nullptr;
+      au.a_plane = ((long long)B * rows_pad + SLACK) * L.KP;
+      au.nkc = planes * (L.KP / KL_KC);
+      au.per_split = (nblk + ks - 1) / ks;
+      au.ugain = ugain;
+      au.sp = reinterpret_cast<float*>(w + L.bs);
+      hipLaunchKernelGGL(k_lsek<EPI_U>, dim3(wg, ks, B), dim3(64 * KL_NW), 0, stream, au);
+    }
+    KlArgs ag{};
+    ag.A = wt;
+    ag.B = vt;
+    ag.a_ld = 2 * kcov;
+    ag.a_rows = rb;
+    ag.a_nkc = total_kc;
+    ag.b_ld = kcov;
+    ag.b_rows = ncp;
+    ag.b_nkc = kcov / KL_KC;
+    ag.rows = rows;
+    ag.row0 = r0;
+    ag.per_split = cps;
+    ag.total_kc = total_kc;
+    ag.ncolt = ncolt;
+    ag.nc = L.ncols;
+    ag.pv = reinterpret_cast<float*>(w + L.bpv);
+    ag.batch = B;
+    hipLaunchKernelGGL(k_lsek<EPI_GEMM>, dim3(wg, ncolt * ks, B), dim3(64 * KL_NW), 0, stream, ag);
+    st = hip_check("wide plan pass launch");
+    if (st != SK_OK) return st;
+  }
+  *ks_out = ks;
+  return SK_OK;
+}
+
+// Value rows of a wide pass (k_prep_vt) for the keys of `side`.
+sk_status wide_values(const sk_problem* p, const void* Kraw, char* w, const Layout& L, int side, const float* M,
+                      int c, int col0, int cb, int ones_col, int* ncp_out, hipStream_t stream) {
+  const int B = (int)p->batch, d = (int)p->d;
+  const int keys = (int)(side == 0 ? p->m : p->n);
+  const int kcov = (keys + KL_BK - 1) / KL_BK * KL_BK;
+  const int ncp = (int)align_up((size_t)L.ncols, KL_BK);
+  const long long nvec = (long long)ncp * (kcov / 8);
+  hipLaunchKernelGGL(k_prep_vt, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, Kraw, L.in_bf16,
+                     reinterpret_cast<const double*>(w + L.cen), M, c, col0, cb, val_parts(L.mode), keys, kcov, d,
+                     ncp, ones_col, reinterpret_cast<u16*>(w + L.vt));
+  *ncp_out = ncp;
+  return hip_check("value rows launch");
+}
+
 // Barycentric projection (and gradient) of the rows of one side: side 0 the
 // points of X against Y, side 1 the points of Y against X.
 sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws, const Layout& L, const float* f,
@@ -2558,6 +2902,25 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   const void* Kraw = side == 0 ? Y : X;
   const float* pot_row = side == 0 ? f : g;
   float* lse = reinterpret_cast<float*>(w + L.scratch);
+
+  if (L.wide) {
+    // the rows' half-step values fix their offsets; then the weights pass with
+    // the coordinates (and a ones column for the weight sums) as values
+    sk_status st = half_step(p, X, Y, ws, L, side == 0 ? g : f, eps, lse, side, stream);
+    int ncp = 0, ks = 0;
+    if (st == SK_OK) st = wide_values(p, Kraw, w, L, side, nullptr, 0, 0, 0, L.ncols - 1, &ncp, stream);
+    if (st == SK_OK)
+      st = wide_pass(p, X, Y, w, L, side == 0 ? g : f, lse, eps, side, reinterpret_cast<const u16*>(w + L.vt), ncp,
+                     nullptr, 1.f, &ks, stream);
+    if (st != SK_OK) return st;
+    const long long total = (long long)B * rows * d;
+    const float lam = (float)(LOG2E / (double)eps);
+    hipLaunchKernelGGL(k_bary_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<const float*>(w + L.bpv), reinterpret_cast<const float*>(w + L.bs), ks, B,
+                       rows, d, L.ncols, val_parts(L.mode), 1, Praw, L.in_bf16, pot_row, lse, qlogw, (double)eps,
+                       nullptr, qnorm, 1.0 / (double)lam, reinterpret_cast<const double*>(w + L.cen), bary, grad);
+    return hip_check("transport merge launch");
+  }
 
   // 1. The key operand of this side for the other potential and eps.  The P.V
   //    pass keeps lazy row offsets, so no half-step runs first: its merge
@@ -2658,6 +3021,24 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
   const double* qnorm = reinterpret_cast<const double*>(w + (side == 0 ? L.xn : L.yn));
   const double* qlogw = reinterpret_cast<const double*>(w + (side == 0 ? L.la : L.lb));
   const u16* Qop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qx : L.qy));
+  if (L.wide) {
+    for (int col0 = 0; col0 < c; col0 += L.wide_cols) {
+      const int cb = std::min(L.wide_cols, c - col0);
+      int ncp = 0, ks = 0;
+      sk_status st = wide_values(p, side == 0 ? Y : X, w, L, side, M, c, col0, cb, L.ncols - 1, &ncp, stream);
+      if (st == SK_OK)
+        st = wide_pass(p, X, Y, w, L, pot_key, lse, eps, side, reinterpret_cast<const u16*>(w + L.vt), ncp, nullptr,
+                       1.f, &ks, stream);
+      if (st != SK_OK) return st;
+      const long long total = (long long)B * rows * cb;
+      hipLaunchKernelGGL(k_apply_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                         reinterpret_cast<const float*>(w + L.bpv), ks, B, rows, cb, L.ncols, c, col0, qlogw, pot_row,
+                         lse, (double)eps, out);
+      st = hip_check("plan-application merge launch");
+      if (st != SK_OK) return st;
+    }
+    return SK_OK;
+  }
   KeyOperand ko;
   sk_status st = prep_keys(p, X, Y, w, L, pot_key, eps, side, stream, &ko);
   if (st != SK_OK) return st;
@@ -2738,10 +3119,27 @@ sk_status apply_uw(const sk_problem* p, const void* X, const void* Y, char* w, c
   const double* qlogw = reinterpret_cast<const double*>(w + (side == 0 ? L.la : L.lb));
   const u16* Qop = reinterpret_cast<const u16*>(w + (side == 0 ? L.qx : L.qy));
   const void* Kraw = side == 0 ? Y : X;
+  u16* U = reinterpret_cast<u16*>(w + L.h_u);
+  if (L.wide) {
+    hipLaunchKernelGGL(k_prep_u, dim3((rows_pad + 255) / 256, B), dim3(256), 0, stream, Vdir, rows, rows_pad, d,
+                       L.KP, L.mode, B, U);
+    int ncp = 0, ks = 0;
+    sk_status st = wide_values(p, Kraw, w, L, side, nullptr, 0, 0, 0, -1, &ncp, stream);
+    // the hi/lo key rows hold 2 lambda (y - c)
+    const float ugain = L.mode == MODE_HILO ? (float)((double)eps / (2.0 * LOG2E)) : 1.f;
+    if (st == SK_OK)
+      st = wide_pass(p, X, Y, w, L, pot_key, lse, eps, side, reinterpret_cast<const u16*>(w + L.vt), ncp, U, ugain,
+                     &ks, stream);
+    if (st != SK_OK) return st;
+    const long long total = (long long)B * rows * d;
+    hipLaunchKernelGGL(k_uw_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<const float*>(w + L.bpv), reinterpret_cast<const float*>(w + L.bs), ks, B,
+                       rows, d, L.ncols, val_parts(L.mode), qlogw, pot_row, lse, (double)eps, quad);
+    return hip_check("row-weighted merge launch");
+  }
   KeyOperand ko;
   sk_status st = prep_keys(p, X, Y, w, L, pot_key, eps, side, stream, &ko);
   if (st != SK_OK) return st;
-  u16* U = reinterpret_cast<u16*>(w + L.h_u);
   hipLaunchKernelGGL(k_prep_u, dim3((rows_pad + 255) / 256, B), dim3(256), 0, stream, Vdir, rows, rows_pad, d, L.KP,
                      L.mode, B, U);
   u16* vt = reinterpret_cast<u16*>(w + L.vt);
@@ -3209,29 +3607,12 @@ size_t sinkhorn_transport_workspace_bytes(const sk_problem* p) {
   return layout_of(p).ttotal;
 }
 
-// Transport, plan products and HVPs keep the query operand of the P.V kernel in
-// registers: d <= SK_MAX_D_TRANSPORT.
-static sk_status check_transport_d(const sk_problem* p) {
-  if (layout_of(p).mode == MODE_HILO) {
-    set_err("d = %lld exceeds SK_MAX_D_SPLIT = %d for transport, plan and HVP calls with fp32 inputs", (long long)p->d,
-            SK_MAX_D_SPLIT);
-    return SK_EUNSUPPORTED;
-  }
-  if (p->d > SK_MAX_D_TRANSPORT) {
-    set_err("d = %lld exceeds SK_MAX_D_TRANSPORT = %d for transport, plan and HVP calls", (long long)p->d,
-            SK_MAX_D_TRANSPORT);
-    return SK_EUNSUPPORTED;
-  }
-  return SK_OK;
-}
-
 static sk_status transport_entry(const sk_problem* p, const void* X, const void* Y, void* ws, size_t ws_bytes,
                                  const float* f, const float* g, float eps, float* bary, float* grad, void* stream,
                                  int side) {
   g_err[0] = 0;
   Layout L;
   sk_status st = check_ws(p, ws, ws_bytes, &L, 1);
-  if (st == SK_OK) st = check_transport_d(p);
   if (st != SK_OK) return st;
   if (!X || !Y || !f || !g || !bary) {
     set_err("X, Y, f, g and bary must be non-NULL device pointers");
@@ -3260,7 +3641,6 @@ static sk_status apply_entry(const sk_problem* p, const void* X, const void* Y, 
   g_err[0] = 0;
   Layout L;
   sk_status st = check_ws(p, ws, ws_bytes, &L, 1);
-  if (st == SK_OK) st = check_transport_d(p);
   if (st != SK_OK) return st;
   if (!X || !Y || !f || !g || !M || !out) {
     set_err("X, Y, f, g, the matrix and out must be non-NULL device pointers");
@@ -3305,7 +3685,6 @@ static sk_status hvp_entry(const sk_problem* p, const void* X, const void* Y, vo
   g_err[0] = 0;
   Layout L;
   sk_status st = check_ws(p, ws, ws_bytes, &L, 2);
-  if (st == SK_OK) st = check_transport_d(p);
   if (st != SK_OK) return st;
   if (!X || !Y || !f || !g || !V || !out) {
     set_err("X, Y, f, g, V and out must be non-NULL device pointers");

@@ -133,12 +133,12 @@ def test_transport_workspace_and_argument_errors(lib):
         assert fn(bp, ptr, ptr, ptr, full, ptr, ptr, 0.1, None, ptr, None) == 1
         assert fn(bp, ptr, ptr, ptr, full, None, ptr, 0.1, ptr, ptr, None) == 1
         assert fn(bp, ptr, ptr, ptr, full, ptr, ptr, 0.0, ptr, ptr, None) == 1
-        assert fn(ctypes.byref(_prob(d=89)), ptr, ptr, ptr, full, ptr, ptr, 0.1, ptr, ptr, None) == 5
-        wide = _prob(1, 300, 200, 300, 1)  # bf16 half-steps go to d = 1024, transport to 256
-        wb = lib.sinkhorn_transport_workspace_bytes(ctypes.byref(wide))
-        assert wb > 0
-        assert fn(ctypes.byref(wide), ptr, ptr, ptr, wb, ptr, ptr, 0.1, ptr, ptr, None) == 5
-        assert b"SK_MAX_D_TRANSPORT" in lib.sinkhorn_last_error()
+        # wide problems (fp32 past d = 88, bf16 past d = 256) take the weights-buffer
+        # passes: their transport workspace holds it, and a smaller one is refused
+        for wide in (_prob(1, 300, 200, 89, 0), _prob(1, 300, 200, 300, 1), _prob(1, 300, 200, 1024, 0)):
+            wb = lib.sinkhorn_transport_workspace_bytes(ctypes.byref(wide))
+            assert wb > lib.sinkhorn_workspace_bytes(ctypes.byref(wide)) > 0
+            assert fn(ctypes.byref(wide), ptr, ptr, ptr, wb - 256, ptr, ptr, 0.1, ptr, ptr, None) == 6
 
 
 def test_cost_field_validation(lib):

@@ -116,13 +116,3 @@ def test_fp32_wide_deterministic_role_swap_and_marginals():
     assert abs(e[0] - ra) <= slack * (1.0 + ra), (e, ra, slack)
     assert e[1] <= 2e-5, e
 
-
-def test_fp32_wide_transport_is_refused():
-    p = make_case(50, 40, 100, seed=2)
-    X, Y, a, b = dev(p)
-    ws = sk.alloc_workspace(X, Y, transport=True)
-    sk.init_norms(X, Y, a, b, ws)
-    f = torch.zeros((1, 50), device="cuda")
-    g = torch.zeros((1, 40), device="cuda")
-    with pytest.raises(sk.SinkhornError, match="SK_EUNSUPPORTED"):
-        sk.barycentric_x(X, Y, ws, f, g, 0.1)
