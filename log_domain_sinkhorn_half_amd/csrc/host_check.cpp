@@ -77,10 +77,10 @@ void check_layout(const sk_problem& p) {
   // transport regions, between total and ttotal
   const size_t kcov = align_up(mx, 256);
   std::vector<R> tregs;
-  tregs.push_back({L.vt, L.wide ? 2 * B * align_up((size_t)L.ncols, 256) * kcov : 2 * B * (size_t)L.max_pad * L.ncols});
+  tregs.push_back({L.vt, L.wide ? 2 * B * (size_t)L.ncols * kcov : 2 * B * (size_t)L.max_pad * L.ncols});
   if (L.wide) tregs.push_back({L.wt, 2 * B * (size_t)L.wt_rows * 2 * kcov});
-  tregs.push_back({L.bpv, std::max<size_t>(L.bpv_bytes, 4 * B * mx * (size_t)L.ncols)});
-  tregs.push_back({L.bs, 4 * 16 * B * mx});
+  tregs.push_back({L.bpv, std::max<size_t>(L.bpv_bytes, 4 * B * (L.wide ? 16 * (size_t)L.wt_rows : mx) * L.ncols)});
+  tregs.push_back({L.bs, 4 * 16 * B * std::max(mx, (size_t)L.wt_rows)});
   tregs.push_back({L.bm, 4 * 16 * B * mx});
   bool tordered = tregs[0].off >= L.total;
   for (size_t k = 0; k < tregs.size(); ++k) {
@@ -88,9 +88,9 @@ void check_layout(const sk_problem& p) {
     tordered &= tregs[k].off % 256 == 0 && tregs[k].off + tregs[k].min_bytes <= next;
   }
   expect(tordered, "transport regions aligned, in order, without overlap", p);
-  expect(!L.wide || (L.ncols % 16 == 0 && L.ncols >= val_parts(L.mode) * (int)d + 1 &&
-                     3 * L.wide_cols + 1 <= L.ncols && L.wide_cols >= APPLY_COLS),
-         "wide value columns hold the parts and the ones column", p);
+  expect(!L.wide || (L.ncols % 256 == 0 && L.ncols >= val_parts(L.mode) * (int)d && 3 * L.wide_cols <= L.ncols &&
+                     L.wide_cols >= APPLY_COLS),
+         "wide value columns: whole 256-column blocks holding the parts", p);
   expect(L.wide == (L.mode == MODE_HILO || (L.mode == MODE_BF16 && p.d > SK_MAX_D_TRANSPORT)),
          "wide passes exactly past the register-resident widths", p);
   expect(L.total <= L.ttotal && L.ttotal <= L.htotal, "nested workspace sizes", p);

@@ -208,10 +208,10 @@ Layout layout_of(const sk_problem* p) {
   // keys of a wide pass, rounded up to whole 256-key blocks
   const size_t kcov = align_up(mx, 256);
   if (L.wide) {
-    // value columns (parts of each coordinate, then the ones column) or three
-    // parts of wide_cols matrix columns and the ones column
-    L.ncols = (int)align_up(std::max<size_t>(val_parts(L.mode) * d + 1, 3 * APPLY_COLS + 1), 16);
-    L.wide_cols = (L.ncols - 1) / 3;
+    // value columns (the parts of each coordinate) or three parts of wide_cols
+    // matrix columns, in whole 256-column blocks of the product
+    L.ncols = (int)align_up(std::max<size_t>(val_parts(L.mode) * d, 3 * APPLY_COLS), 256);
+    L.wide_cols = L.ncols / 3;
     const size_t per_row = 2 * B * 2 * kcov;  // bytes of one weights row (hi and lo) over the batch
     L.wt_rows = (int)std::min(align_up(mx, 256), std::max<size_t>(256, WIDE_WT_BYTES / per_row / 256 * 256));
   } else {
@@ -220,12 +220,15 @@ Layout layout_of(const sk_problem* p) {
     L.wt_rows = 0;
   }
   const size_t split_rows = std::max(B * mx, std::min(16 * B * mx, (size_t)131072));
+  // wide passes merge per row block: 16 splits of one block's partials
+  const size_t part_rows = std::max(mx, (size_t)L.wt_rows);
   L.bpv_bytes = std::max<size_t>(4 * 16 * 16 * B * mx, 4 * split_rows * (size_t)L.ncols);
-  // value operand: [B][max_pad / 32][ncols][32] (narrow) or [B][ncols rounded to 256][kcov] (wide)
-  L.vt = L.wide ? take(2 * B * align_up((size_t)L.ncols, 256) * kcov) : take(2 * B * (size_t)L.max_pad * L.ncols);
+  if (L.wide) L.bpv_bytes = std::max(L.bpv_bytes, 4 * 16 * B * (size_t)L.wt_rows * L.ncols);
+  // value operand: [B][max_pad / 32][ncols][32] (narrow) or [B][ncols][kcov] (wide)
+  L.vt = L.wide ? take(2 * B * (size_t)L.ncols * kcov) : take(2 * B * (size_t)L.max_pad * L.ncols);
   L.wt = L.wide ? take(2 * B * (size_t)L.wt_rows * 2 * kcov) : 0;
   L.bpv = take(L.bpv_bytes);
-  L.bs = take(4 * 16 * B * mx);
+  L.bs = take(4 * 16 * B * part_rows);
   L.bm = take(4 * 16 * B * mx);  // per-split row offsets of the lazy transport pass
   L.ttotal = off;
   // Hessian-vector products: per-row vectors and small matrices, O((n+m) d)

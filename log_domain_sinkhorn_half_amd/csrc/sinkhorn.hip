@@ -1113,10 +1113,9 @@ __device__ __forceinline__ uint2 split_pair(float a, float b) {
 // is compute bound many times over the buffer's traffic):
 //   EPI_W:    the row block's weights 2^(score - M_i), M_i = lambda (|x_i|^2 - T_i)
 //             from the row's half-step value T_i (so a row's weights sum to 1),
-//             written as bf16 hi/lo parts;
+//             written as bf16 hi/lo parts, and their sums per key split;
 //   EPI_U:    with the direction planes as rows and no bias, u_ij = ugain * acc
-//             = (y_j - c) . v_i; the buffered weights are multiplied by u_ij and
-//             their plain sums per key split written out;
+//             = (y_j - c) . v_i; the buffered weights are multiplied by u_ij;
 //   EPI_GEMM: rows = weight rows (K = hi keys then lo keys), columns = value
 //             columns (K wraps over the keys once), partial products per K split.
 // In the weights buffer the 32 keys of a tile sit in the order in which a lane
@@ -1148,8 +1147,8 @@ struct KlArgs {
   float* out;            // potential (LSE without splits)
   float2* part;          // (max, sum) per split (LSE with splits)
   u16* wt;               // weights buffer (W, U)
-  float* pv;             // partial products [split][batch][rows][nc] (GEMM)
-  float* sp;             // plain weight sums [split][batch][rows] (U)
+  float* pv;             // partial products [split][batch][prows][nc] (GEMM)
+  float* sp;             // weight sums [split][batch][prows] (W)
   unsigned* tag;
   unsigned tag_val;
   unsigned* status;
@@ -1157,6 +1156,7 @@ struct KlArgs {
   int a_ld, a_rows, a_row0, a_nkc;
   int b_ld, b_rows, b_nkc;
   int rows, row0, keys;
+  int prows;             // rows per (split, problem) of pv and sp, counted from row0
   int nkc;               // K chunks per key block (LSE, W, U)
   int per_split;         // key blocks (LSE, W, U) or K chunks (GEMM) per split
   int total_kc;          // K chunks in all (GEMM)
@@ -1332,8 +1332,13 @@ __global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2)))
             u16* wp = wrow(c, kb, t);
             float e[16];
             if (EPI == EPI_W) {
+              float sum = 0.f;
 #pragma unroll
-              for (int o = 0; o < 16; ++o) e[o] = __builtin_amdgcn_exp2f(fmaf(acc[c][t][o], a.sc, -Mrow[c]));
+              for (int o = 0; o < 16; ++o) {
+                e[o] = __builtin_amdgcn_exp2f(fmaf(acc[c][t][o], a.sc, -Mrow[c]));
+                sum += e[o];
+              }
+              s[c] += sum;
             } else {
               const u4 h0 = *reinterpret_cast<const u4*>(wp), h1 = *reinterpret_cast<const u4*>(wp + 8);
               const u4 l0 = *reinterpret_cast<const u4*>(wp + a.kcov), l1 = *reinterpret_cast<const u4*>(wp + a.kcov + 8);
@@ -1344,10 +1349,6 @@ __global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2)))
                 e[2 * h] = __uint_as_float(hw[h] << 16) + __uint_as_float(lw[h] << 16);
                 e[2 * h + 1] = __uint_as_float(hw[h] & 0xffff0000u) + __uint_as_float(lw[h] & 0xffff0000u);
               }
-              float sum = 0.f;
-#pragma unroll
-              for (int o = 0; o < 16; ++o) sum += e[o];
-              s[c] += sum;
 #pragma unroll
               for (int o = 0; o < 16; ++o) e[o] *= acc[c][t][o] * a.ugain;
             }
@@ -1364,9 +1365,9 @@ __global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2)))
         const int split = blockIdx.y / a.ncolt;
 #pragma unroll
         for (int c = 0; c < KL_QT; ++c) {
-          const int q = a.row0 + q0 + wq * (KL_QT * 32) + c * 32 + col;
-          if (q >= a.rows) continue;
-          float* dst = a.pv + ((size_t)split * a.batch * a.rows + (size_t)b * a.rows + q) * a.nc;
+          const int ql = q0 + wq * (KL_QT * 32) + c * 32 + col;
+          if (a.row0 + ql >= a.rows) continue;
+          float* dst = a.pv + (((size_t)split * a.batch + b) * a.prows + ql) * a.nc;
 #pragma unroll
           for (int t = 0; t < KL_KT; ++t)
 #pragma unroll
@@ -1411,8 +1412,8 @@ __global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2)))
         }
       }
     }
-  } else if (EPI == EPI_U) {
-    // plain weight sums of the split: both lanes of a row, then both key halves
+  } else if (EPI == EPI_W) {
+    // weight sums of the split: both lanes of a row, then both key halves
 #pragma unroll
     for (int c = 0; c < KL_QT; ++c) s[c] += __shfl_xor(s[c], 32);
     if (wk == 1 && grp == 0) {
@@ -1424,8 +1425,7 @@ __global__ __launch_bounds__(64 * KL_NW) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int c = 0; c < KL_QT; ++c) {
         const int ql = wq * (KL_QT * 32) + c * 32 + col;
-        const int q = a.row0 + q0 + ql;
-        if (q < a.rows) a.sp[(size_t)blockIdx.y * a.batch * a.rows + (size_t)b * a.rows + q] = s[c] + ldm[ql].y;
+        if (a.row0 + q0 + ql < a.rows) a.sp[((size_t)blockIdx.y * a.batch + b) * a.prows + q0 + ql] = s[c] + ldm[ql].y;
       }
     }
   }
@@ -1469,12 +1469,11 @@ __global__ __launch_bounds__(256) void k_prep_keys_hilo(const void* __restrict__
 // coordinates of the key cloud in `parts` bf16 parts (cc = part d + t; one part
 // holds a bf16 input exactly, two parts hold 16 significant bits of an fp32 one,
 // from fp64); with M, three parts of the fp32 matrix columns col0.. (cc = part cb
-// + k, exact).  Row ones_col (if >= 0) holds ones; other rows and padding keys
-// are zero.  One thread per 8 positions.
+// + k, exact).  Other rows and padding keys are zero.  One thread per 8 positions.
 __global__ __launch_bounds__(256) void k_prep_vt(const void* __restrict__ P, int in_bf16,
                                                  const double* __restrict__ cen, const float* __restrict__ M, int c,
                                                  int col0, int cb, int parts, int keys, int kcov, int d, int ncp,
-                                                 int ones_col, u16* __restrict__ vt) {
+                                                 u16* __restrict__ vt) {
   const int b = blockIdx.y;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int per_row = kcov / 8;
@@ -1485,9 +1484,7 @@ __global__ __launch_bounds__(256) void k_prep_vt(const void* __restrict__ P, int
   for (int e = 0; e < 8; ++e) {
     const int p = p0 + e, j = (p / 32) * 32 + lane_key(p % 32);
     u16 val = 0;
-    if (j < keys && cc == ones_col) {
-      val = BF16_ONE;
-    } else if (j < keys && M != nullptr && cc < 3 * cb) {
+    if (j < keys && M != nullptr && cc < 3 * cb) {
       const float x = M[((size_t)b * keys + j) * c + col0 + cc % cb];
       const u16 h0 = bf16_rne(x);
       const float r1 = x - bf16_f(h0);
@@ -1966,15 +1963,24 @@ __global__ __launch_bounds__(64 * bary_NW(MODE, NCH, NCT, NU))
   }
 }
 
+// Rows of a merge: output rows row0 .. row0 + nrows of each problem (`rows`
+// rows per problem in the outputs); the split partials hold prows rows per
+// (split, problem), starting at row row0.  Weight sums: ks_s splits of sp, or
+// with ks_s = 0 the ones column (the last) of the P.V partials.
+struct MergeRows {
+  int rows, row0, nrows, prows, ks_s;
+};
+
 // Barycentric projection and gradient from the split partials, one thread per
 // (problem, row, coordinate): bary = sum_parts sum_splits pv / sum_splits s + c,
 // grad = 2 r (p - bary) with the row mass r = w exp((pot - lse)/eps).
-// With lazy offsets (mpart != nullptr) each split's partials are relative to its
-// own offset mpart (base 2): they are brought to the largest one, and the row's
-// log-sum-exp follows from it and the weight sum, as in the half-step:
-// lse = ||p||^2 - (M + log2 S) / lambda, written to lse for later passes.
+// With lazy offsets (mpart != nullptr; then ks_s is 0 or ks) each split's
+// partials are relative to its own offset mpart (base 2): they are brought to
+// the largest one, and the row's log-sum-exp follows from it and the weight
+// sum, as in the half-step: lse = ||p||^2 - (M + log2 S) / lambda, written to
+// lse for later passes.
 __global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv, const float* __restrict__ sp, int ks,
-                                                    int batch, int rows, int d, int ncols, int parts, int sumcol,
+                                                    int batch, MergeRows mr, int d, int ncols, int parts,
                                                     const void* __restrict__ P, int in_bf16,
                                                     const float* __restrict__ pot, float* __restrict__ lse,
                                                     const double* __restrict__ logw, double eps,
@@ -1982,26 +1988,34 @@ __global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv
                                                     double inv_lam, const double* __restrict__ cen,
                                                     float* __restrict__ bary, float* __restrict__ grad) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long long)batch * rows * d) return;
+  if (idx >= (long long)batch * mr.nrows * d) return;
   const int t = (int)(idx % d);
-  const long long rr = idx / d;  // b * rows + row
+  const int lr = (int)((idx / d) % mr.nrows), b = (int)(idx / ((long long)mr.nrows * d));
+  const long long rr = (long long)b * mr.rows + mr.row0 + lr;  // b * rows + row
+  const size_t pr = (size_t)b * mr.prows + lr;                 // row of the partials within a split
+  const size_t pstride = (size_t)batch * mr.prows;
   double M = 0.0;
   if (mpart != nullptr) {
     M = -INFINITY;
 #pragma unroll 4
-    for (int k = 0; k < ks; ++k) M = fmax(M, (double)mpart[(size_t)k * batch * rows + (size_t)rr]);
+    for (int k = 0; k < ks; ++k) M = fmax(M, (double)mpart[k * pstride + pr]);
   }
   double S = 0.0, num = 0.0;
 #pragma unroll 4
   for (int k = 0; k < ks; ++k) {
-    const size_t base = (size_t)k * batch * rows + (size_t)rr;
+    const size_t base = k * pstride + pr;
     const double sc = mpart != nullptr ? exp2((double)mpart[base] - M) : 1.0;  // 0 for an empty split
-    S += sc * (sumcol ? (double)pv[base * ncols + ncols - 1] : (double)sp[base]);
+    if (mr.ks_s == 0) S += sc * (double)pv[base * ncols + ncols - 1];
     for (int part = 0; part < parts; ++part) num += sc * (double)pv[base * ncols + part * d + t];
   }
+  for (int k = 0; k < mr.ks_s; ++k) {
+    const size_t base = k * pstride + pr;
+    S += (mpart != nullptr ? exp2((double)mpart[base] - M) : 1.0) * (double)sp[base];
+  }
+  const size_t o = (size_t)rr * d + t;
   // the values were centred: the projection moves back by the centre
-  const double bc = num / S + cen[(size_t)(rr / rows) * d + t];
-  bary[idx] = (float)bc;
+  const double bc = num / S + cen[(size_t)b * d + t];
+  bary[o] = (float)bc;
   double row_lse;
   if (mpart != nullptr) {
     row_lse = qnorm[rr] - (M + log2(S)) * inv_lam;
@@ -2010,9 +2024,9 @@ __global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv
     row_lse = (double)lse[rr];
   }
   if (grad != nullptr) {
-    const double x = coord(P, (size_t)idx, in_bf16);
+    const double x = coord(P, o, in_bf16);
     const double mass = exp(logw[rr] + ((double)pot[rr] - row_lse) / eps);
-    grad[idx] = (float)(2.0 * mass * (x - bc));
+    grad[o] = (float)(2.0 * mass * (x - bc));
   }
 }
 
@@ -2085,21 +2099,25 @@ __global__ __launch_bounds__(256) void k_prep_mat(const float* __restrict__ M, i
 
 // out[b][row][col0+k] = r_row * (weighted sum of column k) / (sum of weights),
 // r_row = w exp((pot - lse)/eps) the row mass.  One thread per (problem, row, k).
-__global__ __launch_bounds__(256) void k_apply_merge(const float* __restrict__ pv, int ks, int batch, int rows, int cb,
-                                                     int ncols, int c, int col0, const double* __restrict__ logw,
-                                                     const float* __restrict__ pot, const float* __restrict__ lse,
-                                                     double eps, float* __restrict__ out) {
+__global__ __launch_bounds__(256) void k_apply_merge(const float* __restrict__ pv, const float* __restrict__ sp, int ks,
+                                                     int batch, MergeRows mr, int cb, int ncols, int c, int col0,
+                                                     const double* __restrict__ logw, const float* __restrict__ pot,
+                                                     const float* __restrict__ lse, double eps,
+                                                     float* __restrict__ out) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long long)batch * rows * cb) return;
+  if (idx >= (long long)batch * mr.nrows * cb) return;
   const int k = (int)(idx % cb);
-  const long long rr = idx / cb;
+  const int lr = (int)((idx / cb) % mr.nrows), b = (int)(idx / ((long long)mr.nrows * cb));
+  const long long rr = (long long)b * mr.rows + mr.row0 + lr;
+  const size_t pr = (size_t)b * mr.prows + lr, pstride = (size_t)batch * mr.prows;
   double S = 0.0, num = 0.0;
 #pragma unroll 4
-  for (int sp = 0; sp < ks; ++sp) {
-    const size_t base = ((size_t)sp * batch * rows + (size_t)rr) * ncols;
-    S += (double)pv[base + ncols - 1];
+  for (int q = 0; q < ks; ++q) {
+    const size_t base = (q * pstride + pr) * ncols;
+    if (mr.ks_s == 0) S += (double)pv[base + ncols - 1];
     for (int part = 0; part < 3; ++part) num += (double)pv[base + part * cb + k];
   }
+  for (int q = 0; q < mr.ks_s; ++q) S += (double)sp[q * pstride + pr];
   const double mass = exp(logw[rr] + ((double)pot[rr] - (double)lse[rr]) / eps);
   out[rr * c + col0 + k] = (float)(mass > 0.0 ? mass * num / S : 0.0);
 }
@@ -2408,23 +2426,25 @@ __global__ __launch_bounds__(256) void k_prep_u(const float* __restrict__ V, int
 // Merge of the row-weighted pass: quad_i = r_i (sum_splits sum_parts pv) /
 // (sum_splits s), r_i the row mass, in fp64.  One thread per (problem, row, coordinate).
 __global__ __launch_bounds__(256) void k_uw_merge(const float* __restrict__ pv, const float* __restrict__ sp, int ks,
-                                                  int batch, int rows, int d, int ncols, int parts,
+                                                  int batch, MergeRows mr, int d, int ncols, int parts,
                                                   const double* __restrict__ logw, const float* __restrict__ pot,
                                                   const float* __restrict__ lse, double eps,
                                                   double* __restrict__ quad) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long long)batch * rows * d) return;
+  if (idx >= (long long)batch * mr.nrows * d) return;
   const int t = (int)(idx % d);
-  const long long rr = idx / d;
+  const int lr = (int)((idx / d) % mr.nrows), b = (int)(idx / ((long long)mr.nrows * d));
+  const long long rr = (long long)b * mr.rows + mr.row0 + lr;
+  const size_t pr = (size_t)b * mr.prows + lr, pstride = (size_t)batch * mr.prows;
   double S = 0.0, num = 0.0;
 #pragma unroll 4
   for (int k = 0; k < ks; ++k) {
-    const size_t base = (size_t)k * batch * rows + (size_t)rr;
-    S += (double)sp[base];
+    const size_t base = k * pstride + pr;
     for (int part = 0; part < parts; ++part) num += (double)pv[base * ncols + part * d + t];
   }
+  for (int k = 0; k < mr.ks_s; ++k) S += (double)sp[k * pstride + pr];
   const double mass = exp(logw[rr] + ((double)pot[rr] - (double)lse[rr]) / eps);
-  quad[idx] = mass > 0.0 ? mass * num / S : 0.0;
+  quad[(size_t)rr * d + t] = mass > 0.0 ? mass * num / S : 0.0;
 }
 
 // Centred coordinates of a cloud as an fp32 matrix (rows points per problem).
@@ -2780,14 +2800,14 @@ BaryFn bary_lookup(int mode, int d) {
 }
 
 // Plan pass for wide operands (see EPI_W): per block of L.wt_rows rows of
-// `side`, the weights at the rows' fixed offsets (their half-step values lse),
-// times u_ij when the direction planes U are given (then the plain weight sums
-// per split go to bs), then their product with the value rows vt (ncp rows;
-// L.ncols columns stored) into the split partials bpv.  *ks_out: the number of
-// splits, the same for every row block.
+// `side`, the weights at the rows' fixed offsets (their half-step values lse)
+// with their plain sums per split (into bs), times u_ij when the direction
+// planes U are given, then their product with the value rows (L.vt, L.ncols
+// columns) into the split partials (L.bpv); then `merge` for the block's rows.
+template <class Merge>
 sk_status wide_pass(const sk_problem* p, const void* X, const void* Y, char* w, const Layout& L, const float* pot_key,
-                    const float* lse, float eps, int side, const u16* vt, int ncp, const u16* U, float ugain,
-                    int* ks_out, hipStream_t stream) {
+                    const float* lse, float eps, int side, const u16* U, float ugain, hipStream_t stream,
+                    const Merge& merge) {
   const int B = (int)p->batch;
   const int rows = (int)(side == 0 ? p->n : p->m);
   const int keys = (int)(side == 0 ? p->m : p->n);
@@ -2798,8 +2818,8 @@ sk_status wide_pass(const sk_problem* p, const void* X, const void* Y, char* w, 
   KeyOperand ko;
   sk_status st = prep_keys(p, X, Y, w, L, pot_key, eps, side, stream, &ko);
   if (st != SK_OK) return st;
-  if (L.KP < 2 * KL_KC || ncp % KL_BK != 0) {
-    set_err("internal: wide plan pass with KP = %d, %d value rows", L.KP, ncp);
+  if (L.KP < 2 * KL_KC || L.ncols % KL_BK != 0) {
+    set_err("internal: wide plan pass with KP = %d, %d value columns", L.KP, L.ncols);
     return SK_EUNSUPPORTED;
   }
   const int nblk = (keys + KL_BK - 1) / KL_BK, kcov = nblk * KL_BK;
@@ -2811,17 +2831,18 @@ sk_status wide_pass(const sk_problem* p, const void* X, const void* Y, char* w, 
   st = resident_capacity(reinterpret_cast<const void*>(&k_lsek<EPI_W>), &cap_w, 64 * KL_NW);
   if (st == SK_OK) st = resident_capacity(reinterpret_cast<const void*>(&k_lsek<EPI_GEMM>), &cap_g, 64 * KL_NW);
   if (st != SK_OK) return st;
-  // splits of the product over its K range (hi keys, then lo keys)
-  const int ncolt = ncp / KL_BK, total_kc = 2 * kcov / KL_KC;
-  const int ks_cap = (int)std::min<size_t>(16, std::max<size_t>(1, L.bpv_bytes / (4 * (size_t)B * rows * L.ncols)));
-  int cps = 0;
-  const int ks = choose_key_splits(wg_full * ncolt * B, total_kc, cap_g, &cps, ks_cap);
-  int bps_w = 0;
-  const int ks_w = choose_key_splits(wg_full * B, nblk, cap_w, &bps_w);
+  // splits of the weights pass over key blocks and of the product over its K
+  // range (hi keys, then lo keys); the partials of one row block hold 16 splits
+  const int ncolt = L.ncols / KL_BK, total_kc = 2 * kcov / KL_KC;
+  int cps = 0, bps_w = 0;
+  const int ks = choose_key_splits(wg_full * ncolt * B, total_kc, cap_g, &cps, 16);
+  const int ks_w = choose_key_splits(wg_full * B, nblk, cap_w, &bps_w, 16);
   u16* wt = reinterpret_cast<u16*>(w + L.wt);
+  float* sp = reinterpret_cast<float*>(w + L.bs);
   unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
   for (int r0 = 0; r0 < rows; r0 += rb) {
-    const int wg = (std::min(rb, rows - r0) + KL_BQ - 1) / KL_BQ;
+    const int nrows = std::min(rb, rows - r0);
+    const int wg = (nrows + KL_BQ - 1) / KL_BQ;
     KlArgs aw = kl_scores(L, Qop, ko, rows_pad, keys_pad, rows, keys, B, lam);
     aw.a_row0 = aw.row0 = r0;
     aw.qnorm = qnorm;
@@ -2830,6 +2851,8 @@ sk_status wide_pass(const sk_problem* p, const void* X, const void* Y, char* w, 
     aw.wt_ld = 2 * kcov;
     aw.kcov = kcov;
     aw.wt_rows = rb;
+    aw.prows = rb;
+    aw.sp = sp;
     aw.per_split = bps_w;
     aw.status = status;
     hipLaunchKernelGGL(k_lsek<EPI_W>, dim3(wg, ks_w, B), dim3(64 * KL_NW), 0, stream, aw);
@@ -2838,24 +2861,24 @@ sk_status wide_pass(const sk_problem* p, const void* X, const void* Y, char* w, 
       au.A = U;
       au.hb = nullptr;
       au.tag = nullptr;
+      au.sp = nullptr;
       au.a_plane = ((long long)B * rows_pad + SLACK) * L.KP;
       au.nkc = planes * (L.KP / KL_KC);
-      au.per_split = (nblk + ks - 1) / ks;
       au.ugain = ugain;
-      au.sp = reinterpret_cast<float*>(w + L.bs);
-      hipLaunchKernelGGL(k_lsek<EPI_U>, dim3(wg, ks, B), dim3(64 * KL_NW), 0, stream, au);
+      hipLaunchKernelGGL(k_lsek<EPI_U>, dim3(wg, ks_w, B), dim3(64 * KL_NW), 0, stream, au);
     }
     KlArgs ag{};
     ag.A = wt;
-    ag.B = vt;
+    ag.B = reinterpret_cast<const u16*>(w + L.vt);
     ag.a_ld = 2 * kcov;
     ag.a_rows = rb;
     ag.a_nkc = total_kc;
     ag.b_ld = kcov;
-    ag.b_rows = ncp;
+    ag.b_rows = L.ncols;
     ag.b_nkc = kcov / KL_KC;
     ag.rows = rows;
     ag.row0 = r0;
+    ag.prows = rb;
     ag.per_split = cps;
     ag.total_kc = total_kc;
     ag.ncolt = ncolt;
@@ -2864,24 +2887,22 @@ sk_status wide_pass(const sk_problem* p, const void* X, const void* Y, char* w, 
     ag.batch = B;
     hipLaunchKernelGGL(k_lsek<EPI_GEMM>, dim3(wg, ncolt * ks, B), dim3(64 * KL_NW), 0, stream, ag);
     st = hip_check("wide plan pass launch");
+    if (st == SK_OK) st = merge(MergeRows{rows, r0, nrows, rb, ks_w}, ks);
     if (st != SK_OK) return st;
   }
-  *ks_out = ks;
   return SK_OK;
 }
 
 // Value rows of a wide pass (k_prep_vt) for the keys of `side`.
 sk_status wide_values(const sk_problem* p, const void* Kraw, char* w, const Layout& L, int side, const float* M,
-                      int c, int col0, int cb, int ones_col, int* ncp_out, hipStream_t stream) {
+                      int c, int col0, int cb, hipStream_t stream) {
   const int B = (int)p->batch, d = (int)p->d;
   const int keys = (int)(side == 0 ? p->m : p->n);
   const int kcov = (keys + KL_BK - 1) / KL_BK * KL_BK;
-  const int ncp = (int)align_up((size_t)L.ncols, KL_BK);
-  const long long nvec = (long long)ncp * (kcov / 8);
+  const long long nvec = (long long)L.ncols * (kcov / 8);
   hipLaunchKernelGGL(k_prep_vt, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, Kraw, L.in_bf16,
                      reinterpret_cast<const double*>(w + L.cen), M, c, col0, cb, val_parts(L.mode), keys, kcov, d,
-                     ncp, ones_col, reinterpret_cast<u16*>(w + L.vt));
-  *ncp_out = ncp;
+                     L.ncols, reinterpret_cast<u16*>(w + L.vt));
   return hip_check("value rows launch");
 }
 
@@ -2907,19 +2928,20 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
     // the rows' half-step values fix their offsets; then the weights pass with
     // the coordinates (and a ones column for the weight sums) as values
     sk_status st = half_step(p, X, Y, ws, L, side == 0 ? g : f, eps, lse, side, stream);
-    int ncp = 0, ks = 0;
-    if (st == SK_OK) st = wide_values(p, Kraw, w, L, side, nullptr, 0, 0, 0, L.ncols - 1, &ncp, stream);
-    if (st == SK_OK)
-      st = wide_pass(p, X, Y, w, L, side == 0 ? g : f, lse, eps, side, reinterpret_cast<const u16*>(w + L.vt), ncp,
-                     nullptr, 1.f, &ks, stream);
+    if (st == SK_OK) st = wide_values(p, Kraw, w, L, side, nullptr, 0, 0, 0, stream);
     if (st != SK_OK) return st;
-    const long long total = (long long)B * rows * d;
     const float lam = (float)(LOG2E / (double)eps);
-    hipLaunchKernelGGL(k_bary_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                       reinterpret_cast<const float*>(w + L.bpv), reinterpret_cast<const float*>(w + L.bs), ks, B,
-                       rows, d, L.ncols, val_parts(L.mode), 1, Praw, L.in_bf16, pot_row, lse, qlogw, (double)eps,
-                       nullptr, qnorm, 1.0 / (double)lam, reinterpret_cast<const double*>(w + L.cen), bary, grad);
-    return hip_check("transport merge launch");
+    return wide_pass(p, X, Y, w, L, side == 0 ? g : f, lse, eps, side, nullptr, 1.f, stream,
+                     [&](const MergeRows& mr, int ks) {
+                       const long long total = (long long)B * mr.nrows * d;
+                       hipLaunchKernelGGL(k_bary_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                                          reinterpret_cast<const float*>(w + L.bpv),
+                                          reinterpret_cast<const float*>(w + L.bs), ks, B, mr, d, L.ncols,
+                                          val_parts(L.mode), Praw, L.in_bf16, pot_row, lse, qlogw, (double)eps,
+                                          nullptr, qnorm, 1.0 / (double)lam,
+                                          reinterpret_cast<const double*>(w + L.cen), bary, grad);
+                       return hip_check("transport merge launch");
+                     });
   }
 
   // 1. The key operand of this side for the other potential and eps.  The P.V
@@ -2971,8 +2993,9 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
 
   // 4. Merge the splits, divide, form the gradient.
   const long long total = (long long)B * rows * d;
-  hipLaunchKernelGGL(k_bary_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, bs, ks, B, rows,
-                     d, nc, val_parts(L.mode), sumcol, Praw, L.in_bf16, pot_row, lse, qlogw, (double)eps, bm, qnorm,
+  const MergeRows mr{rows, 0, rows, rows, sumcol ? 0 : ks};
+  hipLaunchKernelGGL(k_bary_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, bs, ks, B, mr,
+                     d, nc, val_parts(L.mode), Praw, L.in_bf16, pot_row, lse, qlogw, (double)eps, bm, qnorm,
                      1.0 / (double)lam, cen, bary, L.cosine ? nullptr : grad);
   st = hip_check("transport merge launch");
   if (st != SK_OK || !L.cosine || grad == nullptr) return st;
@@ -3024,17 +3047,17 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
   if (L.wide) {
     for (int col0 = 0; col0 < c; col0 += L.wide_cols) {
       const int cb = std::min(L.wide_cols, c - col0);
-      int ncp = 0, ks = 0;
-      sk_status st = wide_values(p, side == 0 ? Y : X, w, L, side, M, c, col0, cb, L.ncols - 1, &ncp, stream);
+      sk_status st = wide_values(p, side == 0 ? Y : X, w, L, side, M, c, col0, cb, stream);
       if (st == SK_OK)
-        st = wide_pass(p, X, Y, w, L, pot_key, lse, eps, side, reinterpret_cast<const u16*>(w + L.vt), ncp, nullptr,
-                       1.f, &ks, stream);
-      if (st != SK_OK) return st;
-      const long long total = (long long)B * rows * cb;
-      hipLaunchKernelGGL(k_apply_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                         reinterpret_cast<const float*>(w + L.bpv), ks, B, rows, cb, L.ncols, c, col0, qlogw, pot_row,
-                         lse, (double)eps, out);
-      st = hip_check("plan-application merge launch");
+        st = wide_pass(p, X, Y, w, L, pot_key, lse, eps, side, nullptr, 1.f, stream,
+                       [&](const MergeRows& mr, int ks) {
+                         const long long total = (long long)B * mr.nrows * cb;
+                         hipLaunchKernelGGL(k_apply_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                                            stream, reinterpret_cast<const float*>(w + L.bpv),
+                                            reinterpret_cast<const float*>(w + L.bs), ks, B, mr, cb, L.ncols, c, col0,
+                                            qlogw, pot_row, lse, (double)eps, out);
+                         return hip_check("plan-application merge launch");
+                       });
       if (st != SK_OK) return st;
     }
     return SK_OK;
@@ -3077,8 +3100,9 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
     st = hip_check("plan-application kernel launch");
     if (st != SK_OK) return st;
     const long long total = (long long)B * rows * cb;
-    hipLaunchKernelGGL(k_apply_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, ks, B, rows,
-                       cb, nc, c, col0, qlogw, pot_row, lse, (double)eps, out);
+    const MergeRows mr{rows, 0, rows, rows, 0};
+    hipLaunchKernelGGL(k_apply_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, nullptr, ks,
+                       B, mr, cb, nc, c, col0, qlogw, pot_row, lse, (double)eps, out);
     st = hip_check("plan-application merge launch");
     if (st != SK_OK) return st;
   }
@@ -3123,19 +3147,17 @@ sk_status apply_uw(const sk_problem* p, const void* X, const void* Y, char* w, c
   if (L.wide) {
     hipLaunchKernelGGL(k_prep_u, dim3((rows_pad + 255) / 256, B), dim3(256), 0, stream, Vdir, rows, rows_pad, d,
                        L.KP, L.mode, B, U);
-    int ncp = 0, ks = 0;
-    sk_status st = wide_values(p, Kraw, w, L, side, nullptr, 0, 0, 0, -1, &ncp, stream);
+    sk_status st = wide_values(p, Kraw, w, L, side, nullptr, 0, 0, 0, stream);
+    if (st != SK_OK) return st;
     // the hi/lo key rows hold 2 lambda (y - c)
     const float ugain = L.mode == MODE_HILO ? (float)((double)eps / (2.0 * LOG2E)) : 1.f;
-    if (st == SK_OK)
-      st = wide_pass(p, X, Y, w, L, pot_key, lse, eps, side, reinterpret_cast<const u16*>(w + L.vt), ncp, U, ugain,
-                     &ks, stream);
-    if (st != SK_OK) return st;
-    const long long total = (long long)B * rows * d;
-    hipLaunchKernelGGL(k_uw_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                       reinterpret_cast<const float*>(w + L.bpv), reinterpret_cast<const float*>(w + L.bs), ks, B,
-                       rows, d, L.ncols, val_parts(L.mode), qlogw, pot_row, lse, (double)eps, quad);
-    return hip_check("row-weighted merge launch");
+    return wide_pass(p, X, Y, w, L, pot_key, lse, eps, side, U, ugain, stream, [&](const MergeRows& mr, int ks) {
+      const long long total = (long long)B * mr.nrows * d;
+      hipLaunchKernelGGL(k_uw_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                         reinterpret_cast<const float*>(w + L.bpv), reinterpret_cast<const float*>(w + L.bs), ks, B,
+                         mr, d, L.ncols, val_parts(L.mode), qlogw, pot_row, lse, (double)eps, quad);
+      return hip_check("row-weighted merge launch");
+    });
   }
   KeyOperand ko;
   sk_status st = prep_keys(p, X, Y, w, L, pot_key, eps, side, stream, &ko);
@@ -3177,7 +3199,8 @@ sk_status apply_uw(const sk_problem* p, const void* X, const void* Y, char* w, c
   st = hip_check("row-weighted plan kernel launch");
   if (st != SK_OK) return st;
   const long long total = (long long)B * rows * d;
-  hipLaunchKernelGGL(k_uw_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, bs, ks, B, rows, d,
+  const MergeRows mr{rows, 0, rows, rows, ks};
+  hipLaunchKernelGGL(k_uw_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, bs, ks, B, mr, d,
                      nc, val_parts(L.mode), qlogw, pot_row, lse, (double)eps, quad);
   return hip_check("row-weighted merge launch");
 }
