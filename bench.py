@@ -282,6 +282,20 @@ def gpu_clock_mhz():
         return {"unavailable": type(e).__name__}
 
 
+def warm_for(call, seconds):
+    """Repeat `call` (GPU work) until `seconds` of wall time have passed."""
+    import time
+
+    import torch
+
+    t0 = time.perf_counter()
+    while True:
+        call()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
 def transport_leg(sk, X, Y, a, b, f, g, eps, p, contraction, reps=10):
     """Time the transport application (barycentric projection + gradient) of each
     side at the final potentials.  One call = key preparation plus one streaming
@@ -295,6 +309,9 @@ def transport_leg(sk, X, Y, a, b, f, g, eps, p, contraction, reps=10):
     bx, gx = sk.barycentric_x(X, Y, ws, f, g, eps)
     by, gy = sk.barycentric_y(X, Y, ws, f, g, eps)
     torch.cuda.synchronize()
+    # the GPU idles while the CPU leg runs: bring it back to its clock first
+    warm_for(lambda: (sk.barycentric_x(X, Y, ws, f, g, eps, bary=bx, grad=gx),
+                      sk.barycentric_y(X, Y, ws, f, g, eps, bary=by, grad=gy)), 0.3)
     stream = torch.cuda.current_stream()
     ms = {}
     for side, call, outs in (("x", sk.barycentric_x, (bx, gx)), ("y", sk.barycentric_y, (by, gy))):
@@ -337,6 +354,7 @@ def hvp_leg(sk, X, Y, a, b, f, g, eps, p, cg_iters, contraction, reps=3):
     V = torch.randn((p.batch, p.n, p.d), device="cuda", generator=gen)
     out = sk.hvp_x(X, Y, ws, f, g, eps, V, cg_iters=cg_iters, cg_tol=0.0)
     torch.cuda.synchronize()
+    warm_for(lambda: sk.hvp_x(X, Y, ws, f, g, eps, V, cg_iters=cg_iters, cg_tol=0.0, out=out), 0.3)
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     ev[0].record(stream)
