@@ -641,6 +641,8 @@ __global__ __launch_bounds__(256) void k_prep_bias(const float* __restrict__ pot
 typedef float f16v __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u4 v) { return __builtin_bit_cast(bf16x8, v); }
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // MFMA tile shapes.  A = key operand (rows = keys), B = query operand (columns =
 // queries), D[key][query].  Every lane holds 8 consecutive K slots of one key
@@ -1598,6 +1600,14 @@ __host__ __device__ constexpr int bary_TCB(int nch, int nct) {
 }
 
 
+// Power-of-two scale that brings a cloud's centred coordinates, at most `amax`
+// in magnitude, below 2^14: bf16 values times it are exact fp16 values (down to
+// 2^-27 amax, below which they round, far under the transport's error bound).
+__host__ __device__ inline float fp16_value_scale(float amax) {
+  return amax > 0.f && amax < 3.0e38f ? ldexpf(1.f, 13 - ilogbf(amax)) : 1.f;
+}
+constexpr u16 F16_ONE = 0x3C00;
+
 // Key order inside a 32-key value block: lane group g of the P.V MFMA takes the
 // weights of keys 4g..4g+3 and 16+4g..16+4g+3 as its A operand, so those eight
 // keys sit together at positions 8g..8g+7 and the lane reads its B operand as
@@ -1609,10 +1619,12 @@ __host__ __device__ constexpr int vkey(int k0, int e) { return (k0 / 8) * 4 + (e
 // tile, col = part*d + t (the LDS image of the block, keys in vkey order), and ones in the last
 // column when it is spare (sumcol).  Padding keys and other columns are zero.
 // One thread per 8 keys of one column.
+// half_max != nullptr (bf16 inputs, transport pass): fp16 values scaled by
+// fp16_value_scale(half_max[b]) and an fp16 ones column.
 __global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, int mode, int in_bf16,
                                                    const double* __restrict__ rnorm, const double* __restrict__ cen,
                                                    int keys, int keys_pad, int d, int ncols, int sumcol,
-                                                   u16* __restrict__ vt) {
+                                                   const float* __restrict__ half_max, u16* __restrict__ vt) {
   const int b = blockIdx.y;
   const long long per_blk = (long long)ncols * (VK / 8);
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1621,17 +1633,22 @@ __global__ __launch_bounds__(256) void k_prep_vals(const void* __restrict__ P, i
   const int rem = (int)(idx % per_blk);
   const int c = rem / (VK / 8), k0 = (rem % (VK / 8)) * 8;
   const int part = c / d, t = c % d;
+  const float hs = half_max != nullptr ? fp16_value_scale(half_max[b]) : 1.f;
   u16 v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int j = blk * VK + vkey(k0, e);
     u16 val = 0;
     if (j < keys && sumcol && c == ncols - 1) {
-      val = BF16_ONE;
+      val = half_max != nullptr ? F16_ONE : BF16_ONE;
     } else if (j < keys && part < val_parts(mode)) {
       const size_t r = ((size_t)b * keys + j) * d + t;
       const double c = cen[(size_t)b * d + t];
-      if (mode == MODE_BF16) {
+      if (mode == MODE_BF16 && half_max != nullptr) {
+        // x - c is a bf16 value (see k_bf16_exact); times a power of two it is an fp16 one
+        const float x = (float)((double)bf16_f(static_cast<const u16*>(P)[r]) - c) * hs;
+        val = __builtin_bit_cast(u16, (_Float16)x);
+      } else if (mode == MODE_BF16) {
         val = bf16_rne((float)((double)bf16_f(static_cast<const u16*>(P)[r]) - c));  // exact (see k_bf16_exact)
       } else {
         // x = h0 + h1 + h2 exactly: each remainder is exact in fp32
@@ -1680,6 +1697,10 @@ __global__ __launch_bounds__(64 * bary_NW(MODE, NCH, NCT, NU))
   constexpr int NVV = TCB * NC * (VK / 8);  // 16-byte vectors per chunk of value blocks
   constexpr int NLV = (NVV + NT - 1) / NT;
   constexpr int QPW = R * MW;
+  // bf16 inputs, transport pass: fp16 weights (one P.V product instead of the
+  // hi and lo bf16 parts) against fp16 values; the lazy offsets then keep every
+  // weight below 2^15 and above 2^-24 of the largest (see the raise below)
+  constexpr bool HALF = MODE == MODE_BF16 && LAZY && NU == 0;
   __shared__ __attribute__((aligned(16))) u16 lds[2][(CK + 1) * LROW];
   __shared__ __attribute__((aligned(16))) u16 ldv[2][(TCB * NC + 1) * VROW];
   __shared__ __attribute__((aligned(16))) float ldsb[2][CK];
@@ -1870,7 +1891,7 @@ __global__ __launch_bounds__(64 * bary_NW(MODE, NCH, NCT, NU))
 #pragma unroll
           for (int o = 0; o < 8; ++o) wm = max(wm, __float_as_uint(e[c][o]));
         }
-        if (__any(first || wm > __float_as_uint(0x1p32f))) {
+        if (__any(first || wm > __float_as_uint(HALF ? 0x1p15f : 0x1p32f))) {
           float mx[R];
 #pragma unroll
           for (int c = 0; c < R; ++c) {
@@ -1886,7 +1907,15 @@ __global__ __launch_bounds__(64 * bary_NW(MODE, NCH, NCT, NU))
             const float top = (MODE == MODE_BF16) ? v * lam2 : (mo[c] == -INFINITY ? v : mo[c] + v);
             float mn = mo[c];
             bool coarse = false;
-            if (mo[c] == -INFINITY || !(top - mo[c] <= 32.f)) mn = fmaxf(mo[c], offset_from_max(top + HEADROOM, qg, coarse));
+            if (HALF) {
+              // fp16 weights: an integer offset that puts the block maximum in
+              // (2^13, 2^14] (the bf16 offset enters only through the exponent,
+              // so it needs no bf16 parts)
+              if (mo[c] == -INFINITY || !(top - mo[c] <= 15.f)) mn = fmaxf(mo[c], ceilf(top - 14.f));
+              coarse = !(fabsf(top) < 0x1p22f);
+            } else if (mo[c] == -INFINITY || !(top - mo[c] <= 32.f)) {
+              mn = fmaxf(mo[c], offset_from_max(top + HEADROOM, qg, coarse));
+            }
             flag_if(status, coarse, FLAG_SCORE_RANGE);
             if (!SUMCOL) s[c] = rescale(s[c], mo[c], mn);
             // P.V rows are queries 4grp+r; their offsets live in lanes col = 4grp+r
@@ -1906,6 +1935,31 @@ __global__ __launch_bounds__(64 * bary_NW(MODE, NCH, NCT, NU))
           }
           weights();
         }
+      }
+      if constexpr (HALF) {
+        // fp16 weights (round to nearest) as the A operand; their sums come from
+        // the same rounded values (one dot product with (1, 1) per pair)
+        u4 eh[R];
+#pragma unroll
+        for (int c = 0; c < R; ++c) {
+          uint32_t w[4];
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const f16x2 pr = {(_Float16)e[c][2 * h], (_Float16)e[c][2 * h + 1]};
+            w[h] = __builtin_bit_cast(uint32_t, pr);
+            if (!SUMCOL) s[c] = __builtin_amdgcn_fdot2(pr, f16x2{(_Float16)1.f, (_Float16)1.f}, s[c], false);
+          }
+          eh[c] = u4{w[0], w[1], w[2], w[3]};
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const u4 vv = *reinterpret_cast<const u4*>(&ldv[buf][(vb * NC + ct * 16 + col) * VROW + 8 * grp]);
+#pragma unroll
+          for (int c = 0; c < R; ++c)
+            pv[c][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, eh[c]),
+                                                              __builtin_bit_cast(f16x8, vv), pv[c][ct], 0, 0, 0);
+        }
+        continue;
       }
       // A operand of the P.V step: lane (query col, group grp) holds the
       // weights of keys 4grp..4grp+3 of tile 0 and of tile 1, in that order.
@@ -1992,7 +2046,8 @@ __global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv
                                                     const double* __restrict__ logw, double eps,
                                                     const float* __restrict__ mpart, const double* __restrict__ qnorm,
                                                     double inv_lam, const double* __restrict__ cen,
-                                                    float* __restrict__ bary, float* __restrict__ grad) {
+                                                    const float* __restrict__ half_max, float* __restrict__ bary,
+                                                    float* __restrict__ grad) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)batch * mr.nrows * d) return;
   const int t = (int)(idx % d);
@@ -2019,6 +2074,8 @@ __global__ __launch_bounds__(256) void k_bary_merge(const float* __restrict__ pv
     S += (mpart != nullptr ? exp2((double)mpart[base] - M) : 1.0) * (double)sp[base];
   }
   const size_t o = (size_t)rr * d + t;
+  // fp16 values carry a power-of-two scale (half_max: the key cloud's extent)
+  if (half_max != nullptr) num /= (double)fp16_value_scale(half_max[b]);
   // the values were centred: the projection moves back by the centre
   const double bc = num / S + cen[(size_t)b * d + t];
   bary[o] = (float)bc;
@@ -2945,7 +3002,7 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
                                           reinterpret_cast<const float*>(w + L.bs), ks, B, mr, d, L.ncols,
                                           val_parts(L.mode), Praw, L.in_bf16, pot_row, lse, qlogw, (double)eps,
                                           nullptr, qnorm, 1.0 / (double)lam,
-                                          reinterpret_cast<const double*>(w + L.cen), bary, grad);
+                                          reinterpret_cast<const double*>(w + L.cen), nullptr, bary, grad);
                        return hip_check("transport merge launch");
                      });
   }
@@ -2965,8 +3022,11 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   const double* krn = reinterpret_cast<const double*>(w + (side == 0 ? L.ry : L.rx));
   const double* cen = reinterpret_cast<const double*>(w + L.cen);
   unsigned* status = reinterpret_cast<unsigned*>(w + L.status);
+  // bf16 inputs: fp16 values and weights (the P.V pass's HALF path), scaled by the key cloud's extent
+  const float* half_max =
+      L.mode == MODE_BF16 ? reinterpret_cast<const float*>(w + L.maxabs) + (side == 0 ? B : 0) : nullptr;
   hipLaunchKernelGGL(k_prep_vals, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, Kraw, L.mode,
-                     L.in_bf16, krn, cen, keys, keys_pad, d, nc, sumcol, vt);
+                     L.in_bf16, krn, cen, keys, keys_pad, d, nc, sumcol, half_max, vt);
   st = hip_check("value preparation launch");
   if (st != SK_OK) return st;
 
@@ -3002,7 +3062,7 @@ sk_status transport(const sk_problem* p, const void* X, const void* Y, void* ws,
   const MergeRows mr{rows, 0, rows, rows, sumcol ? 0 : ks};
   hipLaunchKernelGGL(k_bary_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bpv, bs, ks, B, mr,
                      d, nc, val_parts(L.mode), Praw, L.in_bf16, pot_row, lse, qlogw, (double)eps, bm, qnorm,
-                     1.0 / (double)lam, cen, bary, L.cosine ? nullptr : grad);
+                     1.0 / (double)lam, cen, half_max, bary, L.cosine ? nullptr : grad);
   st = hip_check("transport merge launch");
   if (st != SK_OK || !L.cosine || grad == nullptr) return st;
   const double* qrn = reinterpret_cast<const double*>(w + (side == 0 ? L.rx : L.ry));
@@ -3175,7 +3235,7 @@ sk_status apply_uw(const sk_problem* p, const void* X, const void* Y, char* w, c
   const long long nvec = (long long)(keys_pad / VK) * nc * (VK / 8);
   const double* krn = reinterpret_cast<const double*>(w + (side == 0 ? L.ry : L.rx));
   hipLaunchKernelGGL(k_prep_vals, dim3((unsigned)((nvec + 255) / 256), B), dim3(256), 0, stream, Kraw, L.mode,
-                     L.in_bf16, krn, reinterpret_cast<const double*>(w + L.cen), keys, keys_pad, d, nc, 0, vt);
+                     L.in_bf16, krn, reinterpret_cast<const double*>(w + L.cen), keys, keys_pad, d, nc, 0, nullptr, vt);
   st = hip_check("direction and value preparation launch");
   if (st != SK_OK) return st;
   BaryFn fn = uw_lookup(L.mode, d);

@@ -9,9 +9,13 @@ Acceptance bounds, derived from the arithmetic of the two passes:
         of fp32 roundings, d/8 + 2 (measured at eps = 0.01: 4.7e-4 at d = 200 and
         5.8e-4 at d = 256 against bounds of 7.5e-4 and 9.4e-4).  The weights carry the
         score rounding of the half-step kernel (about 1e-6 relative for fp32 operands, 2.5e-5 for bf16
-        operands at lambda = log2(e)/0.01) and a 2^-17 two-part bf16 split; a
-        convex combination moves by at most that relative error times the spread
-        of V.
+        operands at lambda = log2(e)/0.01) and a 2^-17 two-part bf16 split (fp32
+        inputs); a convex combination moves by at most that relative error times the
+        spread of V.  bf16 inputs take fp16 weights (rounded to nearest, 2^-11
+        relative, the sums formed from the same rounded values) against exact fp16
+        values: each normalised weight moves by at most 2^-10 relative, so the average
+        moves by at most 2^-10 times its weighted deviation, which is at most half
+        the range of V's coordinate (Popoviciu); that term is added.
   grad: 2 r_i (tol_bary + |x_i - bary_i| * tol_T / eps), where r_i is the row mass
         and tol_T the half-step bound (1e-3 eps + 1e-5 max|T| for fp32, 2e-2 eps for
         bf16): the mass comes from the row log-sum-exp of the half-step.
@@ -55,6 +59,9 @@ def bounds(p, eps, V, P, bary_ref, mass_ref, T_ref):
         # 8 exact bf16 products, the bias, the base-2 scaling); 5e-4 holds up to d = 128
         rel *= (d / 8 + 2) / (128 / 8 + 2)
     tb = rel * float(np.max(np.abs(V)))
+    if p.dtype == "bf16":
+        # fp16 weights of the transport pass: 2^-10 of half the coordinate's range
+        tb = tb + 2.0 ** -10 * 0.5 * (np.max(V, axis=0) - np.min(V, axis=0))[None, :]
     tT = 2e-2 * eps if p.dtype == "bf16" else 1e-3 * eps + 1e-5 * float(np.max(np.abs(T_ref)))
     dm = np.expm1(tT / eps)  # largest relative error of the row mass
     tg = 2.0 * mass_ref[:, None] * (tb * (1.0 + dm) + np.abs(P - bary_ref) * dm)
@@ -75,8 +82,11 @@ def compare(p, k, side, eps, bary, grad, f, g, rows=None):
     got_b = bary[k] if rows is None else bary[k][rows]
     tb, tg = bounds(p, eps, V, Psel, bary_ref, mass_ref, T_ref)
     assert np.all(np.isfinite(got_b)), f"{side} bary non-finite"
-    err_b = np.max(np.abs(got_b - bary_ref))
-    assert err_b <= tb, f"bary_{side} problem {k}: max err {err_b:.3e} > {tb:.3e}"
+    err = np.abs(got_b - bary_ref)
+    err_b = float(np.max(err))
+    worst = float(np.max(err / np.broadcast_to(tb, err.shape)))
+    print(f"bary_{side} {p.dtype} d={p.d} eps={eps}: max err {err_b:.2e}, worst err/bound {worst:.3f}")
+    assert worst <= 1.0, f"bary_{side} problem {k}: max err {err_b:.3e}, worst err/bound {worst:.3f}"
     if grad is not None:
         got_g = grad[k] if rows is None else grad[k][rows]
         assert np.all(np.isfinite(got_g)), f"{side} grad non-finite"
