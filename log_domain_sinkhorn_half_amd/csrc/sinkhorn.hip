@@ -822,6 +822,15 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
   constexpr int NW = cfg_NW(MODE, NCH), NT = 64 * NW;  // waves, threads per workgroup
   constexpr int NLD = (NVEC + NT - 1) / NT;
   constexpr int QPW = R * MW;      // queries per wave
+  // fp32 split layout with 9..11 K chunks (32x32 tiles, one query tile per
+  // wave, MFMA-bound): exact per-tile maxima move the offsets without ever
+  // recomputing a chunk (see `step`).  Measured at d = 32, n = m = 16384: 16%
+  // faster for unit-variance clouds (whose score spread makes the lazy offsets
+  // redo chunks), 3% slower for clouds scaled by 1/sqrt(d); the batch of 64
+  // problems of 2048 points +23%.  For 2..8 chunks (16x16 tiles, up to four
+  // query tiles) the per-tile maxima cost 10-50%, and 12..19 chunks have no
+  // registers to spare.
+  constexpr bool EXACT = MODE == MODE_SPLIT && NCH >= 9 && NCH <= 11;
   // the last workgroup's query rows may run past the padded rows into the slack rows
   static_assert(NW * QPW - gcd_c(NW * QPW, ROW_PAD) <= SLACK, "query over-read beyond the slack rows");
   static_assert(CK % 4 == 0 && CK / 4 <= NT, "one 4-key bias vector per thread");
@@ -858,8 +867,12 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
   float m[R], s[R];
 #pragma unroll
   for (int c = 0; c < R; ++c) {
-    m[c] = -FLT_MAX;
+    m[c] = EXACT ? 0.f : -FLT_MAX;  // EXACT: the offset slots start at zero
     s[c] = 0.f;
+  }
+  if (EXACT) {
+#pragma unroll
+    for (int c = 0; c < R; ++c) set_offset(bq[c][0], 0.f, grp == 0);
   }
 
   u4 pre[2][NLD];
@@ -957,6 +970,60 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
     // the wait before its LDS store exact).  Keeping two chunks in flight was
     // measured 5-10% slower on the MFMA-heavy shapes and 2% on d <= 3.
     gload(min(ci + 1, c1 - 1), Par<P ^ 1>{});
+
+    if constexpr (EXACT) {
+      // Each tile's scores come out of the MFMA relative to the current offsets.
+      // The first tile of the range sets them (its maximum + HEADROOM); later, a
+      // query whose tile maximum passes its offset by more than HEADROOM gets a
+      // new offset at once: its sum is rescaled by an exact power of two, this
+      // tile's exponents subtract the shift (an exact integer subtraction), and
+      // the query operand carries the new offset into the following tiles.
+      // Weights stay below 2^64 of the offset, so the sums cannot overflow and
+      // no chunk is ever redone (one extra VALU maximum per score, which these
+      // MFMA-bound shapes absorb).  The first tile, and a jump of more than
+      // 1024, score the tile again at the new offsets instead, so the exponent
+      // keeps the rounding of a small magnitude.
+      bool coarse = false;
+#pragma unroll 1
+      for (int t = 0; t < TC; ++t) {
+        Acc acc[R];
+        tile(buf, t, acc);
+        const bool first = ci == c0 && t == 0;
+        float dl[R];
+        bool raise = false, again = first;
+#pragma unroll
+        for (int c = 0; c < R; ++c) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int o = 0; o < NO; ++o) mx = fmaxf(mx, acc[c][o]);
+          mx = lanes_max(mx);
+          dl[c] = 0.f;
+          if (first || mx > HEADROOM) {
+            const float mn = first ? offset_from_max(mx + HEADROOM, qg, coarse)
+                                   : fmaxf(m[c], offset_from_max(m[c] + mx + HEADROOM, qg, coarse));
+            dl[c] = mn - m[c];
+            s[c] = first ? 0.f : rescale(s[c], m[c], mn);
+            m[c] = mn;
+            set_offset(bq[c][0], -mn, grp == 0);
+            raise = true;
+            again |= !(mx <= 1024.f);
+          }
+        }
+        if (__any(again)) {
+          tile(buf, t, acc);
+        } else if (__any(raise)) {
+#pragma unroll
+          for (int c = 0; c < R; ++c)
+#pragma unroll
+            for (int o = 0; o < NO; ++o) acc[c][o] -= dl[c];
+        }
+        accumulate(acc);
+      }
+      flag_if(status, coarse && lane == 0, FLAG_SCORE_RANGE);
+      if (ci + 1 < c1) lstore(Par<P ^ 1>{});
+      __syncthreads();
+      return;
+    }
 
     float ssave[R];
 #pragma unroll
@@ -1591,12 +1658,13 @@ __host__ __device__ constexpr int bary_waves(int mode, int nch, int nct, int nu)
   return nch >= 12 ? (bary_wide8(mode, nch, nct, nu) ? 2 : 1) : 2;
 }
 // 32-key value blocks per LDS chunk of the transport kernel (fewer barriers for
-// small operands; two blocks for 3..10 K chunks with at most 8 value tiles, where
-// the registers, not LDS, already hold one workgroup per CU: measured -4.7% per
+// small operands; two blocks for 3..10 K chunks with 6..8 value tiles, where the
+// registers, not LDS, already hold one workgroup per CU: measured -4.7% per
 // transport call at d = 128 bf16, -1.3% for 64 problems at d = 32; four blocks
-// were slower)
+// were slower, and for the one-tile plan products of the HVP's conjugate
+// gradients two blocks halve the workgroups per CU: +33% per HVP)
 __host__ __device__ constexpr int bary_TCB(int nch, int nct) {
-  return (nch <= 2 && nct <= 4) ? 4 : ((nch >= 3 && nch <= 10 && nct <= 8) ? 2 : 1);
+  return (nch <= 2 && nct <= 4) ? 4 : ((nch >= 3 && nch <= 10 && nct >= 6 && nct <= 8) ? 2 : 1);
 }
 
 
