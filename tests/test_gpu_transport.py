@@ -153,6 +153,28 @@ def test_transport_batched_and_without_grad():
         compare(p, k, "y", eps, by, gy, f, g)
 
 
+@pytest.mark.parametrize("shift", [0.0, 40.0])
+def test_transport_bf16_batched_translated_zero_weights(shift):
+    """bf16 inputs (fp16 weights and values in the transport pass): three problems of
+    different spread, moved by `shift` in every coordinate (the library centres the
+    clouds and scales their coordinates into fp16 per problem), with zero weights."""
+    from log_domain_sinkhorn_half_amd.inputs import translate
+
+    p = make_case(150, 170, 48, batch=3, seed=61, weights="softmax", dtype="bf16", scale=1.0 / np.sqrt(48))
+    p.X[1] *= 4.0  # a wider problem next to narrow ones (rounded to bf16 again by translate)
+    p.Y[1] *= 4.0
+    p = translate(p, shift)
+    p.a[0, 3] = 0.0
+    p.b[2, 7] = 0.0
+    for eps in (0.5, 0.02):
+        f, g = oracle_potentials(p, eps)
+        bx, gx, by, gy = run_gpu(p, f, g, eps)
+        for k in range(p.batch):
+            compare(p, k, "x", eps, bx, gx, f, g)
+            compare(p, k, "y", eps, by, gy, f, g)
+        assert np.all(gx[0, 3] == 0.0)  # a point of zero weight carries no mass
+
+
 def test_transport_zero_weight_and_translation_balance():
     p = make_case(120, 150, 3, seed=21, weights="softmax")
     p.a[0, 5] = 0.0
