@@ -801,14 +801,26 @@ __device__ __forceinline__ void write_next_bias(const NextBias& nb, int b, int q
   }
 }
 
-// TCX overrides the key tiles per chunk (0: cfg_TC), for small problems.
-template <int MODE, int NCH, int TCX = 0>
+// The plan applied to one vector, sum_j P_ij w_j (the page's part "3. Hessiano
+// in Streaming": each conjugate-gradient step of the Hessian solve is such a
+// product), through the half-step kernel: the offsets are fixed by the rows'
+// half-step values T_i (M_i = lambda (|x_i|^2 - T_i), so the weights 2^(s - M_i)
+// sum to about 1) and the kernel sums w_j 2^(s - M_i) beside 2^(s - M_i), one
+// fp32 FMA per score; the split partials (W, S) go to k_wv_merge.
+struct WvArgs {
+  const float* w;    // the vector, [batch][keys] fp32
+  const float* lse;  // the rows' half-step values T_i, [batch][rows]
+};
+
+// TCX overrides the key tiles per chunk (0: cfg_TC), for small problems.  WV:
+// the one-vector plan product above instead of the half-step.
+template <int MODE, int NCH, int TCX = 0, bool WV = false>
 __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves_per_eu(cfg_waves(MODE, NCH)))) void k_lse(
     const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb,
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, float* __restrict__ out,
     float2* __restrict__ part, int rows, int rows_pad, int keys, int keys_pad, int chunks_per_split, int batch,
     float lam2, double inv_lam, unsigned* __restrict__ tag, unsigned tag_val, unsigned* __restrict__ status,
-    NextBias nb) {
+    NextBias nb, WvArgs wv) {
   constexpr int MW = cfg_MW(MODE, NCH), R = cfg_R(MODE, NCH), TC = TCX ? TCX : cfg_TC(MODE, NCH);
   using T = Tile<MW>;
   using Acc = typename T::Acc;
@@ -830,7 +842,8 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
   // problems of 2048 points +23%.  For 2..8 chunks (16x16 tiles, up to four
   // query tiles) the per-tile maxima cost 10-50%, and 12..19 chunks have no
   // registers to spare.
-  constexpr bool EXACT = MODE == MODE_SPLIT && NCH >= 9 && NCH <= 11;
+  constexpr bool EXACT = !WV && MODE == MODE_SPLIT && NCH >= 9 && NCH <= 11;
+  static_assert(!WV || CK <= NT, "one vector element per thread and chunk");
   // the last workgroup's query rows may run past the padded rows into the slack rows
   static_assert(NW * QPW - gcd_c(NW * QPW, ROW_PAD) <= SLACK, "query over-read beyond the slack rows");
   static_assert(CK % 4 == 0 && CK / 4 <= NT, "one 4-key bias vector per thread");
@@ -839,6 +852,7 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
   // One spare row per buffer takes the stores of threads past the end of a chunk.
   __shared__ __attribute__((aligned(16))) u16 lds[2][(CK + 1) * LROW];
   __shared__ __attribute__((aligned(16))) float ldsb[2][CK];
+  __shared__ __attribute__((aligned(16))) float ldsw[WV ? 2 : 1][WV ? CK : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane / MW, col = lane % MW;
@@ -874,9 +888,41 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
 #pragma unroll
     for (int c = 0; c < R; ++c) set_offset(bq[c][0], 0.f, grp == 0);
   }
+  // WV: fixed offsets.  On the fp32 path the query operand carries the grid
+  // multiple mo of M_i and the rest, sub (below the grid quantum), scales the
+  // row's two sums alike, so it is subtracted on the VALU only where it could
+  // overflow them (fine).  On the bf16 path m = M_i enters the exponent's FMA.
+  float ws[R], sub[R];
+  bool fine = false;
+  if constexpr (WV) {
+    bool coarse = false;
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      ws[c] = 0.f;
+      sub[c] = 0.f;
+      const int q = qbase + MW * c + col;
+      double M = 0.0;
+      if (q < rows) {
+        const size_t r = (size_t)b * rows + q;
+        M = (qnorm[r] - (double)wv.lse[r]) / inv_lam;
+      }
+      if (!(fabs(M) < 1e30)) M = 0.0;
+      if (MODE == MODE_SPLIT) {
+        const float mo = offset_from_max((float)M, qg, coarse);
+        set_offset(bq[c][0], -mo, grp == 0);
+        sub[c] = (float)(M - (double)mo);
+        fine |= !(sub[c] <= 32.f);
+      } else {
+        m[c] = (float)M;
+      }
+    }
+    flag_if(status, coarse && lane == 0, FLAG_SCORE_RANGE);
+    fine = __any(fine);
+  }
 
   u4 pre[2][NLD];
   f4 preb[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  float prew[2] = {0.f, 0.f};
   // Loads past the end of a chunk land in the slack rows that follow every
   // operand buffer, so they need no guard; their LDS stores go to a spare row.
   auto gload = [&](int chunk, auto par) {
@@ -885,6 +931,10 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
 #pragma unroll
     for (int i = 0; i < NLD; ++i) pre[P][i] = *reinterpret_cast<const u4*>(src + (size_t)(tid + NT * i) * 8);
     if (MODE == MODE_BF16) preb[P] = *reinterpret_cast<const f4*>(hbb + (size_t)chunk * CK + (tid % (CK / 4)) * 4);
+    if (WV) {
+      const int j = chunk * CK + tid;  // keys past the end (zero weight) take 0
+      prew[P] = (tid < CK && j < keys) ? wv.w[(size_t)b * keys + j] : 0.f;
+    }
   };
   auto lstore = [&](auto par) {
     constexpr int P = decltype(par)::value;
@@ -894,6 +944,7 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
       *reinterpret_cast<u4*>(&lds[P][(v / VPR) * LROW + (v % VPR) * 8]) = pre[P][i];
     }
     if (MODE == MODE_BF16 && tid < CK / 4) *reinterpret_cast<f4*>(&ldsb[P][tid * 4]) = preb[P];
+    if (WV && tid < CK) ldsw[WV ? P : 0][tid] = prew[P];
   };
   // Scores of key tile t of the chunk in buffer buf against the R query tiles.
   auto tile = [&](int buf, int t, Acc (&acc)[R]) {
@@ -948,6 +999,39 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
       s[c] += e[0];
     }
   };
+  // WV: s += sum of the weights and ws += sum of weight x vector element over
+  // a lane's outputs of key tile t (its vector elements from LDS, four keys per
+  // 16-byte read).
+  auto accumulate_w = [&](const Acc (&acc)[R], int buf, int t, auto fine_c) {
+    constexpr bool FINE = decltype(fine_c)::value;
+    float wl[NO];
+#pragma unroll
+    for (int o = 0; o < NO; o += 4) {
+      const f4 v = *reinterpret_cast<const f4*>(&ldsw[WV ? buf : 0][t * MW + T::key_of(o, grp)]);
+      wl[o] = v[0];
+      wl[o + 1] = v[1];
+      wl[o + 2] = v[2];
+      wl[o + 3] = v[3];
+    }
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      float e[NO];
+#pragma unroll
+      for (int o = 0; o < NO; ++o) e[o] = __builtin_amdgcn_exp2f(FINE ? acc[c][o] - sub[c] : expo(acc[c][o], c));
+      float w0 = 0.f, w1 = 0.f;
+#pragma unroll
+      for (int o = 0; o < NO; o += 2) {
+        w0 = fmaf(e[o], wl[o], w0);
+        w1 = fmaf(e[o + 1], wl[o + 1], w1);
+      }
+      ws[c] += w0 + w1;
+#pragma unroll
+      for (int w = 1; w < NO; w *= 2)
+#pragma unroll
+        for (int o = 0; o + w < NO; o += 2 * w) e[o] += e[o + w];
+      s[c] += e[0];
+    }
+  };
   // combine a value over the lanes that hold the same query
   auto lanes_max = [&](float v) {
 #pragma unroll
@@ -970,6 +1054,21 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
     // the wait before its LDS store exact).  Keeping two chunks in flight was
     // measured 5-10% slower on the MFMA-heavy shapes and 2% on d <= 3.
     gload(min(ci + 1, c1 - 1), Par<P ^ 1>{});
+
+    if constexpr (WV) {
+#pragma unroll 1
+      for (int t = 0; t < TC; ++t) {
+        Acc acc[R];
+        tile(buf, t, acc);
+        if (fine)
+          accumulate_w(acc, buf, t, std::true_type{});
+        else
+          accumulate_w(acc, buf, t, std::false_type{});
+      }
+      if (ci + 1 < c1) lstore(Par<P ^ 1>{});
+      __syncthreads();
+      return;
+    }
 
     if constexpr (EXACT) {
       // Each tile's scores come out of the MFMA relative to the current offsets.
@@ -1122,6 +1221,16 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
       if (ci + 1 < c1) step(ci + 1, Par<1>{});
     }
   }  // c0 < c1 (an empty key range leaves m = -FLT_MAX, s = 0: a neutral partial)
+
+  if constexpr (WV) {
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      const float st = lanes_sum(s[c]), wt = lanes_sum(ws[c]);
+      const int q = qbase + MW * c + col;
+      if (grp == 0 && q < rows) part[(size_t)blk.y * batch * rows + (size_t)b * rows + q] = make_float2(wt, st);
+    }
+    return;
+  }
 
 #pragma unroll
   for (int c = 0; c < R; ++c) {
@@ -2253,6 +2362,26 @@ __global__ __launch_bounds__(256) void k_apply_merge(const float* __restrict__ p
   out[rr * c + col0 + k] = (float)(mass > 0.0 ? mass * num / S : 0.0);
 }
 
+// One-vector plan product from the weighted half-step's split partials (W, S),
+// one thread per (problem, row): out = r sum W / sum S with the row mass
+// r = w exp((pot - lse)/eps) (the plan's row sums), as in k_apply_merge.
+__global__ __launch_bounds__(256) void k_wv_merge(const float2* __restrict__ part, int ks, int batch, int rows,
+                                                  const double* __restrict__ logw, const float* __restrict__ pot,
+                                                  const float* __restrict__ lse, double eps,
+                                                  float* __restrict__ out) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)batch * rows;
+  if (idx >= total) return;
+  double W = 0.0, S = 0.0;
+  for (int q = 0; q < ks; ++q) {
+    const float2 v = part[q * total + idx];
+    W += (double)v.x;
+    S += (double)v.y;
+  }
+  const double mass = exp(logw[idx] + ((double)pot[idx] - (double)lse[idx]) / eps);
+  out[idx] = (float)(mass > 0.0 ? mass * W / S : 0.0);
+}
+
 // Row masses r = w exp((pot - lse)/eps).
 __global__ __launch_bounds__(256) void k_mass(const double* __restrict__ logw, const float* __restrict__ pot,
                                               const float* __restrict__ lse, double eps, long long total,
@@ -2619,28 +2748,28 @@ __global__ __launch_bounds__(256) void k_hvp_final(const void* __restrict__ P, i
 // Host side
 // ---------------------------------------------------------------------------
 using LseFn = void (*)(const u16*, const u16*, const float*, const float*, const double*, float*, float2*, int, int,
-                       int, int, int, int, float, double, unsigned*, unsigned, unsigned*, NextBias);
+                       int, int, int, int, float, double, unsigned*, unsigned, unsigned*, NextBias, WvArgs);
 
-template <int MODE, int NCH>
+template <int MODE, int NCH, bool WV>
 LseFn lse_fn() {
   // bf16 operands past 256 slots take the K-looped kernel (k_lsek)
   if constexpr ((MODE == MODE_SPLIT && NCH <= MAX_NCH_SPLIT) || (MODE == MODE_BF16 && NCH <= 8))
-    return &k_lse<MODE, NCH>;
+    return &k_lse<MODE, NCH, 0, WV>;
   else
     return nullptr;
 }
 
-template <int MODE, int... N>
+template <int MODE, bool WV, int... N>
 LseFn lse_lookup_impl(int nch, std::integer_sequence<int, N...>) {
   LseFn fn = nullptr;
-  ((nch == N + 1 ? (fn = lse_fn<MODE, N + 1>(), 0) : 0), ...);
+  ((nch == N + 1 ? (fn = lse_fn<MODE, N + 1, WV>(), 0) : 0), ...);
   return fn;
 }
 
-template <int MODE>
+template <int MODE, bool WV = false>
 LseFn lse_lookup(int nch) {
   constexpr int MAXN = MODE == MODE_SPLIT ? MAX_NCH_SPLIT : MAX_NCH_BF16;
-  return lse_lookup_impl<MODE>(nch, std::make_integer_sequence<int, MAXN>{});
+  return lse_lookup_impl<MODE, WV>(nch, std::make_integer_sequence<int, MAXN>{});
 }
 
 sk_status hip_check(const char* what) {
@@ -2899,7 +3028,7 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   float2* part = ks > 1 ? reinterpret_cast<float2*>(w + L.part) : nullptr;
   hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NW), 0, stream, Qop, ko.K, ko.hb, ko.qgrid, qnorm, pot_out,
                      part, rows, rows_pad, keys, keys_pad, cps, B, 2.f * lam, inv_lam, ko.tag,
-                     __builtin_bit_cast(unsigned, lam), status, ks == 1 ? nb : NextBias{});
+                     __builtin_bit_cast(unsigned, lam), status, ks == 1 ? nb : NextBias{}, WvArgs{});
   st = hip_check("half-step kernel launch");
   if (st != SK_OK || ks == 1) return st;
   const int total = B * rows;
@@ -3167,6 +3296,8 @@ BaryFn apply_lookup(int mode, int d, int nct) {
 // out[b][row][k] = sum_j P_ij M[b][j][k] (k < c) for one side (side 0: rows are
 // the points of X, keys those of Y), at potentials pot_row / pot_key whose
 // half-step values for the rows are lse.  Columns go in passes of APPLY_COLS.
+unsigned blocks_for(long long n) { return (unsigned)((n + 255) / 256); }
+
 sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w, const Layout& L,
                      const float* pot_row, const float* pot_key, const float* lse, float eps, int side,
                      const float* M, int c, float* out, hipStream_t stream) {
@@ -3204,6 +3335,39 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
   float* bs = reinterpret_cast<float*>(w + L.bs);
   const float lam = (float)(LOG2E / (double)eps);
   const int nch = L.KP / 32;
+  if (c == 1) {
+    // one vector (each conjugate-gradient product of the HVP): the half-step
+    // kernel sums w_j 2^(s - M_i) beside the weights, one FMA per score, in
+    // place of the hi/lo bf16 product with a 16-column value tile
+    LseFn fn = (L.mode == MODE_SPLIT) ? lse_lookup<MODE_SPLIT, true>(nch) : lse_lookup<MODE_BF16, true>(nch);
+    int tc = cfg_TC(L.mode, nch);
+    if (L.mode == MODE_SPLIT && nch == 1 && keys < SMALL_KEYS) {
+      fn = &k_lse<MODE_SPLIT, 1, SMALL_TC, true>;
+      tc = SMALL_TC;
+    }
+    if (fn == nullptr) {
+      set_err("no plan-product kernel for %d K chunks", nch);
+      return SK_EUNSUPPORTED;
+    }
+    const int NW = cfg_NW(L.mode, nch), MW = cfg_MW(L.mode, nch);
+    const int wg_x = (rows + NW * cfg_R(L.mode, nch) * MW - 1) / (NW * cfg_R(L.mode, nch) * MW);
+    const int total_chunks = (keys + tc * MW - 1) / (tc * MW);
+    int capacity = 0;
+    st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity, 64 * NW);
+    if (st != SK_OK) return st;
+    int cps = 0;
+    const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps);
+    float2* part = reinterpret_cast<float2*>(w + L.part);
+    hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NW), 0, stream, Qop, ko.K, ko.hb, ko.qgrid, qnorm, nullptr,
+                       part, rows, rows_pad, keys, keys_pad, cps, B, 2.f * lam, 1.0 / (double)lam, ko.tag,
+                       __builtin_bit_cast(unsigned, lam), reinterpret_cast<unsigned*>(w + L.status), NextBias{},
+                       WvArgs{M, lse});
+    st = hip_check("plan-product kernel launch");
+    if (st != SK_OK) return st;
+    hipLaunchKernelGGL(k_wv_merge, dim3(blocks_for((long long)B * rows)), dim3(256), 0, stream, part, ks, B, rows,
+                       qlogw, pot_row, lse, (double)eps, out);
+    return hip_check("plan-product merge launch");
+  }
   for (int col0 = 0; col0 < c; col0 += APPLY_COLS) {
     const int cb = std::min(APPLY_COLS, c - col0);
     const int nct = apply_tiles(cb), nc = nct * 16;
@@ -3339,7 +3503,6 @@ sk_status apply_uw(const sk_problem* p, const void* X, const void* Y, char* w, c
   return hip_check("row-weighted merge launch");
 }
 
-unsigned blocks_for(long long n) { return (unsigned)((n + 255) / 256); }
 
 // Hessian of the entropic OT value in the points of one cloud (side 0: X,
 // side 1: Y) applied to V, at potentials (f, g) taken as optimal.  Moving the

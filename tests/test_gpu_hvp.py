@@ -72,7 +72,11 @@ def check_apply(p, eps, f, g, side, M, got):
                                            (200, 333, 64, "fp32", 21), (150, 140, 4, "fp32", 70),
                                            (100, 90, 128, "bf16", 7), (63, 65, 8, "bf16", 64),
                                            (40, 50, 88, "fp32", 65), (50, 45, 256, "bf16", 3),
-                                           (140, 300, 32, "fp32", 1), (90, 120, 40, "fp32", 30)])
+                                           (140, 300, 32, "fp32", 1), (90, 120, 40, "fp32", 30),
+                                           # one column: the weighted half-step kernel (bf16 d = 128 and 8,
+                                           # fp32 d = 88, and d = 3 past the small-key chunking)
+                                           (100, 90, 128, "bf16", 1), (70, 1500, 8, "bf16", 1),
+                                           (40, 50, 88, "fp32", 1), (130, 17000, 3, "fp32", 1)])
 def test_apply_plan(n, m, d, dtype, c):
     p = make_case(n, m, d, seed=17 * n + c, weights="softmax", dtype=dtype, scale=1.0 / np.sqrt(d))
     eps = 0.1
@@ -218,16 +222,16 @@ def test_hvp_multiblock_against_dense_oracle(side):
 
 
 # ---------------------------------------------------------------------------
-# plan products at the full sizes of the 8192^2 d = 64 (fp32) and the
-# 65536 x 32768 d = 128 (bf16) workloads, on sampled rows computed by the oracle
-# one at a time; c = 1, 64 (one pass) and 65 (two passes) columns
+# plan products at the full sizes of the 8192^2 d = 64 (fp32), the 70000^2 d = 3
+# (fp32) and the 65536 x 32768 d = 128 (bf16) workloads, on sampled rows computed
+# by the oracle one at a time; c = 1, 64 (one pass) and 65 (two passes) columns
 # ---------------------------------------------------------------------------
 def _sample(n, k, seed):
     rng = np.random.default_rng(seed)
     return np.sort(np.concatenate([rng.choice(n, size=k, replace=False), [0, n - 1]]))
 
 
-@pytest.mark.parametrize("cfg,c", [(2, 1), (2, 65), (4, 1), (4, 64), (4, 65)])
+@pytest.mark.parametrize("cfg,c", [(2, 1), (2, 65), (3, 1), (4, 1), (4, 64), (4, 65)])
 def test_apply_plan_full_size_sampled_rows(cfg, c):
     from log_domain_sinkhorn_half_amd.inputs import make_config, random_potential
 
