@@ -30,6 +30,11 @@ constexpr float HEADROOM = 64.f;
 // Below this many keys the d <= 3 half-step uses SMALL_TC key tiles per chunk.
 constexpr int SMALL_KEYS = 16384;
 constexpr int SMALL_TC = 4;
+// At most this many scores per problem (rows x keys) the d <= 3 half-step runs
+// TINY_R query tiles per wave, TINY_TC key tiles per chunk and no key split.
+constexpr long long TINY_WORK = 1LL << 21;
+constexpr int TINY_R = 1;
+constexpr int TINY_TC = 8;
 // Key-operand segments per thread of k_prep_keys when every segment is rebuilt
 // (1: the most parallel; measured fastest for full rebuilds).
 constexpr int PREP_SEGS = 1;

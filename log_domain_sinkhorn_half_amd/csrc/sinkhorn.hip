@@ -812,16 +812,17 @@ struct WvArgs {
   const float* lse;  // the rows' half-step values T_i, [batch][rows]
 };
 
-// TCX overrides the key tiles per chunk (0: cfg_TC), for small problems.  WV:
-// the one-vector plan product above instead of the half-step.
-template <int MODE, int NCH, int TCX = 0, bool WV = false>
+// TCX overrides the key tiles per chunk (0: cfg_TC) and RX the query tiles per
+// wave (0: cfg_R), for small problems.  WV: the one-vector plan product above
+// instead of the half-step.
+template <int MODE, int NCH, int TCX = 0, bool WV = false, int RX = 0>
 __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves_per_eu(cfg_waves(MODE, NCH)))) void k_lse(
     const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb,
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, float* __restrict__ out,
     float2* __restrict__ part, int rows, int rows_pad, int keys, int keys_pad, int chunks_per_split, int batch,
     float lam2, double inv_lam, unsigned* __restrict__ tag, unsigned tag_val, unsigned* __restrict__ status,
     NextBias nb, WvArgs wv) {
-  constexpr int MW = cfg_MW(MODE, NCH), R = cfg_R(MODE, NCH), TC = TCX ? TCX : cfg_TC(MODE, NCH);
+  constexpr int MW = cfg_MW(MODE, NCH), R = RX ? RX : cfg_R(MODE, NCH), TC = TCX ? TCX : cfg_TC(MODE, NCH);
   using T = Tile<MW>;
   using Acc = typename T::Acc;
   constexpr int KP = NCH * 32;
@@ -1056,14 +1057,31 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
     gload(min(ci + 1, c1 - 1), Par<P ^ 1>{});
 
     if constexpr (WV) {
-#pragma unroll 1
-      for (int t = 0; t < TC; ++t) {
-        Acc acc[R];
-        tile(buf, t, acc);
+      if constexpr (MODE == MODE_SPLIT && NCH == 1 && TC == 8) {
+        // d <= 3: unrolled as in the half-step (one tile's MFMAs overlap the
+        // previous tile's exps), with the rare fine offsets as a separate copy
+        auto tiles = [&](auto fine_c) {
+#pragma unroll
+          for (int t = 0; t < TC; ++t) {
+            Acc acc[R];
+            tile(buf, t, acc);
+            accumulate_w(acc, buf, t, fine_c);
+          }
+        };
         if (fine)
-          accumulate_w(acc, buf, t, std::true_type{});
+          tiles(std::true_type{});
         else
-          accumulate_w(acc, buf, t, std::false_type{});
+          tiles(std::false_type{});
+      } else {
+#pragma unroll 1
+        for (int t = 0; t < TC; ++t) {
+          Acc acc[R];
+          tile(buf, t, acc);
+          if (fine)
+            accumulate_w(acc, buf, t, std::true_type{});
+          else
+            accumulate_w(acc, buf, t, std::false_type{});
+        }
       }
       if (ci + 1 < c1) lstore(Par<P ^ 1>{});
       __syncthreads();
@@ -3006,8 +3024,16 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
   }
 
   LseFn fn = (L.mode == MODE_SPLIT) ? lse_lookup<MODE_SPLIT>(nch) : lse_lookup<MODE_BF16>(nch);
-  int tc = cfTC;
-  if (L.mode == MODE_SPLIT && nch == 1 && keys < SMALL_KEYS) {
+  int tc = cfTC, rq = cfR;
+  bool one_split = false;
+  if (L.mode == MODE_SPLIT && nch == 1 && (long long)rows * keys <= TINY_WORK) {
+    // a tiny problem: one query tile per wave and no key split, so that the
+    // half-step is one launch (a split merge would cost as much as the scores)
+    fn = &k_lse<MODE_SPLIT, 1, TINY_TC, false, TINY_R>;
+    tc = TINY_TC;
+    rq = TINY_R;
+    one_split = true;
+  } else if (L.mode == MODE_SPLIT && nch == 1 && keys < SMALL_KEYS) {
     // fewer keys than a few workgroups' worth of 256-key chunks: 128-key chunks fill the GPU better
     fn = &k_lse<MODE_SPLIT, 1, SMALL_TC>;
     tc = SMALL_TC;
@@ -3017,14 +3043,14 @@ sk_status half_step(const sk_problem* p, const void* X, const void* Y, void* ws,
     return SK_EUNSUPPORTED;
   }
   const int NW = cfg_NW(L.mode, nch);
-  const int wg_x = (rows + NW * cfR * cfMW - 1) / (NW * cfR * cfMW);
+  const int wg_x = (rows + NW * rq * cfMW - 1) / (NW * rq * cfMW);
   const int CK = tc * cfMW;
   const int total_chunks = (keys + CK - 1) / CK;
   int capacity = 0;
   st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity, 64 * NW);
   if (st != SK_OK) return st;
-  int cps = 0;
-  const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps);
+  int cps = total_chunks;
+  const int ks = one_split ? 1 : choose_key_splits(wg_x * B, total_chunks, capacity, &cps);
   float2* part = ks > 1 ? reinterpret_cast<float2*>(w + L.part) : nullptr;
   hipLaunchKernelGGL(fn, dim3(wg_x, ks, B), dim3(64 * NW), 0, stream, Qop, ko.K, ko.hb, ko.qgrid, qnorm, pot_out,
                      part, rows, rows_pad, keys, keys_pad, cps, B, 2.f * lam, inv_lam, ko.tag,
