@@ -77,6 +77,9 @@ SHAPES = [
     (1, 1, 3), (1, 7, 3), (7, 1, 2), (63, 65, 3), (65, 63, 4), (1000, 777, 3), (777, 1000, 1),
     (300, 513, 5), (513, 300, 9), (257, 1029, 17), (1030, 255, 32), (129, 700, 64), (700, 129, 88),
     (200, 333, 80), (150, 140, 4), (140, 150, 12),
+    # d <= 3 past 2^21 scores with fewer than 16384 keys: 128-key chunks and key splits
+    # (the smaller d <= 3 shapes above take one launch without splits)
+    (3001, 1500, 3), (1500, 3001, 2),
 ]
 
 
