@@ -239,8 +239,10 @@ sk_status sinkhorn_barycentric_y(const sk_problem* p, const void* X, const void*
  * Ottimizzazione del Secondo Ordine"), streamed like the transport calls, the plan never formed:
  *   sinkhorn_apply_plan_x:  out[b][i][k] = sum_j P_ij V[b][j][k]   V [batch][m][c] -> out [batch][n][c]
  *   sinkhorn_apply_plan_y:  out[b][j][k] = sum_i P_ij U[b][i][k]   U [batch][n][c] -> out [batch][m][c]
- * fp32 DEVICE arrays; c >= 1 columns (processed in passes of 64).  Each value is
- * carried as three exact bf16 parts.  Workspace: sinkhorn_transport_workspace_bytes.
+ * fp32 DEVICE arrays; c >= 1 columns.  c = 1 multiplies each fp32 weight with the
+ * fp32 vector element on the vector unit; c > 1 is processed in passes of 64
+ * columns, each value carried as three exact bf16 parts into the matrix product.
+ * Workspace: sinkhorn_transport_workspace_bytes.
  * --------------------------------------------------------------------------- */
 sk_status sinkhorn_apply_plan_x(const sk_problem* p, const void* X, const void* Y, void* ws,
                                 size_t ws_bytes, const float* f, const float* g, float eps,
