@@ -112,7 +112,7 @@ struct Layout {
   size_t vt, bpv, bs, bm, ttotal;
   // Hessian-vector products (after `ttotal`)
   size_t h_lse_r, h_lse_k, h_mr, h_mk, h_py, h_mat, h_w, h_g, h_quad, h_zr, h_cr, h_rhs, h_dg, h_res,
-      h_pd, h_pdf, h_t, h_q, h_st, h_part, h_u, htotal;
+      h_pd, h_pdf, h_t, h_q, h_st, h_part, h_u, h_wsr, h_wsk, htotal;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -259,6 +259,8 @@ Layout layout_of(const sk_problem* p) {
   L.h_q = take(4 * bm);
   L.h_st = take(8 * 8 * (size_t)B);
   L.h_part = take(8 * 3 * (size_t)B * ((mx + CG_BLK - 1) / CG_BLK));
+  L.h_wsr = take(8 * bm);  // row mass / weight sum of the CG plan passes, moving side
+  L.h_wsk = take(8 * bm);  // the same, fixed side
   L.htotal = off;
   return L;
 }

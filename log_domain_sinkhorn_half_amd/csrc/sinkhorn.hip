@@ -814,8 +814,10 @@ struct WvArgs {
 
 // TCX overrides the key tiles per chunk (0: cfg_TC) and RX the query tiles per
 // wave (0: cfg_R), for small problems.  WV: the one-vector plan product above
-// instead of the half-step.
-template <int MODE, int NCH, int TCX = 0, bool WV = false, int RX = 0>
+// instead of the half-step, 1 with the weight sums, 2 without them (the sums
+// depend on the potentials and offsets only, so repeated products with the same
+// potentials reuse those of their first pass).
+template <int MODE, int NCH, int TCX = 0, int WV = 0, int RX = 0>
 __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves_per_eu(cfg_waves(MODE, NCH)))) void k_lse(
     const u16* __restrict__ Q, const u16* __restrict__ K, const float* __restrict__ hb,
     const float* __restrict__ qgrid, const double* __restrict__ qnorm, float* __restrict__ out,
@@ -1026,11 +1028,13 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
         w1 = fmaf(e[o + 1], wl[o + 1], w1);
       }
       ws[c] += w0 + w1;
+      if constexpr (WV == 1) {
 #pragma unroll
-      for (int w = 1; w < NO; w *= 2)
+        for (int w = 1; w < NO; w *= 2)
 #pragma unroll
-        for (int o = 0; o + w < NO; o += 2 * w) e[o] += e[o + w];
-      s[c] += e[0];
+          for (int o = 0; o + w < NO; o += 2 * w) e[o] += e[o + w];
+        s[c] += e[0];
+      }
     }
   };
   // combine a value over the lanes that hold the same query
@@ -1243,7 +1247,7 @@ __global__ __launch_bounds__(64 * cfg_NW(MODE, NCH)) __attribute__((amdgpu_waves
   if constexpr (WV) {
 #pragma unroll
     for (int c = 0; c < R; ++c) {
-      const float st = lanes_sum(s[c]), wt = lanes_sum(ws[c]);
+      const float st = WV == 1 ? lanes_sum(s[c]) : 0.f, wt = lanes_sum(ws[c]);
       const int q = qbase + MW * c + col;
       if (grp == 0 && q < rows) part[(size_t)blk.y * batch * rows + (size_t)b * rows + q] = make_float2(wt, st);
     }
@@ -2383,10 +2387,12 @@ __global__ __launch_bounds__(256) void k_apply_merge(const float* __restrict__ p
 // One-vector plan product from the weighted half-step's split partials (W, S),
 // one thread per (problem, row): out = r sum W / sum S with the row mass
 // r = w exp((pot - lse)/eps) (the plan's row sums), as in k_apply_merge.
+// mode 1 also stores r / sum S per row in scale; mode 2 takes that factor from
+// scale (partials without sums): out = sum W * scale.
 __global__ __launch_bounds__(256) void k_wv_merge(const float2* __restrict__ part, int ks, int batch, int rows,
                                                   const double* __restrict__ logw, const float* __restrict__ pot,
-                                                  const float* __restrict__ lse, double eps,
-                                                  float* __restrict__ out) {
+                                                  const float* __restrict__ lse, double eps, int mode,
+                                                  double* __restrict__ scale, float* __restrict__ out) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)batch * rows;
   if (idx >= total) return;
@@ -2396,7 +2402,17 @@ __global__ __launch_bounds__(256) void k_wv_merge(const float2* __restrict__ par
     W += (double)v.x;
     S += (double)v.y;
   }
+  if (mode == 2) {
+    out[idx] = (float)(W * scale[idx]);
+    return;
+  }
   const double mass = exp(logw[idx] + ((double)pot[idx] - (double)lse[idx]) / eps);
+  if (mode == 1) {
+    const double sc = (mass > 0.0 && S > 0.0) ? mass / S : 0.0;
+    scale[idx] = sc;
+    out[idx] = (float)(W * sc);
+    return;
+  }
   out[idx] = (float)(mass > 0.0 ? mass * W / S : 0.0);
 }
 
@@ -2768,7 +2784,7 @@ __global__ __launch_bounds__(256) void k_hvp_final(const void* __restrict__ P, i
 using LseFn = void (*)(const u16*, const u16*, const float*, const float*, const double*, float*, float2*, int, int,
                        int, int, int, int, float, double, unsigned*, unsigned, unsigned*, NextBias, WvArgs);
 
-template <int MODE, int NCH, bool WV>
+template <int MODE, int NCH, int WV>
 LseFn lse_fn() {
   // bf16 operands past 256 slots take the K-looped kernel (k_lsek)
   if constexpr ((MODE == MODE_SPLIT && NCH <= MAX_NCH_SPLIT) || (MODE == MODE_BF16 && NCH <= 8))
@@ -2777,14 +2793,14 @@ LseFn lse_fn() {
     return nullptr;
 }
 
-template <int MODE, bool WV, int... N>
+template <int MODE, int WV, int... N>
 LseFn lse_lookup_impl(int nch, std::integer_sequence<int, N...>) {
   LseFn fn = nullptr;
   ((nch == N + 1 ? (fn = lse_fn<MODE, N + 1, WV>(), 0) : 0), ...);
   return fn;
 }
 
-template <int MODE, bool WV = false>
+template <int MODE, int WV = 0>
 LseFn lse_lookup(int nch) {
   constexpr int MAXN = MODE == MODE_SPLIT ? MAX_NCH_SPLIT : MAX_NCH_BF16;
   return lse_lookup_impl<MODE, WV>(nch, std::make_integer_sequence<int, MAXN>{});
@@ -3324,9 +3340,13 @@ BaryFn apply_lookup(int mode, int d, int nct) {
 // half-step values for the rows are lse.  Columns go in passes of APPLY_COLS.
 unsigned blocks_for(long long n) { return (unsigned)((n + 255) / 256); }
 
+// wmode (one column only): 0 plain; 1 also store the rows' mass / weight sum in
+// wscale; 2 reuse wscale and skip the weight sums (same potentials, offsets and
+// side as the call that stored it).
 sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w, const Layout& L,
                      const float* pot_row, const float* pot_key, const float* lse, float eps, int side,
-                     const float* M, int c, float* out, hipStream_t stream) {
+                     const float* M, int c, float* out, hipStream_t stream, int wmode = 0,
+                     double* wscale = nullptr) {
   const int B = (int)p->batch, d = (int)p->d;
   const int rows = (int)(side == 0 ? p->n : p->m);
   const int keys = (int)(side == 0 ? p->m : p->n);
@@ -3365,12 +3385,18 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
     // one vector (each conjugate-gradient product of the HVP): the half-step
     // kernel sums w_j 2^(s - M_i) beside the weights, one FMA per score, in
     // place of the hi/lo bf16 product with a 16-column value tile
-    LseFn fn = (L.mode == MODE_SPLIT) ? lse_lookup<MODE_SPLIT, true>(nch) : lse_lookup<MODE_BF16, true>(nch);
+    // the launch shape comes from the kernel with sums in both cases, so that the
+    // passes of one side split their keys alike and sum in the same order
+    const bool sums = wmode != 2;
+    LseFn fn1 = (L.mode == MODE_SPLIT) ? lse_lookup<MODE_SPLIT, 1>(nch) : lse_lookup<MODE_BF16, 1>(nch);
+    LseFn fn2 = (L.mode == MODE_SPLIT) ? lse_lookup<MODE_SPLIT, 2>(nch) : lse_lookup<MODE_BF16, 2>(nch);
     int tc = cfg_TC(L.mode, nch);
     if (L.mode == MODE_SPLIT && nch == 1 && keys < SMALL_KEYS) {
-      fn = &k_lse<MODE_SPLIT, 1, SMALL_TC, true>;
+      fn1 = &k_lse<MODE_SPLIT, 1, SMALL_TC, 1>;
+      fn2 = &k_lse<MODE_SPLIT, 1, SMALL_TC, 2>;
       tc = SMALL_TC;
     }
+    LseFn fn = sums ? fn1 : fn2;
     if (fn == nullptr) {
       set_err("no plan-product kernel for %d K chunks", nch);
       return SK_EUNSUPPORTED;
@@ -3379,7 +3405,7 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
     const int wg_x = (rows + NW * cfg_R(L.mode, nch) * MW - 1) / (NW * cfg_R(L.mode, nch) * MW);
     const int total_chunks = (keys + tc * MW - 1) / (tc * MW);
     int capacity = 0;
-    st = resident_capacity(reinterpret_cast<const void*>(fn), &capacity, 64 * NW);
+    st = resident_capacity(reinterpret_cast<const void*>(fn1), &capacity, 64 * NW);
     if (st != SK_OK) return st;
     int cps = 0;
     const int ks = choose_key_splits(wg_x * B, total_chunks, capacity, &cps);
@@ -3391,7 +3417,7 @@ sk_status apply_plan(const sk_problem* p, const void* X, const void* Y, char* w,
     st = hip_check("plan-product kernel launch");
     if (st != SK_OK) return st;
     hipLaunchKernelGGL(k_wv_merge, dim3(blocks_for((long long)B * rows)), dim3(256), 0, stream, part, ks, B, rows,
-                       qlogw, pot_row, lse, (double)eps, out);
+                       qlogw, pot_row, lse, (double)eps, wscale != nullptr ? wmode : 0, wscale, out);
     return hip_check("plan-product merge launch");
   }
   for (int col0 = 0; col0 < c; col0 += APPLY_COLS) {
@@ -3602,11 +3628,16 @@ sk_status hvp(const sk_problem* p, const void* X, const void* Y, char* w, const 
   st = hip_check("CG set-up launch");
   if (st != SK_OK) return st;
   const double tol2 = (double)cg_tol * (double)cg_tol;
+  // the plan passes' weight sums depend on the potentials and offsets only: the
+  // first iteration stores mass / sum per row and side, later ones reuse it
+  double* wsr = reinterpret_cast<double*>(w + L.h_wsr);
+  double* wsk = reinterpret_cast<double*>(w + L.h_wsk);
   for (int64_t it = 0; it < cg_iters; ++it) {
-    st = apply_plan(p, X, Y, w, L, pot_r, pot_k, lse_r, eps, side, pdf, 1, tv, s);
+    const int wm = it == 0 ? 1 : 2;
+    st = apply_plan(p, X, Y, w, L, pot_r, pot_k, lse_r, eps, side, pdf, 1, tv, s, wm, wsr);
     if (st != SK_OK) return st;
     hipLaunchKernelGGL(k_div_mass, dim3(blocks_for(nr)), dim3(256), 0, s, tv, mr, nr);
-    st = apply_plan(p, X, Y, w, L, pot_k, pot_r, lse_k, eps, 1 - side, tv, 1, qv, s);
+    st = apply_plan(p, X, Y, w, L, pot_k, pot_r, lse_k, eps, 1 - side, tv, 1, qv, s, wm, wsk);
     if (st != SK_OK) return st;
     double* st_in = (it % 2 == 0) ? st_a : st_b;
     double* st_out = (it % 2 == 0) ? st_b : st_a;
