@@ -801,9 +801,11 @@ __device__ __forceinline__ void write_next_bias(const NextBias& nb, int b, int q
   }
 }
 
-// The plan applied to one vector, sum_j P_ij w_j (the page's part "3. Hessiano
-// in Streaming": each conjugate-gradient step of the Hessian solve is such a
-// product), through the half-step kernel: the offsets are fixed by the rows'
+// The plan applied to one vector, sum_j P_ij w_j (page "FlashSinkhorn: Trasporto
+// Ottimo Entropico Consapevole delle I/O su GPU", section "Metodologia", part
+// "3. Differenziazione e Ottimizzazione del Secondo Ordine": the streaming HVP
+// is a sequence of such vector-transport products, one per conjugate-gradient
+// step of the Hessian solve here), through the half-step kernel: the offsets are fixed by the rows'
 // half-step values T_i (M_i = lambda (|x_i|^2 - T_i), so the weights 2^(s - M_i)
 // sum to about 1) and the kernel sums w_j 2^(s - M_i) beside 2^(s - M_i), one
 // fp32 FMA per score; the split partials (W, S) go to k_wv_merge.
