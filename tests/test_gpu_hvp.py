@@ -324,3 +324,39 @@ def test_apply_plan_full_size_batched_sampled(c):
             assert np.all(np.isfinite(got)), (side, k)
             assert np.all(err <= tol), f"{side} problem {k}: worst err/tol {(err / tol).max():.3f}"
 
+
+@pytest.mark.parametrize("cfg,lin_tol", [(2, 1e-3), (3, 1e-4), (4, 2e-3)])
+def test_hvp_full_size_symmetric_and_linear(cfg, lin_tol):
+    """Properties that hold at any size, at the 8192^2 d = 64, 70000^2 d = 3 and
+    65536 x 32768 d = 128 (bf16, annealed) workloads: after the workload's own solve,
+    <U, H V> = <V, H U> and H(2U - V/2) = 2 HU - HV/2 (CG to 1e-7).  Measured: symmetric
+    to about 1e-8, linear to 8e-5, 3e-6 and 3.4e-4 relative."""
+    from log_domain_sinkhorn_half_amd.inputs import make_config
+
+    p = make_config(cfg)
+    X, Y, a, b = dev(p)
+    sched = [float(e) for e in p.eps]
+    if len(sched) > 1:
+        f, g = sk.solve(X, Y, a, b, sched, len(sched))
+    else:
+        f, g = sk.solve(X, Y, a, b, sched[0], p.iters)
+    eps = sched[-1]
+    rng = np.random.default_rng(cfg)
+    U = rng.standard_normal((1, p.n, p.d)).astype(np.float32)
+    V = rng.standard_normal((1, p.n, p.d)).astype(np.float32)
+    W = (2.0 * U - 0.5 * V).astype(np.float32)
+    ws = sk.alloc_workspace(X, Y, hvp=True)
+    sk.init_norms(X, Y, a, b, ws)
+    h = {}
+    for nm, A in (("U", U), ("V", V), ("W", W)):
+        h[nm] = sk.hvp_x(X, Y, ws, f, g, eps, torch.from_numpy(A).cuda(), cg_iters=400,
+                         cg_tol=1e-7).cpu().numpy().astype(np.float64)
+    assert all(np.all(np.isfinite(v)) for v in h.values())
+    lhs = float((U[0] * h["V"][0]).sum())
+    rhs = float((V[0] * h["U"][0]).sum())
+    scale = float(np.abs(U[0] * h["V"][0]).sum() + np.abs(V[0] * h["U"][0]).sum())
+    assert abs(lhs - rhs) <= 1e-6 * scale, abs(lhs - rhs) / scale
+    lin = 2.0 * h["U"][0] - 0.5 * h["V"][0]
+    rel = np.max(np.abs(h["W"][0] - lin)) / np.max(np.abs(lin))
+    assert rel <= lin_tol, rel
+
