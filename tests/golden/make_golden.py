@@ -12,9 +12,10 @@ oracle then runs one iteration per call, carrying g between calls, which is the
 same loop as a single call (the f half-step reads only the incoming g).
 
 Only `oracle` and the seeded input generator are used: no value here comes from
-the HIP path.  Runtime: workload 2 about three minutes, workload 3 about an hour
-on 6 cores, workload 4 about three hours on 8 cores, workload 5 (all 64
-problems) about a quarter of an hour.  For a batched workload the indices run
+the HIP path.  Runtime: workload 2 (8192^2, d = 64) about three minutes,
+workload 3 (70000^2, d = 3) about an hour on 6 cores, workload 4 (65536 x 32768,
+d = 128, bf16) about three hours on 8 cores, workload 5 (64 problems of 2048^2,
+d = 32) about a quarter of an hour.  For a batched workload the indices run
 over the problem-major flattened potentials.
 
     python tests/golden/make_golden.py 2 3 [--threads N]
